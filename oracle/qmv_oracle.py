@@ -1,0 +1,164 @@
+"""Plain, slow, obviously-correct CPU oracle for affine-quantized matmul.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``): the product path never
+imports this module, and this module imports nothing from the product path.
+
+What the method computes (sources are the four pages of the reference):
+
+* mlxcel epic #570 "realize low-precision / quantized performance on the
+  OpenXLA (IREE) backend", section "Context": MLX 4/8-bit weights stay
+  resident packed, a ``ui32`` payload plus f16 per-group scales and biases.
+* mlxcel #574 "track(upstream-iree): fused dequant->matmul for the packed int8
+  bandwidth win", section "What is already in-tree": the graph bit-unpacks the
+  codes, then dequantizes each as ``q*scale + bias``; the result is bit-identical
+  to a host dequant.  Same issue, "The blocker": a fused kernel must give the
+  result of dequant followed by the matmul, without writing the f32 weight out.
+* ExecuTorch PR #17187 "Metal backend: import qmv_impl from MLX",
+  "Description": the operation is a linear layer with floating-point
+  activations and 4-bit weights, including M = 1 with N not a multiple of 4.
+
+Readings where the pages are silent:
+
+* Codes are packed LSB-first: code i of a word occupies bits [b*i, b*i + b).
+* ``W`` is ``[N, K*b/32]`` uint32 (out-features x in-features), so
+  ``y = x @ dequant(W).T``; scales and biases are ``[N, K/group_size]``.
+* The fused output is compared against the f64 value before any rounding; the
+  standalone dequant output is the f32 value ``RN_f32(q*s + b)``, and f16 or
+  bf16 outputs are round-to-nearest-even of that f32 value (two steps).
+
+Everything is numpy in float64; the only library primitive is numpy's matmul
+(BLAS f64), whose summation order is irrelevant at the oracle's accuracy.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+__all__ = [
+    "unpack_codes",
+    "widen_sb",
+    "dequant_f64",
+    "matmul_ref",
+    "matmul_ref_rows",
+    "dequant_ref_out",
+    "f32_to_bf16_bits",
+]
+
+
+def unpack_codes(w_words: np.ndarray, K: int, bits: int) -> np.ndarray:
+    """Bit-unpack a ``[N, K*bits/32]`` uint32 payload into ``[N, K]`` int64 codes.
+
+    Follows mlxcel #574, "What is already in-tree" ("bit-unpack"), with the
+    LSB-first reading: code ``k`` of row ``n`` is
+    ``(W[n, k // P] >> (bits * (k % P))) & (2**bits - 1)`` with ``P = 32 // bits``.
+    """
+    if bits not in (4, 8):
+        raise ValueError(f"bits must be 4 or 8, got {bits}")
+    per_word = 32 // bits
+    w = np.asarray(w_words, dtype=np.uint32)
+    if w.ndim != 2 or w.shape[1] * per_word != K:
+        raise ValueError(f"payload shape {w.shape} does not hold K={K} {bits}-bit codes")
+    k = np.arange(K)
+    word = w[:, k // per_word].astype(np.int64)
+    shift = (bits * (k % per_word)).astype(np.int64)
+    return (word >> shift) & ((1 << bits) - 1)
+
+
+def widen_sb(sb_bits: np.ndarray, sb_dtype: str) -> np.ndarray:
+    """Widen stored f16 / bf16 scale or bias bit patterns (uint16) to float64.
+
+    epic #570 "Context" names f16 scales/biases for the packed path and bf16
+    ones for dequant-at-load; #574 "Unblock criteria" asks for bf16 on the
+    packed path too.  Both widen exactly: f16 through numpy's half type, bf16 by
+    placing its 16 bits on top of an IEEE single (bf16 is the upper half of f32).
+    """
+    u = np.asarray(sb_bits, dtype=np.uint16)
+    if sb_dtype == "f16":
+        return u.view(np.float16).astype(np.float64)
+    if sb_dtype == "bf16":
+        return (u.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    raise ValueError(f"unknown scale/bias dtype {sb_dtype!r}")
+
+
+def dequant_f64(w_words, scales, biases, K: int, bits: int, group_size: int,
+                sb_dtype: str) -> np.ndarray:
+    """Reconstruct the ``[N, K]`` weight in float64: ``w = q * scale + bias``.
+
+    mlxcel #574 "What is already in-tree": bit-unpack, then ``q*scale + bias``
+    with one (scale, bias) pair per group of ``group_size`` consecutive codes
+    along K.  For f16 scale/bias the f64 result is exact (q*s has at most 19
+    significant bits and the sum spans fewer than 53 bits).
+    """
+    if K % group_size != 0:
+        raise ValueError("K must be a multiple of group_size")
+    q = unpack_codes(w_words, K, bits).astype(np.float64)
+    s = widen_sb(scales, sb_dtype)
+    b = widen_sb(biases, sb_dtype)
+    G = K // group_size
+    if s.shape != (q.shape[0], G) or b.shape != (q.shape[0], G):
+        raise ValueError(f"scales/biases must be [N, K/group_size] = {(q.shape[0], G)}")
+    g_of_k = np.arange(K) // group_size
+    return q * s[:, g_of_k] + b[:, g_of_k]
+
+
+def matmul_ref(x, w_words, scales, biases, K: int, bits: int, group_size: int,
+               sb_dtype: str) -> np.ndarray:
+    """Float64 ``y = x @ dequant(W).T`` (before any output rounding).
+
+    The fused kernel is defined (mlxcel #574 "The blocker"; epic #570 "The
+    measured fusion gate") as giving the result of dequant followed by the
+    matmul.  ``x`` is ``[M, K]`` f16 activations (ExecuTorch #17187
+    "Description": floating-point activations), widened exactly to f64.
+    """
+    xf = np.asarray(x, dtype=np.float16).astype(np.float64)
+    w = dequant_f64(w_words, scales, biases, K, bits, group_size, sb_dtype)
+    return xf @ w.T
+
+
+def matmul_ref_rows(x, w_words, scales, biases, rows, K: int, bits: int,
+                    group_size: int, sb_dtype: str) -> np.ndarray:
+    """``matmul_ref`` restricted to output columns ``rows`` (rows of W).
+
+    Output column ``n`` depends only on row ``n`` of W, its scales and biases,
+    so this equals ``matmul_ref(...)[:, rows]``; it lets tests check sampled
+    outputs of full-size problems without dequantizing every row.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    return matmul_ref(x, np.asarray(w_words)[rows], np.asarray(scales)[rows],
+                      np.asarray(biases)[rows], K, bits, group_size, sb_dtype)
+
+
+def f32_to_bf16_bits(v32: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (nearest, ties to even); returns uint16 bits.
+
+    Uses PyTorch's CPU float32 -> bfloat16 conversion as the library routine
+    (round-to-nearest-even; NaN becomes the quiet NaN 0x7FC0).
+    """
+    t = torch.from_numpy(np.ascontiguousarray(v32, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def dequant_ref_out(w_words, scales, biases, K: int, bits: int, group_size: int,
+                    sb_dtype: str, out_dtype: str) -> np.ndarray:
+    """The standalone dequant output, which the GPU must match bit for bit.
+
+    mlxcel #574 "What is already in-tree": the in-graph reconstruction is
+    bit-identical to the host dequant, and the reconstructed weight the pages
+    speak of is f32 (epic #570 "The measured fusion gate").  So:
+
+    * ``"f32"``: ``RN_f32(q*s + b)``, returned as float32.  Rounding the exact
+      f64 value once is the same as one f32 multiply-add, because ``q*s`` is
+      exact in f32 and double rounding through f64 (53 >= 2*24 + 2 bits) of a
+      single addition is innocuous.
+    * ``"f16"``: float16 of that f32 value (round to nearest even), float16 array.
+    * ``"bf16"``: bf16 of that f32 value (round to nearest even), uint16 bits.
+    """
+    w32 = dequant_f64(w_words, scales, biases, K, bits, group_size, sb_dtype).astype(np.float32)
+    if out_dtype == "f32":
+        return w32
+    if out_dtype == "f16":
+        return w32.astype(np.float16)
+    if out_dtype == "bf16":
+        return f32_to_bf16_bits(w32)
+    raise ValueError(f"unknown output dtype {out_dtype!r}")
