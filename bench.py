@@ -1,0 +1,379 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused affine-quantized matmul on one MI355X.
+
+Headline (one JSON line on stdout): fused 4-bit qGEMV HBM GB/s at M=1 on the
+Llama-3.2-1B-shaped decode projections (q/o 2048x2048, k/v 512x2048,
+gate/up 8192x2048, down 2048x8192, lm_head 128256x2048; N x K, g64, f16
+scales/biases, f16 x ~ N(0,1)).  One step = one mxq_qmv call per projection
+(8 launches).  The projection set is replicated REPLICAS times with distinct
+seeded weights (~1.1 GB in total) and the steps cycle through the replicas,
+so every step streams its weights from HBM, not from the 256 MB Infinity
+Cache.  value = algorithmic bytes per step / time per step.
+
+Extra objects on the same line:
+  roofline      the dominant kernel (most time per step), timed per launch with
+                HIP events on the launch stream: algorithmic bytes / duration,
+                against the 8 TB/s HBM peak;  traffic from committed rocprofv3
+                PMC counters when they match the current kernel source;
+  cpu_baseline  the f64 CPU oracle on a bounded sample, single BLAS thread;
+  decode_step   16 layers x {q,k,v,o,gate,up,down} + lm_head (113 launches,
+                ~697 MB of distinct weights): bytes/step, GB/s, steps/s;
+  qmm           M=512 prefill on gate/up (8192x2048) and down (2048x8192),
+                f16 and bf16 scales: TFLOP/s and MFMA utilisation (of the
+                2.5 PFLOP/s dense f16 peak);
+  dequant       standalone dequant of the lm_head weights to f32, GB/s.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fused 4-bit qGEMV HBM GB/s (% of peak) at M=1; qGEMM TFLOP/s at M=512"
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qmv_traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "dequant_matmul_qmv_amd", "csrc", f)
+                  for f in ("qmv.hip", "mxq_device.h")]
+
+
+def log(msg: str):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def call_bytes(M, N, K, bits=4, group_size=64):
+    """Algorithmic bytes of one fused call: codes + scales + biases + x + y."""
+    G = K // group_size
+    return N * K * bits // 8 + 2 * N * G * 2 + M * K * 2 + M * N * 2
+
+
+class Call:
+    """One pre-marshalled mxq_qmv / mxq_qmm launch (raw pointers only)."""
+
+    def __init__(self, lib, fn, x, w, s, b, y, M, N, K, bits, gs, sb_code, name):
+        self.fn = getattr(lib, fn)
+        self.tensors = (x, w, s, b, y)  # keep alive
+        self.args = (x.data_ptr(), w.data_ptr(), s.data_ptr(), b.data_ptr(), y.data_ptr(),
+                     M, N, K, bits, gs, sb_code)
+        self.name = name
+        self.M, self.N, self.K = M, N, K
+        self.bytes = call_bytes(M, N, K, bits, gs)
+
+    def __call__(self, stream_handle):
+        st = self.fn(*self.args, stream_handle)
+        if st != 0:
+            raise RuntimeError(f"{self.name}: libmxq status {st}")
+
+
+def make_qmv_set(mxq, lib, synth, torch, config, replica, shapes, dev, sb="f16"):
+    import numpy as np
+    calls = []
+    sbt = torch.float16 if sb == "f16" else torch.bfloat16
+    for idx, (name, N, K) in enumerate(shapes):
+        w, s, b = synth.make_weights(N, K, 4, 64, sb, seed=synth.proj_seed(config, replica, idx))
+        x = synth.make_x(1, K, seed=synth.proj_seed(config, replica, idx) + 500)
+        tw = torch.from_numpy(w.view(np.int32)).to(dev)
+        ts = torch.from_numpy(s.view(np.int16)).view(sbt).to(dev)
+        tb = torch.from_numpy(b.view(np.int16)).view(sbt).to(dev)
+        tx = torch.from_numpy(x).to(dev)
+        ty = torch.empty((1, N), dtype=torch.float16, device=dev)
+        calls.append(Call(lib, "mxq_qmv", tx, tw, ts, tb, ty, 1, N, K, 4, 64,
+                          0 if sb == "f16" else 1, name))
+    return calls
+
+
+def time_steps(torch, steps_fns, warmup, steps):
+    """Run warmup then exactly `steps` steps; returns seconds per step."""
+    n = len(steps_fns)
+    for i in range(warmup):
+        steps_fns[i % n]()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        steps_fns[i % n]()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def capture(torch, fn):
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()  # one eager run on the capture stream first
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def cur_stream(torch):
+    import ctypes
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def per_launch_times(torch, sets, reps):
+    """Eager launches with an event pair around each; returns {name: [ms, ...]}."""
+    out = {}
+    pairs = []
+    st = cur_stream(torch)
+    for r in range(reps):
+        for c in sets[r % len(sets)]:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            c(st)
+            e1.record()
+            pairs.append((c, e0, e1))
+    torch.cuda.synchronize()
+    for c, e0, e1 in pairs:
+        out.setdefault(c.name, []).append(e0.elapsed_time(e1))
+    return out
+
+
+def read_traffic(kernel_desc: str, per_launch_alg_bytes: float):
+    """HBM bytes per launch from committed rocprofv3 PMC counters, if current."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha") != kernel_source_sha() or t.get("kernel") != kernel_desc:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(synth, budget_s=12.0):
+    """The f64 oracle on a bounded sample, one BLAS thread: GB/s of algorithmic bytes."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    shapes = list(synth.LLAMA_1B_PROJ) + [("lm_head[0:8016]", 8016, 2048)]
+    probs = []
+    for idx, (name, N, K) in enumerate(shapes):
+        w, s, b = synth.make_weights(N, K, 4, 64, "f16", seed=synth.proj_seed(1, 0, idx))
+        x = synth.make_x(1, K, seed=synth.proj_seed(1, 0, idx) + 500)
+        probs.append((x, w, s, b, N, K))
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    if ctx:
+        ctx.__enter__()
+    try:
+        done_bytes, t0, passes = 0, time.perf_counter(), 0
+        while True:
+            for x, w, s, b, N, K in probs:
+                oracle.matmul_ref(x, w, s, b, K, 4, 64, "f16")
+                done_bytes += call_bytes(1, N, K)
+            passes += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or passes >= 20:
+                break
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    return {"value": round(done_bytes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{passes} pass(es) over layer-0 q,k,v,o,gate,up,down + lm_head rows 0..8015 "
+                      f"(M=1, 4-bit g64, f16 scales), f64 numpy oracle, 1 BLAS thread, "
+                      f"{el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--replicas", type=int, default=6)
+    ap.add_argument("--mode", choices=["graph", "eager"], default="graph",
+                    help="launch the timed steps by HIP-graph replay or eagerly")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip decode_step, qmm and dequant legs")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the fused quantized matmul has no multi-GPU path in this "
+              "library (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np  # noqa: F401
+    import torch
+
+    import dequant_matmul_qmv_amd as mxq
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    lib = mxq.load(build_if_missing=True)
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+
+    # ---------------- headline: the projection set at M=1 ------------------
+    shapes = list(synth.LLAMA_1B_PROJ) + [synth.LLAMA_1B_LM_HEAD]
+    log(f"generating {args.replicas} replicas of the decode projection set ...")
+    sets = [make_qmv_set(mxq, lib, synth, torch, 1, r, shapes, dev) for r in range(args.replicas)]
+    bytes_per_step = sum(c.bytes for c in sets[0])
+
+    def eager_step(s):
+        return lambda: [c(cur_stream(torch)) for c in s]
+
+    eager_fns = [eager_step(s) for s in sets]
+    if args.mode == "graph":
+        graphs = [capture(torch, fn) for fn in eager_fns]
+        step_fns = [g.replay for g in graphs]
+    else:
+        step_fns = eager_fns
+    log("timing headline steps ...")
+    if torch.distributed.is_available() and torch.distributed.is_initialized():
+        torch.distributed.barrier()
+    torch.cuda.synchronize()
+    sec = time_steps(torch, step_fns, args.warmup, args.steps)
+    value = bytes_per_step / sec / 1e9
+    eager_sec = time_steps(torch, eager_fns, 10, min(args.steps, 100)) if args.mode == "graph" else sec
+
+    # ---------------- roofline of the dominant kernel -----------------------
+    times = per_launch_times(torch, sets, reps=max(2 * args.replicas, 24))
+    by_kernel = {}
+    for c in sets[0]:
+        desc = mxq.mxq_describe("qmv", c.M, c.N, c.K, 4, 64, "f16")
+        d = by_kernel.setdefault(desc, {"bytes": 0, "ms": 0.0, "launches": 0, "names": []})
+        ms = float(np.median(times[c.name]))
+        d["bytes"] += c.bytes
+        d["ms"] += ms
+        d["launches"] += 1
+        d["names"].append(c.name)
+    dom_desc, dom = max(by_kernel.items(), key=lambda kv: kv[1]["ms"])
+    avg_ms = dom["ms"] / dom["launches"]
+    avg_bytes = dom["bytes"] / dom["launches"]
+    achieved = avg_bytes / (avg_ms / 1e3) / 1e9
+    traffic = read_traffic(dom_desc, avg_bytes)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": dom_desc, "launches_per_step": dom["launches"], "projections": dom["names"],
+                "avg_launch_us": round(avg_ms * 1e3, 3), "alg_bytes_per_launch": int(avg_bytes)}
+    per_proj = {c.name: {"us": round(float(np.median(times[c.name])) * 1e3, 2),
+                         "GB/s": round(c.bytes / (float(np.median(times[c.name])) / 1e3) / 1e9, 1)}
+                for c in sets[0]}
+
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "Llama-3.2-1B-shaped decode projections q,k,v,o,gate,up,down,lm_head "
+                               "(N x K: 2048x2048, 512x2048, 512x2048, 2048x2048, 8192x2048, 8192x2048, "
+                               "2048x8192, 128256x2048), M=1, 4-bit codes g64, f16 scales/biases, "
+                               "f16 x ~ N(0,1)",
+                   "replicas": args.replicas, "launches_per_step": len(sets[0]),
+                   "bytes_per_step": bytes_per_step, "launch_mode": args.mode},
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "eager_GB/s": round(bytes_per_step / eager_sec / 1e9, 1),
+        "per_projection": per_proj,
+        "roofline": roofline,
+    }
+    del sets, step_fns, eager_fns
+    if args.mode == "graph":
+        del graphs
+    torch.cuda.empty_cache()
+
+    # ---------------- extras ------------------------------------------------
+    if not args.no_extras:
+        log("decode step (16 layers + lm_head) ...")
+        layers = []
+        for layer in range(synth.LLAMA_1B_LAYERS):
+            layers += make_qmv_set(mxq, lib, synth, torch, 3, layer, list(synth.LLAMA_1B_PROJ), dev)
+        layers += make_qmv_set(mxq, lib, synth, torch, 3, 99, [synth.LLAMA_1B_LM_HEAD], dev)
+        dbytes = sum(c.bytes for c in layers)
+        dfn = lambda: [c(cur_stream(torch)) for c in layers]  # noqa: E731
+        g = capture(torch, dfn)
+        dsec = time_steps(torch, [g.replay], 5, 50)
+        dsec_e = time_steps(torch, [dfn], 3, 20)
+        result["decode_step"] = {"launches": len(layers), "bytes_per_step": dbytes,
+                                 "weight_bytes_per_step": sum(c.N * c.K // 2 + c.N * (c.K // 64) * 4 for c in layers),
+                                 "graph_us_per_step": round(dsec * 1e6, 1), "graph_GB/s": round(dbytes / dsec / 1e9, 1),
+                                 "graph_steps_per_s": round(1 / dsec, 1),
+                                 "eager_us_per_step": round(dsec_e * 1e6, 1), "eager_GB/s": round(dbytes / dsec_e / 1e9, 1)}
+        del layers, g
+        torch.cuda.empty_cache()
+
+        log("qmm M=512 ...")
+        qmm = {}
+        for sb in ("f16", "bf16"):
+            sbt = torch.float16 if sb == "f16" else torch.bfloat16
+            calls = []
+            for idx, (name, N, K) in enumerate([("gate", 8192, 2048), ("up", 8192, 2048), ("down", 2048, 8192)]):
+                w, s, b = synth.make_weights(N, K, 4, 64, sb, seed=synth.proj_seed(4, 0, idx))
+                x = synth.make_x(512, K, seed=synth.proj_seed(4, 0, idx) + 500)
+                calls.append(Call(lib, "mxq_qmm", torch.from_numpy(x).to(dev),
+                                  torch.from_numpy(w.view(np.int32)).to(dev),
+                                  torch.from_numpy(s.view(np.int16)).view(sbt).to(dev),
+                                  torch.from_numpy(b.view(np.int16)).view(sbt).to(dev),
+                                  torch.empty((512, N), dtype=torch.float16, device=dev),
+                                  512, N, K, 4, 64, 0 if sb == "f16" else 1, name))
+            t = per_launch_times(torch, [calls], reps=30)
+            entry = {}
+            tot_flop, tot_ms = 0, 0.0
+            for c in calls:
+                ms = float(np.median(t[c.name]))
+                flop = 2 * c.M * c.N * c.K
+                entry[c.name] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(flop / (ms / 1e3) / 1e12, 1)}
+                tot_flop += flop
+                tot_ms += ms
+            tf = tot_flop / (tot_ms / 1e3) / 1e12
+            entry["TFLOP/s"] = round(tf, 1)
+            entry["mfma_util"] = round(tf / MFMA_F16_PEAK_TFLOPS, 4)
+            entry["kernel"] = mxq.mxq_describe("qmm", 512, 8192, 2048, 4, 64, sb)
+            qmm[sb] = entry
+        result["qmm"] = qmm
+
+        log("dequant ...")
+        w, s, b = synth.make_weights(128256, 2048, 4, 64, "f16", seed=7)
+        tw = torch.from_numpy(w.view(np.int32)).to(dev)
+        ts = torch.from_numpy(s.view(np.int16)).view(torch.float16).to(dev)
+        tb = torch.from_numpy(b.view(np.int16)).view(torch.float16).to(dev)
+        out = torch.empty((128256, 2048), dtype=torch.float32, device=dev)
+        for _ in range(3):
+            mxq.mxq_dequant(tw, ts, tb, out, bits=4)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            mxq.mxq_dequant(tw, ts, tb, out, bits=4)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 10
+        dq_bytes = 128256 * 2048 // 2 + 128256 * 32 * 4 + 128256 * 2048 * 4
+        result["dequant"] = {"shape": "128256x2048 4-bit -> f32", "us": round(ms * 1e3, 1),
+                             "GB/s": round(dq_bytes / (ms / 1e3) / 1e9, 1)}
+        del out, tw
+
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        result["cpu_baseline"] = cpu_baseline(synth)
+    else:
+        result["cpu_baseline"] = None
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

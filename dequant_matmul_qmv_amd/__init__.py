@@ -1,0 +1,24 @@
+"""MI355X (gfx950) matmul over MLX-style affine-quantized packed weights.
+
+The public calls mirror the C ABI of libmxq.so (``include/mxq.h``):
+``mxq_qmv`` (decode), ``mxq_qmm`` (prefill), ``mxq_dequant`` (bit-exact
+standalone dequant) and ``mxq_pack`` (host packer).
+"""
+
+from ._lib import (  # noqa: F401
+    MXQ_BF16,
+    MXQ_ERR_HIP,
+    MXQ_ERR_INVALID_ARG,
+    MXQ_ERR_MISALIGNED,
+    MXQ_ERR_UNSUPPORTED,
+    MXQ_F16,
+    MXQ_F32,
+    MXQ_OK,
+    MxqError,
+    load,
+    mxq_dequant,
+    mxq_describe,
+    mxq_pack,
+    mxq_qmm,
+    mxq_qmv,
+)

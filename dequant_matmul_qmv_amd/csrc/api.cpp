@@ -1,0 +1,302 @@
+// extern "C" entry points of libmxq: argument validation (fail-fast, before
+// any launch -- the spirit of mlxcel #574's "fail fast instead of faulting
+// mid-run" guards in "What is already in-tree"), dispatch, and the host packer.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <string>
+#include <unordered_set>
+
+#include "../../include/mxq.h"
+#include "mxq_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+mxq_status fail(mxq_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int log2_group(int g) { return g == 32 ? 5 : g == 64 ? 6 : g == 128 ? 7 : -1; }
+
+constexpr int kMaxDevices = 64;
+std::mutex g_mu;
+mxq::DeviceInfo g_dev[kMaxDevices];
+std::unordered_set<std::string>* g_lds_done = nullptr;
+
+// Shared validation of the fused entry points; fills the common fields.
+mxq_status check_fused(const char* who, const void* x, const uint32_t* w, const void* scales,
+                       const void* biases, void* y, int64_t M, int64_t N, int64_t K, int bits,
+                       int group_size, mxq_dtype sb_dtype) {
+  const std::string f(who);
+  if (M < 0 || N < 0 || K < 0) return fail(MXQ_ERR_INVALID_ARG, f + ": M, N and K must be >= 0");
+  if (bits != 4 && bits != 8) return fail(MXQ_ERR_UNSUPPORTED, f + ": bits must be 4 or 8");
+  if (log2_group(group_size) < 0)
+    return fail(MXQ_ERR_UNSUPPORTED, f + ": group_size must be 32, 64 or 128");
+  if (K % group_size != 0) return fail(MXQ_ERR_UNSUPPORTED, f + ": K must be a multiple of group_size");
+  if (sb_dtype != MXQ_F16 && sb_dtype != MXQ_BF16)
+    return fail(MXQ_ERR_UNSUPPORTED, f + ": scales/biases must be MXQ_F16 or MXQ_BF16");
+  if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX)
+    return fail(MXQ_ERR_UNSUPPORTED, f + ": M, N and K must each fit in 32 bits");
+  if (M == 0 || N == 0) return MXQ_OK;
+  if (!y) return fail(MXQ_ERR_INVALID_ARG, f + ": y must not be null");
+  if (K > 0 && (!x || !w || !scales || !biases))
+    return fail(MXQ_ERR_INVALID_ARG, f + ": x, w, scales and biases must not be null");
+  if (K > 0 && !aligned(w, 16)) return fail(MXQ_ERR_MISALIGNED, f + ": w must be 16-byte aligned");
+  if (!aligned(x, 2) || !aligned(y, 2) || (K > 0 && (!aligned(scales, 2) || !aligned(biases, 2))))
+    return fail(MXQ_ERR_MISALIGNED, f + ": x, y, scales and biases must be 2-byte aligned");
+  return MXQ_OK;
+}
+
+mxq_status hip_fail(const char* who, hipError_t e) {
+  return fail(MXQ_ERR_HIP, std::string(who) + ": " + hipGetErrorName(e) + ": " + hipGetErrorString(e));
+}
+
+// M-sliced qmv over the whole M range.
+mxq_status run_qmv(const char* who, const void* x, const uint32_t* w, const void* scales,
+                   const void* biases, void* y, int64_t M, int64_t N, int64_t K, int bits,
+                   int group_size, mxq_dtype sb_dtype, void* stream) {
+  mxq::DeviceInfo dev;
+  hipError_t e = mxq::device_info(&dev);
+  if (e != hipSuccess) return hip_fail(who, e);
+  int mt_max = 8;
+  while (mt_max > 1 && mxq::qmv_lds_need(bits, mt_max, K) > dev.lds_per_block) mt_max--;
+  if (mxq::qmv_lds_need(bits, 1, K) > dev.lds_per_block)
+    return fail(MXQ_ERR_UNSUPPORTED, std::string(who) + ": K too large for the activation staging buffer");
+  mxq::QmvArgs a{};
+  a.w = w;
+  a.s = static_cast<const uint16_t*>(scales);
+  a.b = static_cast<const uint16_t*>(biases);
+  a.N = N;
+  a.K = K;
+  a.bits = bits;
+  a.glog2 = log2_group(group_size);
+  a.sb_bf16 = sb_dtype == MXQ_BF16;
+  a.rows_per_wave = 0;
+  a.stream = static_cast<hipStream_t>(stream);
+  for (int64_t m0 = 0; m0 < M; m0 += mt_max) {
+    const int mt = static_cast<int>((M - m0) < mt_max ? (M - m0) : mt_max);
+    a.x = static_cast<const uint16_t*>(x) + m0 * K;
+    a.y = static_cast<uint16_t*>(y) + m0 * N;
+    a.x_vec = aligned(a.x, 16) ? 1 : 0;
+    e = mxq::launch_qmv_slice(a, dev, mt);
+    if (e != hipSuccess) return hip_fail(who, e);
+  }
+  return MXQ_OK;
+}
+
+}  // namespace
+
+namespace mxq {
+
+hipError_t device_info(DeviceInfo* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_mu);
+  DeviceInfo& d = g_dev[dev];
+  if (d.device != dev) {
+    int cu = 0, lds_blk = 0, lds_cu = 0;
+    if ((e = hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&lds_blk, hipDeviceAttributeMaxSharedMemoryPerBlock, dev)) != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev)) != hipSuccess)
+      lds_cu = lds_blk;
+    d.num_cu = cu > 0 ? cu : 1;
+    d.lds_per_block = static_cast<size_t>(lds_blk > 0 ? lds_blk : 65536);
+    d.lds_per_cu = static_cast<size_t>(lds_cu > 0 ? lds_cu : d.lds_per_block);
+    d.device = dev;
+  }
+  *out = d;
+  return hipSuccess;
+}
+
+hipError_t ensure_dynamic_lds(const void* kernel, size_t bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const std::string key = std::to_string(reinterpret_cast<uintptr_t>(kernel)) + ":" +
+                          std::to_string(dev) + ":" + std::to_string(bytes);
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (!g_lds_done) g_lds_done = new std::unordered_set<std::string>();
+    if (g_lds_done->count(key)) return hipSuccess;
+  }
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_lds_done->insert(key);
+  return hipSuccess;
+}
+
+}  // namespace mxq
+
+extern "C" {
+
+int mxq_abi_version(void) { return MXQ_ABI_VERSION; }
+
+const char* mxq_status_str(mxq_status s) {
+  switch (s) {
+    case MXQ_OK: return "MXQ_OK";
+    case MXQ_ERR_INVALID_ARG: return "MXQ_ERR_INVALID_ARG";
+    case MXQ_ERR_UNSUPPORTED: return "MXQ_ERR_UNSUPPORTED";
+    case MXQ_ERR_MISALIGNED: return "MXQ_ERR_MISALIGNED";
+    case MXQ_ERR_HIP: return "MXQ_ERR_HIP";
+  }
+  return "MXQ_ERR_UNKNOWN";
+}
+
+const char* mxq_last_error(void) { return g_last_error.c_str(); }
+
+mxq_status mxq_qmv(const void* x, const uint32_t* w, const void* scales, const void* biases,
+                   void* y, int64_t M, int64_t N, int64_t K, int bits, int group_size,
+                   mxq_dtype sb_dtype, void* stream) {
+  g_last_error.clear();
+  mxq_status st = check_fused("mxq_qmv", x, w, scales, biases, y, M, N, K, bits, group_size, sb_dtype);
+  if (st != MXQ_OK || M == 0 || N == 0) return st;
+  if (K == 0) {
+    hipError_t e = mxq::launch_zero_fill(static_cast<uint16_t*>(y), M * N, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MXQ_OK : hip_fail("mxq_qmv", e);
+  }
+  return run_qmv("mxq_qmv", x, w, scales, biases, y, M, N, K, bits, group_size, sb_dtype, stream);
+}
+
+mxq_status mxq_qmm(const void* x, const uint32_t* w, const void* scales, const void* biases,
+                   void* y, int64_t M, int64_t N, int64_t K, int bits, int group_size,
+                   mxq_dtype sb_dtype, void* stream) {
+  g_last_error.clear();
+  mxq_status st = check_fused("mxq_qmm", x, w, scales, biases, y, M, N, K, bits, group_size, sb_dtype);
+  if (st != MXQ_OK || M == 0 || N == 0) return st;
+  if (K == 0) {
+    hipError_t e = mxq::launch_zero_fill(static_cast<uint16_t*>(y), M * N, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MXQ_OK : hip_fail("mxq_qmm", e);
+  }
+  // The MFMA kernel stages x with 16-byte loads and walks K in stages of 64.
+  if (M <= 8 || K % 64 != 0 || !aligned(x, 16))
+    return run_qmv("mxq_qmm", x, w, scales, biases, y, M, N, K, bits, group_size, sb_dtype, stream);
+  mxq::DeviceInfo dev;
+  hipError_t e = mxq::device_info(&dev);
+  if (e != hipSuccess) return hip_fail("mxq_qmm", e);
+  mxq::QmmArgs a{};
+  a.x = static_cast<const uint16_t*>(x);
+  a.w = w;
+  a.s = static_cast<const uint16_t*>(scales);
+  a.b = static_cast<const uint16_t*>(biases);
+  a.y = static_cast<uint16_t*>(y);
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.bits = bits;
+  a.group_size = group_size;
+  a.sb_bf16 = sb_dtype == MXQ_BF16;
+  a.stream = static_cast<hipStream_t>(stream);
+  e = mxq::launch_qmm(a, dev);
+  return e == hipSuccess ? MXQ_OK : hip_fail("mxq_qmm", e);
+}
+
+mxq_status mxq_dequant(const uint32_t* w, const void* scales, const void* biases, void* out,
+                       int64_t N, int64_t K, int bits, int group_size, mxq_dtype sb_dtype,
+                       mxq_dtype out_dtype, void* stream) {
+  g_last_error.clear();
+  if (N < 0 || K < 0) return fail(MXQ_ERR_INVALID_ARG, "mxq_dequant: N and K must be >= 0");
+  if (bits != 4 && bits != 8) return fail(MXQ_ERR_UNSUPPORTED, "mxq_dequant: bits must be 4 or 8");
+  if (log2_group(group_size) < 0)
+    return fail(MXQ_ERR_UNSUPPORTED, "mxq_dequant: group_size must be 32, 64 or 128");
+  if (K % group_size != 0) return fail(MXQ_ERR_UNSUPPORTED, "mxq_dequant: K must be a multiple of group_size");
+  if (sb_dtype != MXQ_F16 && sb_dtype != MXQ_BF16)
+    return fail(MXQ_ERR_UNSUPPORTED, "mxq_dequant: scales/biases must be MXQ_F16 or MXQ_BF16");
+  if (out_dtype != MXQ_F16 && out_dtype != MXQ_BF16 && out_dtype != MXQ_F32)
+    return fail(MXQ_ERR_UNSUPPORTED, "mxq_dequant: out_dtype must be MXQ_F16, MXQ_BF16 or MXQ_F32");
+  if (N > INT32_MAX || K > INT32_MAX) return fail(MXQ_ERR_UNSUPPORTED, "mxq_dequant: N and K must fit in 32 bits");
+  if (N == 0 || K == 0) return MXQ_OK;
+  if (!w || !scales || !biases || !out) return fail(MXQ_ERR_INVALID_ARG, "mxq_dequant: null pointer");
+  if (!aligned(w, 16) || !aligned(out, 16))
+    return fail(MXQ_ERR_MISALIGNED, "mxq_dequant: w and out must be 16-byte aligned");
+  if (!aligned(scales, 2) || !aligned(biases, 2))
+    return fail(MXQ_ERR_MISALIGNED, "mxq_dequant: scales and biases must be 2-byte aligned");
+  mxq::DeviceInfo dev;
+  hipError_t e = mxq::device_info(&dev);
+  if (e != hipSuccess) return hip_fail("mxq_dequant", e);
+  mxq::DequantArgs a{};
+  a.w = w;
+  a.s = static_cast<const uint16_t*>(scales);
+  a.b = static_cast<const uint16_t*>(biases);
+  a.out = out;
+  a.N = N;
+  a.K = K;
+  a.bits = bits;
+  a.glog2 = log2_group(group_size);
+  a.sb_bf16 = sb_dtype == MXQ_BF16;
+  a.out_dtype = static_cast<int>(out_dtype);
+  a.stream = static_cast<hipStream_t>(stream);
+  e = mxq::launch_dequant(a, dev);
+  return e == hipSuccess ? MXQ_OK : hip_fail("mxq_dequant", e);
+}
+
+const char* mxq_describe(const char* op, int64_t M, int64_t N, int64_t K, int bits,
+                         int group_size, mxq_dtype sb_dtype) {
+  thread_local std::string desc;
+  const std::string o = op ? op : "";
+  if ((o != "qmv" && o != "qmm") || M <= 0 || N <= 0 || K <= 0 || (bits != 4 && bits != 8) ||
+      log2_group(group_size) < 0 || K % group_size != 0 || (sb_dtype != MXQ_F16 && sb_dtype != MXQ_BF16)) {
+    desc = "invalid";
+    return desc.c_str();
+  }
+  mxq::DeviceInfo dev;
+  if (mxq::device_info(&dev) != hipSuccess) {
+    desc = "no device";
+    return desc.c_str();
+  }
+  const char* sb = sb_dtype == MXQ_BF16 ? "bf16" : "f16";
+  const bool mfma = o == "qmm" && M > 8 && K % 64 == 0;
+  if (mfma) {
+    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+    desc = "qmm_kernel<bits=" + std::to_string(bits) + ",sb=" + sb + ",gs=" + std::to_string(group_size) +
+           "> grid=" + std::to_string(tiles) + " block=256 tile=128x128";
+    return desc.c_str();
+  }
+  int mt_max = 8;
+  while (mt_max > 1 && mxq::qmv_lds_need(bits, mt_max, K) > dev.lds_per_block) mt_max--;
+  desc.clear();
+  for (int64_t m0 = 0; m0 < M; m0 += mt_max) {
+    const int mt = static_cast<int>((M - m0) < mt_max ? (M - m0) : mt_max);
+    const mxq::QmvPlan p = mxq::qmv_plan(dev, N, K, bits, mt, 0);
+    if (!desc.empty()) desc += "; ";
+    desc += "qmv_kernel<bits=" + std::to_string(bits) + ",sb=" + sb + ",mt=" + std::to_string(mt) +
+            ",rows=" + std::to_string(p.rows) + "> grid=" + std::to_string(p.grid) +
+            " block=256 lds=" + std::to_string(p.lds);
+  }
+  return desc.c_str();
+}
+
+mxq_status mxq_pack(const uint8_t* codes, uint32_t* w, int64_t N, int64_t K, int bits) {
+  g_last_error.clear();
+  if (bits != 4 && bits != 8) return fail(MXQ_ERR_UNSUPPORTED, "mxq_pack: bits must be 4 or 8");
+  if (N < 0 || K < 0) return fail(MXQ_ERR_INVALID_ARG, "mxq_pack: N and K must be >= 0");
+  const int per = 32 / bits;
+  if (K % per != 0) return fail(MXQ_ERR_UNSUPPORTED, "mxq_pack: K must be a multiple of 32/bits");
+  if (N == 0 || K == 0) return MXQ_OK;
+  if (!codes || !w) return fail(MXQ_ERR_INVALID_ARG, "mxq_pack: null pointer");
+  const uint32_t limit = 1u << bits;
+  const int64_t kw = K / per;
+  for (int64_t n = 0; n < N; ++n) {
+    const uint8_t* c = codes + n * K;
+    uint32_t* o = w + n * kw;
+    for (int64_t j = 0; j < kw; ++j) {
+      uint32_t word = 0;
+      for (int i = 0; i < per; ++i) {
+        const uint32_t v = c[j * per + i];
+        if (v >= limit) return fail(MXQ_ERR_INVALID_ARG, "mxq_pack: code does not fit in `bits` bits");
+        word |= v << (bits * i);  // field i holds code i: least significant first
+      }
+      o[j] = word;
+    }
+  }
+  return MXQ_OK;
+}
+
+}  // extern "C"

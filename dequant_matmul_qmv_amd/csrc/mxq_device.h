@@ -1,0 +1,116 @@
+// Device-side helpers shared by the gfx950 kernels of libmxq.
+//
+// Packed layout (mlxcel epic #570 "Context": a uint32 payload plus per-group
+// f16 / bf16 scales and biases; mlxcel #574 "What is already in-tree":
+// bit-unpack, then q*scale + bias).  Code i of a word sits in bits
+// [bits*i, bits*i + bits), least significant field first.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxq {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f16x __attribute__((ext_vector_type(16)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
+__device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+// Exact widening of a stored scale / bias to f32.
+template <bool BF16>
+__device__ __forceinline__ float sb_to_f32(uint16_t u) {
+  if constexpr (BF16) {
+    return __uint_as_float(static_cast<uint32_t>(u) << 16);
+  } else {
+    return static_cast<float>(__builtin_bit_cast(_Float16, u));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Exact f16 codes by exponent injection.  OR-ing a code c < 1024 into the
+// mantissa of the f16 1024.0 (bits 0x6400) gives the f16 value 1024 + c, and
+// subtracting 1024 afterwards is exact, so each half below holds the integer
+// code itself.  One v_and_or_b32 builds two codes at once; the pairs come out
+// as (c0, c4), (c1, c5), (c2, c6), (c3, c7) for a 4-bit word and (c0, c2),
+// (c1, c3) for an 8-bit word, and the activations are staged in that same
+// order, so each v_dot2 multiplies matching (code, x) pairs.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kMagic = 0x64006400u;
+
+__device__ __forceinline__ h2 sub1024(uint32_t u) {
+  const h2 k = {static_cast<_Float16>(1024.0f), static_cast<_Float16>(1024.0f)};
+  return as_h2(u) - k;
+}
+
+// 4-bit word -> 4 pairs of exact f16 codes.
+__device__ __forceinline__ void unpack_w4(uint32_t w, h2 (&q)[4]) {
+  q[0] = sub1024((w & 0x000F000Fu) | kMagic);
+  q[1] = sub1024(((w >> 4) & 0x000F000Fu) | kMagic);
+  q[2] = sub1024(((w >> 8) & 0x000F000Fu) | kMagic);
+  q[3] = sub1024(((w >> 12) & 0x000F000Fu) | kMagic);
+}
+
+// 8-bit word -> 2 pairs of exact f16 codes.
+__device__ __forceinline__ void unpack_w8(uint32_t w, h2 (&q)[2]) {
+  q[0] = sub1024((w & 0x00FF00FFu) | kMagic);
+  q[1] = sub1024(((w >> 8) & 0x00FF00FFu) | kMagic);
+}
+
+// Reorder 8 consecutive f16 activations x0..x7 (as 4 dwords (x0,x1) (x2,x3)
+// (x4,x5) (x6,x7)) into the pair order of unpack_w4: (x0,x4) (x1,x5) (x2,x6)
+// (x3,x7).  v_perm_b32 selects bytes from two dwords.
+__device__ __forceinline__ u4 perm_x_w4(u4 v) {
+  u4 o;
+  // __builtin_amdgcn_perm(hi, lo, sel): byte selectors 0-3 pick lo, 4-7 pick hi.
+  o.x = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);  // (x0 from v.x lo, x4 from v.z lo)
+  o.y = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);  // (x1, x5)
+  o.z = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);  // (x2, x6)
+  o.w = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);  // (x3, x7)
+  return o;
+}
+
+// Reorder two 8-bit words' activations x0..x3 | x4..x7 into (x0,x2) (x1,x3) |
+// (x4,x6) (x5,x7), the pair order of unpack_w8.
+__device__ __forceinline__ u4 perm_x_w8(u4 v) {
+  u4 o;
+  o.x = __builtin_amdgcn_perm(v.y, v.x, 0x05040100u);  // (x0, x2)
+  o.y = __builtin_amdgcn_perm(v.y, v.x, 0x07060302u);  // (x1, x3)
+  o.z = __builtin_amdgcn_perm(v.w, v.z, 0x05040100u);  // (x4, x6)
+  o.w = __builtin_amdgcn_perm(v.w, v.z, 0x07060302u);  // (x5, x7)
+  return o;
+}
+
+// Sum of 8 f16 values held as 4 dwords, in f32, fixed order.
+__device__ __forceinline__ float sum8_f32(u4 v) {
+  const h2 one = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+  float s = __builtin_amdgcn_fdot2(as_h2(v.x), one, 0.0f, false);
+  s = __builtin_amdgcn_fdot2(as_h2(v.y), one, s, false);
+  s = __builtin_amdgcn_fdot2(as_h2(v.z), one, s, false);
+  s = __builtin_amdgcn_fdot2(as_h2(v.w), one, s, false);
+  return s;
+}
+
+// Round-to-nearest-even f32 -> f16 bits, of the f32 value itself.  The empty
+// asm makes v opaque: without it the compiler folds a preceding f32 add/fma
+// and this conversion into one v_fma_mixlo_f16, which rounds the exact sum
+// straight to f16 -- a different (single) rounding that differs whenever the
+// f32 rounding lands exactly on an f16 tie.
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float v) {
+  asm("" : "+v"(v));
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
+}
+
+// Round-to-nearest-even f32 -> bf16 bits; NaN becomes the quiet NaN 0x7FC0.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float v) {
+  uint32_t u = __float_as_uint(v);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+}  // namespace mxq

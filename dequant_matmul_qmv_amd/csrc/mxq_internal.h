@@ -1,0 +1,82 @@
+// Host-side internals shared by the launch code of libmxq (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mxq {
+
+struct DeviceInfo {
+  int device = -1;
+  int num_cu = 0;
+  size_t lds_per_block = 0;  // largest dynamic LDS one workgroup may use
+  size_t lds_per_cu = 0;
+};
+
+// Cached per device; returns hipSuccess and fills `out` for the current device.
+hipError_t device_info(DeviceInfo* out);
+
+// Raise a kernel's dynamic-LDS limit once per (kernel, device).
+hipError_t ensure_dynamic_lds(const void* kernel, size_t bytes);
+
+struct QmvArgs {
+  const uint16_t* x;   // f16 bits [M, K] of this slice
+  const uint32_t* w;
+  const uint16_t* s;
+  const uint16_t* b;
+  uint16_t* y;         // f16 bits [M, N] of this slice
+  int64_t N, K;
+  int bits;
+  int glog2;           // log2(group_size)
+  bool sb_bf16;
+  int x_vec;           // x is 16-byte aligned
+  int rows_per_wave;   // 0 = pick automatically
+  hipStream_t stream;
+};
+
+size_t qmv_lds_need(int bits, int mt, int64_t K);
+
+// Launch shape of one qmv slice: template MT (activation rows) and R (rows of
+// W per wave per step), grid size and dynamic LDS bytes.
+struct QmvPlan {
+  int mt, rows, grid;
+  size_t lds;
+};
+QmvPlan qmv_plan(const DeviceInfo& dev, int64_t N, int64_t K, int bits, int mt, int rows_override);
+hipError_t launch_qmv_slice(const QmvArgs& a, const DeviceInfo& dev, int mt);
+
+struct QmmArgs {
+  const uint16_t* x;
+  const uint32_t* w;
+  const uint16_t* s;
+  const uint16_t* b;
+  uint16_t* y;
+  int64_t M, N, K;
+  int bits;
+  int group_size;
+  bool sb_bf16;
+  hipStream_t stream;
+};
+
+hipError_t launch_qmm(const QmmArgs& a, const DeviceInfo& dev);
+
+struct DequantArgs {
+  const uint32_t* w;
+  const uint16_t* s;
+  const uint16_t* b;
+  void* out;
+  int64_t N, K;
+  int bits;
+  int glog2;
+  bool sb_bf16;
+  int out_dtype;  // mxq_dtype value
+  hipStream_t stream;
+};
+
+hipError_t launch_dequant(const DequantArgs& a, const DeviceInfo& dev);
+
+// y[0 .. count) = +0 (f16 bits), used for K == 0.
+hipError_t launch_zero_fill(uint16_t* y, int64_t count, hipStream_t stream);
+
+}  // namespace mxq

@@ -1,0 +1,148 @@
+/*
+ * mxq.h -- C ABI of libmxq.so: matmul over affine-quantized, packed weights
+ * on AMD MI355X (gfx950).
+ *
+ * The operation (mlxcel #574 "track(upstream-iree): fused dequant->matmul for
+ * the packed int8 bandwidth win", section "What is already in-tree"; mlxcel epic
+ * #570, section "Context"): weights stay resident as b-bit codes packed into
+ * uint32 words plus one f16 (or bf16) scale and bias per group of `group_size`
+ * codes along K; each weight is w = q * scale + bias.  The fused entry points
+ * compute y = x * W^T without ever writing W to memory, which is exactly what the
+ * unfused graph of epic #570 ("The measured fusion gate") fails to do.
+ *
+ * Layouts (all row-major, all device memory unless stated):
+ *   x       f16   [M, K]            activations
+ *   w       u32   [N, K*bits/32]    packed codes of W[N, K]; code k of row n is
+ *                                   (w[n][k / P] >> (bits * (k % P))) & (2^bits - 1),
+ *                                   P = 32 / bits (least significant field first)
+ *   scales  f16|bf16 [N, K/group_size]   (sb_dtype applies to scales and biases)
+ *   biases  f16|bf16 [N, K/group_size]
+ *   y       f16   [M, N]            output, round-to-nearest-even of an f32 sum
+ *
+ * Supported: bits in {4, 8}; group_size in {32, 64, 128}; K a multiple of
+ * group_size.  M, N, K >= 0; M*N == 0 is a no-op that touches no pointer;
+ * K == 0 with M*N > 0 writes y = +0 and reads nothing (x, w, scales and
+ * biases may then be null).
+ *
+ * Alignment: w must be 16-byte aligned (every row then is, since a row holds
+ * a multiple of four words); x, scales, biases and y must be 2-byte aligned
+ * (an x that is also 16-byte aligned is staged with wider loads); the
+ * dequant output `out` must be 16-byte aligned.
+ *
+ * Ownership and threading: every pointer is owned by the caller and must stay
+ * valid until the enqueued work has finished.  The library allocates no
+ * device memory and needs no workspace; it keeps only a per-device cache of
+ * device properties.  Calls are thread-safe.
+ *
+ * Asynchrony: a call validates its arguments synchronously, enqueues its
+ * kernel(s) on `stream` (a hipStream_t; NULL means the null stream) and
+ * returns.  Faults inside a kernel surface at the caller's next
+ * synchronisation, as for any HIP launch.  No exception crosses this ABI.
+ *
+ * Errors: a status other than MXQ_OK means nothing was enqueued (except
+ * MXQ_ERR_HIP, returned when the launch itself failed); mxq_last_error()
+ * then returns a thread-local message with the detail.
+ */
+#ifndef MXQ_H
+#define MXQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mxq_status {
+  MXQ_OK = 0,
+  MXQ_ERR_INVALID_ARG = 1,  /* null pointer where data is needed, negative size */
+  MXQ_ERR_UNSUPPORTED = 2,  /* bits, group_size, dtype, K % group_size, too-large K */
+  MXQ_ERR_MISALIGNED = 3,   /* a pointer breaks the alignment rules above */
+  MXQ_ERR_HIP = 4           /* the HIP runtime reported an error at launch */
+} mxq_status;
+
+typedef enum mxq_dtype {
+  MXQ_F16 = 0,
+  MXQ_BF16 = 1,
+  MXQ_F32 = 2
+} mxq_dtype;
+
+/* Bumped whenever a signature in this header changes. */
+#define MXQ_ABI_VERSION 1
+int mxq_abi_version(void);
+
+/*
+ * mxq_qmv -- fused dequant + matmul tuned for decode (M = 1 .. 8).
+ *
+ * Computes y[m, n] = RN_f16( sum_k x[m, k] * (q[n, k] * s[n, g(k)] + b[n, g(k)]) )
+ * with g(k) = k / group_size, accumulating in f32 (the scale and bias are
+ * applied per group to partial sums, which is the same value up to f32
+ * rounding).  The sum of epic #570's "dequant -> matmul" without the weight
+ * ever leaving registers.  Accepts any M >= 0; M > 8 is processed in
+ * slices of at most 8 rows (each slice re-reads W).  N need not be a
+ * multiple of anything (ExecuTorch PR #17187 "Description": M = 1 with N not
+ * a multiple of 4).
+ * Results match the f64 definition within |y - y_ref| <= 2e-3 (1 + |y_ref|)
+ * and are bit-identical from run to run.
+ */
+mxq_status mxq_qmv(const void* x, const uint32_t* w, const void* scales, const void* biases,
+                   void* y, int64_t M, int64_t N, int64_t K, int bits, int group_size,
+                   mxq_dtype sb_dtype, void* stream);
+
+/*
+ * mxq_qmm -- the same operation tuned for prefill (M >= 64): codes are
+ * staged through LDS as exact f16 integers and contracted with f16 MFMA
+ * (f32 accumulation); each group's partial products are then scaled by the
+ * group's f32 scale and the bias is added as bias * sum_{k in group} x
+ * (the zero-point decomposition mlxcel #574 cites in "Upstream status
+ * refresh").  Same arguments, layouts, accuracy and determinism as mxq_qmv;
+ * calls with M <= 8 take the mxq_qmv kernel.
+ */
+mxq_status mxq_qmm(const void* x, const uint32_t* w, const void* scales, const void* biases,
+                   void* y, int64_t M, int64_t N, int64_t K, int bits, int group_size,
+                   mxq_dtype sb_dtype, void* stream);
+
+/*
+ * mxq_dequant -- standalone dequantization: out[n, k] = q * s + b.
+ *
+ * The reconstruction mlxcel #574 ("What is already in-tree") requires to be
+ * bit-identical to a host dequant.  out_dtype MXQ_F32 gives RN_f32(q*s + b)
+ * (one rounding: q*s is exact in f32); MXQ_F16 / MXQ_BF16 give the
+ * round-to-nearest-even of that f32 value (a NaN becomes 0x7FC0 in bf16).
+ * `out` is [N, K] row-major, device memory.  Bit-exact by contract.
+ */
+mxq_status mxq_dequant(const uint32_t* w, const void* scales, const void* biases, void* out,
+                       int64_t N, int64_t K, int bits, int group_size, mxq_dtype sb_dtype,
+                       mxq_dtype out_dtype, void* stream);
+
+/*
+ * mxq_pack -- HOST packer for the layout above (no GPU involved).
+ *
+ * codes: host uint8 [N, K], each < 2^bits; w: host uint32 [N, K*bits/32]
+ * written by the call.  K must be a multiple of 32/bits.  Returns
+ * MXQ_ERR_INVALID_ARG if a code does not fit in `bits` bits (w is then left
+ * partially written).  Synchronous.
+ */
+mxq_status mxq_pack(const uint8_t* codes, uint32_t* w, int64_t N, int64_t K, int bits);
+
+/*
+ * mxq_describe -- diagnostic: the kernel instantiation(s) and launch shape
+ * that mxq_qmv (op "qmv") or mxq_qmm (op "qmm") would use for these sizes on
+ * the current device, e.g. "qmv_kernel<bits=4,sb=f16,mt=1,rows=4> grid=2048
+ * block=256 lds=4352".  Returns a thread-local string, valid until the next
+ * call on the thread; "invalid" for unsupported arguments and "no device"
+ * without a GPU.  Enqueues nothing.
+ */
+const char* mxq_describe(const char* op, int64_t M, int64_t N, int64_t K, int bits,
+                         int group_size, mxq_dtype sb_dtype);
+
+/* Static, human-readable name of a status. */
+const char* mxq_status_str(mxq_status s);
+
+/* Thread-local detail of the last non-OK status on this thread ("" if none). */
+const char* mxq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXQ_H */

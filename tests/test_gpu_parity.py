@@ -1,0 +1,253 @@
+"""HIP path vs the CPU oracle, element by element, through libmxq's C ABI.
+
+Bars: dequant bit-exact; fused outputs |y - y_ref| <= 2e-3 * (1 + |y_ref|)
+against the f64 oracle value (before any rounding); integer and one-hot cases
+bit-exact; repeated runs bit-identical.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import dequant_matmul_qmv_amd as mxq
+import oracle
+import synth
+from tests import pins
+from tests.gpu_util import assert_close, note, to_dev, y_host
+
+pytestmark = pytest.mark.gpu
+
+OUT_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def _dequant_bits(t: torch.Tensor, out: str) -> np.ndarray:
+    torch.cuda.synchronize()
+    a = t.cpu()
+    if out == "f32":
+        return a.numpy().view(np.uint32)
+    return a.view(torch.int16).numpy().view(np.uint16)
+
+
+def _oracle_bits(p, out):
+    r = oracle.dequant_ref_out(p.w, p.scales, p.biases, p.K, p.bits, p.group_size, p.sb_dtype, out)
+    if out == "f32":
+        return r.view(np.uint32)
+    if out == "f16":
+        return r.view(np.uint16)
+    return r
+
+
+# ----------------------------------------------------------------- dequant ---
+DQ_CASES = [
+    (1, 32, 4, 32, "f16"), (3, 64, 4, 64, "bf16"), (5, 128, 8, 128, "f16"),
+    (7, 96, 8, 32, "bf16"), (33, 256, 4, 64, "f16"), (512, 2048, 4, 64, "f16"),
+    (1023, 8192, 8, 64, "bf16"), (130, 640, 4, 128, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", DQ_CASES, ids=str)
+@pytest.mark.parametrize("out", ["f32", "f16", "bf16"])
+def test_dequant_bitexact(case, out):
+    N, K, bits, gs, sb = case
+    p = synth.make_problem(1, N, K, bits, gs, sb, seed=N + K + bits)
+    _, w, s, b = to_dev(p)
+    note(f"dequant N={N} K={K} bits={bits} gs={gs} sb={sb} out={out}")
+    got = _dequant_bits(mxq.mxq_dequant(w, s, b, bits=bits, group_size=gs, out_dtype=OUT_DT[out]), out)
+    want = _oracle_bits(p, out)
+    assert np.array_equal(got, want), f"{np.sum(got != want)} mismatching values"
+
+
+def test_dequant_hand_values():
+    for r in pins.load_hand_dequant():
+        bits = 8 if r["q"] > 15 else 4
+        per = 32 // bits
+        K = 64
+        codes = np.zeros((1, K), np.uint8)
+        codes[0, 5] = r["q"]
+        w = torch.from_numpy(mxq.mxq_pack(codes, bits).view(np.int32)).cuda()
+        sbt = torch.float16 if r["sb"] == "f16" else torch.bfloat16
+        s = torch.tensor([[r["s"]]], dtype=torch.int32).to(torch.int16).view(sbt).cuda()
+        b = torch.tensor([[r["b"]]], dtype=torch.int32).to(torch.int16).view(sbt).cuda()
+        note(f"dequant hand value {r}")
+        o32 = _dequant_bits(mxq.mxq_dequant(w, s, b, bits=bits, group_size=64), "f32")
+        o16 = _dequant_bits(mxq.mxq_dequant(w, s, b, bits=bits, group_size=64, out_dtype=torch.float16), "f16")
+        obf = _dequant_bits(mxq.mxq_dequant(w, s, b, bits=bits, group_size=64, out_dtype=torch.bfloat16), "bf16")
+        assert int(o32[0, 5]) == r["f32"] and int(o16[0, 5]) == r["f16"] and int(obf[0, 5]) == r["bf16"], r
+        assert per > 0
+
+
+# ------------------------------------------------------------------- fused ---
+def _run(entry, p, **kw):
+    x, w, s, b = to_dev(p)
+    fn = mxq.mxq_qmv if entry == "qmv" else mxq.mxq_qmm
+    return y_host(fn(x, w, s, b, bits=p.bits, group_size=p.group_size, **kw))
+
+
+def _ref(p):
+    return oracle.matmul_ref(p.x, p.w, p.scales, p.biases, p.K, p.bits, p.group_size, p.sb_dtype)
+
+
+SMALL = [
+    # M, N, K, bits, gs, sb
+    (1, 1, 32, 4, 32, "f16"), (1, 3, 64, 4, 64, "f16"), (1, 5, 128, 8, 128, "bf16"),
+    (2, 7, 96, 8, 32, "f16"), (3, 130, 2048, 4, 64, "bf16"), (4, 257, 2080, 4, 32, "f16"),
+    (5, 66, 4096, 8, 64, "f16"), (6, 31, 1024, 4, 128, "bf16"), (7, 513, 2048, 8, 64, "bf16"),
+    (8, 1000, 2048, 4, 64, "f16"), (9, 40, 512, 4, 64, "f16"), (17, 33, 256, 8, 32, "bf16"),
+    (1, 2049, 2048, 4, 64, "f16"), (1, 64, 6144, 4, 64, "f16"),
+]
+
+
+@pytest.mark.parametrize("entry", ["qmv", "qmm"])
+@pytest.mark.parametrize("case", SMALL, ids=str)
+def test_fused_small(entry, case):
+    M, N, K, bits, gs, sb = case
+    p = synth.make_problem(M, N, K, bits, gs, sb, seed=M * 7 + N + K)
+    note(f"{entry} {case}")
+    assert_close(_run(entry, p), _ref(p), f"{entry} {case}")
+
+
+def test_small_qmv_problem():
+    """Single 4-bit qmv: M=1, N=512, K=2048, g64, f16 scales/biases, seed 0."""
+    p = synth.small_qmv_problem()
+    note("qmv small problem")
+    assert_close(_run("qmv", p), _ref(p), "qmv small problem")
+
+
+@pytest.mark.parametrize("entry", ["qmv", "qmm"])
+@pytest.mark.parametrize("case", list(synth.edge_cases()), ids=lambda c: f"M{c['M']}N{c['N']}b{c['bits']}{c['sb_dtype']}")
+def test_edge_cases_8bit_and_tails(entry, case):
+    """M in {1,2,4,8}, K=8192, N in {2048,1023,2050}, 4/8-bit, f16/bf16 scales."""
+    p = synth.make_problem(**case)
+    note(f"{entry} edge {case}")
+    assert_close(_run(entry, p), _ref(p), f"{entry} {case}")
+
+
+QMM = [
+    (64, 128, 64, 4, 64, "f16"), (64, 256, 2048, 8, 64, "bf16"), (100, 130, 512, 4, 32, "f16"),
+    (128, 128, 1024, 4, 128, "bf16"), (200, 333, 2048, 4, 64, "f16"), (129, 64, 8192, 8, 64, "f16"),
+    (256, 1000, 2048, 4, 64, "bf16"), (65, 1, 256, 4, 64, "f16"), (512, 96, 1024, 8, 128, "f16"),
+]
+
+
+@pytest.mark.parametrize("case", QMM, ids=str)
+def test_qmm_mfma(case):
+    M, N, K, bits, gs, sb = case
+    p = synth.make_problem(M, N, K, bits, gs, sb, seed=M + N + K + 5)
+    note(f"qmm mfma {case}")
+    assert_close(_run("qmm", p), _ref(p), f"qmm {case}")
+
+
+@pytest.mark.parametrize("proj", ["gate", "down"])
+@pytest.mark.parametrize("sb", ["f16", "bf16"])
+def test_prefill_full_size_sampled(proj, sb):
+    """M=512 prefill at gate/up (8192 x 2048) and down (2048 x 8192), sampled columns."""
+    N, K = (8192, 2048) if proj == "gate" else (2048, 8192)
+    p = synth.make_problem(512, N, K, 4, 64, sb, seed=synth.proj_seed(4, 0, 4 if proj == "gate" else 6))
+    note(f"qmm full size {proj} {sb}")
+    y = _run("qmm", p)
+    rows = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(1).integers(0, N, 96)]))
+    ref = oracle.matmul_ref_rows(p.x, p.w, p.scales, p.biases, rows, K, 4, 64, sb)
+    assert_close(y[:, rows], ref, f"qmm {proj} {sb} sampled")
+
+
+@pytest.mark.parametrize("name,N,K", [*synth.LLAMA_1B_PROJ, synth.LLAMA_1B_LM_HEAD])
+def test_decode_projections_full_size(name, N, K):
+    """Llama-3.2-1B-shaped M=1 decode projections at full size (sampled rows for lm_head)."""
+    p = synth.make_problem(1, N, K, 4, 64, "f16", seed=synth.proj_seed(1, 0, 0) + N + K)
+    note(f"qmv decode {name} {N}x{K}")
+    y = _run("qmv", p)
+    if N > 20000:
+        rows = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(2).integers(0, N, 2048)]))
+        ref = oracle.matmul_ref_rows(p.x, p.w, p.scales, p.biases, rows, K, 4, 64, "f16")
+        assert_close(y[:, rows], ref, f"qmv {name} sampled")
+    else:
+        assert_close(y, _ref(p), f"qmv {name}")
+
+
+# ------------------------------------------------------- exact special cases ---
+@pytest.mark.parametrize("entry,M", [("qmv", 1), ("qmv", 8), ("qmm", 64), ("qmm", 128)])
+@pytest.mark.parametrize("bits,sb", [(4, "f16"), (8, "bf16")])
+def test_one_hot_bitexact(entry, M, bits, sb):
+    """x rows one-hot at k_m: y[m, n] = f16(f32(w[n, k_m])) exactly."""
+    K, N = 512, 70
+    p = synth.make_problem(M, N, K, bits, 64, sb, seed=400 + M + bits)
+    ks = np.random.default_rng(M).integers(0, K, M)
+    x = np.zeros((M, K), np.float16)
+    x[np.arange(M), ks] = 1.0
+    p.x = x
+    note(f"one-hot {entry} M={M} bits={bits}")
+    y = _run(entry, p)
+    w32 = oracle.dequant_ref_out(p.w, p.scales, p.biases, K, bits, 64, sb, "f32")
+    want = w32[:, ks].T.astype(np.float16)
+    assert np.array_equal(y.view(np.uint16), want.view(np.uint16))
+
+
+@pytest.mark.parametrize("entry,M", [("qmv", 3), ("qmm", 96)])
+@pytest.mark.parametrize("bits", [4, 8])
+def test_integer_case_bitexact(entry, M, bits):
+    """scale 1, bias 0, x in {-1,0,1}: y is an integer; its f16 rounding must match."""
+    K, N = 128, 50
+    rng = np.random.default_rng(bits + M)
+    p = synth.make_problem(M, N, K, bits, 64, "f16", seed=9)
+    p.scales = np.full_like(p.scales, 0x3C00)
+    p.biases = np.zeros_like(p.biases)
+    p.x = rng.integers(-1, 2, size=(M, K)).astype(np.float16)
+    note(f"integer {entry} M={M} bits={bits}")
+    y = _run(entry, p)
+    want = _ref(p).astype(np.float16)
+    assert np.array_equal(y.view(np.uint16), want.view(np.uint16))
+
+
+@pytest.mark.parametrize("entry,M", [("qmv", 1), ("qmv", 5), ("qmm", 200)])
+def test_deterministic(entry, M):
+    p = synth.make_problem(M, 3000, 2048, 4, 64, "bf16", seed=77)
+    x, w, s, b = to_dev(p)
+    fn = mxq.mxq_qmv if entry == "qmv" else mxq.mxq_qmm
+    note(f"determinism {entry} M={M}")
+    y1 = y_host(fn(x, w, s, b, bits=4))
+    y2 = y_host(fn(x, w, s, b, bits=4))
+    assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16))
+
+
+def test_empty_and_k_zero():
+    dev = "cuda:0"
+    x = torch.zeros((0, 64), dtype=torch.float16, device=dev)
+    w = torch.zeros((5, 8), dtype=torch.int32, device=dev)
+    s = torch.zeros((5, 1), dtype=torch.float16, device=dev)
+    note("empty M")
+    assert mxq.mxq_qmv(x, w, s, s).shape == (0, 5)
+    x = torch.ones((3, 0), dtype=torch.float16, device=dev)
+    w = torch.zeros((4, 0), dtype=torch.int32, device=dev)
+    s = torch.zeros((4, 0), dtype=torch.float16, device=dev)
+    y = torch.full((3, 4), 7.0, dtype=torch.float16, device=dev)
+    note("K = 0")
+    for fn in (mxq.mxq_qmv, mxq.mxq_qmm):
+        y.fill_(7.0)
+        fn(x, w, s, s, y)
+        torch.cuda.synchronize()
+        assert torch.equal(y.cpu(), torch.zeros((3, 4), dtype=torch.float16))
+
+
+def test_nonzero_stream_and_offsets():
+    """Work enqueued on a side stream; x passed as an unaligned slice (scalar staging)."""
+    p = synth.make_problem(3, 300, 1024, 4, 64, "f16", seed=5)
+    x, w, s, b = to_dev(p)
+    xbig = torch.zeros((3 * 1024 + 1,), dtype=torch.float16, device="cuda:0")
+    xbig[1:].copy_(x.reshape(-1))
+    xu = xbig[1:].view(3, 1024)
+    st = torch.cuda.Stream()
+    note("side stream + unaligned x")
+    with torch.cuda.stream(st):
+        y = mxq.mxq_qmv(xu, w, s, b, bits=4, stream=st)
+    st.synchronize()
+    assert_close(y.cpu().numpy(), _ref(p), "side stream")
+
+
+def test_misaligned_w_rejected_on_device():
+    p = synth.make_problem(1, 4, 64, 4, 64, "f16", seed=1)
+    x, w, s, b = to_dev(p)
+    wbig = torch.zeros((4 * 8 + 1,), dtype=torch.int32, device="cuda:0")
+    wv = wbig[1:].view(4, 8)
+    with pytest.raises(mxq.MxqError) as e:
+        mxq.mxq_qmv(x, wv, s, b, bits=4)
+    assert e.value.status == mxq.MXQ_ERR_MISALIGNED
