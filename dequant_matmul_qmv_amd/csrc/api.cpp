@@ -264,7 +264,7 @@ const char* mxq_describe(const char* op, int64_t M, int64_t N, int64_t K, int bi
   desc.clear();
   for (int64_t m0 = 0; m0 < M; m0 += mt_max) {
     const int mt = static_cast<int>((M - m0) < mt_max ? (M - m0) : mt_max);
-    const mxq::QmvPlan p = mxq::qmv_plan(dev, N, K, bits, mt, 0);
+    const mxq::QmvPlan p = mxq::qmv_plan(dev, N, K, bits, sb_dtype == MXQ_BF16, mt, 0);
     if (!desc.empty()) desc += "; ";
     desc += "qmv_kernel<bits=" + std::to_string(bits) + ",sb=" + sb + ",mt=" + std::to_string(mt) +
             ",rows=" + std::to_string(p.rows) + "> grid=" + std::to_string(p.grid) +

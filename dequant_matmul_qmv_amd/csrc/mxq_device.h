@@ -47,6 +47,33 @@ __device__ __forceinline__ h2 sub1024(uint32_t u) {
   return as_h2(u) - k;
 }
 
+// (a & mask) | c in one v_and_or_b32.  gfx9 VOP3 takes no literal constants
+// and reads at most one SGPR, so the mask goes in an SGPR and c in a VGPR;
+// left to itself the compiler splits this into v_and + v_or.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t c) {
+  uint32_t d;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(mask), "v"(c));
+  return d;
+}
+
+// 4-bit word -> four f16 pairs with one shift: (c0, c4), (16*c1, 16*c5),
+// (c2, c6), (16*c3, 16*c7).  The odd codes stay in mantissa bits 4..7 (value
+// 1024 + 16*c), so they come out scaled by 16; callers accumulate their dot
+// products separately and fold the 1/16 back with one exact f32 multiply-add.
+__device__ __forceinline__ void unpack_w4_x16(uint32_t w, uint32_t magic, h2 (&q)[4]) {
+  const uint32_t hi = w >> 8;
+  q[0] = sub1024(and_or(w, 0x000F000Fu, magic));
+  q[1] = sub1024(and_or(w, 0x00F000F0u, magic));
+  q[2] = sub1024(and_or(hi, 0x000F000Fu, magic));
+  q[3] = sub1024(and_or(hi, 0x00F000F0u, magic));
+}
+
+// 8-bit word -> (c0, c2), (c1, c3) with one shift and two v_and_or_b32.
+__device__ __forceinline__ void unpack_w8_ao(uint32_t w, uint32_t magic, h2 (&q)[2]) {
+  q[0] = sub1024(and_or(w, 0x00FF00FFu, magic));
+  q[1] = sub1024(and_or(w >> 8, 0x00FF00FFu, magic));
+}
+
 // 4-bit word -> 4 pairs of exact f16 codes.
 __device__ __forceinline__ void unpack_w4(uint32_t w, h2 (&q)[4]) {
   q[0] = sub1024((w & 0x000F000Fu) | kMagic);

@@ -42,8 +42,10 @@ size_t qmv_lds_need(int bits, int mt, int64_t K);
 struct QmvPlan {
   int mt, rows, grid;
   size_t lds;
+  const void* kernel;
 };
-QmvPlan qmv_plan(const DeviceInfo& dev, int64_t N, int64_t K, int bits, int mt, int rows_override);
+QmvPlan qmv_plan(const DeviceInfo& dev, int64_t N, int64_t K, int bits, bool sb_bf16, int mt,
+                 int rows_override);
 hipError_t launch_qmv_slice(const QmvArgs& a, const DeviceInfo& dev, int mt);
 
 struct QmmArgs {

@@ -28,6 +28,10 @@
 //    6*R*M.  Everything is in a fixed order: results are deterministic.
 //  * Workgroups are persistent (grid-stride over row blocks) so the x staging
 //    is paid once per workgroup, not once per row block.
+#include <map>
+#include <mutex>
+#include <tuple>
+
 #include "mxq_device.h"
 #include "mxq_internal.h"
 
@@ -46,6 +50,13 @@ __host__ __device__ constexpr size_t qmv_lds_bytes(int MT, int K) {
          (SegTraits<BITS>::kChunksPerSeg * 16 + 4);
 }
 
+// Loads of one work item: R rows x one 16-byte segment, plus their scales and biases.
+template <int R>
+struct QmvItem {
+  u4 w[R];
+  uint16_t s[R], b[R];
+};
+
 template <int BITS, bool SB_BF16, int MT, int R>
 __global__ __launch_bounds__(256) void qmv_kernel(const uint16_t* __restrict__ x,
                                                   const uint32_t* __restrict__ W,
@@ -55,6 +66,7 @@ __global__ __launch_bounds__(256) void qmv_kernel(const uint16_t* __restrict__ x
                                                   int glog2, int x_vec) {
   constexpr int CPS = SegTraits<BITS>::kChunksPerSeg;
   constexpr int CODES = SegTraits<BITS>::kCodesPerSeg;
+  constexpr int NP = (BITS == 4) ? 16 : 8;  // f16 code pairs per segment
   constexpr int V = R * MT;
   constexpr int VP = V <= 1 ? 1 : V <= 2 ? 2 : V <= 4 ? 4 : V <= 8 ? 8 : V <= 16 ? 16 : 32;
   static_assert(V <= 32, "too many live outputs per lane");
@@ -65,6 +77,43 @@ __global__ __launch_bounds__(256) void qmv_kernel(const uint16_t* __restrict__ x
   const int G = K >> glog2;          // groups per row
   u4* xs = reinterpret_cast<u4*>(smem);                                     // [MT][CPS][nseg]
   float* xsum = reinterpret_cast<float*>(smem + static_cast<size_t>(MT) * CPS * nseg * 16);  // [MT][nseg]
+
+  const int lane = threadIdx.x & (kWave - 1);
+  // wave-uniform values live in scalar registers: all row addressing is scalar,
+  // and each load adds one 32-bit per-lane offset to a scalar base (the caller
+  // guarantees W, S and B are each below 4 GiB)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int waves_per_block = blockDim.x >> 6;
+  const int nrb = (N + R - 1) / R;
+  const int jn = (nseg + kWave - 1) / kWave;
+  const int stride = gridDim.x * waves_per_block;
+  const uint32_t wrow_bytes = static_cast<uint32_t>(kw) * 4u;
+  const uint32_t sbrow_bytes = static_cast<uint32_t>(G) * 2u;
+  const char* Wb = reinterpret_cast<const char*>(W);
+  const char* Sb = reinterpret_cast<const char*>(S);
+  const char* Bb = reinterpret_cast<const char*>(B);
+
+  // Loads are unconditional and branch-free (indices clamped into range) so the
+  // compiler's load counters stay exact: a conditional load would make it wait
+  // for every outstanding load, including the prefetched ones.
+  auto load_item = [&](QmvItem<R>& it, int rbl, int jl) {
+    const int seg = min(lane + jl * kWave, nseg - 1);
+    const uint32_t wl = static_cast<uint32_t>(seg) * 16u;
+    const uint32_t sl = static_cast<uint32_t>((seg * CODES) >> glog2) * 2u;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint32_t row = static_cast<uint32_t>(min(rbl * R + r, N - 1));  // tail rows re-read the last row; never stored
+      it.w[r] = *reinterpret_cast<const u4*>(Wb + (row * wrow_bytes + wl));
+      it.s[r] = *reinterpret_cast<const uint16_t*>(Sb + (row * sbrow_bytes + sl));
+      it.b[r] = *reinterpret_cast<const uint16_t*>(Bb + (row * sbrow_bytes + sl));
+    }
+  };
+
+  // The first item's loads go out before the x staging, to overlap the two.
+  int rb = blockIdx.x * waves_per_block + wave;
+  int j = 0;
+  QmvItem<R> cur, alt;
+  load_item(cur, min(rb, nrb - 1), 0);
 
   // ---- stage x (reordered) and its per-segment sums into LDS -------------
   for (int u = threadIdx.x; u < MT * nseg; u += blockDim.x) {
@@ -91,79 +140,110 @@ __global__ __launch_bounds__(256) void qmv_kernel(const uint16_t* __restrict__ x
     xsum[m * nseg + seg] = sum;
   }
   __syncthreads();
+  if (rb >= nrb) return;  // no block-level barrier follows
 
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x >> 6;
-  const int waves_per_block = blockDim.x >> 6;
-  const int nrb = (N + R - 1) / R;
-  const int jn = (nseg + kWave - 1) / kWave;
+  const uint32_t magic = kMagic;
+  float acc[R][MT];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[r][m] = 0.0f;
 
-  for (int rb = blockIdx.x * waves_per_block + wave; rb < nrb; rb += gridDim.x * waves_per_block) {
-    const int row0 = rb * R;
-    float acc[R][MT];
+  // segment dot product of one row's codes with one activation row's pairs
+  auto seg_dot = [&](const h2 (&q)[NP], const uint32_t (&xp)[NP]) {
+    if constexpr (BITS == 4) {
+      // even pairs carry codes, odd pairs 16 x codes (see unpack_w4_x16)
+      float de = 0.0f, dd = 0.0f;
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+      for (int p = 0; p < NP; p += 2) {
+        de = __builtin_amdgcn_fdot2(q[p], as_h2(xp[p]), de, false);
+        dd = __builtin_amdgcn_fdot2(q[p + 1], as_h2(xp[p + 1]), dd, false);
+      }
+      return __builtin_fmaf(dd, 0.0625f, de);
+    } else {
+      float d = 0.0f;
 #pragma unroll
-      for (int m = 0; m < MT; ++m) acc[r][m] = 0.0f;
+      for (int p = 0; p < NP; ++p) d = __builtin_amdgcn_fdot2(q[p], as_h2(xp[p]), d, false);
+      return d;
+    }
+  };
+  auto unpack_row = [&](const u4& wv, h2 (&q)[NP]) {
+    const uint32_t wr[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (BITS == 4) {
+        h2 t[4];
+        unpack_w4_x16(wr[i], magic, t);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) q[4 * i + p] = t[p];
+      } else {
+        h2 t[2];
+        unpack_w8_ao(wr[i], magic, t);
+        q[2 * i] = t[0];
+        q[2 * i + 1] = t[1];
+      }
+    }
+  };
+  auto load_x = [&](int m, int seg, uint32_t (&xp)[NP]) {
+#pragma unroll
+    for (int c = 0; c < CPS; ++c) {
+      const u4 xv = xs[(m * CPS + c) * nseg + seg];
+      xp[4 * c] = xv.x;
+      xp[4 * c + 1] = xv.y;
+      xp[4 * c + 2] = xv.z;
+      xp[4 * c + 3] = xv.w;
+    }
+  };
 
-    for (int j = 0; j < jn; ++j) {
-      const int seg = lane + j * kWave;
-      if (seg < nseg) {
-        const int grp = (seg * CODES) >> glog2;
-        u4 wv[R];
-        float sc[R], bi[R];
+  // Compute one item (row block rbl, segment step jl); when it completes the
+  // row block, reduce the partial sums across the wave and store them.
+  auto step = [&](const QmvItem<R>& it, int rbl, int jl, bool block_done) {
+    // Branch-free: lanes past the end of the row (ragged last step) compute on a
+    // clamped, valid segment and discard the result with a select, so every
+    // path consumes the loads (keeping the compiler's load counters exact).
+    const int seg_raw = lane + jl * kWave;
+    const bool active = seg_raw < nseg;
+    const int seg = min(seg_raw, nseg - 1);
+    if constexpr (MT <= 2) {
+      // few activation rows: keep them in registers, unpack one W row at a time
+      uint32_t xp[MT][NP];
+      float xsm[MT];
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const int row = min(row0 + r, N - 1);  // tail rows re-read the last row; never stored
-          wv[r] = *reinterpret_cast<const u4*>(W + static_cast<size_t>(row) * kw + seg * 4);
-          sc[r] = sb_to_f32<SB_BF16>(S[static_cast<size_t>(row) * G + grp]);
-          bi[r] = sb_to_f32<SB_BF16>(B[static_cast<size_t>(row) * G + grp]);
-        }
-        // codes of the R rows, unpacked once: 16 (4-bit) or 8 (8-bit) pairs per row
-        constexpr int NP = (BITS == 4) ? 16 : 8;
-        h2 q[R][NP];
+      for (int m = 0; m < MT; ++m) {
+        load_x(m, seg, xp[m]);
+        xsm[m] = xsum[m * nseg + seg];
+      }
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const uint32_t wr[4] = {wv[r].x, wv[r].y, wv[r].z, wv[r].w};
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if constexpr (BITS == 4) {
-              h2 t[4];
-              unpack_w4(wr[i], t);
-#pragma unroll
-              for (int p = 0; p < 4; ++p) q[r][4 * i + p] = t[p];
-            } else {
-              h2 t[2];
-              unpack_w8(wr[i], t);
-              q[r][2 * i] = t[0];
-              q[r][2 * i + 1] = t[1];
-            }
-          }
-        }
+      for (int r = 0; r < R; ++r) {
+        h2 q[NP];
+        unpack_row(it.w[r], q);
+        const float sc = sb_to_f32<SB_BF16>(it.s[r]);
+        const float bi = sb_to_f32<SB_BF16>(it.b[r]);
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-          // x pairs in the same order as q: chunk c holds pairs 4c..4c+3
-          uint32_t xp[NP];
+          const float t = __builtin_fmaf(bi, xsm[m], __builtin_fmaf(sc, seg_dot(q, xp[m]), acc[r][m]));
+          acc[r][m] = active ? t : acc[r][m];
+        }
+      }
+    } else {
+      // many activation rows: unpack all R rows once, stream x rows from LDS
+      h2 q[R][NP];
 #pragma unroll
-          for (int c = 0; c < CPS; ++c) {
-            const u4 xv = xs[(m * CPS + c) * nseg + seg];
-            xp[4 * c] = xv.x;
-            xp[4 * c + 1] = xv.y;
-            xp[4 * c + 2] = xv.z;
-            xp[4 * c + 3] = xv.w;
-          }
-          const float xsm = xsum[m * nseg + seg];
+      for (int r = 0; r < R; ++r) unpack_row(it.w[r], q[r]);
 #pragma unroll
-          for (int r = 0; r < R; ++r) {
-            float d = 0.0f;
+      for (int m = 0; m < MT; ++m) {
+        uint32_t xp[NP];
+        load_x(m, seg, xp);
+        const float xsm = xsum[m * nseg + seg];
 #pragma unroll
-            for (int p = 0; p < NP; ++p) d = __builtin_amdgcn_fdot2(q[r][p], as_h2(xp[p]), d, false);
-            acc[r][m] = __builtin_fmaf(sc[r], d, acc[r][m]);
-            acc[r][m] = __builtin_fmaf(bi[r], xsm, acc[r][m]);
-          }
+        for (int r = 0; r < R; ++r) {
+          const float t = __builtin_fmaf(sb_to_f32<SB_BF16>(it.b[r]), xsm,
+                                         __builtin_fmaf(sb_to_f32<SB_BF16>(it.s[r]), seg_dot(q[r], xp), acc[r][m]));
+          acc[r][m] = active ? t : acc[r][m];
         }
       }
     }
+    if (!block_done) return;
 
     // ---- transpose butterfly over the 64 lanes -------------------------
     float v[VP];
@@ -199,87 +279,160 @@ __global__ __launch_bounds__(256) void qmv_kernel(const uint16_t* __restrict__ x
       if (idx < V) {
         const int r = idx / MT;
         const int m = idx - r * MT;
-        const int row = row0 + r;
+        const int row = rbl * R + r;
         if (row < N) y[static_cast<size_t>(m) * N + row] = f32_to_f16_bits(v[0]);
       }
     }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) acc[r][m] = 0.0f;
+  };
+
+  // Ping-pong over two item buffers: the next item's loads are in flight while
+  // the current item is computed, and no register copy of in-flight data is
+  // ever made (a copy would force a wait for those loads).
+  auto advance = [&](int& rbv, int& jv) {
+    if (++jv == jn) {
+      jv = 0;
+      rbv += stride;
+    }
+  };
+  while (true) {
+    int rb2 = rb, j2 = j;
+    advance(rb2, j2);
+    bool more = rb2 < nrb;
+    load_item(alt, more ? rb2 : rb, more ? j2 : j);  // past the end: harmless reload
+    __builtin_amdgcn_sched_barrier(0);  // keep the whole load block ahead of the compute
+    step(cur, rb, j, j2 == 0);
+    if (!more) break;
+    rb = rb2;
+    j = j2;
+    advance(rb2, j2);
+    more = rb2 < nrb;
+    load_item(cur, more ? rb2 : rb, more ? j2 : j);
+    __builtin_amdgcn_sched_barrier(0);
+    step(alt, rb, j, j2 == 0);
+    if (!more) break;
+    rb = rb2;
+    j = j2;
   }
 }
 
 // ---------------------------------------------------------------------------
-// Host-side launcher: picks MT/R instantiation; validation happens in api.cpp.
+// Host side: instantiation table, occupancy-sized persistent grid, launch.
+// Validation happens in api.cpp before any of this runs.
 // ---------------------------------------------------------------------------
-template <int BITS, bool SB_BF16, int MT, int R>
-static hipError_t launch_qmv_t(const QmvArgs& a, int grid, size_t lds) {
-  auto kern = qmv_kernel<BITS, SB_BF16, MT, R>;
-  if (lds > 65536) {
-    hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), lds);
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, a.stream, a.x, a.w, a.s, a.b, a.y,
-                     static_cast<int>(a.N), static_cast<int>(a.K), a.glog2, a.x_vec);
-  return hipGetLastError();
-}
+namespace {
 
 template <int BITS, bool SB_BF16, int R>
-static hipError_t launch_qmv_mt(const QmvArgs& a, int mt, int grid, size_t lds) {
+const void* qmv_ptr_mt(int mt) {
   switch (mt) {
-    case 1: return launch_qmv_t<BITS, SB_BF16, 1, R>(a, grid, lds);
-    case 2: return launch_qmv_t<BITS, SB_BF16, 2, R>(a, grid, lds);
-    case 3: return launch_qmv_t<BITS, SB_BF16, 3, R>(a, grid, lds);
-    case 4: return launch_qmv_t<BITS, SB_BF16, 4, R>(a, grid, lds);
-    case 5: return launch_qmv_t<BITS, SB_BF16, 5, R>(a, grid, lds);
-    case 6: return launch_qmv_t<BITS, SB_BF16, 6, R>(a, grid, lds);
-    case 7: return launch_qmv_t<BITS, SB_BF16, 7, R>(a, grid, lds);
-    default: return launch_qmv_t<BITS, SB_BF16, 8, R>(a, grid, lds);
+    case 1: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 1, R>);
+    case 2: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 2, R>);
+    case 3: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 3, R>);
+    case 4: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 4, R>);
+    case 5: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 5, R>);
+    case 6: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 6, R>);
+    case 7: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 7, R>);
+    default: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 8, R>);
   }
 }
 
 template <int BITS, bool SB_BF16>
-static hipError_t launch_qmv_bits(const QmvArgs& a, int mt, int R, int grid, size_t lds) {
-  // R * MT live outputs per lane are capped at 32.
-  if (R == 4 && mt <= 8) return launch_qmv_mt<BITS, SB_BF16, 4>(a, mt, grid, lds);
-  if (R == 2) return launch_qmv_mt<BITS, SB_BF16, 2>(a, mt, grid, lds);
-  return launch_qmv_mt<BITS, SB_BF16, 1>(a, mt, grid, lds);
+const void* qmv_ptr_r(int mt, int R) {
+  if (R == 4) return qmv_ptr_mt<BITS, SB_BF16, 4>(mt);
+  if (R == 2) return qmv_ptr_mt<BITS, SB_BF16, 2>(mt);
+  return qmv_ptr_mt<BITS, SB_BF16, 1>(mt);
 }
+
+const void* qmv_kernel_ptr(int bits, bool bf16, int mt, int R) {
+  if (bits == 4) return bf16 ? qmv_ptr_r<4, true>(mt, R) : qmv_ptr_r<4, false>(mt, R);
+  return bf16 ? qmv_ptr_r<8, true>(mt, R) : qmv_ptr_r<8, false>(mt, R);
+}
+
+// Rows of W per wave step and the grid.  A large N streams best with about
+// 8-16 MiB of weight loads in flight in total (measured on MI355X with the
+// read probe and launch sweeps: more outstanding requests lower the achieved
+// bandwidth): R = 4 rows of one 16-byte segment per lane (R = 2 when a row
+// spans several segment steps) and 2 workgroups of 4 waves per CU, each wave
+// holding two items in flight.  A small N cannot fill the chip anyway: one
+// row per wave step and as many waves as the rows allow.
+struct RowsGrid {
+  int rows;
+  int blocks_per_cu_cap;  // 0: occupancy-limited
+};
+
+RowsGrid qmv_pick_rows(const DeviceInfo& dev, int64_t N, int64_t K, int bits, int mt) {
+  const int64_t nseg = K * bits / 128;
+  RowsGrid rg{1, 0};
+  if (N >= static_cast<int64_t>(dev.num_cu) * 32) {
+    rg.rows = nseg <= kWave ? 4 : 2;
+    rg.blocks_per_cu_cap = 2;
+  }
+  while (rg.rows > 1 && rg.rows * mt > 16) rg.rows /= 2;  // bound live accumulators and registers
+  return rg;
+}
+
+std::mutex g_occ_mu;
+std::map<std::tuple<int, const void*, size_t>, int> g_occ;  // (device, kernel, lds) -> blocks/CU
+
+int blocks_per_cu(const DeviceInfo& dev, const void* kern, size_t lds) {
+  const auto key = std::make_tuple(dev.device, kern, lds);
+  {
+    std::lock_guard<std::mutex> lk(g_occ_mu);
+    auto it = g_occ.find(key);
+    if (it != g_occ.end()) return it->second;
+  }
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, 256, lds) != hipSuccess || nb < 1) {
+    (void)hipGetLastError();
+    nb = 1;
+  }
+  std::lock_guard<std::mutex> lk(g_occ_mu);
+  g_occ[key] = nb;
+  return nb;
+}
+
+}  // namespace
 
 size_t qmv_lds_need(int bits, int mt, int64_t K) {
   return bits == 4 ? qmv_lds_bytes<4>(mt, static_cast<int>(K))
                    : qmv_lds_bytes<8>(mt, static_cast<int>(K));
 }
 
-int qmv_pick_rows(const DeviceInfo& dev, int64_t N, int mt) {
-  const int64_t target = static_cast<int64_t>(dev.num_cu) * 8;  // waves to fill the chip
-  int R = 1;
-  if ((N + 3) / 4 >= target) R = 4;
-  else if ((N + 1) / 2 >= target) R = 2;
-  while (R > 1 && R * mt > 16) R /= 2;  // bound live accumulators and LDS reads
-  return R;
-}
-
-QmvPlan qmv_plan(const DeviceInfo& dev, int64_t N, int64_t K, int bits, int mt, int rows_override) {
+QmvPlan qmv_plan(const DeviceInfo& dev, int64_t N, int64_t K, int bits, bool sb_bf16, int mt,
+                 int rows_override) {
   QmvPlan p{};
   p.mt = mt;
-  p.rows = rows_override > 0 ? rows_override : qmv_pick_rows(dev, N, mt);
+  const RowsGrid rg = qmv_pick_rows(dev, N, K, bits, mt);
+  p.rows = rows_override > 0 ? rows_override : rg.rows;
   p.lds = qmv_lds_need(bits, mt, K);
+  p.kernel = qmv_kernel_ptr(bits, sb_bf16, mt, p.rows);
+  if (p.lds > 65536 && ensure_dynamic_lds(p.kernel, p.lds) != hipSuccess) (void)hipGetLastError();
   const int64_t nrb = (N + p.rows - 1) / p.rows;
   const int64_t blocks_needed = (nrb + 3) / 4;
-  int per_cu = static_cast<int>(dev.lds_per_cu / (p.lds > 0 ? p.lds : 1));
-  per_cu = per_cu < 1 ? 1 : (per_cu > 8 ? 8 : per_cu);
+  int per_cu = blocks_per_cu(dev, p.kernel, p.lds);
+  if (rg.blocks_per_cu_cap > 0 && per_cu > rg.blocks_per_cu_cap) per_cu = rg.blocks_per_cu_cap;
   const int64_t cap = static_cast<int64_t>(dev.num_cu) * per_cu;
   p.grid = static_cast<int>(blocks_needed < cap ? blocks_needed : cap);
   return p;
 }
 
 hipError_t launch_qmv_slice(const QmvArgs& a, const DeviceInfo& dev, int mt) {
-  const QmvPlan p = qmv_plan(dev, a.N, a.K, a.bits, mt, a.rows_per_wave);
-  const int R = p.rows, grid = p.grid;
-  const size_t lds = p.lds;
-  if (a.bits == 4)
-    return a.sb_bf16 ? launch_qmv_bits<4, true>(a, mt, R, grid, lds)
-                     : launch_qmv_bits<4, false>(a, mt, R, grid, lds);
-  return a.sb_bf16 ? launch_qmv_bits<8, true>(a, mt, R, grid, lds)
-                   : launch_qmv_bits<8, false>(a, mt, R, grid, lds);
+  const QmvPlan p = qmv_plan(dev, a.N, a.K, a.bits, a.sb_bf16, mt, a.rows_per_wave);
+  if (p.lds > 65536) {
+    hipError_t e = ensure_dynamic_lds(p.kernel, p.lds);
+    if (e != hipSuccess) return e;
+  }
+  const uint16_t* x = a.x;
+  const uint32_t* w = a.w;
+  const uint16_t* s = a.s;
+  const uint16_t* b = a.b;
+  uint16_t* y = a.y;
+  int N = static_cast<int>(a.N), K = static_cast<int>(a.K), glog2 = a.glog2, xv = a.x_vec;
+  void* args[] = {&x, &w, &s, &b, &y, &N, &K, &glog2, &xv};
+  return hipLaunchKernel(p.kernel, dim3(p.grid), dim3(256), args, p.lds, a.stream);
 }
 
 }  // namespace mxq
