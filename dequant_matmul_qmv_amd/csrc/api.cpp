@@ -254,9 +254,10 @@ const char* mxq_describe(const char* op, int64_t M, int64_t N, int64_t K, int bi
   const char* sb = sb_dtype == MXQ_BF16 ? "bf16" : "f16";
   const bool mfma = o == "qmm" && M > 8 && K % 64 == 0;
   if (mfma) {
-    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+    const int64_t tiles = ((M + mxq::kQmmTileM - 1) / mxq::kQmmTileM) * ((N + mxq::kQmmTileN - 1) / mxq::kQmmTileN);
     desc = "qmm_kernel<bits=" + std::to_string(bits) + ",sb=" + sb + ",gs=" + std::to_string(group_size) +
-           "> grid=" + std::to_string(tiles) + " block=256 tile=128x128";
+           ",tile=" + std::to_string(mxq::kQmmTileM) + "x" + std::to_string(mxq::kQmmTileN) +
+           "> grid=" + std::to_string(tiles) + " block=512";
     return desc.c_str();
   }
   int mt_max = 8;

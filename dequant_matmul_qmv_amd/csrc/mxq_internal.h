@@ -62,6 +62,7 @@ struct QmmArgs {
 };
 
 hipError_t launch_qmm(const QmmArgs& a, const DeviceInfo& dev);
+constexpr int kQmmTileM = 64, kQmmTileN = 128;
 
 struct DequantArgs {
   const uint32_t* w;

@@ -12,41 +12,49 @@
 // products exact in f32, so P_g comes out of the MFMA with f32 accumulation
 // only, and scale and bias are applied per group in f32.
 //
-// Tiling: a 256-thread workgroup owns a 128 x 128 tile of y and walks K in
-// stages of 64 codes.  Per stage, x[128 x 64] (reordered into the unpack's
-// pair order) and the unpacked codes q[128 x 64] go to LDS with a padded row
-// stride (144 B, so the MFMA operand reads of 32 rows hit distinct banks);
-// the next stage's global loads are issued before the current stage's MFMAs.
-// Each wave computes a 64 x 64 sub-tile as 2 x 2 blocks of
-// v_mfma_f32_32x32x16_f16 into per-group accumulators P, and at each group's
-// end folds them into the output accumulators with the group's f32 scale and
-// bias.  Tiles are assigned so that consecutive tiles on one XCD (dispatch
-// is round-robin over the 8 XCDs) share the same slice of W, for L2 reuse.
+// Tiling: a workgroup owns a BM x BN tile of y and walks K in stages of 64
+// codes.  Per stage, x[BM x 64] (reordered into the unpack's pair order) and
+// the unpacked codes q[BN x 64] go to LDS (double-buffered, one barrier per
+// stage) with a padded row stride (144 B, so the MFMA operand reads of 32
+// rows hit distinct banks); global loads run two stages ahead in registers.
+// Each wave computes its sub-tile as 32 x 32 blocks of v_mfma_f32_32x32x16_f16
+// into per-group accumulators P; at each group's end the VALU folds P into
+// the output accumulators with the group's f32 scale, and every two groups
+// the bias term sum_g b[n,g] X_g[m] goes through the matrix cores as one exact
+// f32 v_mfma_f32_32x32x2_f32 (X_g in f32 from LDS, b widened to f32).  Tiles
+// are assigned so that consecutive tiles on one XCD (dispatch is round-robin
+// over the 8 XCDs) share the same slice of W, for L2 reuse.
 #include "mxq_device.h"
 #include "mxq_internal.h"
 
 namespace mxq {
 
 namespace {
-constexpr int BM = 128;
-constexpr int BN = 128;
 constexpr int KT = 64;        // codes per stage
 constexpr int LDK = KT + 8;   // padded LDS row stride in halves (144 bytes)
 }  // namespace
 
-template <int BITS, bool SB_BF16, int GS>
-__global__ __launch_bounds__(256) void qmm_kernel(const uint16_t* __restrict__ x,
+template <int BITS, bool SB_BF16, int GS, int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) void qmm_kernel(const uint16_t* __restrict__ x,
                                                   const uint32_t* __restrict__ W,
                                                   const uint16_t* __restrict__ S,
                                                   const uint16_t* __restrict__ B,
                                                   uint16_t* __restrict__ y, int M, int N, int K,
                                                   int tiles_m, int tiles_n) {
-  constexpr int WPS = KT * BITS / 32;       // words per row per stage: 8 or 16
-  constexpr int WPT = WPS / 2;              // words per thread: 4 or 8
-  constexpr int KSPG = GS / 16;             // MFMA k-steps per group: 2, 4, 8
-  __shared__ __align__(16) uint16_t xA[BM * LDK];
-  __shared__ __align__(16) uint16_t qB[BN * LDK];
-  __shared__ __align__(16) float xsum[2][BM];
+  constexpr int NT = 64 * WM * WN;             // threads per workgroup
+  constexpr int WPS = KT * BITS / 32;          // words per W row per stage: 8 or 16
+  constexpr int U4R = WPS / 4;                 // 16-byte chunks per W row per stage: 2 or 4
+  constexpr int CODES_U4 = 128 / BITS;         // codes per 16-byte chunk: 32 or 16
+  constexpr int XCH = BM * 8 / NT;             // x chunks (8 halves) per thread per stage
+  constexpr int WCH = (BN * U4R + NT - 1) / NT;  // W chunks per thread per stage
+  constexpr int TWM = BM / WM, TWN = BN / WN;  // wave sub-tile
+  constexpr int MB = TWM / 32, NB = TWN / 32;  // 32x32 MFMA blocks per wave
+  constexpr int KSPG = GS / 16;                // MFMA k-steps per group
+  static_assert(TWM % 32 == 0 && TWN % 32 == 0 && XCH >= 1 && (BM * 8) % NT == 0, "tile");
+
+  __shared__ __align__(16) uint16_t xA[2][BM * LDK];
+  __shared__ __align__(16) uint16_t qB[2][BN * LDK];
+  __shared__ __align__(16) float xg[4][BM];  // sums of x per group, ring of 4 groups
 
   // ---- tile assignment (XCD-aware when the tile count allows it) ---------
   const int T = tiles_m * tiles_n;
@@ -59,181 +67,205 @@ __global__ __launch_bounds__(256) void qmm_kernel(const uint16_t* __restrict__ x
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   const int G = K / GS;
   const int kw = K * BITS / 32;
   const int nkt = K / KT;
 
-  // staging roles: row t/2, half t&1 of the stage
-  const int srow = t >> 1, shalf = t & 1;
-  const int xm = m0 + srow;
-  const bool xvalid = xm < M;
-  const uint16_t* xrow = x + static_cast<size_t>(xvalid ? xm : 0) * K + 32 * shalf;
-  const int wn_row = min(n0 + srow, N - 1);
-  const uint32_t* wrow = W + static_cast<size_t>(wn_row) * kw + WPT * shalf;
-
-  u4 xr[4];
-  u4 wr[WPT / 4];
+  // ---- global -> registers for one stage ---------------------------------
+  u4 xr[XCH];
+  u4 wr[WCH];
   auto gload = [&](int kt) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      xr[c] = xvalid ? *reinterpret_cast<const u4*>(xrow + kt * KT + 8 * c) : u4{0, 0, 0, 0};
+    for (int i = 0; i < XCH; ++i) {
+      const int c = t + NT * i;
+      const int row = c >> 3, ch = c & 7;
+      const int m = m0 + row;
+      xr[i] = (m < M) ? *reinterpret_cast<const u4*>(x + static_cast<size_t>(m) * K + kt * KT + ch * 8)
+                      : u4{0, 0, 0, 0};
+    }
 #pragma unroll
-    for (int c = 0; c < WPT / 4; ++c)
-      wr[c] = *reinterpret_cast<const u4*>(wrow + kt * WPS + 4 * c);
+    for (int i = 0; i < WCH; ++i) {
+      const int c = min(t + NT * i, BN * U4R - 1);
+      const int row = c / U4R, q4 = c % U4R;
+      const int n = min(n0 + row, N - 1);
+      wr[i] = *reinterpret_cast<const u4*>(W + static_cast<size_t>(n) * kw + kt * WPS + q4 * 4);
+    }
   };
 
-  f16x acc[2][2], P[2][2];
+  // ---- registers -> LDS for one stage (reorder x, unpack codes, x sums) --
+  float xrun[XCH];  // running x sums for groups spanning two stages
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < XCH; ++i) xrun[i] = 0.0f;
+  auto lstore = [&](int kt, int buf) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int i = 0; i < XCH; ++i) {
+      const int c = t + NT * i;
+      const int row = c >> 3, ch = c & 7;
+      const u4 p = (BITS == 4) ? perm_x_w4(xr[i]) : perm_x_w8(xr[i]);
+      *reinterpret_cast<u4*>(&xA[buf][row * LDK + ch * 8]) = p;
+      // sums of x over each group, reduced over the 8 lanes that hold one row
+      float part = sum8_f32(xr[i]);
+      part += __shfl_xor(part, 1, 64);
+      part += __shfl_xor(part, 2, 64);
+      if constexpr (GS == 32) {
+        if ((ch & 3) == 0) xg[(2 * kt + (ch >> 2)) & 3][row] = part;
+      } else {
+        part += __shfl_xor(part, 4, 64);
+        if constexpr (GS == 64) {
+          if (ch == 0) xg[kt & 3][row] = part;
+        } else {
+          xrun[i] += part;
+          if ((kt & 1) && ch == 0) xg[(kt >> 1) & 3][row] = xrun[i];
+          if (kt & 1) xrun[i] = 0.0f;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < WCH; ++i) {
+      const int c = t + NT * i;
+      if (c < BN * U4R) {
+        const int row = c / U4R, q4 = c % U4R;
+        uint16_t* dst = &qB[buf][row * LDK + q4 * CODES_U4];
+        const uint32_t wv[4] = {wr[i].x, wr[i].y, wr[i].z, wr[i].w};
+        if constexpr (BITS == 4) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            h2 q[4];
+            unpack_w4(wv[k], q);
+            *reinterpret_cast<u4*>(dst + 8 * k) = u4{as_u32(q[0]), as_u32(q[1]), as_u32(q[2]), as_u32(q[3])};
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            h2 qa[2], qb[2];
+            unpack_w8(wv[2 * k], qa);
+            unpack_w8(wv[2 * k + 1], qb);
+            *reinterpret_cast<u4*>(dst + 8 * k) = u4{as_u32(qa[0]), as_u32(qa[1]), as_u32(qb[0]), as_u32(qb[1])};
+          }
+        }
+      }
+    }
+  };
+
+  f16x acc[MB][NB], P[MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f, P[i][j][r] = 0.0f;
 
-  // output-column rows of W this lane's accumulators belong to (for s, b)
-  int ncol[2];
+  // output column (row of W) of each n-block for this lane, clamped for loads
+  int ncol[NB];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) ncol[j] = min(n0 + wn * 64 + j * 32 + (lane & 31), N - 1);
+  for (int j = 0; j < NB; ++j) ncol[j] = min(n0 + wn * TWN + j * 32 + (lane & 31), N - 1);
+  const int hi = lane >> 5;  // k index of this lane in the 32x32x2 f32 MFMA
 
-  float xg_run = 0.0f;  // running sum of x over a 128-wide group (GS == 128)
+  // Per group: acc += s * P (VALU).  Per pair of groups (or a last odd group):
+  // acc += X^T b as one exact f32 MFMA, X = sums of x per group (the bias term).
+  auto group_end = [&](int g) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const float sc = sb_to_f32<SB_BF16>(S[static_cast<size_t>(ncol[j]) * G + g]);
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(sc, P[i][j][r], acc[i][j][r]);
+    }
+    if ((g & 1) || g == G - 1) {
+      const int gk = (g & ~1) + hi;  // this lane's group of the pair
+      const bool ok = gk < G;
+      float xa[MB], bb[NB];
+#pragma unroll
+      for (int i = 0; i < MB; ++i) xa[i] = ok ? xg[gk & 3][wm * TWM + i * 32 + (lane & 31)] : 0.0f;
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        bb[j] = ok ? sb_to_f32<SB_BF16>(B[static_cast<size_t>(ncol[j]) * G + gk]) : 0.0f;
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(xa[i], bb[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // ---- prologue: stage 0 in LDS, stage 1 in registers ---------------------
   gload(0);
+  lstore(0, 0);
+  __syncthreads();
+  if (nkt > 1) gload(1);
+
   for (int kt = 0; kt < nkt; ++kt) {
-    __syncthreads();  // previous stage's LDS reads are done
-    // x -> LDS in pair order, plus the sums of x per group
-    float part = 0.0f;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      part += sum8_f32(xr[c]);
-      const u4 p = (BITS == 4) ? perm_x_w4(xr[c]) : perm_x_w8(xr[c]);
-      *reinterpret_cast<u4*>(&xA[srow * LDK + 32 * shalf + 8 * c]) = p;
-    }
-    // codes -> LDS as exact f16 integers, same pair order
-    if constexpr (BITS == 4) {
-      const uint32_t wv[4] = {wr[0].x, wr[0].y, wr[0].z, wr[0].w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        h2 q[4];
-        unpack_w4(wv[i], q);
-        *reinterpret_cast<u4*>(&qB[srow * LDK + 32 * shalf + 8 * i]) =
-            u4{as_u32(q[0]), as_u32(q[1]), as_u32(q[2]), as_u32(q[3])};
-      }
-    } else {
-      const uint32_t wv[8] = {wr[0].x, wr[0].y, wr[0].z, wr[0].w, wr[1].x, wr[1].y, wr[1].z, wr[1].w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        h2 qa[2], qb[2];
-        unpack_w8(wv[2 * i], qa);
-        unpack_w8(wv[2 * i + 1], qb);
-        *reinterpret_cast<u4*>(&qB[srow * LDK + 32 * shalf + 8 * i]) =
-            u4{as_u32(qa[0]), as_u32(qa[1]), as_u32(qb[0]), as_u32(qb[1])};
-      }
-    }
-    if constexpr (GS == 32) {
-      xsum[shalf][srow] = part;
-    } else {
-      const float tot = part + __shfl_xor(part, 1, 64);
-      if constexpr (GS == 64) {
-        if (shalf == 0) xsum[0][srow] = tot;
-      } else {
-        xg_run += tot;
-        if ((kt & 1) && shalf == 0) xsum[0][srow] = xg_run;
-        if (kt & 1) xg_run = 0.0f;
-      }
-    }
-    __syncthreads();
-    if (kt + 1 < nkt) gload(kt + 1);
-
-    // scales / biases of the groups that end in this stage
-    constexpr int GEND = (GS == 32) ? 2 : 1;
-    float sv[GEND][2], bv[GEND][2];
-    const bool ends = (GS != 128) || (kt & 1);
-    if (ends) {
-#pragma unroll
-      for (int e = 0; e < GEND; ++e) {
-        const int g = (GS == 32) ? 2 * kt + e : (GS == 64 ? kt : kt >> 1);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          sv[e][j] = sb_to_f32<SB_BF16>(S[static_cast<size_t>(ncol[j]) * G + g]);
-          bv[e][j] = sb_to_f32<SB_BF16>(B[static_cast<size_t>(ncol[j]) * G + g]);
-        }
-      }
-    }
-
+    const int buf = kt & 1;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      // group boundaries: compile-time for groups inside one stage, else by stage parity
+      // group boundaries: compile-time when groups fit in a stage, else by stage parity
       const bool first = (GS <= KT) ? (kk % KSPG == 0) : (kk == 0 && !(kt & 1));
       const bool last = (GS <= KT) ? (kk % KSPG == KSPG - 1) : (kk == 3 && (kt & 1));
-      h8 a[2], b[2];
+      h8 a[MB], b[NB];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        a[i] = *reinterpret_cast<const h8*>(&xA[(wm * 64 + i * 32 + (lane & 31)) * LDK + kk * 16 + 8 * (lane >> 5)]);
+      for (int i = 0; i < MB; ++i)
+        a[i] = *reinterpret_cast<const h8*>(&xA[buf][(wm * TWM + i * 32 + (lane & 31)) * LDK + kk * 16 + 8 * hi]);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        b[j] = *reinterpret_cast<const h8*>(&qB[(wn * 64 + j * 32 + (lane & 31)) * LDK + kk * 16 + 8 * (lane >> 5)]);
+      for (int j = 0; j < NB; ++j)
+        b[j] = *reinterpret_cast<const h8*>(&qB[buf][(wn * TWN + j * 32 + (lane & 31)) * LDK + kk * 16 + 8 * hi]);
       const f16x zero = {};
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < MB; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < NB; ++j)
           P[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], first ? zero : P[i][j], 0, 0, 0);
-      if (last) {
-        const int e = (GS == 32) ? (kk >> 1) : 0;
-        const int sub = e;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          float xg[16];
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const float4 v = *reinterpret_cast<const float4*>(
-                &xsum[sub][wm * 64 + i * 32 + 8 * q4 + 4 * (lane >> 5)]);
-            xg[4 * q4] = v.x, xg[4 * q4 + 1] = v.y, xg[4 * q4 + 2] = v.z, xg[4 * q4 + 3] = v.w;
-          }
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              acc[i][j][r] = __builtin_fmaf(sv[e][j], P[i][j][r], acc[i][j][r]);
-              acc[i][j][r] = __builtin_fmaf(bv[e][j], xg[r], acc[i][j][r]);
-            }
-        }
-      }
+      if (last) group_end((kt * KT + kk * 16) / GS);
     }
+    if (kt + 1 < nkt) lstore(kt + 1, buf ^ 1);
+    __syncthreads();
+    if (kt + 2 < nkt) gload(kt + 2);
   }
 
   // ---- store: lane holds column n, rows 8*(r/4) + 4*(lane/32) + r%4 -------
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = n0 + wn * 64 + j * 32 + (lane & 31);
+    for (int j = 0; j < NB; ++j) {
+      const int n = n0 + wn * TWN + j * 32 + (lane & 31);
       if (n >= N) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int m = m0 + wm * TWM + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
         if (m < M) y[static_cast<size_t>(m) * N + n] = f32_to_f16_bits(acc[i][j][r]);
       }
     }
 }
 
-template <int BITS, bool SB_BF16>
-static hipError_t launch_qmm_t(const QmmArgs& a) {
+template <int BITS, bool SB_BF16, int BM, int BN, int WM, int WN>
+static hipError_t launch_qmm_tile(const QmmArgs& a) {
   const int tiles_m = static_cast<int>((a.M + BM - 1) / BM);
   const int tiles_n = static_cast<int>((a.N + BN - 1) / BN);
-  const dim3 grid(tiles_m * tiles_n), block(256);
+  const dim3 grid(tiles_m * tiles_n), block(64 * WM * WN);
   const int M = static_cast<int>(a.M), N = static_cast<int>(a.N), K = static_cast<int>(a.K);
   switch (a.group_size) {
-    case 32: hipLaunchKernelGGL((qmm_kernel<BITS, SB_BF16, 32>), grid, block, 0, a.stream, a.x, a.w, a.s, a.b, a.y, M, N, K, tiles_m, tiles_n); break;
-    case 64: hipLaunchKernelGGL((qmm_kernel<BITS, SB_BF16, 64>), grid, block, 0, a.stream, a.x, a.w, a.s, a.b, a.y, M, N, K, tiles_m, tiles_n); break;
-    default: hipLaunchKernelGGL((qmm_kernel<BITS, SB_BF16, 128>), grid, block, 0, a.stream, a.x, a.w, a.s, a.b, a.y, M, N, K, tiles_m, tiles_n); break;
+    case 32: hipLaunchKernelGGL((qmm_kernel<BITS, SB_BF16, 32, BM, BN, WM, WN>), grid, block, 0, a.stream, a.x, a.w, a.s, a.b, a.y, M, N, K, tiles_m, tiles_n); break;
+    case 64: hipLaunchKernelGGL((qmm_kernel<BITS, SB_BF16, 64, BM, BN, WM, WN>), grid, block, 0, a.stream, a.x, a.w, a.s, a.b, a.y, M, N, K, tiles_m, tiles_n); break;
+    default: hipLaunchKernelGGL((qmm_kernel<BITS, SB_BF16, 128, BM, BN, WM, WN>), grid, block, 0, a.stream, a.x, a.w, a.s, a.b, a.y, M, N, K, tiles_m, tiles_n); break;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_qmm(const QmmArgs& a, const DeviceInfo&) {
-  if (a.bits == 4) return a.sb_bf16 ? launch_qmm_t<4, true>(a) : launch_qmm_t<4, false>(a);
-  return a.sb_bf16 ? launch_qmm_t<8, true>(a) : launch_qmm_t<8, false>(a);
+// Launch shape: 64 x 128 tiles, 8 waves as 2 x 4 (a 32 x 32 sub-tile per wave).
+// Measured on MI355X at M = 512 against 128x128 / 64x64 / 128x64 / 256x64
+// tiles with 4 to 16 waves: fastest on both the 8192 x 2048 and the
+// 2048 x 8192 weight shapes (more waves per CU overlap one wave's MFMAs with
+// another's staging and epilogue work).
+constexpr int kWavesM = 2, kWavesN = 4;
+
+template <int BITS, bool SB_BF16>
+static hipError_t launch_qmm_t(const QmmArgs& a, const DeviceInfo&) {
+  return launch_qmm_tile<BITS, SB_BF16, kQmmTileM, kQmmTileN, kWavesM, kWavesN>(a);
+}
+
+hipError_t launch_qmm(const QmmArgs& a, const DeviceInfo& dev) {
+  if (a.bits == 4) return a.sb_bf16 ? launch_qmm_t<4, true>(a, dev) : launch_qmm_t<4, false>(a, dev);
+  return a.sb_bf16 ? launch_qmm_t<8, true>(a, dev) : launch_qmm_t<8, false>(a, dev);
 }
 
 }  // namespace mxq

@@ -366,7 +366,7 @@ struct RowsGrid {
 RowsGrid qmv_pick_rows(const DeviceInfo& dev, int64_t N, int64_t K, int bits, int mt) {
   const int64_t nseg = K * bits / 128;
   RowsGrid rg{1, 0};
-  if (N >= static_cast<int64_t>(dev.num_cu) * 32) {
+  if (N >= static_cast<int64_t>(dev.num_cu) * 64) {
     rg.rows = nseg <= kWave ? 4 : 2;
     rg.blocks_per_cu_cap = 2;
   }
