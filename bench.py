@@ -161,6 +161,73 @@ def read_traffic(kernel_desc: str, per_launch_alg_bytes: float):
     return t.get("hbm_bytes_per_launch")
 
 
+COPY_BYTES = 256 << 20
+
+
+def traffic_pass():
+    """Workload for the rocprofv3 --pmc passes: a copy of known size (calibration),
+    then the dominant kernel's launches (lm_head qmv, rotating two weight sets)."""
+    import torch
+
+    import dequant_matmul_qmv_amd as mxq
+    import synth
+    lib = mxq.load()
+    dev = "cuda:0"
+    src = torch.randint(0, 1 << 30, (COPY_BYTES // 4,), dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    sets = [make_qmv_set(mxq, lib, synth, torch, 1, r, [synth.LLAMA_1B_LM_HEAD], dev) for r in range(2)]
+    for i in range(6):
+        sets[i % 2][0](cur_stream(torch))
+    torch.cuda.synchronize()
+    N, K = synth.LLAMA_1B_LM_HEAD[1:]
+    meta = {"kernel": mxq.mxq_describe("qmv", 1, N, K, 4, 64, "f16"), "source_sha": kernel_source_sha(),
+            "alg_bytes_per_launch": call_bytes(1, N, K)}
+    print(json.dumps(meta), flush=True)
+
+
+def write_traffic(fetch_csv: str, write_csv: str, meta_json: str):
+    """Turn two rocprofv3 counter CSVs into profiles/qmv_traffic.json.
+
+    FETCH_SIZE and WRITE_SIZE are read in KiB per dispatch; each is scaled by the
+    factor that makes the calibration copy (COPY_BYTES read, COPY_BYTES written)
+    come out exact."""
+    import csv
+    import statistics
+    meta = json.loads(open(meta_json).read().strip().splitlines()[-1])
+
+    def per_kernel(path, counter):
+        vals = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    def calib(vals):
+        # the copy kernel's large dispatches (the COPY_BYTES calibration copies)
+        big = [x for k, v in vals.items() if "copy" in k.lower() for x in v if x * 1024 > COPY_BYTES / 8]
+        return "copy", COPY_BYTES / (statistics.median(big) * 1024)
+
+    fv, wv = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    qmv_name = next(k for k in fv if "qmv_kernel" in k)
+    _, ff = calib(fv)
+    _, fw = calib(wv)
+    fetch = statistics.median(fv[qmv_name]) * 1024 * ff
+    write = statistics.median(wv[qmv_name]) * 1024 * fw
+    out = dict(meta, kernel_symbol=qmv_name.split("(")[0], fetch_bytes_per_launch=round(fetch),
+               write_bytes_per_launch=round(write), hbm_bytes_per_launch=round(fetch + write),
+               fetch_scale=round(ff, 4), write_scale=round(fw, 4),
+               calibration_bytes=COPY_BYTES, launches=len(fv[qmv_name]))
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
 def cpu_baseline(synth, budget_s=12.0):
     """The f64 oracle on a bounded sample, one BLAS thread: GB/s of algorithmic bytes."""
     import numpy as np
@@ -208,7 +275,17 @@ def main():
                          "HIP-graph replay")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip decode_step, qmm and dequant legs")
+    ap.add_argument("--traffic-pass", action="store_true",
+                    help="only run the workload of the rocprofv3 --pmc traffic passes")
+    ap.add_argument("--write-traffic", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "META_JSON"),
+                    help="write profiles/qmv_traffic.json from two rocprofv3 counter CSVs")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
+        return
+    if args.traffic_pass:
+        traffic_pass()
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
