@@ -4,8 +4,10 @@
 Headline (one JSON line on stdout): fused 4-bit qGEMV HBM GB/s at M=1 on the
 Llama-3.2-1B-shaped decode projections (q/o 2048x2048, k/v 512x2048,
 gate/up 8192x2048, down 2048x8192, lm_head 128256x2048; N x K, g64, f16
-scales/biases, f16 x ~ N(0,1)).  One step = one mxq_qmv call per projection
-(8 launches).  The projection set is replicated REPLICAS times with distinct
+scales/biases, f16 x ~ N(0,1)).  One step = every projection once, launched
+as a decoder layer allows: projections reading the same activation share one
+mxq_qmv_grouped launch -- {q,k,v}, {o}, {gate,up}, {down}, {lm_head}, 5
+launches (the 8-launch and 1-launch plans are reported too).  The projection set is replicated REPLICAS times with distinct
 seeded weights (~1.1 GB in total) and the steps cycle through the replicas,
 so every step streams its weights from HBM, not from the 256 MB Infinity
 Cache.  value = algorithmic bytes per step / time per step.
@@ -79,6 +81,22 @@ class Call:
         st = self.fn(*self.args, stream_handle)
         if st != 0:
             raise RuntimeError(f"{self.name}: libmxq status {st}")
+
+
+class GroupCall:
+    """One pre-marshalled mxq_qmv_grouped launch over a list of Call problems."""
+
+    def __init__(self, lib, mxq, calls):
+        self.fn = lib.mxq_qmv_grouped
+        self.arr = (mxq.QmvProblem * len(calls))(*[
+            mxq.QmvProblem(c.args[0], c.args[1], c.args[2], c.args[3], c.args[4], c.N, c.K) for c in calls])
+        self.calls = calls
+        self.bytes = sum(c.bytes for c in calls)
+
+    def __call__(self, stream_handle):
+        st = self.fn(self.arr, len(self.calls), 1, 4, 64, 0, stream_handle)
+        if st != 0:
+            raise RuntimeError(f"grouped launch: libmxq status {st}")
 
 
 def make_qmv_set(mxq, lib, synth, torch, config, replica, shapes, dev, sb="f16"):
@@ -273,6 +291,10 @@ def main():
     ap.add_argument("--mode", choices=["graph", "eager"], default="eager",
                     help="launch the timed steps eagerly (pre-marshalled C-ABI calls) or by "
                          "HIP-graph replay")
+    ap.add_argument("--launch-plan", choices=["layer", "separate", "single"], default="layer",
+                    help="layer: {q,k,v},{o},{gate,up},{down},{lm_head} (grouped where a decoder "
+                         "layer shares the activation); separate: one launch per projection; "
+                         "single: one grouped launch for all eight")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip decode_step, qmm and dequant legs")
     ap.add_argument("--traffic-pass", action="store_true",
@@ -312,32 +334,71 @@ def main():
     sets = [make_qmv_set(mxq, lib, synth, torch, 1, r, shapes, dev) for r in range(args.replicas)]
     bytes_per_step = sum(c.bytes for c in sets[0])
 
-    def eager_step(s):
-        return lambda: [c(cur_stream(torch)) for c in s]
+    def plan_launches(calls, plan):
+        """The launches of one step.  `layer`: projections that read the same
+        activation in a decoder layer share one grouped launch -- {q,k,v}, {o},
+        {gate,up}, {down}, {lm_head}; `separate`: one mxq_qmv per projection;
+        `single`: all eight projections in one grouped launch."""
+        by = {c.name: c for c in calls}
+        if plan == "separate":
+            return list(calls)
+        if plan == "single":
+            return [GroupCall(lib, mxq, calls)]
+        return [GroupCall(lib, mxq, [by["q"], by["k"], by["v"]]), by["o"],
+                GroupCall(lib, mxq, [by["gate"], by["up"]]), by["down"], by["lm_head"]]
 
-    eager_fns = [eager_step(s) for s in sets]
-    graphs = [capture(torch, fn) for fn in eager_fns]
-    graph_fns = [g.replay for g in graphs]
-    step_fns = graph_fns if args.mode == "graph" else eager_fns
+    def step_fn(launches):
+        return lambda: [c(cur_stream(torch)) for c in launches]
+
+    plans = {p: [plan_launches(s, p) for s in sets] for p in ("layer", "separate", "single")}
+    fns = {p: [step_fn(l) for l in plans[p]] for p in plans}
+    head_plan = args.launch_plan
+    graphs = [capture(torch, fn) for fn in fns[head_plan]]
+    step_fns = [g.replay for g in graphs] if args.mode == "graph" else fns[head_plan]
     log("timing headline steps ...")
     if torch.distributed.is_available() and torch.distributed.is_initialized():
         torch.distributed.barrier()
     torch.cuda.synchronize()
     sec = time_steps(torch, step_fns, args.warmup, args.steps)
     value = bytes_per_step / sec / 1e9
-    other_sec = time_steps(torch, eager_fns if args.mode == "graph" else graph_fns, 10, min(args.steps, 200))
+    other = {}
+    for p in plans:
+        if p != head_plan:
+            other[p] = time_steps(torch, fns[p], args.warmup, args.steps)
+    graph_sec = time_steps(torch, [g.replay for g in graphs], 10, min(args.steps, 200)) \
+        if args.mode != "graph" else time_steps(torch, fns[head_plan], 10, min(args.steps, 200))
 
     # ---------------- roofline of the dominant kernel -----------------------
-    times = per_launch_times(torch, sets, reps=max(2 * args.replicas, 24))
+    # per-launch HIP events around the headline plan's launches; a launch is
+    # attributed to the kernel instantiation of its largest problem
+    head_launches = plans[head_plan]
+    pairs = []
+    st = cur_stream(torch)
+    for r in range(max(2 * args.replicas, 24)):
+        for li, c in enumerate(head_launches[r % len(head_launches)]):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            c(st)
+            e1.record()
+            pairs.append((li, e0, e1))
+    torch.cuda.synchronize()
+    launch_ms = {}
+    for li, e0, e1 in pairs:
+        launch_ms.setdefault(li, []).append(e0.elapsed_time(e1))
     by_kernel = {}
-    for c in sets[0]:
-        desc = mxq.mxq_describe("qmv", c.M, c.N, c.K, 4, 64, "f16")
+    per_launch = {}
+    for li, c in enumerate(head_launches[0]):
+        probs = c.calls if isinstance(c, GroupCall) else [c]
+        big = max(probs, key=lambda q: q.N)
+        desc = mxq.mxq_describe("qmv", 1, big.N, big.K, 4, 64, "f16")
+        ms = float(np.median(launch_ms[li]))
         d = by_kernel.setdefault(desc, {"bytes": 0, "ms": 0.0, "launches": 0, "names": []})
-        ms = float(np.median(times[c.name]))
         d["bytes"] += c.bytes
         d["ms"] += ms
         d["launches"] += 1
-        d["names"].append(c.name)
+        name = "+".join(q.name for q in probs)
+        d["names"].append(name)
+        per_launch[name] = {"us": round(ms * 1e3, 2), "GB/s": round(c.bytes / (ms / 1e3) / 1e9, 1)}
     dom_desc, dom = max(by_kernel.items(), key=lambda kv: kv[1]["ms"])
     avg_ms = dom["ms"] / dom["launches"]
     avg_bytes = dom["bytes"] / dom["launches"]
@@ -347,9 +408,6 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": dom_desc, "launches_per_step": dom["launches"], "projections": dom["names"],
                 "avg_launch_us": round(avg_ms * 1e3, 3), "alg_bytes_per_launch": int(avg_bytes)}
-    per_proj = {c.name: {"us": round(float(np.median(times[c.name])) * 1e3, 2),
-                         "GB/s": round(c.bytes / (float(np.median(times[c.name])) / 1e3) / 1e9, 1)}
-                for c in sets[0]}
 
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
@@ -360,14 +418,16 @@ def main():
                                "(N x K: 2048x2048, 512x2048, 512x2048, 2048x2048, 8192x2048, 8192x2048, "
                                "2048x8192, 128256x2048), M=1, 4-bit codes g64, f16 scales/biases, "
                                "f16 x ~ N(0,1)",
-                   "replicas": args.replicas, "launches_per_step": len(sets[0]),
+                   "replicas": args.replicas, "launch_plan": head_plan,
+                   "launches_per_step": len(plans[head_plan][0]),
                    "bytes_per_step": bytes_per_step, "launch_mode": args.mode},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        ("eager_GB/s" if args.mode == "graph" else "graph_GB/s"): round(bytes_per_step / other_sec / 1e9, 1),
-        "per_projection": per_proj,
+        "other_launch_plans_GB/s": {p: round(bytes_per_step / t / 1e9, 1) for p, t in other.items()},
+        ("graph_GB/s" if args.mode != "graph" else "eager_GB/s"): round(bytes_per_step / graph_sec / 1e9, 1),
+        "per_launch": per_launch,
         "roofline": roofline,
     }
-    del sets, step_fns, eager_fns, graph_fns, graphs
+    del sets, plans, fns, step_fns, graphs, head_launches
     torch.cuda.empty_cache()
 
     # ---------------- extras ------------------------------------------------
@@ -375,19 +435,30 @@ def main():
         log("decode step (16 layers + lm_head) ...")
         layers = []
         for layer in range(synth.LLAMA_1B_LAYERS):
-            layers += make_qmv_set(mxq, lib, synth, torch, 3, layer, list(synth.LLAMA_1B_PROJ), dev)
-        layers += make_qmv_set(mxq, lib, synth, torch, 3, 99, [synth.LLAMA_1B_LM_HEAD], dev)
-        dbytes = sum(c.bytes for c in layers)
-        dfn = lambda: [c(cur_stream(torch)) for c in layers]  # noqa: E731
-        g = capture(torch, dfn)
-        dsec = time_steps(torch, [g.replay], 5, 50)
-        dsec_e = time_steps(torch, [dfn], 3, 20)
-        result["decode_step"] = {"launches": len(layers), "bytes_per_step": dbytes,
-                                 "weight_bytes_per_step": sum(c.N * c.K // 2 + c.N * (c.K // 64) * 4 for c in layers),
-                                 "graph_us_per_step": round(dsec * 1e6, 1), "graph_GB/s": round(dbytes / dsec / 1e9, 1),
-                                 "graph_steps_per_s": round(1 / dsec, 1),
-                                 "eager_us_per_step": round(dsec_e * 1e6, 1), "eager_GB/s": round(dbytes / dsec_e / 1e9, 1)}
-        del layers, g
+            layers.append(make_qmv_set(mxq, lib, synth, torch, 3, layer, list(synth.LLAMA_1B_PROJ), dev))
+        head = make_qmv_set(mxq, lib, synth, torch, 3, 99, [synth.LLAMA_1B_LM_HEAD], dev)
+        flat = [c for lay in layers for c in lay] + head
+        dbytes = sum(c.bytes for c in flat)
+        grouped = []
+        for lay in layers:
+            by = {c.name: c for c in lay}
+            grouped += [GroupCall(lib, mxq, [by["q"], by["k"], by["v"]]), by["o"],
+                        GroupCall(lib, mxq, [by["gate"], by["up"]]), by["down"]]
+        grouped += head
+        entry = {"bytes_per_step": dbytes,
+                 "weight_bytes_per_step": sum(c.N * c.K // 2 + c.N * (c.K // 64) * 4 for c in flat)}
+        for label, launches in (("separate", flat), ("layer", grouped)):
+            fn = step_fn(launches)
+            g = capture(torch, fn)
+            gsec = time_steps(torch, [g.replay], 5, 50)
+            esec = time_steps(torch, [fn], 3, 20)
+            entry[label] = {"launches": len(launches),
+                            "graph_us_per_step": round(gsec * 1e6, 1), "graph_GB/s": round(dbytes / gsec / 1e9, 1),
+                            "graph_steps_per_s": round(1 / gsec, 1),
+                            "eager_us_per_step": round(esec * 1e6, 1), "eager_GB/s": round(dbytes / esec / 1e9, 1)}
+            del g
+        result["decode_step"] = entry
+        del layers, head, flat, grouped
         torch.cuda.empty_cache()
 
         log("qmm M=512 ...")
@@ -439,6 +510,44 @@ def main():
         result["dequant"] = {"shape": "128256x2048 4-bit -> f32", "us": round(ms * 1e3, 1),
                              "GB/s": round(dq_bytes / (ms / 1e3) / 1e9, 1)}
         del out, tw
+        torch.cuda.empty_cache()
+
+        # Dense f16 comparator (context, not the product): the same shapes with
+        # plain f16 weights through PyTorch's GEMM (hipBLASLt).  The pages'
+        # acceptance for the packed path is that it beats f16-resident weights.
+        log("dense f16 comparator ...")
+        gen = torch.Generator(device=dev).manual_seed(11)
+        dense = []
+        for name, N, K in shapes:
+            wd = (torch.randn((N, K), device=dev, generator=gen) * 0.02).half()
+            xd = torch.randn((1, K), device=dev, generator=gen).half()
+            dense.append((name, xd, wd))
+        dfn = lambda: [torch.nn.functional.linear(xd, wd) for _, xd, wd in dense]  # noqa: E731
+        fsec = time_steps(torch, [dfn], 20, 200)
+        f16_bytes = sum(wd.numel() * 2 + xd.numel() * 2 + wd.shape[0] * 2 for _, xd, wd in dense)
+        packed_sec = bytes_per_step / (value * 1e9)
+        cmp = {"decode_step_us": round(fsec * 1e6, 2), "weight_bytes_per_step": f16_bytes,
+               "GB/s": round(f16_bytes / fsec / 1e9, 1),
+               "packed_speedup_vs_f16": round(fsec / packed_sec, 3)}
+        del dense
+        prefill = {}
+        for name, N, K in (("gate", 8192, 2048), ("down", 2048, 8192)):
+            wd = (torch.randn((N, K), device=dev, generator=gen) * 0.02).half()
+            xd = torch.randn((512, K), device=dev, generator=gen).half()
+            for _ in range(3):
+                torch.nn.functional.linear(xd, wd)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(20):
+                torch.nn.functional.linear(xd, wd)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / 20
+            prefill[name] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(2 * 512 * N * K / (ms / 1e3) / 1e12, 1)}
+            del wd, xd
+        cmp["prefill_m512"] = prefill
+        result["dense_f16_comparator"] = cmp
+        torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")

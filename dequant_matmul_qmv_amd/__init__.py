@@ -21,4 +21,6 @@ from ._lib import (  # noqa: F401
     mxq_pack,
     mxq_qmm,
     mxq_qmv,
+    mxq_qmv_grouped,
+    QmvProblem,
 )

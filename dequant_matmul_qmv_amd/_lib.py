@@ -36,12 +36,22 @@ class MxqError(RuntimeError):
         self.detail = detail
 
 
+class QmvProblem(ctypes.Structure):
+    """ctypes mirror of ``mxq_qmv_problem`` (include/mxq.h)."""
+
+    _fields_ = [("x", ctypes.c_void_p), ("w", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("biases", ctypes.c_void_p), ("y", ctypes.c_void_p), ("N", ctypes.c_int64),
+                ("K", ctypes.c_int64)]
+
+
 def _declare(lib):
     c_i64, c_int, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
     fused = [vp, vp, vp, vp, vp, c_i64, c_i64, c_i64, c_int, c_int, c_int, vp]
     for name in ("mxq_qmv", "mxq_qmm"):
         f = getattr(lib, name)
         f.argtypes, f.restype = fused, c_int
+    lib.mxq_qmv_grouped.argtypes = [ctypes.POINTER(QmvProblem), c_int, c_i64, c_int, c_int, c_int, vp]
+    lib.mxq_qmv_grouped.restype = c_int
     lib.mxq_dequant.argtypes = [vp, vp, vp, vp, c_i64, c_i64, c_int, c_int, c_int, c_int, vp]
     lib.mxq_dequant.restype = c_int
     lib.mxq_pack.argtypes = [vp, vp, c_i64, c_i64, c_int]
@@ -146,6 +156,39 @@ def _fused(name, x, w, scales, biases, y, bits, group_size, stream):
 def mxq_qmv(x, w, scales, biases, y=None, *, bits: int = 4, group_size: int = 64, stream=None):
     """y = x @ dequant(w).T via the decode kernel (any M; tuned for M <= 8)."""
     return _fused("mxq_qmv", x, w, scales, biases, y, bits, group_size, stream)
+
+
+def mxq_qmv_grouped(problems, *, bits: int = 4, group_size: int = 64, stream=None):
+    """Several independent qmv problems in one launch.
+
+    ``problems`` is a sequence of ``(x, w, scales, biases)`` or
+    ``(x, w, scales, biases, y)`` tuples of device tensors sharing M, bits,
+    group size and scale dtype; returns the list of y tensors."""
+    torch = _torch()
+    lib = load()
+    if not problems:
+        return []
+    arr = (QmvProblem * len(problems))()
+    ys, M0, sb0, dev0 = [], None, None, None
+    for i, prob in enumerate(problems):
+        x, w, s, b = prob[:4]
+        y = prob[4] if len(prob) > 4 else None
+        M, N, K = _check_packed(x, w, s, b, bits, group_size, f"mxq_qmv_grouped[{i}]")
+        if M0 is None:
+            M0, sb0, dev0 = M, _sb_code(s), x.device
+        elif M != M0 or _sb_code(s) != sb0 or x.device != dev0:
+            raise ValueError("mxq_qmv_grouped: problems must share M, scale dtype and device")
+        if y is None:
+            y = torch.empty((M, N), dtype=torch.float16, device=x.device)
+        elif y.dtype != torch.float16 or tuple(y.shape) != (M, N) or not y.is_contiguous() \
+                or y.device != x.device:
+            raise ValueError(f"mxq_qmv_grouped[{i}]: y must be a contiguous float16 [M, N] tensor")
+        arr[i] = QmvProblem(x.data_ptr(), w.data_ptr(), s.data_ptr(), b.data_ptr(), y.data_ptr(), N, K)
+        ys.append(y)
+    with torch.cuda.device(dev0):
+        st = lib.mxq_qmv_grouped(arr, len(problems), M0, bits, group_size, sb0, _stream_handle(dev0, stream))
+    _check(lib, st)
+    return ys
 
 
 def mxq_qmm(x, w, scales, biases, y=None, *, bits: int = 4, group_size: int = 64, stream=None):

@@ -6,6 +6,7 @@
 #include <mutex>
 #include <string>
 #include <unordered_set>
+#include <vector>
 
 #include "../../include/mxq.h"
 #include "mxq_internal.h"
@@ -89,6 +90,38 @@ mxq_status run_qmv(const char* who, const void* x, const uint32_t* w, const void
   return MXQ_OK;
 }
 
+// Grouped qmv over problems that all passed validation and have N, K > 0.
+mxq_status run_qmv_grouped(const char* who, const mxq_qmv_problem* pr, int count, int64_t M, int bits,
+                           int group_size, mxq_dtype sb_dtype, void* stream) {
+  mxq::DeviceInfo dev;
+  hipError_t e = mxq::device_info(&dev);
+  if (e != hipSuccess) return hip_fail(who, e);
+  int64_t kmax = 0;
+  for (int i = 0; i < count; ++i) kmax = pr[i].K > kmax ? pr[i].K : kmax;
+  if (mxq::qmv_lds_need(bits, 1, kmax) > dev.lds_per_block)
+    return fail(MXQ_ERR_UNSUPPORTED, std::string(who) + ": K too large for the activation staging buffer");
+  int mt_max = 8;
+  while (mt_max > 1 && mxq::qmv_lds_need(bits, mt_max, kmax) > dev.lds_per_block) mt_max--;
+  mxq::QmvProblem chunk[mxq::kMaxGroup];
+  for (int64_t m0 = 0; m0 < M; m0 += mt_max) {
+    const int mt = static_cast<int>((M - m0) < mt_max ? (M - m0) : mt_max);
+    for (int c0 = 0; c0 < count; c0 += mxq::kMaxGroup) {
+      const int n = (count - c0) < mxq::kMaxGroup ? (count - c0) : mxq::kMaxGroup;
+      for (int i = 0; i < n; ++i) {
+        const mxq_qmv_problem& q = pr[c0 + i];
+        chunk[i] = mxq::QmvProblem{static_cast<const uint16_t*>(q.x) + m0 * q.K, q.w,
+                                   static_cast<const uint16_t*>(q.scales),
+                                   static_cast<const uint16_t*>(q.biases),
+                                   static_cast<uint16_t*>(q.y) + m0 * q.N, q.N, q.K};
+      }
+      e = mxq::launch_qmv_group(chunk, n, bits, log2_group(group_size), sb_dtype == MXQ_BF16, dev, mt,
+                                static_cast<hipStream_t>(stream));
+      if (e != hipSuccess) return hip_fail(who, e);
+    }
+  }
+  return MXQ_OK;
+}
+
 }  // namespace
 
 namespace mxq {
@@ -163,6 +196,34 @@ mxq_status mxq_qmv(const void* x, const uint32_t* w, const void* scales, const v
     return e == hipSuccess ? MXQ_OK : hip_fail("mxq_qmv", e);
   }
   return run_qmv("mxq_qmv", x, w, scales, biases, y, M, N, K, bits, group_size, sb_dtype, stream);
+}
+
+mxq_status mxq_qmv_grouped(const mxq_qmv_problem* problems, int count, int64_t M, int bits,
+                           int group_size, mxq_dtype sb_dtype, void* stream) {
+  g_last_error.clear();
+  if (count < 0) return fail(MXQ_ERR_INVALID_ARG, "mxq_qmv_grouped: count must be >= 0");
+  if (count > 0 && !problems) return fail(MXQ_ERR_INVALID_ARG, "mxq_qmv_grouped: problems is null");
+  std::vector<mxq_qmv_problem> live;
+  for (int i = 0; i < count; ++i) {
+    const mxq_qmv_problem& q = problems[i];
+    const std::string who = "mxq_qmv_grouped[" + std::to_string(i) + "]";
+    mxq_status st = check_fused(who.c_str(), q.x, q.w, q.scales, q.biases, q.y, M, q.N, q.K, bits,
+                                group_size, sb_dtype);
+    if (st != MXQ_OK) return st;
+    if (M > 0 && q.N > 0) live.push_back(q);
+  }
+  std::vector<mxq_qmv_problem> work;
+  for (const mxq_qmv_problem& q : live) {
+    if (q.K == 0) {
+      hipError_t e = mxq::launch_zero_fill(static_cast<uint16_t*>(q.y), M * q.N, static_cast<hipStream_t>(stream));
+      if (e != hipSuccess) return hip_fail("mxq_qmv_grouped", e);
+    } else {
+      work.push_back(q);
+    }
+  }
+  if (work.empty()) return MXQ_OK;
+  return run_qmv_grouped("mxq_qmv_grouped", work.data(), static_cast<int>(work.size()), M, bits,
+                         group_size, sb_dtype, stream);
 }
 
 mxq_status mxq_qmm(const void* x, const uint32_t* w, const void* scales, const void* biases,
@@ -268,7 +329,7 @@ const char* mxq_describe(const char* op, int64_t M, int64_t N, int64_t K, int bi
     const mxq::QmvPlan p = mxq::qmv_plan(dev, N, K, bits, sb_dtype == MXQ_BF16, mt, 0);
     if (!desc.empty()) desc += "; ";
     desc += "qmv_kernel<bits=" + std::to_string(bits) + ",sb=" + sb + ",mt=" + std::to_string(mt) +
-            ",rows=" + std::to_string(p.rows) + "> grid=" + std::to_string(p.grid) +
+            ",rows=" + std::to_string(p.rows) + (p.xdirect ? ",xreg" : "") + "> grid=" + std::to_string(p.grid) +
             " block=256 lds=" + std::to_string(p.lds);
   }
   return desc.c_str();

@@ -20,6 +20,33 @@ hipError_t device_info(DeviceInfo* out);
 // Raise a kernel's dynamic-LDS limit once per (kernel, device).
 hipError_t ensure_dynamic_lds(const void* kernel, size_t bytes);
 
+// Up to kMaxGroup independent qmv problems sharing one launch (bits, group
+// size, scale dtype and the activation row count are common).  Passed by value
+// as the kernel argument: no device allocation, safe under graph capture.
+constexpr int kMaxGroup = 16;
+struct QmvBatch {
+  const uint16_t* x[kMaxGroup];
+  const uint32_t* w[kMaxGroup];
+  const uint16_t* s[kMaxGroup];
+  const uint16_t* b[kMaxGroup];
+  uint16_t* y[kMaxGroup];
+  int N[kMaxGroup];
+  int K[kMaxGroup];
+  int xvec[kMaxGroup];
+  int block_begin[kMaxGroup + 1];
+  int count;
+  int glog2;
+};
+
+struct QmvProblem {
+  const uint16_t* x;   // f16 bits [M, K] of this slice
+  const uint32_t* w;
+  const uint16_t* s;
+  const uint16_t* b;
+  uint16_t* y;         // f16 bits [M, N] of this slice
+  int64_t N, K;
+};
+
 struct QmvArgs {
   const uint16_t* x;   // f16 bits [M, K] of this slice
   const uint32_t* w;
@@ -41,12 +68,18 @@ size_t qmv_lds_need(int bits, int mt, int64_t K);
 // W per wave per step), grid size and dynamic LDS bytes.
 struct QmvPlan {
   int mt, rows, grid;
+  bool xdirect;  // activations loaded straight into registers (no LDS staging)
   size_t lds;
   const void* kernel;
 };
 QmvPlan qmv_plan(const DeviceInfo& dev, int64_t N, int64_t K, int bits, bool sb_bf16, int mt,
                  int rows_override);
+QmvPlan qmv_plan_group(const DeviceInfo& dev, const int64_t* Ns, const int64_t* Ks, int count, int bits,
+                       bool sb_bf16, int mt, int* grids);
 hipError_t launch_qmv_slice(const QmvArgs& a, const DeviceInfo& dev, int mt);
+// One launch for `count` (<= kMaxGroup) problems with a common mt (rows of x).
+hipError_t launch_qmv_group(const QmvProblem* probs, int count, int bits, int glog2, bool sb_bf16,
+                            const DeviceInfo& dev, int mt, hipStream_t stream);
 
 struct QmmArgs {
   const uint16_t* x;

@@ -57,13 +57,20 @@ struct QmvItem {
   uint16_t s[R], b[R];
 };
 
-template <int BITS, bool SB_BF16, int MT, int R>
-__global__ __launch_bounds__(256) void qmv_kernel(const uint16_t* __restrict__ x,
-                                                  const uint32_t* __restrict__ W,
-                                                  const uint16_t* __restrict__ S,
-                                                  const uint16_t* __restrict__ B,
-                                                  uint16_t* __restrict__ y, int N, int K,
-                                                  int glog2, int x_vec) {
+template <int BITS, bool SB_BF16, int MT, int R, bool XD>
+__global__ __launch_bounds__(256) void qmv_kernel(const QmvBatch batch) {
+  // This workgroup's problem: blocks [block_begin[p], block_begin[p+1]) of the
+  // grid belong to problem p (wave-uniform scalar search over <= 16 entries).
+  int p = 0;
+  while (p + 1 < batch.count && static_cast<int>(blockIdx.x) >= batch.block_begin[p + 1]) ++p;
+  const int blk = static_cast<int>(blockIdx.x) - batch.block_begin[p];
+  const int nblk = batch.block_begin[p + 1] - batch.block_begin[p];
+  const uint16_t* __restrict__ x = batch.x[p];
+  const uint32_t* __restrict__ W = batch.w[p];
+  const uint16_t* __restrict__ S = batch.s[p];
+  const uint16_t* __restrict__ B = batch.b[p];
+  uint16_t* __restrict__ y = batch.y[p];
+  const int N = batch.N[p], K = batch.K[p], x_vec = batch.xvec[p], glog2 = batch.glog2;
   constexpr int CPS = SegTraits<BITS>::kChunksPerSeg;
   constexpr int CODES = SegTraits<BITS>::kCodesPerSeg;
   constexpr int NP = (BITS == 4) ? 16 : 8;  // f16 code pairs per segment
@@ -86,7 +93,7 @@ __global__ __launch_bounds__(256) void qmv_kernel(const uint16_t* __restrict__ x
   const int waves_per_block = blockDim.x >> 6;
   const int nrb = (N + R - 1) / R;
   const int jn = (nseg + kWave - 1) / kWave;
-  const int stride = gridDim.x * waves_per_block;
+  const int stride = nblk * waves_per_block;
   const uint32_t wrow_bytes = static_cast<uint32_t>(kw) * 4u;
   const uint32_t sbrow_bytes = static_cast<uint32_t>(G) * 2u;
   const char* Wb = reinterpret_cast<const char*>(W);
@@ -110,37 +117,71 @@ __global__ __launch_bounds__(256) void qmv_kernel(const uint16_t* __restrict__ x
   };
 
   // The first item's loads go out before the x staging, to overlap the two.
-  int rb = blockIdx.x * waves_per_block + wave;
+  int rb = blk * waves_per_block + wave;
   int j = 0;
   QmvItem<R> cur, alt;
   load_item(cur, min(rb, nrb - 1), 0);
 
-  // ---- stage x (reordered) and its per-segment sums into LDS -------------
-  for (int u = threadIdx.x; u < MT * nseg; u += blockDim.x) {
-    const int m = u / nseg;
-    const int seg = u - m * nseg;
+  // ---- activations -------------------------------------------------------
+  // XD (a row fits in one segment step, M <= 2): each lane's segment of x is
+  // the same for the whole kernel, so it goes straight into registers with the
+  // first weight loads -- no LDS, no barrier.  Otherwise x is staged once per
+  // workgroup in LDS, reordered, with its per-segment sums.
+  auto load_x_global = [&](int m, int seg, u4 (&v)[CPS]) {
     const uint16_t* xp = x + static_cast<size_t>(m) * K + seg * CODES;
-    float sum = 0.0f;
 #pragma unroll
     for (int c = 0; c < CPS; ++c) {
-      u4 v;
       if (x_vec) {
-        v = *reinterpret_cast<const u4*>(xp + 8 * c);
+        v[c] = *reinterpret_cast<const u4*>(xp + 8 * c);
       } else {
         uint32_t t[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           t[i] = static_cast<uint32_t>(xp[8 * c + 2 * i]) |
                  (static_cast<uint32_t>(xp[8 * c + 2 * i + 1]) << 16);
-        v = u4{t[0], t[1], t[2], t[3]};
+        v[c] = u4{t[0], t[1], t[2], t[3]};
       }
-      sum += sum8_f32(v);
-      xs[(m * CPS + c) * nseg + seg] = (BITS == 4) ? perm_x_w4(v) : perm_x_w8(v);
     }
-    xsum[m * nseg + seg] = sum;
+  };
+  constexpr int NPX = (BITS == 4) ? 16 : 8;
+  uint32_t xreg[XD ? MT : 1][NPX];
+  float xsreg[XD ? MT : 1];
+  if constexpr (XD) {
+    const int seg = min(lane, nseg - 1);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      u4 v[CPS];
+      load_x_global(m, seg, v);
+      float sum = 0.0f;
+#pragma unroll
+      for (int c = 0; c < CPS; ++c) {
+        sum += sum8_f32(v[c]);
+        const u4 p = (BITS == 4) ? perm_x_w4(v[c]) : perm_x_w8(v[c]);
+        xreg[m][4 * c] = p.x;
+        xreg[m][4 * c + 1] = p.y;
+        xreg[m][4 * c + 2] = p.z;
+        xreg[m][4 * c + 3] = p.w;
+      }
+      xsreg[m] = sum;
+    }
+    if (rb >= nrb) return;
+  } else {
+    for (int u = threadIdx.x; u < MT * nseg; u += blockDim.x) {
+      const int m = u / nseg;
+      const int seg = u - m * nseg;
+      u4 v[CPS];
+      load_x_global(m, seg, v);
+      float sum = 0.0f;
+#pragma unroll
+      for (int c = 0; c < CPS; ++c) {
+        sum += sum8_f32(v[c]);
+        xs[(m * CPS + c) * nseg + seg] = (BITS == 4) ? perm_x_w4(v[c]) : perm_x_w8(v[c]);
+      }
+      xsum[m * nseg + seg] = sum;
+    }
+    __syncthreads();
+    if (rb >= nrb) return;  // no block-level barrier follows
   }
-  __syncthreads();
-  if (rb >= nrb) return;  // no block-level barrier follows
 
   const uint32_t magic = kMagic;
   float acc[R][MT];
@@ -185,6 +226,11 @@ __global__ __launch_bounds__(256) void qmv_kernel(const uint16_t* __restrict__ x
     }
   };
   auto load_x = [&](int m, int seg, uint32_t (&xp)[NP]) {
+    if constexpr (XD) {
+#pragma unroll
+      for (int p = 0; p < NP; ++p) xp[p] = xreg[m][p];
+      return;
+    }
 #pragma unroll
     for (int c = 0; c < CPS; ++c) {
       const u4 xv = xs[(m * CPS + c) * nseg + seg];
@@ -211,7 +257,7 @@ __global__ __launch_bounds__(256) void qmv_kernel(const uint16_t* __restrict__ x
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
         load_x(m, seg, xp[m]);
-        xsm[m] = xsum[m * nseg + seg];
+        xsm[m] = XD ? xsreg[m] : xsum[m * nseg + seg];
       }
 #pragma unroll
       for (int r = 0; r < R; ++r) {
@@ -234,7 +280,7 @@ __global__ __launch_bounds__(256) void qmv_kernel(const uint16_t* __restrict__ x
       for (int m = 0; m < MT; ++m) {
         uint32_t xp[NP];
         load_x(m, seg, xp);
-        const float xsm = xsum[m * nseg + seg];
+        const float xsm = XD ? xsreg[XD ? m : 0] : xsum[m * nseg + seg];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           const float t = __builtin_fmaf(sb_to_f32<SB_BF16>(it.b[r]), xsm,
@@ -291,7 +337,9 @@ __global__ __launch_bounds__(256) void qmv_kernel(const uint16_t* __restrict__ x
 
   // Ping-pong over two item buffers: the next item's loads are in flight while
   // the current item is computed, and no register copy of in-flight data is
-  // ever made (a copy would force a wait for those loads).
+  // ever made (a copy would force a wait for those loads).  Loads are never
+  // conditional: past the last item a wave re-reads the item it just loaded
+  // (a cache hit), which keeps the compiler's load counters exact.
   auto advance = [&](int& rbv, int& jv) {
     if (++jv == jn) {
       jv = 0;
@@ -302,7 +350,7 @@ __global__ __launch_bounds__(256) void qmv_kernel(const uint16_t* __restrict__ x
     int rb2 = rb, j2 = j;
     advance(rb2, j2);
     bool more = rb2 < nrb;
-    load_item(alt, more ? rb2 : rb, more ? j2 : j);  // past the end: harmless reload
+    load_item(alt, more ? rb2 : rb, more ? j2 : j);
     __builtin_amdgcn_sched_barrier(0);  // keep the whole load block ahead of the compute
     step(cur, rb, j, j2 == 0);
     if (!more) break;
@@ -326,29 +374,33 @@ __global__ __launch_bounds__(256) void qmv_kernel(const uint16_t* __restrict__ x
 namespace {
 
 template <int BITS, bool SB_BF16, int R>
-const void* qmv_ptr_mt(int mt) {
+const void* qmv_ptr_mt(int mt, bool xd) {
+  if (xd) {
+    if (mt == 1) return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 1, R, true>);
+    return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 2, R, true>);
+  }
   switch (mt) {
-    case 1: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 1, R>);
-    case 2: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 2, R>);
-    case 3: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 3, R>);
-    case 4: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 4, R>);
-    case 5: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 5, R>);
-    case 6: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 6, R>);
-    case 7: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 7, R>);
-    default: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 8, R>);
+    case 1: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 1, R, false>);
+    case 2: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 2, R, false>);
+    case 3: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 3, R, false>);
+    case 4: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 4, R, false>);
+    case 5: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 5, R, false>);
+    case 6: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 6, R, false>);
+    case 7: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 7, R, false>);
+    default: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 8, R, false>);
   }
 }
 
 template <int BITS, bool SB_BF16>
-const void* qmv_ptr_r(int mt, int R) {
-  if (R == 4) return qmv_ptr_mt<BITS, SB_BF16, 4>(mt);
-  if (R == 2) return qmv_ptr_mt<BITS, SB_BF16, 2>(mt);
-  return qmv_ptr_mt<BITS, SB_BF16, 1>(mt);
+const void* qmv_ptr_r(int mt, int R, bool xd) {
+  if (R == 4) return qmv_ptr_mt<BITS, SB_BF16, 4>(mt, xd);
+  if (R == 2) return qmv_ptr_mt<BITS, SB_BF16, 2>(mt, xd);
+  return qmv_ptr_mt<BITS, SB_BF16, 1>(mt, xd);
 }
 
-const void* qmv_kernel_ptr(int bits, bool bf16, int mt, int R) {
-  if (bits == 4) return bf16 ? qmv_ptr_r<4, true>(mt, R) : qmv_ptr_r<4, false>(mt, R);
-  return bf16 ? qmv_ptr_r<8, true>(mt, R) : qmv_ptr_r<8, false>(mt, R);
+const void* qmv_kernel_ptr(int bits, bool bf16, int mt, int R, bool xd) {
+  if (bits == 4) return bf16 ? qmv_ptr_r<4, true>(mt, R, xd) : qmv_ptr_r<4, false>(mt, R, xd);
+  return bf16 ? qmv_ptr_r<8, true>(mt, R, xd) : qmv_ptr_r<8, false>(mt, R, xd);
 }
 
 // Rows of W per wave step and the grid.  A large N streams best with about
@@ -358,20 +410,13 @@ const void* qmv_kernel_ptr(int bits, bool bf16, int mt, int R) {
 // spans several segment steps) and 2 workgroups of 4 waves per CU, each wave
 // holding two items in flight.  A small N cannot fill the chip anyway: one
 // row per wave step and as many waves as the rows allow.
-struct RowsGrid {
-  int rows;
-  int blocks_per_cu_cap;  // 0: occupancy-limited
-};
+bool qmv_large(const DeviceInfo& dev, int64_t N) { return N >= static_cast<int64_t>(dev.num_cu) * 64; }
 
-RowsGrid qmv_pick_rows(const DeviceInfo& dev, int64_t N, int64_t K, int bits, int mt) {
-  const int64_t nseg = K * bits / 128;
-  RowsGrid rg{1, 0};
-  if (N >= static_cast<int64_t>(dev.num_cu) * 64) {
-    rg.rows = nseg <= kWave ? 4 : 2;
-    rg.blocks_per_cu_cap = 2;
-  }
-  while (rg.rows > 1 && rg.rows * mt > 16) rg.rows /= 2;  // bound live accumulators and registers
-  return rg;
+int qmv_pick_rows(const DeviceInfo& dev, int64_t N, int64_t K, int bits, int mt) {
+  int rows = 1;
+  if (qmv_large(dev, N)) rows = (K * bits / 128 <= kWave) ? 4 : 2;
+  while (rows > 1 && rows * mt > 16) rows /= 2;  // bound live accumulators and registers
+  return rows;
 }
 
 std::mutex g_occ_mu;
@@ -401,38 +446,85 @@ size_t qmv_lds_need(int bits, int mt, int64_t K) {
                    : qmv_lds_bytes<8>(mt, static_cast<int>(K));
 }
 
-QmvPlan qmv_plan(const DeviceInfo& dev, int64_t N, int64_t K, int bits, bool sb_bf16, int mt,
-                 int rows_override) {
+// One instantiation serves every problem of a group: R from the problem with
+// the most rows, activations in registers only if every row fits in one
+// segment step, LDS sized for the largest K.  Each problem gets its own block
+// range, sized as it would be alone.
+QmvPlan qmv_plan_group(const DeviceInfo& dev, const int64_t* Ns, const int64_t* Ks, int count, int bits,
+                       bool sb_bf16, int mt, int* grids) {
   QmvPlan p{};
   p.mt = mt;
-  const RowsGrid rg = qmv_pick_rows(dev, N, K, bits, mt);
-  p.rows = rows_override > 0 ? rows_override : rg.rows;
-  p.lds = qmv_lds_need(bits, mt, K);
-  p.kernel = qmv_kernel_ptr(bits, sb_bf16, mt, p.rows);
+  int big = 0;
+  bool xd = mt <= 2;
+  size_t lds = 0;
+  for (int i = 0; i < count; ++i) {
+    if (Ns[i] > Ns[big]) big = i;
+    xd = xd && (Ks[i] * bits / 128 <= kWave);
+    const size_t l = qmv_lds_need(bits, mt, Ks[i]);
+    lds = l > lds ? l : lds;
+  }
+  p.rows = qmv_pick_rows(dev, Ns[big], Ks[big], bits, mt);
+  p.xdirect = xd;
+  p.lds = xd ? 0 : lds;
+  p.kernel = qmv_kernel_ptr(bits, sb_bf16, mt, p.rows, p.xdirect);
   if (p.lds > 65536 && ensure_dynamic_lds(p.kernel, p.lds) != hipSuccess) (void)hipGetLastError();
-  const int64_t nrb = (N + p.rows - 1) / p.rows;
-  const int64_t blocks_needed = (nrb + 3) / 4;
-  int per_cu = blocks_per_cu(dev, p.kernel, p.lds);
-  if (rg.blocks_per_cu_cap > 0 && per_cu > rg.blocks_per_cu_cap) per_cu = rg.blocks_per_cu_cap;
-  const int64_t cap = static_cast<int64_t>(dev.num_cu) * per_cu;
-  p.grid = static_cast<int>(blocks_needed < cap ? blocks_needed : cap);
+  const int occ = blocks_per_cu(dev, p.kernel, p.lds);
+  p.grid = 0;
+  for (int i = 0; i < count; ++i) {
+    const int64_t nrb = (Ns[i] + p.rows - 1) / p.rows;
+    const int64_t blocks_needed = (nrb + 3) / 4;
+    const int per_cu = qmv_large(dev, Ns[i]) && occ > 2 ? 2 : occ;
+    const int64_t cap = static_cast<int64_t>(dev.num_cu) * per_cu;
+    const int g = static_cast<int>(blocks_needed < cap ? blocks_needed : cap);
+    if (grids) grids[i] = g;
+    p.grid += g;
+  }
   return p;
 }
 
-hipError_t launch_qmv_slice(const QmvArgs& a, const DeviceInfo& dev, int mt) {
-  const QmvPlan p = qmv_plan(dev, a.N, a.K, a.bits, a.sb_bf16, mt, a.rows_per_wave);
+QmvPlan qmv_plan(const DeviceInfo& dev, int64_t N, int64_t K, int bits, bool sb_bf16, int mt,
+                 int rows_override) {
+  (void)rows_override;
+  return qmv_plan_group(dev, &N, &K, 1, bits, sb_bf16, mt, nullptr);
+}
+
+hipError_t launch_qmv_group(const QmvProblem* probs, int count, int bits, int glog2, bool sb_bf16,
+                            const DeviceInfo& dev, int mt, hipStream_t stream) {
+  int64_t Ns[kMaxGroup], Ks[kMaxGroup];
+  int grids[kMaxGroup];
+  for (int i = 0; i < count; ++i) {
+    Ns[i] = probs[i].N;
+    Ks[i] = probs[i].K;
+  }
+  const QmvPlan p = qmv_plan_group(dev, Ns, Ks, count, bits, sb_bf16, mt, grids);
   if (p.lds > 65536) {
     hipError_t e = ensure_dynamic_lds(p.kernel, p.lds);
     if (e != hipSuccess) return e;
   }
-  const uint16_t* x = a.x;
-  const uint32_t* w = a.w;
-  const uint16_t* s = a.s;
-  const uint16_t* b = a.b;
-  uint16_t* y = a.y;
-  int N = static_cast<int>(a.N), K = static_cast<int>(a.K), glog2 = a.glog2, xv = a.x_vec;
-  void* args[] = {&x, &w, &s, &b, &y, &N, &K, &glog2, &xv};
-  return hipLaunchKernel(p.kernel, dim3(p.grid), dim3(256), args, p.lds, a.stream);
+  QmvBatch batch{};
+  batch.count = count;
+  batch.glog2 = glog2;
+  int begin = 0;
+  for (int i = 0; i < count; ++i) {
+    batch.x[i] = probs[i].x;
+    batch.w[i] = probs[i].w;
+    batch.s[i] = probs[i].s;
+    batch.b[i] = probs[i].b;
+    batch.y[i] = probs[i].y;
+    batch.N[i] = static_cast<int>(probs[i].N);
+    batch.K[i] = static_cast<int>(probs[i].K);
+    batch.xvec[i] = (reinterpret_cast<uintptr_t>(probs[i].x) & 15u) == 0 ? 1 : 0;
+    batch.block_begin[i] = begin;
+    begin += grids[i];
+  }
+  batch.block_begin[count] = begin;
+  void* args[] = {&batch};
+  return hipLaunchKernel(p.kernel, dim3(begin), dim3(256), args, p.lds, stream);
+}
+
+hipError_t launch_qmv_slice(const QmvArgs& a, const DeviceInfo& dev, int mt) {
+  QmvProblem pr{a.x, a.w, a.s, a.b, a.y, a.N, a.K};
+  return launch_qmv_group(&pr, 1, a.bits, a.glog2, a.sb_bf16, dev, mt, a.stream);
 }
 
 }  // namespace mxq

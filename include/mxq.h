@@ -89,6 +89,39 @@ mxq_status mxq_qmv(const void* x, const uint32_t* w, const void* scales, const v
                    mxq_dtype sb_dtype, void* stream);
 
 /*
+ * One problem of a grouped qmv call: y = x * dequant(w)^T with the layouts
+ * above.  Pointers are device pointers; N and K are this problem's sizes.
+ */
+typedef struct mxq_qmv_problem {
+  const void* x;          /* f16 [M, K] */
+  const uint32_t* w;      /* u32 [N, K*bits/32], 16-byte aligned */
+  const void* scales;     /* f16|bf16 [N, K/group_size] */
+  const void* biases;     /* f16|bf16 [N, K/group_size] */
+  void* y;                /* f16 [M, N] */
+  int64_t N;
+  int64_t K;
+} mxq_qmv_problem;
+
+/* Problems per kernel launch of mxq_qmv_grouped (larger counts use several launches). */
+#define MXQ_MAX_GROUP 16
+
+/*
+ * mxq_qmv_grouped -- several independent mxq_qmv problems in one kernel launch.
+ *
+ * Cuts the launches per decode step (mlxcel epic #570, "The measured fusion
+ * gate": ~678 dispatches per step; mlxcel #574, "Unblock criteria": the
+ * dispatch count materially reduced).  All problems share M, bits, group_size
+ * and sb_dtype; each has its own x, w, scales, biases, y, N and K (e.g. the
+ * q, k and v projections of one layer, or gate and up).  `problems` is a host
+ * array of `count` entries, read during the call only.  Results satisfy the
+ * mxq_qmv contract (same tolerance, deterministic); they need not be
+ * bit-identical to separate mxq_qmv calls.  Every problem is validated as in
+ * mxq_qmv before anything is launched.
+ */
+mxq_status mxq_qmv_grouped(const mxq_qmv_problem* problems, int count, int64_t M, int bits,
+                           int group_size, mxq_dtype sb_dtype, void* stream);
+
+/*
  * mxq_qmm -- the same operation tuned for prefill (M >= 64): codes are
  * staged through LDS as exact f16 integers and contracted with f16 MFMA
  * (f32 accumulation); each group's partial products are then scaled by the

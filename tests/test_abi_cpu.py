@@ -166,3 +166,22 @@ def test_product_path_does_not_import_oracle():
             if f.endswith((".py", ".hip", ".cpp", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.replace("mlxcel", ""), f
+
+
+def test_grouped_validation():
+    lib = mxq.load()
+    P = FAKE
+    Q = mxq.QmvProblem
+    good = Q(P, P, P, P, P, 4, 64)
+    arr = (Q * 3)(good, good, Q(P, P + 4, P, P, P, 4, 64))
+    assert lib.mxq_qmv_grouped(arr, 3, 1, 4, 64, 0, None) == mxq.MXQ_ERR_MISALIGNED
+    assert b"mxq_qmv_grouped[2]" in lib.mxq_last_error()
+    arr = (Q * 2)(good, Q(P, P, P, P, P, 4, 96))
+    assert lib.mxq_qmv_grouped(arr, 2, 1, 4, 64, 0, None) == mxq.MXQ_ERR_UNSUPPORTED
+    arr = (Q * 1)(good)
+    assert lib.mxq_qmv_grouped(arr, 1, 1, 5, 64, 0, None) == mxq.MXQ_ERR_UNSUPPORTED
+    assert lib.mxq_qmv_grouped(arr, -1, 1, 4, 64, 0, None) == mxq.MXQ_ERR_INVALID_ARG
+    assert lib.mxq_qmv_grouped(None, 2, 1, 4, 64, 0, None) == mxq.MXQ_ERR_INVALID_ARG
+    assert lib.mxq_qmv_grouped(None, 0, 1, 4, 64, 0, None) == mxq.MXQ_OK
+    empty = (Q * 2)(Q(None, None, None, None, None, 0, 64), Q(None, None, None, None, None, 0, 0))
+    assert lib.mxq_qmv_grouped(empty, 2, 1, 4, 64, 0, None) == mxq.MXQ_OK

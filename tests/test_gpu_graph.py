@@ -1,0 +1,73 @@
+"""libmxq launches captured in a HIP graph: every replay equals the eager result.
+
+The graph is replayed several times with new inputs copied into the captured
+buffers between replays (eager work and synchronisation in between), and each
+replay is compared bit for bit with an eager call on the same inputs.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import dequant_matmul_qmv_amd as mxq
+import synth
+from tests.gpu_util import note, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def test_graph_replay_matches_eager():
+    dev = "cuda:0"
+    pv = synth.make_problem(1, 3000, 2048, 4, 64, "f16", seed=61)
+    pm = synth.make_problem(80, 500, 1024, 8, 64, "bf16", seed=62)
+    xv, wv, sv, bv = to_dev(pv)
+    xm, wm, sm, bm = to_dev(pm)
+    yv = torch.empty((1, 3000), dtype=torch.float16, device=dev)
+    ym = torch.empty((80, 500), dtype=torch.float16, device=dev)
+    dq = torch.empty((500, 1024), dtype=torch.float32, device=dev)
+
+    def work():
+        mxq.mxq_qmv(xv, wv, sv, bv, yv, bits=4)
+        mxq.mxq_qmm(xm, wm, sm, bm, ym, bits=8)
+        mxq.mxq_dequant(wm, sm, bm, dq, bits=8)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        work()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    note("graph capture of qmv + qmm + dequant")
+    with torch.cuda.graph(g):
+        work()
+    torch.cuda.synchronize()
+
+    rng = np.random.default_rng(5)
+    for rep in range(4):
+        new_xv = torch.from_numpy(rng.standard_normal((1, 2048)).astype(np.float16)).to(dev)
+        new_xm = torch.from_numpy(rng.standard_normal((80, 1024)).astype(np.float16)).to(dev)
+        xv.copy_(new_xv)
+        xm.copy_(new_xm)
+        torch.cuda.synchronize()
+        note(f"graph replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        got_v, got_m, got_d = yv.clone(), ym.clone(), dq.clone()
+        ev = mxq.mxq_qmv(new_xv, wv, sv, bv, bits=4)
+        em = mxq.mxq_qmm(new_xm, wm, sm, bm, bits=8)
+        ed = mxq.mxq_dequant(wm, sm, bm, bits=8)
+        torch.cuda.synchronize()
+        assert torch.equal(got_v.view(torch.int16), ev.view(torch.int16)), rep
+        assert torch.equal(got_m.view(torch.int16), em.view(torch.int16)), rep
+        assert torch.equal(got_d.view(torch.int32), ed.view(torch.int32)), rep
+
+
+def test_describe_on_device():
+    d = mxq.mxq_describe("qmv", 1, 128256, 2048, 4, 64, "f16")
+    assert d.startswith("qmv_kernel<bits=4,sb=f16,mt=1,rows=4"), d
+    d = mxq.mxq_describe("qmv", 20, 100, 2048, 8, 64, "bf16")
+    assert d.count("qmv_kernel") == 3, d          # M=20 -> slices of 8, 8, 4
+    d = mxq.mxq_describe("qmm", 512, 8192, 2048, 4, 64, "f16")
+    assert d.startswith("qmm_kernel<bits=4,sb=f16,gs=64,tile=64x128>"), d
+    assert mxq.mxq_describe("qmm", 4, 100, 2048, 4, 64, "f16").startswith("qmv_kernel")

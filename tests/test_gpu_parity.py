@@ -228,13 +228,14 @@ def test_empty_and_k_zero():
         assert torch.equal(y.cpu(), torch.zeros((3, 4), dtype=torch.float16))
 
 
-def test_nonzero_stream_and_offsets():
-    """Work enqueued on a side stream; x passed as an unaligned slice (scalar staging)."""
-    p = synth.make_problem(3, 300, 1024, 4, 64, "f16", seed=5)
+@pytest.mark.parametrize("M", [1, 3])
+def test_nonzero_stream_and_offsets(M):
+    """Work enqueued on a side stream; x passed as an unaligned slice (scalar loads)."""
+    p = synth.make_problem(M, 300, 1024, 4, 64, "f16", seed=5)
     x, w, s, b = to_dev(p)
-    xbig = torch.zeros((3 * 1024 + 1,), dtype=torch.float16, device="cuda:0")
+    xbig = torch.zeros((M * 1024 + 1,), dtype=torch.float16, device="cuda:0")
     xbig[1:].copy_(x.reshape(-1))
-    xu = xbig[1:].view(3, 1024)
+    xu = xbig[1:].view(M, 1024)
     st = torch.cuda.Stream()
     note("side stream + unaligned x")
     with torch.cuda.stream(st):
@@ -251,3 +252,36 @@ def test_misaligned_w_rejected_on_device():
     with pytest.raises(mxq.MxqError) as e:
         mxq.mxq_qmv(x, wv, s, b, bits=4)
     assert e.value.status == mxq.MXQ_ERR_MISALIGNED
+
+
+@pytest.mark.parametrize("M", [1, 3, 12])
+def test_grouped_qmv(M):
+    """Grouped launches: mixed N and K (one launch stages x in LDS for K=8192),
+    more problems than one launch holds, and empty / K=0 problems."""
+    specs = [(2048, 2048), (512, 2048), (1023, 2048), (8192, 2048), (2050, 8192), (7, 64)] * 3 + [(5, 128), (3, 256)]
+    probs, dev_probs = [], []
+    for i, (N, K) in enumerate(specs):
+        p = synth.make_problem(M, N, K, 4, 64, "bf16" if M == 3 else "f16", seed=900 + 17 * i + M)
+        probs.append(p)
+        dev_probs.append(to_dev(p))
+    note(f"grouped qmv M={M} count={len(specs)}")
+    ys = mxq.mxq_qmv_grouped(dev_probs, bits=4)
+    torch.cuda.synchronize()
+    assert len(ys) == len(specs)
+    for i, (p, y) in enumerate(zip(probs, ys)):
+        assert_close(y.cpu().numpy(), _ref(p), f"grouped[{i}] N={p.N} K={p.K}")
+
+
+def test_grouped_qmv_empty_and_k_zero():
+    dev = "cuda:0"
+    p = synth.make_problem(2, 300, 1024, 8, 64, "f16", seed=3)
+    x, w, s, b = to_dev(p)
+    x0 = torch.zeros((2, 0), dtype=torch.float16, device=dev)
+    w0 = torch.zeros((4, 0), dtype=torch.int32, device=dev)
+    s0 = torch.zeros((4, 0), dtype=torch.float16, device=dev)
+    y0 = torch.full((2, 4), 3.0, dtype=torch.float16, device=dev)
+    note("grouped with a K=0 problem")
+    ys = mxq.mxq_qmv_grouped([(x, w, s, b), (x0, w0, s0, s0, y0)], bits=8)
+    torch.cuda.synchronize()
+    assert_close(ys[0].cpu().numpy(), _ref(p), "grouped K>0")
+    assert torch.equal(y0.cpu(), torch.zeros((2, 4), dtype=torch.float16))
