@@ -102,19 +102,28 @@ __global__ __launch_bounds__(256) void qmv_kernel(const QmvBatch batch) {
 
   // Loads are unconditional and branch-free (indices clamped into range) so the
   // compiler's load counters stay exact: a conditional load would make it wait
-  // for every outstanding load, including the prefetched ones.
-  auto load_item = [&](QmvItem<R>& it, int rbl, int jl) {
+  // for every outstanding load, including the prefetched ones.  Past a wave's
+  // last item the loads are dummies aimed at the activation row (a few KiB,
+  // cache-resident) by a wave-uniform select of the base pointers: with row 0
+  // every offset ends within K*BITS/8 <= 2*K bytes, the row's size, and the
+  // 16-byte loads start from x rounded down to 16 bytes (same page as x).
+  const char* Xb = reinterpret_cast<const char*>(x);
+  const char* Xw = Xb - (reinterpret_cast<uintptr_t>(x) & 15u);
+  auto load_item = [&](QmvItem<R>& it, int rbl, int jl, bool dummy) {
     const int seg = min(lane + jl * kWave, nseg - 1);
     const uint32_t wl = static_cast<uint32_t>(seg) * 16u;
     const uint32_t sl = static_cast<uint32_t>((seg * CODES) >> glog2) * 2u;
+    const char* wbase = dummy ? Xw : Wb;
+    const char* sbase = dummy ? Xb : Sb;
+    const char* bbase = dummy ? Xb : Bb;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const uint32_t row = static_cast<uint32_t>(min(rbl * R + r, N - 1));  // tail rows re-read the last row; never stored
+      const uint32_t row = dummy ? 0u : static_cast<uint32_t>(min(rbl * R + r, N - 1));  // tail rows re-read the last row; never stored
       // W, scales and biases are each read exactly once: non-temporal loads keep
       // them from displacing reusable lines (measured ~7% faster on lm_head)
-      it.w[r] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(Wb + (row * wrow_bytes + wl)));
-      it.s[r] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(Sb + (row * sbrow_bytes + sl)));
-      it.b[r] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(Bb + (row * sbrow_bytes + sl)));
+      it.w[r] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(wbase + (row * wrow_bytes + wl)));
+      it.s[r] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(sbase + (row * sbrow_bytes + sl)));
+      it.b[r] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(bbase + (row * sbrow_bytes + sl)));
     }
   };
 
@@ -122,7 +131,7 @@ __global__ __launch_bounds__(256) void qmv_kernel(const QmvBatch batch) {
   int rb = blk * waves_per_block + wave;
   int j = 0;
   QmvItem<R> cur, alt;
-  load_item(cur, min(rb, nrb - 1), 0);
+  load_item(cur, min(rb, nrb - 1), 0, false);
 
   // ---- activations -------------------------------------------------------
   // XD (a row fits in one segment step, M <= 2): each lane's segment of x is
@@ -340,33 +349,34 @@ __global__ __launch_bounds__(256) void qmv_kernel(const QmvBatch batch) {
   // Ping-pong over two item buffers: the next item's loads are in flight while
   // the current item is computed, and no register copy of in-flight data is
   // ever made (a copy would force a wait for those loads).  Loads are never
-  // conditional: past the last item a wave re-reads the item it just loaded
-  // (a cache hit), which keeps the compiler's load counters exact.
+  // conditional: the one load past a wave's last item (even item count) is a
+  // dummy of load_item, which keeps the compiler's load counters exact.  The
+  // loop has a single exit: with two exits the compiler's wait analysis merges
+  // them into the loop header and makes every iteration wait for the prefetch.
   auto advance = [&](int& rbv, int& jv) {
     if (++jv == jn) {
       jv = 0;
       rbv += stride;
     }
   };
-  while (true) {
-    int rb2 = rb, j2 = j;
-    advance(rb2, j2);
-    bool more = rb2 < nrb;
-    load_item(alt, more ? rb2 : rb, more ? j2 : j);
+  const int n_items = ((nrb - 1 - rb) / stride + 1) * jn;  // this wave's items, >= 1
+  int rb2 = rb, j2 = j;
+  int i = 0;  // index of the item held in cur
+  for (; i + 1 < n_items; i += 2) {
+    advance(rb2, j2);  // item i + 1 exists
+    load_item(alt, rb2, j2, false);
     __builtin_amdgcn_sched_barrier(0);  // keep the whole load block ahead of the compute
     step(cur, rb, j, j2 == 0);
-    if (!more) break;
     rb = rb2;
     j = j2;
-    advance(rb2, j2);
-    more = rb2 < nrb;
-    load_item(cur, more ? rb2 : rb, more ? j2 : j);
+    advance(rb2, j2);  // item i + 2, a dummy past the end
+    load_item(cur, rb2, j2, i + 2 >= n_items);
     __builtin_amdgcn_sched_barrier(0);
     step(alt, rb, j, j2 == 0);
-    if (!more) break;
     rb = rb2;
     j = j2;
   }
+  if (i < n_items) step(cur, rb, j, true);  // odd count: the last item, which ends its row block
 }
 
 // ---------------------------------------------------------------------------
