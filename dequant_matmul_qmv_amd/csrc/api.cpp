@@ -315,10 +315,12 @@ const char* mxq_describe(const char* op, int64_t M, int64_t N, int64_t K, int bi
   const char* sb = sb_dtype == MXQ_BF16 ? "bf16" : "f16";
   const bool mfma = o == "qmm" && M > 8 && K % 64 == 0;
   if (mfma) {
-    const int64_t tiles = ((M + mxq::kQmmTileM - 1) / mxq::kQmmTileM) * ((N + mxq::kQmmTileN - 1) / mxq::kQmmTileN);
+    const mxq::QmmTile tl = mxq::qmm_pick_tile(M, N, dev);
+    const int64_t bm = 64 * tl.mb, bn = 64 * tl.nb;
+    const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
     desc = "qmm_kernel<bits=" + std::to_string(bits) + ",sb=" + sb + ",gs=" + std::to_string(group_size) +
-           ",tile=" + std::to_string(mxq::kQmmTileM) + "x" + std::to_string(mxq::kQmmTileN) +
-           "> grid=" + std::to_string(tiles) + " block=512";
+           ",tile=" + std::to_string(bm) + "x" + std::to_string(bn) + "> grid=" + std::to_string(tiles) +
+           " block=512";
     return desc.c_str();
   }
   int mt_max = 8;

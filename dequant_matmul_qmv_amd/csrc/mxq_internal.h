@@ -95,7 +95,11 @@ struct QmmArgs {
 };
 
 hipError_t launch_qmm(const QmmArgs& a, const DeviceInfo& dev);
-constexpr int kQmmTileM = 64, kQmmTileN = 128;
+// MFMA blocks (32 x 32) per wave along M and N; the tile is (64*mb) x (64*nb).
+struct QmmTile {
+  int mb, nb;
+};
+QmmTile qmm_pick_tile(int64_t M, int64_t N, const DeviceInfo& dev);
 
 struct DequantArgs {
   const uint32_t* w;

@@ -10,51 +10,152 @@
 // costs ~2^-12 relative per weight, which over K = 8192 breaks the
 // 2e-3 (1 + |y|) tolerance.  Codes (0..255) and x are exact in f16 and their
 // products exact in f32, so P_g comes out of the MFMA with f32 accumulation
-// only, and scale and bias are applied per group in f32.
+// only; the scale is applied per group in f32 on the VALU.
 //
-// Tiling: a workgroup owns a BM x BN tile of y and walks K in stages of 64
-// codes.  Per stage, x[BM x 64] (reordered into the unpack's pair order) and
-// the unpacked codes q[BN x 64] go to LDS (double-buffered, one barrier per
-// stage) with a padded row stride (144 B, so the MFMA operand reads of 32
-// rows hit distinct banks); global loads run two stages ahead in registers.
-// Each wave computes its sub-tile as 32 x 32 blocks of v_mfma_f32_32x32x16_f16
-// into per-group accumulators P; at each group's end the VALU folds P into
-// the output accumulators with the group's f32 scale, and every two groups
-// the bias term sum_g b[n,g] X_g[m] goes through the matrix cores as one exact
-// f32 v_mfma_f32_32x32x2_f32 (X_g in f32 from LDS, b widened to f32).  Tiles
-// are assigned so that consecutive tiles on one XCD (dispatch is round-robin
-// over the 8 XCDs) share the same slice of W, for L2 reuse.
+// The bias term sum_g b[n,g] X_g[m] is itself a small GEMM over the group
+// index, run on the matrix cores every 16 groups as bf16 MFMAs with K = 16
+// groups: X_g (f32) is split exactly into three bf16 parts (24 bits), b is
+// exact in bf16 (bf16 scales) or split exactly into two bf16 parts (f16
+// scales), and the products that matter at f32 precision are accumulated
+// straight into the output accumulators.  That costs 3 or 5 MFMAs per 16
+// groups instead of one f32 operation per output per group.
+//
+// Measured on this part: VALU and MFMA work of one SIMD do not overlap (their
+// times add), a 32x32x16 f16 MFMA issues every 32 cycles given two independent
+// accumulators, and LDS reads run at ~150 B/clk per CU.  So the kernel keeps
+// VALU work per MFMA small and gives each wave a 64 x 64 sub-tile (2 x 2 MFMA
+// blocks, 32 flop per LDS byte) where the tile count allows.
+//
+// Tiling: a workgroup of 4 waves (2 x 2) owns a BM x BN tile of y and walks K
+// in stages of 64 codes.  Per stage, x[BM x 64] (reordered into the unpack's
+// pair order) and the unpacked codes q[BN x 64] go to LDS (double-buffered,
+// one barrier per stage) with a padded row stride (144 B, so the MFMA operand
+// reads of 32 rows hit distinct banks); the per-group x sums, scales and
+// biases go to LDS rings of 32 groups.  Global loads run two stages ahead in
+// registers and are never conditional (rows and stages clamped), which keeps
+// the compiler's load counters exact.  Tiles are assigned so that consecutive
+// tiles on one XCD (dispatch is round-robin over the 8 XCDs) share a slice
+// of W, for L2 reuse.
+#include <type_traits>
+
 #include "mxq_device.h"
 #include "mxq_internal.h"
 
 namespace mxq {
 
 namespace {
-constexpr int KT = 64;        // codes per stage
-constexpr int LDK = KT + 8;   // padded LDS row stride in halves (144 bytes)
+constexpr int KT = 64;            // codes per stage
+constexpr int LDK = KT;           // LDS row of the x / code tiles: 64 halves (128 B), 16-byte pieces XOR-swizzled
+constexpr int RING = 24;          // groups held by the x-sum / scale / bias rings (a bias block + lookahead)
+constexpr int XGS = RING + 4;     // x-sum ring row stride in floats (112 B)
+constexpr int SBS = RING + 4;     // scale / bias ring row stride in halves (56 B: rows on distinct banks)
+constexpr int BIAS_BLOCK = 16;    // groups per bias MFMA (its K)
+
+// Position of 16-byte piece c (8 halves) within LDS row r: rows are 128 B, so
+// without the XOR the 32 rows an MFMA operand read touches would share banks.
+__device__ __forceinline__ int swz(int r, int c) { return ((c ^ (r & 7)) << 3); }
+
+typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ bf8 as_bf8(const u4& v) { return __builtin_bit_cast(bf8, v); }
+__device__ __forceinline__ h8 as_h8(const u4& v) { return __builtin_bit_cast(h8, v); }
+
+// upper halves of two f32 bit patterns -> one packed pair of bf16 (a low, b high)
+__device__ __forceinline__ uint32_t pack_hi16(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+// Exact split of f32 values into bf16 parts by truncation: v = hi + mid + lo
+// with each part a bf16 value (hi keeps the top 8 significant bits, the
+// remainder is exact in f32, and so on).  Returned as packed bf16 fragments.
+__device__ __forceinline__ void split3_bf16(const float (&v)[8], u4& hi, u4& mid, u4& lo) {
+  uint32_t h[8], m[8], l[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const uint32_t u = __float_as_uint(v[t]);
+    h[t] = u & 0xFFFF0000u;
+    const float r1 = v[t] - __uint_as_float(h[t]);
+    m[t] = __float_as_uint(r1) & 0xFFFF0000u;
+    l[t] = __float_as_uint(r1 - __uint_as_float(m[t]));
+  }
+  hi = u4{pack_hi16(h[0], h[1]), pack_hi16(h[2], h[3]), pack_hi16(h[4], h[5]), pack_hi16(h[6], h[7])};
+  mid = u4{pack_hi16(m[0], m[1]), pack_hi16(m[2], m[3]), pack_hi16(m[4], m[5]), pack_hi16(m[6], m[7])};
+  lo = u4{pack_hi16(l[0], l[1]), pack_hi16(l[2], l[3]), pack_hi16(l[4], l[5]), pack_hi16(l[6], l[7])};
+}
+
+// f16 bias values -> exact two-part bf16 split (an f16 has 11 significant
+// bits: 8 in hi, at most 3 in lo; bf16's exponent range covers f16's).
+__device__ __forceinline__ void split2_f16_to_bf16(const u4& v, u4& hi, u4& lo) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t h[8], l[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const uint16_t bits = static_cast<uint16_t>(w[t >> 1] >> (16 * (t & 1)));
+    const float f = static_cast<float>(__builtin_bit_cast(_Float16, bits));
+    h[t] = __float_as_uint(f) & 0xFFFF0000u;
+    l[t] = __float_as_uint(f - __uint_as_float(h[t]));
+  }
+  hi = u4{pack_hi16(h[0], h[1]), pack_hi16(h[2], h[3]), pack_hi16(h[4], h[5]), pack_hi16(h[6], h[7])};
+  lo = u4{pack_hi16(l[0], l[1]), pack_hi16(l[2], l[3]), pack_hi16(l[4], l[5]), pack_hi16(l[6], l[7])};
+}
 }  // namespace
 
-template <int BITS, bool SB_BF16, int GS, int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(64 * WM * WN) void qmm_kernel(const uint16_t* __restrict__ x,
+// Sum of v over aligned groups of 8 lanes (4 when GS == 32), in every lane of
+// the group, through DPP lane swizzles (no LDS traffic).
+template <int LANES>
+__device__ __forceinline__ float lane_group_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true));   // quad_perm 1,0,3,2
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true));   // quad_perm 2,3,0,1
+  if constexpr (LANES == 8)
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, true));  // row_half_mirror
+  return v;
+}
+
+template <int BITS, int GS, int MB, int NB>
+struct QmmCfg {
+  static constexpr int NT = 512;                     // 8 waves: 2 pipelines x (2 x 2)
+  static constexpr int BM = 64 * MB, BN = 64 * NB;   // workgroup tile
+  static constexpr int TWM = 32 * MB, TWN = 32 * NB; // wave sub-tile
+  static constexpr int WPS = KT * BITS / 32;         // words per W row per stage: 8 or 16
+  static constexpr int U4R = WPS / 4;                // 16-byte chunks per W row per stage: 2 or 4
+  static constexpr int CODES_U4 = 128 / BITS;        // codes per 16-byte chunk: 32 or 16
+  static constexpr int XCS = BM * 8;                 // x chunks (8 halves) per stage
+  static constexpr int WCS = BN * U4R;               // W chunks per stage
+  static constexpr int XCH = 2 * XCS / NT;           // x chunks per thread per stage pair
+  static constexpr int WCH = (2 * WCS + NT - 1) / NT;  // W chunks per thread per stage pair
+  static constexpr int GPS = GS <= KT ? KT / GS : 1;    // groups touched per stage
+  static constexpr int KSPG = GS <= KT ? GS / 16 : 4;   // MFMA k-steps per group (per stage for GS = 128)
+  static constexpr int NBUF = 4;                     // stage buffers: a pair in compute, a pair being filled
+  static constexpr size_t tile_bytes = static_cast<size_t>(NBUF * (BM + BN) * LDK) * 2;
+  static constexpr size_t lds_bytes = tile_bytes + static_cast<size_t>(BM * XGS) * 4 +
+                                      static_cast<size_t>(2 * BN * SBS) * 2;
+  static_assert(XCH >= 1 && (2 * XCS) % NT == 0, "x staging");
+  static_assert(2 * GPS * BN <= NT, "one scale/bias load per thread per stage pair");
+  static_assert(static_cast<size_t>(4 * 64 * 16 * MB * NB) * 4 <= tile_bytes, "pipeline reduction fits");
+};
+
+// Each workgroup runs two pipelines of four waves over the same BM x BN tile:
+// pipeline 0 computes the even stages, pipeline 1 the odd ones, each into its
+// own accumulators, and the two are added at the end.  Two waves per SIMD
+// double the VALU issue rate of one and hide each other's waits.
+template <int BITS, bool SB_BF16, int GS, int MB, int NB>
+__global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x,
                                                   const uint32_t* __restrict__ W,
                                                   const uint16_t* __restrict__ S,
                                                   const uint16_t* __restrict__ B,
                                                   uint16_t* __restrict__ y, int M, int N, int K,
                                                   int tiles_m, int tiles_n) {
-  constexpr int NT = 64 * WM * WN;             // threads per workgroup
-  constexpr int WPS = KT * BITS / 32;          // words per W row per stage: 8 or 16
-  constexpr int U4R = WPS / 4;                 // 16-byte chunks per W row per stage: 2 or 4
-  constexpr int CODES_U4 = 128 / BITS;         // codes per 16-byte chunk: 32 or 16
-  constexpr int XCH = BM * 8 / NT;             // x chunks (8 halves) per thread per stage
-  constexpr int WCH = (BN * U4R + NT - 1) / NT;  // W chunks per thread per stage
-  constexpr int TWM = BM / WM, TWN = BN / WN;  // wave sub-tile
-  constexpr int MB = TWM / 32, NB = TWN / 32;  // 32x32 MFMA blocks per wave
-  constexpr int KSPG = GS / 16;                // MFMA k-steps per group
-  static_assert(TWM % 32 == 0 && TWN % 32 == 0 && XCH >= 1 && (BM * 8) % NT == 0, "tile");
+  using C = QmmCfg<BITS, GS, MB, NB>;
+  constexpr int BM = C::BM, BN = C::BN, TWM = C::TWM, TWN = C::TWN, NT = C::NT;
+  constexpr int XCH = C::XCH, WCH = C::WCH, U4R = C::U4R, WPS = C::WPS, GPS = C::GPS;
+  constexpr int XCS = C::XCS, WCS = C::WCS;
 
-  __shared__ __align__(16) uint16_t xA[2][BM * LDK];
-  __shared__ __align__(16) uint16_t qB[2][BN * LDK];
-  __shared__ __align__(16) float xg[4][BM];  // sums of x per group, ring of 4 groups
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint16_t* xA = reinterpret_cast<uint16_t*>(smem);              // [NBUF][BM][LDK]
+  uint16_t* qB = xA + C::NBUF * BM * LDK;                        // [NBUF][BN][LDK]
+  float* xg = reinterpret_cast<float*>(smem + C::tile_bytes);    // [BM][XGS]: x sums, ring of 32 groups
+  uint16_t* sq = reinterpret_cast<uint16_t*>(xg + BM * XGS);     // [BN][SBS]: scales, ring of 32 groups
+  uint16_t* bq = sq + BN * SBS;                                  // [BN][SBS]: biases, ring of 32 groups
 
   // ---- tile assignment (XCD-aware when the tile count allows it) ---------
   const int T = tiles_m * tiles_n;
@@ -66,74 +167,92 @@ __global__ __launch_bounds__(64 * WM * WN) void qmm_kernel(const uint16_t* __res
 
   const int t = threadIdx.x;
   const int lane = t & 63;
-  const int wave = t >> 6;
-  const int wm = wave / WN, wn = wave % WN;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int pipe = wave >> 2;             // 0: even stages, 1: odd stages
+  const int wm = (wave >> 1) & 1, wn = wave & 1;
+  const int hi = lane >> 5;               // k half of this lane in the 32x32 MFMA operands
   const int G = K / GS;
   const int kw = K * BITS / 32;
   const int nkt = K / KT;
+  const int npair = (nkt + 1) >> 1;       // stage pairs
 
-  // ---- global -> registers for one stage ---------------------------------
+  // ---- global -> registers for one stage pair ------------------------------
+  // Thread t also fetches one scale and one bias of the pair: stage t / (GPS*BN),
+  // its ((t / BN) % GPS)-th group, tile row t % BN.
+  const int sb_row = min(n0 + (t % BN), N - 1);
+  const int sb_st = min(t / (GPS * BN), 1);
+  const int sb_e = (t / BN) % GPS;
+  const bool sb_store = t < 2 * GPS * BN && (GS != 128 || sb_st == 0);
+  auto stage_group = [&](int kt, int e) __attribute__((always_inline)) { return GS <= KT ? kt * GPS + e : kt >> 1; };
+
   u4 xr[XCH];
   u4 wr[WCH];
-  auto gload = [&](int kt) {
+  uint16_t sv, bv;
+  auto gload = [&](int pr) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < XCH; ++i) {
       const int c = t + NT * i;
-      const int row = c >> 3, ch = c & 7;
-      const int m = m0 + row;
-      xr[i] = (m < M) ? *reinterpret_cast<const u4*>(x + static_cast<size_t>(m) * K + kt * KT + ch * 8)
-                      : u4{0, 0, 0, 0};
+      const int kt = min(2 * pr + c / XCS, nkt - 1);
+      const int cc = c % XCS;
+      const int m = min(m0 + (cc >> 3), M - 1);  // rows past M only feed output rows past M
+      xr[i] = *reinterpret_cast<const u4*>(x + static_cast<size_t>(m) * K + kt * KT + (cc & 7) * 8);
     }
 #pragma unroll
     for (int i = 0; i < WCH; ++i) {
-      const int c = min(t + NT * i, BN * U4R - 1);
-      const int row = c / U4R, q4 = c % U4R;
-      const int n = min(n0 + row, N - 1);
-      wr[i] = *reinterpret_cast<const u4*>(W + static_cast<size_t>(n) * kw + kt * WPS + q4 * 4);
+      const int c = min(t + NT * i, 2 * WCS - 1);
+      const int kt = min(2 * pr + c / WCS, nkt - 1);
+      const int cc = c % WCS;
+      const int n = min(n0 + cc / U4R, N - 1);
+      wr[i] = *reinterpret_cast<const u4*>(W + static_cast<size_t>(n) * kw + kt * WPS + (cc % U4R) * 4);
     }
+    const int kt = min(2 * pr + sb_st, nkt - 1);
+    const size_t so = static_cast<size_t>(sb_row) * G + stage_group(kt, sb_e);
+    sv = S[so];
+    bv = B[so];
   };
 
-  // ---- registers -> LDS for one stage (reorder x, unpack codes, x sums) --
-  float xrun[XCH];  // running x sums for groups spanning two stages
-#pragma unroll
-  for (int i = 0; i < XCH; ++i) xrun[i] = 0.0f;
-  auto lstore = [&](int kt, int buf) {
+  // ---- registers -> LDS for one stage pair (reorder x, unpack codes, sums)
+  auto lstore = [&](int pr) __attribute__((always_inline)) {
+    float gsum[XCH];
 #pragma unroll
     for (int i = 0; i < XCH; ++i) {
       const int c = t + NT * i;
-      const int row = c >> 3, ch = c & 7;
+      const int kt = 2 * pr + c / XCS;
+      const int cc = c % XCS;
+      const int row = cc >> 3, ch = cc & 7;
       const u4 p = (BITS == 4) ? perm_x_w4(xr[i]) : perm_x_w8(xr[i]);
-      *reinterpret_cast<u4*>(&xA[buf][row * LDK + ch * 8]) = p;
-      // sums of x over each group, reduced over the 8 lanes that hold one row
-      float part = sum8_f32(xr[i]);
-      part += __shfl_xor(part, 1, 64);
-      part += __shfl_xor(part, 2, 64);
+      *reinterpret_cast<u4*>(&xA[((kt & 3) * BM + row) * LDK + swz(row, ch)]) = p;
+      // sums of x over each group, over the 8 (GS = 32: 4) lanes that hold one row
+      gsum[i] = lane_group_sum<GS == 32 ? 4 : 8>(sum8_f32(xr[i]));
       if constexpr (GS == 32) {
-        if ((ch & 3) == 0) xg[(2 * kt + (ch >> 2)) & 3][row] = part;
-      } else {
-        part += __shfl_xor(part, 4, 64);
-        if constexpr (GS == 64) {
-          if (ch == 0) xg[kt & 3][row] = part;
-        } else {
-          xrun[i] += part;
-          if ((kt & 1) && ch == 0) xg[(kt >> 1) & 3][row] = xrun[i];
-          if (kt & 1) xrun[i] = 0.0f;
-        }
+        if ((ch & 3) == 0 && kt < nkt) xg[row * XGS + (2 * kt + (ch >> 2)) % RING] = gsum[i];
+      } else if constexpr (GS == 64) {
+        if (ch == 0 && kt < nkt) xg[row * XGS + kt % RING] = gsum[i];
+      }
+    }
+    if constexpr (GS == 128) {
+      // a group is the stage pair: the same thread holds (row, ch) of both stages
+#pragma unroll
+      for (int i = 0; i < XCH / 2; ++i) {
+        const int cc = (t + NT * i) % XCS;
+        if ((cc & 7) == 0) xg[(cc >> 3) * XGS + pr % RING] = gsum[i] + gsum[i + XCH / 2];
       }
     }
 #pragma unroll
     for (int i = 0; i < WCH; ++i) {
       const int c = t + NT * i;
-      if (c < BN * U4R) {
-        const int row = c / U4R, q4 = c % U4R;
-        uint16_t* dst = &qB[buf][row * LDK + q4 * CODES_U4];
+      const int kt = 2 * pr + c / WCS;
+      if (c < 2 * WCS && kt < nkt) {
+        const int cc = c % WCS;
+        const int row = cc / U4R, c0 = (cc % U4R) * (C::CODES_U4 / 8);  // first 16-byte piece
+        uint16_t* dst = &qB[((kt & 3) * BN + row) * LDK];
         const uint32_t wv[4] = {wr[i].x, wr[i].y, wr[i].z, wr[i].w};
         if constexpr (BITS == 4) {
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
             h2 q[4];
             unpack_w4(wv[k], q);
-            *reinterpret_cast<u4*>(dst + 8 * k) = u4{as_u32(q[0]), as_u32(q[1]), as_u32(q[2]), as_u32(q[3])};
+            *reinterpret_cast<u4*>(dst + swz(row, c0 + k)) = u4{as_u32(q[0]), as_u32(q[1]), as_u32(q[2]), as_u32(q[3])};
           }
         } else {
 #pragma unroll
@@ -141,10 +260,16 @@ __global__ __launch_bounds__(64 * WM * WN) void qmm_kernel(const uint16_t* __res
             h2 qa[2], qb[2];
             unpack_w8(wv[2 * k], qa);
             unpack_w8(wv[2 * k + 1], qb);
-            *reinterpret_cast<u4*>(dst + 8 * k) = u4{as_u32(qa[0]), as_u32(qa[1]), as_u32(qb[0]), as_u32(qb[1])};
+            *reinterpret_cast<u4*>(dst + swz(row, c0 + k)) = u4{as_u32(qa[0]), as_u32(qa[1]), as_u32(qb[0]), as_u32(qb[1])};
           }
         }
       }
+    }
+    const int kt = 2 * pr + sb_st;
+    if (sb_store && kt < nkt) {
+      const int slot = stage_group(kt, sb_e) % RING;
+      sq[(t % BN) * SBS + slot] = sv;
+      bq[(t % BN) * SBS + slot] = bv;
     }
   };
 
@@ -156,116 +281,196 @@ __global__ __launch_bounds__(64 * WM * WN) void qmm_kernel(const uint16_t* __res
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f, P[i][j][r] = 0.0f;
 
-  // output column (row of W) of each n-block for this lane, clamped for loads
-  int ncol[NB];
-#pragma unroll
-  for (int j = 0; j < NB; ++j) ncol[j] = min(n0 + wn * TWN + j * 32 + (lane & 31), N - 1);
-  const int hi = lane >> 5;  // k index of this lane in the 32x32x2 f32 MFMA
+  const int arow = wm * TWM + (lane & 31);  // tile row of this lane's A operand (+ i*32)
+  const int bcol = wn * TWN + (lane & 31);  // tile column of this lane's B operand / output (+ j*32)
 
-  // Per group: acc += s * P (VALU).  Per pair of groups (or a last odd group):
-  // acc += X^T b as one exact f32 MFMA, X = sums of x per group (the bias term).
-  auto group_end = [&](int g) {
+  // Bias term for groups [g0, g0 + ng): acc += X^T b on the matrix cores.
+  auto bias_block = [&](int g0, int ng) __attribute__((always_inline)) {
+    const int gb = 8 * hi;                       // this lane's first group of the block
+    const int cnt = min(max(ng - gb, 0), 8);     // valid groups among this lane's 8
+    const int slot = (g0 + gb) % RING;          // 8 consecutive slots (RING is a multiple of 8)
+    u4 bhi[NB], blo[NB];
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-      const float sc = sb_to_f32<SB_BF16>(S[static_cast<size_t>(ncol[j]) * G + g]);
+      const uint2* bp = reinterpret_cast<const uint2*>(&bq[(bcol + j * 32) * SBS + slot]);  // 8-byte aligned
+      const uint2 b01 = bp[0], b23 = bp[1];
+      uint32_t w[4] = {b01.x, b01.y, b23.x, b23.y};
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t keep = (2 * p + 1 < cnt) ? 0xFFFFFFFFu : (2 * p < cnt ? 0x0000FFFFu : 0u);
+        w[p] &= keep;  // groups past the end may hold stale ring entries
+      }
+      const u4 v = u4{w[0], w[1], w[2], w[3]};
+      if constexpr (SB_BF16) {
+        bhi[j] = v;
+      } else {
+        split2_f16_to_bf16(v, bhi[j], blo[j]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      const float* xp = &xg[(arow + i * 32) * XGS + slot];
+      const float4 a0 = *reinterpret_cast<const float4*>(xp);
+      const float4 a1 = *reinterpret_cast<const float4*>(xp + 4);
+      float xv[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+      for (int u = 0; u < 8; ++u) xv[u] = (u < cnt) ? xv[u] : 0.0f;
+      u4 xh, xm, xl;
+      split3_bf16(xv, xh, xm, xl);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        f16x a = acc[i][j];
+        a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(xh), as_bf8(bhi[j]), a, 0, 0, 0);
+        a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(xm), as_bf8(bhi[j]), a, 0, 0, 0);
+        a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(xl), as_bf8(bhi[j]), a, 0, 0, 0);
+        if constexpr (!SB_BF16) {
+          a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(xh), as_bf8(blo[j]), a, 0, 0, 0);
+          a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(xm), as_bf8(blo[j]), a, 0, 0, 0);
+        }
+        acc[i][j] = a;
+      }
+    }
+  };
+
+  // End of group g (for GS = 128: of this pipeline's half of it): acc += s * P
+  // on the VALU; the bias MFMAs when g closes a block of 16 groups.
+  auto group_end = [&](int g, bool closes) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const float sc = sb_to_f32<SB_BF16>(sq[(bcol + j * 32) * SBS + g % RING]);
 #pragma unroll
       for (int i = 0; i < MB; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(sc, P[i][j][r], acc[i][j][r]);
     }
-    if ((g & 1) || g == G - 1) {
-      const int gk = (g & ~1) + hi;  // this lane's group of the pair
-      const bool ok = gk < G;
-      float xa[MB], bb[NB];
-#pragma unroll
-      for (int i = 0; i < MB; ++i) xa[i] = ok ? xg[gk & 3][wm * TWM + i * 32 + (lane & 31)] : 0.0f;
-#pragma unroll
-      for (int j = 0; j < NB; ++j)
-        bb[j] = ok ? sb_to_f32<SB_BF16>(B[static_cast<size_t>(ncol[j]) * G + gk]) : 0.0f;
-#pragma unroll
-      for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int j = 0; j < NB; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(xa[i], bb[j], acc[i][j], 0, 0, 0);
+    if (closes && ((g & (BIAS_BLOCK - 1)) == BIAS_BLOCK - 1 || g == G - 1)) {
+      const int g0 = g & ~(BIAS_BLOCK - 1);
+      bias_block(g0, g - g0 + 1);
     }
   };
 
-  // ---- prologue: stage 0 in LDS, stage 1 in registers ---------------------
-  gload(0);
-  lstore(0, 0);
-  __syncthreads();
-  if (nkt > 1) gload(1);
-
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int buf = kt & 1;
+  // This pipeline's stage kt from its LDS buffer.
+  auto compute = [&](int kt) __attribute__((always_inline)) {
+    const uint16_t* xs = xA + (kt & 3) * BM * LDK;
+    const uint16_t* qs = qB + (kt & 3) * BN * LDK;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      // group boundaries: compile-time when groups fit in a stage, else by stage parity
-      const bool first = (GS <= KT) ? (kk % KSPG == 0) : (kk == 0 && !(kt & 1));
-      const bool last = (GS <= KT) ? (kk % KSPG == KSPG - 1) : (kk == 3 && (kt & 1));
+      const bool first = kk % C::KSPG == 0;
+      const bool last = kk % C::KSPG == C::KSPG - 1;
       h8 a[MB], b[NB];
 #pragma unroll
       for (int i = 0; i < MB; ++i)
-        a[i] = *reinterpret_cast<const h8*>(&xA[buf][(wm * TWM + i * 32 + (lane & 31)) * LDK + kk * 16 + 8 * hi]);
+        a[i] = *reinterpret_cast<const h8*>(&xs[(arow + i * 32) * LDK + swz(arow, 2 * kk + hi)]);
 #pragma unroll
       for (int j = 0; j < NB; ++j)
-        b[j] = *reinterpret_cast<const h8*>(&qB[buf][(wn * TWN + j * 32 + (lane & 31)) * LDK + kk * 16 + 8 * hi]);
+        b[j] = *reinterpret_cast<const h8*>(&qs[(bcol + j * 32) * LDK + swz(bcol, 2 * kk + hi)]);
       const f16x zero = {};
 #pragma unroll
       for (int i = 0; i < MB; ++i)
 #pragma unroll
         for (int j = 0; j < NB; ++j)
           P[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], first ? zero : P[i][j], 0, 0, 0);
-      if (last) group_end((kt * KT + kk * 16) / GS);
+      if (last) {
+        if constexpr (GS == 128) {
+          group_end(kt >> 1, (kt & 1) || kt == nkt - 1);
+        } else {
+          group_end((kt * KT + kk * 16) / GS, true);
+        }
+      }
     }
-    if (kt + 1 < nkt) lstore(kt + 1, buf ^ 1);
+  };
+
+  // One stage pair per iteration: stage pair pr + 1 (in registers since the
+  // last iteration) into the two buffers not being read, prefetch pair pr + 2
+  // (clamped: the tail re-reads the last pair, never stored), compute this
+  // pipeline's stage of pair pr, one barrier.
+  // ---- prologue: pair 0 in LDS, pair 1 in registers -------------------------
+  gload(0);
+  lstore(0);
+  gload(min(1, npair - 1));
+  __syncthreads();
+
+  // A single loop exit keeps the compiler's wait analysis exact.
+  for (int pr = 0; pr < npair; ++pr) {
+    if (pr + 1 < npair) lstore(pr + 1);
+    gload(min(pr + 2, npair - 1));
+    const int kt = 2 * pr + pipe;
+    if (kt < nkt) compute(kt);
     __syncthreads();
-    if (kt + 2 < nkt) gload(kt + 2);
   }
 
-  // ---- store: lane holds column n, rows 8*(r/4) + 4*(lane/32) + r%4 -------
+  // ---- add the two pipelines' accumulators, store -------------------------
+  float* red = reinterpret_cast<float*>(smem);  // [4 waves][MB*NB*16][64], over the stage buffers
+  const int q = wave & 3;
+  if (pipe == 1) {
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) red[((q * MB * NB + i * NB + j) * 16 + r) * 64 + lane] = acc[i][j][r];
+  }
+  __syncthreads();
+  if (pipe == 1) return;
+  // lane holds column n, rows 8*(r/4) + 4*(lane/32) + r%4 of each 32x32 block
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-      const int n = n0 + wn * TWN + j * 32 + (lane & 31);
-      if (n >= N) continue;
+      const int n = n0 + bcol + j * 32;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
+        const float v = acc[i][j][r] + red[((q * MB * NB + i * NB + j) * 16 + r) * 64 + lane];
         const int m = m0 + wm * TWM + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-        if (m < M) y[static_cast<size_t>(m) * N + n] = f32_to_f16_bits(acc[i][j][r]);
+        if (m < M && n < N) y[static_cast<size_t>(m) * N + n] = f32_to_f16_bits(v);
       }
     }
 }
 
-template <int BITS, bool SB_BF16, int BM, int BN, int WM, int WN>
-static hipError_t launch_qmm_tile(const QmmArgs& a) {
-  const int tiles_m = static_cast<int>((a.M + BM - 1) / BM);
-  const int tiles_n = static_cast<int>((a.N + BN - 1) / BN);
-  const dim3 grid(tiles_m * tiles_n), block(64 * WM * WN);
+template <int BITS, bool SB_BF16, int GS, int MB, int NB>
+static hipError_t launch_qmm_cfg(const QmmArgs& a) {
+  using C = QmmCfg<BITS, GS, MB, NB>;
+  const void* kern = reinterpret_cast<const void*>(&qmm_kernel<BITS, SB_BF16, GS, MB, NB>);
+  hipError_t e = ensure_dynamic_lds(kern, C::lds_bytes);
+  if (e != hipSuccess) return e;
+  const int tiles_m = static_cast<int>((a.M + C::BM - 1) / C::BM);
+  const int tiles_n = static_cast<int>((a.N + C::BN - 1) / C::BN);
   const int M = static_cast<int>(a.M), N = static_cast<int>(a.N), K = static_cast<int>(a.K);
-  switch (a.group_size) {
-    case 32: hipLaunchKernelGGL((qmm_kernel<BITS, SB_BF16, 32, BM, BN, WM, WN>), grid, block, 0, a.stream, a.x, a.w, a.s, a.b, a.y, M, N, K, tiles_m, tiles_n); break;
-    case 64: hipLaunchKernelGGL((qmm_kernel<BITS, SB_BF16, 64, BM, BN, WM, WN>), grid, block, 0, a.stream, a.x, a.w, a.s, a.b, a.y, M, N, K, tiles_m, tiles_n); break;
-    default: hipLaunchKernelGGL((qmm_kernel<BITS, SB_BF16, 128, BM, BN, WM, WN>), grid, block, 0, a.stream, a.x, a.w, a.s, a.b, a.y, M, N, K, tiles_m, tiles_n); break;
-  }
+  hipLaunchKernelGGL((qmm_kernel<BITS, SB_BF16, GS, MB, NB>), dim3(tiles_m * tiles_n), dim3(C::NT), C::lds_bytes,
+                     a.stream, a.x, a.w, a.s, a.b, a.y, M, N, K, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
-// Launch shape: 64 x 128 tiles, 8 waves as 2 x 4 (a 32 x 32 sub-tile per wave).
-// Measured on MI355X at M = 512 against 128x128 / 64x64 / 128x64 / 256x64
-// tiles with 4 to 16 waves: fastest on both the 8192 x 2048 and the
-// 2048 x 8192 weight shapes (more waves per CU overlap one wave's MFMAs with
-// another's staging and epilogue work).
-constexpr int kWavesM = 2, kWavesN = 4;
+template <int MB, int NB>
+static hipError_t launch_qmm_shape(const QmmArgs& a) {
+  const int gs = a.group_size;
+  if (a.bits == 4) {
+    if (a.sb_bf16) {
+      return gs == 32 ? launch_qmm_cfg<4, true, 32, MB, NB>(a)
+                      : gs == 64 ? launch_qmm_cfg<4, true, 64, MB, NB>(a) : launch_qmm_cfg<4, true, 128, MB, NB>(a);
+    }
+    return gs == 32 ? launch_qmm_cfg<4, false, 32, MB, NB>(a)
+                    : gs == 64 ? launch_qmm_cfg<4, false, 64, MB, NB>(a) : launch_qmm_cfg<4, false, 128, MB, NB>(a);
+  }
+  if (a.sb_bf16) {
+    return gs == 32 ? launch_qmm_cfg<8, true, 32, MB, NB>(a)
+                    : gs == 64 ? launch_qmm_cfg<8, true, 64, MB, NB>(a) : launch_qmm_cfg<8, true, 128, MB, NB>(a);
+  }
+  return gs == 32 ? launch_qmm_cfg<8, false, 32, MB, NB>(a)
+                  : gs == 64 ? launch_qmm_cfg<8, false, 64, MB, NB>(a) : launch_qmm_cfg<8, false, 128, MB, NB>(a);
+}
 
-template <int BITS, bool SB_BF16>
-static hipError_t launch_qmm_t(const QmmArgs& a, const DeviceInfo&) {
-  return launch_qmm_tile<BITS, SB_BF16, kQmmTileM, kQmmTileN, kWavesM, kWavesN>(a);
+// Tile policy: 128 x 128 tiles (64 x 64 per wave) when they alone give every
+// CU a tile, else 64 x 64 tiles, which quadruple the tile count.
+QmmTile qmm_pick_tile(int64_t M, int64_t N, const DeviceInfo& dev) {
+  const int64_t big = ((M + 127) / 128) * ((N + 127) / 128);
+  return big >= dev.num_cu ? QmmTile{2, 2} : QmmTile{1, 1};
 }
 
 hipError_t launch_qmm(const QmmArgs& a, const DeviceInfo& dev) {
-  if (a.bits == 4) return a.sb_bf16 ? launch_qmm_t<4, true>(a, dev) : launch_qmm_t<4, false>(a, dev);
-  return a.sb_bf16 ? launch_qmm_t<8, true>(a, dev) : launch_qmm_t<8, false>(a, dev);
+  const QmmTile tl = qmm_pick_tile(a.M, a.N, dev);
+  if (tl.mb == 2 && tl.nb == 2) return launch_qmm_shape<2, 2>(a);
+  return launch_qmm_shape<1, 1>(a);
 }
 
 }  // namespace mxq

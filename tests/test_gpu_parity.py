@@ -129,7 +129,15 @@ QMM = [
 ]
 
 
-@pytest.mark.parametrize("case", QMM, ids=str)
+# Shapes with enough 128 x 128 tiles to take the large-tile kernel (>= one per
+# CU), with ragged M / N, an odd stage count and a partial bias block.
+QMM_BIG = [
+    (130, 32768, 256, 4, 64, "f16"), (256, 16400, 512, 8, 128, "bf16"), (200, 20000, 320, 4, 32, "f16"),
+    (192, 24576, 1088, 8, 64, "f16"), (136, 33000, 192, 4, 64, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", QMM + QMM_BIG, ids=str)
 def test_qmm_mfma(case):
     M, N, K, bits, gs, sb = case
     p = synth.make_problem(M, N, K, bits, gs, sb, seed=M + N + K + 5)
