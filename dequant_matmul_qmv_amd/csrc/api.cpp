@@ -237,7 +237,7 @@ mxq_status mxq_qmm(const void* x, const uint32_t* w, const void* scales, const v
     return e == hipSuccess ? MXQ_OK : hip_fail("mxq_qmm", e);
   }
   // The MFMA kernel stages x with 16-byte loads and walks K in stages of 64.
-  if (M <= 8 || K % 64 != 0 || !aligned(x, 16))
+  if (!mxq::qmm_mfma_shape(M, K) || !aligned(x, 16))
     return run_qmv("mxq_qmm", x, w, scales, biases, y, M, N, K, bits, group_size, sb_dtype, stream);
   mxq::DeviceInfo dev;
   hipError_t e = mxq::device_info(&dev);
@@ -313,7 +313,7 @@ const char* mxq_describe(const char* op, int64_t M, int64_t N, int64_t K, int bi
     return desc.c_str();
   }
   const char* sb = sb_dtype == MXQ_BF16 ? "bf16" : "f16";
-  const bool mfma = o == "qmm" && M > 8 && K % 64 == 0;
+  const bool mfma = o == "qmm" && mxq::qmm_mfma_shape(M, K);
   if (mfma) {
     const mxq::QmmTile tl = mxq::qmm_pick_tile(M, N, dev);
     const int64_t bm = 64 * tl.mb, bn = 64 * tl.nb;

@@ -100,6 +100,10 @@ struct QmmTile {
   int mb, nb;
 };
 QmmTile qmm_pick_tile(int64_t M, int64_t N, const DeviceInfo& dev);
+// Shapes the MFMA kernel takes: M > 8 (smaller M runs the qmv kernel), K a
+// multiple of its 64-code stage, and K < 2^24 so that every per-lane offset
+// within a tile (at most 128 rows of x, W, scales) fits in 32 bits.
+inline bool qmm_mfma_shape(int64_t M, int64_t K) { return M > 8 && K % 64 == 0 && K < (int64_t{1} << 24); }
 
 struct DequantArgs {
   const uint32_t* w;

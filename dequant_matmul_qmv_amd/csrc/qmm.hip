@@ -55,6 +55,7 @@ constexpr int BIAS_BLOCK = 16;    // groups per bias MFMA (its K)
 // without the XOR the 32 rows an MFMA operand read touches would share banks.
 __device__ __forceinline__ int swz(int r, int c) { return ((c ^ (r & 7)) << 3); }
 
+
 typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ bf8 as_bf8(const u4& v) { return __builtin_bit_cast(bf8, v); }
@@ -100,6 +101,34 @@ __device__ __forceinline__ void split2_f16_to_bf16(const u4& v, u4& hi, u4& lo) 
 }
 }  // namespace
 
+// Codes in natural k order for the MFMA B operand (the x tile is then used as
+// stored, with no reordering).  A byte-select puts byte i of the word, twice,
+// under the f16 exponent of 1024 (the selector's byte 5 is magic's 0x64); the
+// mask keeps the low nibble in the low half (1024 + c) and the high nibble in
+// the high half (1024 + 16 c); one packed f16 fma, exact, maps them to
+// (c_lo, c_hi).  8-bit words: bytes 2i and 2i + 1 under the exponent, then -1024.
+struct Unpack4 {
+  uint32_t magic;   // kMagic
+  h2 scale;         // (1, 1/16)
+};
+__device__ __forceinline__ u4 unpack4_natural(uint32_t w, const Unpack4& u) {
+  const h2 off = {static_cast<_Float16>(-1024.0f), static_cast<_Float16>(-64.0f)};
+  uint32_t p[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t sel = 0x05000500u | (static_cast<uint32_t>(i) << 16) | static_cast<uint32_t>(i);
+    const uint32_t t = __builtin_amdgcn_perm(u.magic, w, sel) & 0x64F0640Fu;
+    p[i] = as_u32(__builtin_elementwise_fma(as_h2(t), u.scale, off));
+  }
+  return u4{p[0], p[1], p[2], p[3]};
+}
+__device__ __forceinline__ u4 unpack8_natural(uint32_t w0, uint32_t w1, uint32_t magic) {
+  const uint32_t sel_lo = 0x05010500u, sel_hi = 0x05030502u;
+  const uint32_t p0 = __builtin_amdgcn_perm(magic, w0, sel_lo), p1 = __builtin_amdgcn_perm(magic, w0, sel_hi);
+  const uint32_t p2 = __builtin_amdgcn_perm(magic, w1, sel_lo), p3 = __builtin_amdgcn_perm(magic, w1, sel_hi);
+  return u4{as_u32(sub1024(p0)), as_u32(sub1024(p1)), as_u32(sub1024(p2)), as_u32(sub1024(p3))};
+}
+
 // Sum of v over aligned groups of 8 lanes (4 when GS == 32), in every lane of
 // the group, through DPP lane swizzles (no LDS traffic).
 template <int LANES>
@@ -114,6 +143,7 @@ __device__ __forceinline__ float lane_group_sum(float v) {
 template <int BITS, int GS, int MB, int NB>
 struct QmmCfg {
   static constexpr int NT = 512;                     // 8 waves: 2 pipelines x (2 x 2)
+  static constexpr int PT = 256;                     // threads of one pipeline
   static constexpr int BM = 64 * MB, BN = 64 * NB;   // workgroup tile
   static constexpr int TWM = 32 * MB, TWN = 32 * NB; // wave sub-tile
   static constexpr int WPS = KT * BITS / 32;         // words per W row per stage: 8 or 16
@@ -121,23 +151,30 @@ struct QmmCfg {
   static constexpr int CODES_U4 = 128 / BITS;        // codes per 16-byte chunk: 32 or 16
   static constexpr int XCS = BM * 8;                 // x chunks (8 halves) per stage
   static constexpr int WCS = BN * U4R;               // W chunks per stage
-  static constexpr int XCH = 2 * XCS / NT;           // x chunks per thread per stage pair
-  static constexpr int WCH = (2 * WCS + NT - 1) / NT;  // W chunks per thread per stage pair
-  static constexpr int GPS = GS <= KT ? KT / GS : 1;    // groups touched per stage
-  static constexpr int KSPG = GS <= KT ? GS / 16 : 4;   // MFMA k-steps per group (per stage for GS = 128)
-  static constexpr int NBUF = 4;                     // stage buffers: a pair in compute, a pair being filled
+  static constexpr int XCH = XCS / PT;               // x chunks per thread per stage
+  static constexpr int WCH = (WCS + PT - 1) / PT;    // W chunks per thread per stage
+  // Ring groups: the unit of the scale / bias bookkeeping.  A group of 32 or
+  // 64 codes is one ring group; a group of 128 codes is split into its two
+  // stages (each scaled by, and biased with, the group's scale and bias).
+  static constexpr int RGC = GS < KT ? GS : KT;      // codes per ring group
+  static constexpr int RPS = KT / RGC;               // ring groups per stage: 2 or 1
+  static constexpr int KSPR = RGC / 16;              // MFMA k-steps per ring group
+  static constexpr int NBUF = 4;                     // stage buffers: two computed, two being staged
   static constexpr size_t tile_bytes = static_cast<size_t>(NBUF * (BM + BN) * LDK) * 2;
   static constexpr size_t lds_bytes = tile_bytes + static_cast<size_t>(BM * XGS) * 4 +
                                       static_cast<size_t>(2 * BN * SBS) * 2;
-  static_assert(XCH >= 1 && (2 * XCS) % NT == 0, "x staging");
-  static_assert(2 * GPS * BN <= NT, "one scale/bias load per thread per stage pair");
+  static_assert(XCH >= 1 && XCS % PT == 0, "x staging");
+  static_assert(RPS * BN <= PT, "one scale/bias load per thread per stage");
   static_assert(static_cast<size_t>(4 * 64 * 16 * MB * NB) * 4 <= tile_bytes, "pipeline reduction fits");
 };
 
-// Each workgroup runs two pipelines of four waves over the same BM x BN tile:
-// pipeline 0 computes the even stages, pipeline 1 the odd ones, each into its
-// own accumulators, and the two are added at the end.  Two waves per SIMD
-// double the VALU issue rate of one and hide each other's waits.
+// Each workgroup runs two pipelines of four waves (2 x 2, a TWM x TWN sub-tile
+// each) over the same BM x BN tile; waves w and w + 4 share a SIMD.  Pipeline
+// p owns the stages t with t % 2 == p: it stages them into LDS itself and
+// computes them into its own accumulators, added at the end.  In each
+// iteration pipeline 0 computes and then stages, pipeline 1 stages and then
+// computes, so on every SIMD one wave's MFMAs run against the other wave's
+// unpack / load / LDS work; one barrier per iteration.
 template <int BITS, bool SB_BF16, int GS, int MB, int NB>
 __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x,
                                                   const uint32_t* __restrict__ W,
@@ -146,16 +183,16 @@ __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x
                                                   uint16_t* __restrict__ y, int M, int N, int K,
                                                   int tiles_m, int tiles_n) {
   using C = QmmCfg<BITS, GS, MB, NB>;
-  constexpr int BM = C::BM, BN = C::BN, TWM = C::TWM, TWN = C::TWN, NT = C::NT;
-  constexpr int XCH = C::XCH, WCH = C::WCH, U4R = C::U4R, WPS = C::WPS, GPS = C::GPS;
+  constexpr int BM = C::BM, BN = C::BN, TWM = C::TWM, TWN = C::TWN, PT = C::PT;
+  constexpr int XCH = C::XCH, WCH = C::WCH, U4R = C::U4R, WPS = C::WPS, RPS = C::RPS;
   constexpr int XCS = C::XCS, WCS = C::WCS;
 
   extern __shared__ __align__(16) unsigned char smem[];
-  uint16_t* xA = reinterpret_cast<uint16_t*>(smem);              // [NBUF][BM][LDK]
-  uint16_t* qB = xA + C::NBUF * BM * LDK;                        // [NBUF][BN][LDK]
-  float* xg = reinterpret_cast<float*>(smem + C::tile_bytes);    // [BM][XGS]: x sums, ring of 32 groups
-  uint16_t* sq = reinterpret_cast<uint16_t*>(xg + BM * XGS);     // [BN][SBS]: scales, ring of 32 groups
-  uint16_t* bq = sq + BN * SBS;                                  // [BN][SBS]: biases, ring of 32 groups
+  uint16_t* xA = reinterpret_cast<uint16_t*>(smem);              // [NBUF][BM][LDK] x, natural k order
+  uint16_t* qB = xA + C::NBUF * BM * LDK;                        // [NBUF][BN][LDK] codes as exact f16
+  float* xg = reinterpret_cast<float*>(smem + C::tile_bytes);    // [BM][XGS]: x sums, ring of groups
+  uint16_t* sq = reinterpret_cast<uint16_t*>(xg + BM * XGS);     // [BN][SBS]: scales, ring of groups
+  uint16_t* bq = sq + BN * SBS;                                  // [BN][SBS]: biases, ring of groups
 
   // ---- tile assignment (XCD-aware when the tile count allows it) ---------
   const int T = tiles_m * tiles_n;
@@ -166,111 +203,102 @@ __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x
   const int m0 = tm * BM, n0 = tn * BN;
 
   const int t = threadIdx.x;
+  const int tl = t & (PT - 1);            // thread within its pipeline
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int pipe = wave >> 2;             // 0: even stages, 1: odd stages
+  const int pipe = wave >> 2;
   const int wm = (wave >> 1) & 1, wn = wave & 1;
   const int hi = lane >> 5;               // k half of this lane in the 32x32 MFMA operands
   const int G = K / GS;
   const int kw = K * BITS / 32;
   const int nkt = K / KT;
-  const int npair = (nkt + 1) >> 1;       // stage pairs
+  const int GR = nkt * RPS;               // ring groups
 
-  // ---- global -> registers for one stage pair ------------------------------
-  // Thread t also fetches one scale and one bias of the pair: stage t / (GPS*BN),
-  // its ((t / BN) % GPS)-th group, tile row t % BN.
-  const int sb_row = min(n0 + (t % BN), N - 1);
-  const int sb_st = min(t / (GPS * BN), 1);
-  const int sb_e = (t / BN) % GPS;
-  const bool sb_store = t < 2 * GPS * BN && (GS != 128 || sb_st == 0);
-  auto stage_group = [&](int kt, int e) __attribute__((always_inline)) { return GS <= KT ? kt * GPS + e : kt >> 1; };
+  Unpack4 up4;
+  up4.magic = kMagic;
+  up4.scale = h2{static_cast<_Float16>(1.0f), static_cast<_Float16>(0.0625f)};
+
+  // Loads address a wave-uniform base advanced per stage plus a 32-bit lane
+  // offset fixed for the kernel (the host routes shapes whose in-tile offsets
+  // would not fit in 32 bits to the qmv kernel).  Thread tl also fetches one
+  // scale and one bias per stage: tile row tl % BN, the stage's
+  // (tl / BN)-th ring group (clamped: extra threads duplicate a load and
+  // later store the same value to the same place).
+  const char* xbase = reinterpret_cast<const char*>(x + static_cast<size_t>(m0) * K);
+  const char* wbase = reinterpret_cast<const char*>(W + static_cast<size_t>(n0) * kw);
+  const char* sbase = reinterpret_cast<const char*>(S + static_cast<size_t>(n0) * G);
+  const char* bbase = reinterpret_cast<const char*>(B + static_cast<size_t>(n0) * G);
+  uint32_t xoff[XCH];
+#pragma unroll
+  for (int i = 0; i < XCH; ++i) {
+    const int c = tl + PT * i;
+    const int row = min(m0 + (c >> 3), M - 1) - m0;  // rows past M only feed output rows past M
+    xoff[i] = static_cast<uint32_t>(row * K + (c & 7) * 8) * 2u;
+  }
+  uint32_t woff[WCH];
+#pragma unroll
+  for (int i = 0; i < WCH; ++i) {
+    const int c = min(tl + PT * i, WCS - 1);
+    const int row = min(n0 + c / U4R, N - 1) - n0;
+    woff[i] = static_cast<uint32_t>(row * kw + (c % U4R) * 4) * 4u;
+  }
+  const int sb_row = tl % BN;
+  const int sb_e = min(tl / BN, RPS - 1);
+  const uint32_t sboff = static_cast<uint32_t>(min(n0 + sb_row, N - 1) - n0) * static_cast<uint32_t>(G) * 2u;
+  // real group of ring group rg
+  auto group_of = [&](int rg) __attribute__((always_inline)) { return GS <= KT ? rg : rg >> 1; };
 
   u4 xr[XCH];
   u4 wr[WCH];
   uint16_t sv, bv;
-  auto gload = [&](int pr) __attribute__((always_inline)) {
+  auto gload = [&](int kt) __attribute__((always_inline)) {
+    kt = min(kt, nkt - 1);  // the tail re-reads the last stage; it is never stored where it is read
 #pragma unroll
-    for (int i = 0; i < XCH; ++i) {
-      const int c = t + NT * i;
-      const int kt = min(2 * pr + c / XCS, nkt - 1);
-      const int cc = c % XCS;
-      const int m = min(m0 + (cc >> 3), M - 1);  // rows past M only feed output rows past M
-      xr[i] = *reinterpret_cast<const u4*>(x + static_cast<size_t>(m) * K + kt * KT + (cc & 7) * 8);
-    }
+    for (int i = 0; i < XCH; ++i)
+      xr[i] = *reinterpret_cast<const u4*>(xbase + static_cast<size_t>(kt) * (KT * 2) + xoff[i]);
 #pragma unroll
-    for (int i = 0; i < WCH; ++i) {
-      const int c = min(t + NT * i, 2 * WCS - 1);
-      const int kt = min(2 * pr + c / WCS, nkt - 1);
-      const int cc = c % WCS;
-      const int n = min(n0 + cc / U4R, N - 1);
-      wr[i] = *reinterpret_cast<const u4*>(W + static_cast<size_t>(n) * kw + kt * WPS + (cc % U4R) * 4);
-    }
-    const int kt = min(2 * pr + sb_st, nkt - 1);
-    const size_t so = static_cast<size_t>(sb_row) * G + stage_group(kt, sb_e);
-    sv = S[so];
-    bv = B[so];
+    for (int i = 0; i < WCH; ++i)
+      wr[i] = *reinterpret_cast<const u4*>(wbase + static_cast<size_t>(kt) * (WPS * 4) + woff[i]);
+    const size_t go = static_cast<size_t>(group_of(kt * RPS + sb_e)) * 2;
+    sv = *reinterpret_cast<const uint16_t*>(sbase + go + sboff);
+    bv = *reinterpret_cast<const uint16_t*>(bbase + go + sboff);
   };
 
-  // ---- registers -> LDS for one stage pair (reorder x, unpack codes, sums)
-  auto lstore = [&](int pr) __attribute__((always_inline)) {
-    float gsum[XCH];
+  // registers -> LDS for stage kt: x as loaded, codes unpacked to exact f16,
+  // x sums, scale and bias per ring group.  Stages past the last go to a
+  // buffer and ring slots nothing reads.
+  auto lstore = [&](int kt) __attribute__((always_inline)) {
+    uint16_t* xs = xA + (kt & 3) * BM * LDK;
+    uint16_t* qs = qB + (kt & 3) * BN * LDK;
 #pragma unroll
     for (int i = 0; i < XCH; ++i) {
-      const int c = t + NT * i;
-      const int kt = 2 * pr + c / XCS;
-      const int cc = c % XCS;
-      const int row = cc >> 3, ch = cc & 7;
-      const u4 p = (BITS == 4) ? perm_x_w4(xr[i]) : perm_x_w8(xr[i]);
-      *reinterpret_cast<u4*>(&xA[((kt & 3) * BM + row) * LDK + swz(row, ch)]) = p;
-      // sums of x over each group, over the 8 (GS = 32: 4) lanes that hold one row
-      gsum[i] = lane_group_sum<GS == 32 ? 4 : 8>(sum8_f32(xr[i]));
-      if constexpr (GS == 32) {
-        if ((ch & 3) == 0 && kt < nkt) xg[row * XGS + (2 * kt + (ch >> 2)) % RING] = gsum[i];
-      } else if constexpr (GS == 64) {
-        if (ch == 0 && kt < nkt) xg[row * XGS + kt % RING] = gsum[i];
-      }
-    }
-    if constexpr (GS == 128) {
-      // a group is the stage pair: the same thread holds (row, ch) of both stages
-#pragma unroll
-      for (int i = 0; i < XCH / 2; ++i) {
-        const int cc = (t + NT * i) % XCS;
-        if ((cc & 7) == 0) xg[(cc >> 3) * XGS + pr % RING] = gsum[i] + gsum[i + XCH / 2];
-      }
+      const int c = tl + PT * i;
+      const int row = c >> 3, ch = c & 7;
+      *reinterpret_cast<u4*>(&xs[row * LDK + swz(row, ch)]) = xr[i];
+      // x sums over each ring group, over the 8 (32-code groups: 4) lanes that
+      // hold one row; every lane of the group writes the same value
+      const float gsum = lane_group_sum<C::RGC == 32 ? 4 : 8>(sum8_f32(xr[i]));
+      xg[row * XGS + (kt * RPS + (RPS == 2 ? (ch >> 2) : 0)) % RING] = gsum;
     }
 #pragma unroll
     for (int i = 0; i < WCH; ++i) {
-      const int c = t + NT * i;
-      const int kt = 2 * pr + c / WCS;
-      if (c < 2 * WCS && kt < nkt) {
-        const int cc = c % WCS;
-        const int row = cc / U4R, c0 = (cc % U4R) * (C::CODES_U4 / 8);  // first 16-byte piece
-        uint16_t* dst = &qB[((kt & 3) * BN + row) * LDK];
-        const uint32_t wv[4] = {wr[i].x, wr[i].y, wr[i].z, wr[i].w};
-        if constexpr (BITS == 4) {
+      const int c = min(tl + PT * i, WCS - 1);  // extra threads rewrite the last chunk
+      const int row = c / U4R, c0 = (c % U4R) * (C::CODES_U4 / 8);  // first 16-byte piece
+      uint16_t* dst = &qs[row * LDK];
+      const uint32_t wv[4] = {wr[i].x, wr[i].y, wr[i].z, wr[i].w};
+      if constexpr (BITS == 4) {
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            h2 q[4];
-            unpack_w4(wv[k], q);
-            *reinterpret_cast<u4*>(dst + swz(row, c0 + k)) = u4{as_u32(q[0]), as_u32(q[1]), as_u32(q[2]), as_u32(q[3])};
-          }
-        } else {
+        for (int k = 0; k < 4; ++k)
+          *reinterpret_cast<u4*>(dst + swz(row, c0 + k)) = unpack4_natural(wv[k], up4);
+      } else {
 #pragma unroll
-          for (int k = 0; k < 2; ++k) {
-            h2 qa[2], qb[2];
-            unpack_w8(wv[2 * k], qa);
-            unpack_w8(wv[2 * k + 1], qb);
-            *reinterpret_cast<u4*>(dst + swz(row, c0 + k)) = u4{as_u32(qa[0]), as_u32(qa[1]), as_u32(qb[0]), as_u32(qb[1])};
-          }
-        }
+        for (int k = 0; k < 2; ++k)
+          *reinterpret_cast<u4*>(dst + swz(row, c0 + k)) = unpack8_natural(wv[2 * k], wv[2 * k + 1], up4.magic);
       }
     }
-    const int kt = 2 * pr + sb_st;
-    if (sb_store && kt < nkt) {
-      const int slot = stage_group(kt, sb_e) % RING;
-      sq[(t % BN) * SBS + slot] = sv;
-      bq[(t % BN) * SBS + slot] = bv;
-    }
+    const int slot = (kt * RPS + sb_e) % RING;
+    sq[sb_row * SBS + slot] = sv;
+    bq[sb_row * SBS + slot] = bv;
   };
 
   f16x acc[MB][NB], P[MB][NB];
@@ -284,7 +312,7 @@ __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x
   const int arow = wm * TWM + (lane & 31);  // tile row of this lane's A operand (+ i*32)
   const int bcol = wn * TWN + (lane & 31);  // tile column of this lane's B operand / output (+ j*32)
 
-  // Bias term for groups [g0, g0 + ng): acc += X^T b on the matrix cores.
+  // Bias term for ring groups [g0, g0 + ng): acc += X^T b on the matrix cores.
   auto bias_block = [&](int g0, int ng) __attribute__((always_inline)) {
     const int gb = 8 * hi;                       // this lane's first group of the block
     const int cnt = min(max(ng - gb, 0), 8);     // valid groups among this lane's 8
@@ -296,9 +324,9 @@ __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x
       const uint2 b01 = bp[0], b23 = bp[1];
       uint32_t w[4] = {b01.x, b01.y, b23.x, b23.y};
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const uint32_t keep = (2 * p + 1 < cnt) ? 0xFFFFFFFFu : (2 * p < cnt ? 0x0000FFFFu : 0u);
-        w[p] &= keep;  // groups past the end may hold stale ring entries
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t keep = (2 * q + 1 < cnt) ? 0xFFFFFFFFu : (2 * q < cnt ? 0x0000FFFFu : 0u);
+        w[q] &= keep;  // groups past the end may hold stale ring entries
       }
       const u4 v = u4{w[0], w[1], w[2], w[3]};
       if constexpr (SB_BF16) {
@@ -332,31 +360,15 @@ __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x
     }
   };
 
-  // End of group g (for GS = 128: of this pipeline's half of it): acc += s * P
-  // on the VALU; the bias MFMAs when g closes a block of 16 groups.
-  auto group_end = [&](int g, bool closes) __attribute__((always_inline)) {
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const float sc = sb_to_f32<SB_BF16>(sq[(bcol + j * 32) * SBS + g % RING]);
-#pragma unroll
-      for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(sc, P[i][j][r], acc[i][j][r]);
-    }
-    if (closes && ((g & (BIAS_BLOCK - 1)) == BIAS_BLOCK - 1 || g == G - 1)) {
-      const int g0 = g & ~(BIAS_BLOCK - 1);
-      bias_block(g0, g - g0 + 1);
-    }
-  };
-
-  // This pipeline's stage kt from its LDS buffer.
+  // This pipeline's stage kt from its LDS buffer: per ring group, P from the
+  // MFMAs, acc += s * P on the VALU, and the bias MFMAs when the ring group
+  // closes a block of 16.
   auto compute = [&](int kt) __attribute__((always_inline)) {
     const uint16_t* xs = xA + (kt & 3) * BM * LDK;
     const uint16_t* qs = qB + (kt & 3) * BN * LDK;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const bool first = kk % C::KSPG == 0;
-      const bool last = kk % C::KSPG == C::KSPG - 1;
+      const bool first = kk % C::KSPR == 0;
       h8 a[MB], b[NB];
 #pragma unroll
       for (int i = 0; i < MB; ++i)
@@ -370,32 +382,46 @@ __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x
 #pragma unroll
         for (int j = 0; j < NB; ++j)
           P[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], first ? zero : P[i][j], 0, 0, 0);
-      if (last) {
-        if constexpr (GS == 128) {
-          group_end(kt >> 1, (kt & 1) || kt == nkt - 1);
-        } else {
-          group_end((kt * KT + kk * 16) / GS, true);
+      if (kk % C::KSPR == C::KSPR - 1) {
+        const int rg = kt * RPS + kk / C::KSPR;
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const float sc = sb_to_f32<SB_BF16>(sq[(bcol + j * 32) * SBS + rg % RING]);
+#pragma unroll
+          for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(sc, P[i][j][r], acc[i][j][r]);
+        }
+        if ((rg & (BIAS_BLOCK - 1)) == BIAS_BLOCK - 1 || rg == GR - 1) {
+          const int g0 = rg & ~(BIAS_BLOCK - 1);
+          bias_block(g0, rg - g0 + 1);
         }
       }
     }
   };
 
-  // One stage pair per iteration: stage pair pr + 1 (in registers since the
-  // last iteration) into the two buffers not being read, prefetch pair pr + 2
-  // (clamped: the tail re-reads the last pair, never stored), compute this
-  // pipeline's stage of pair pr, one barrier.
-  // ---- prologue: pair 0 in LDS, pair 1 in registers -------------------------
-  gload(0);
-  lstore(0);
-  gload(min(1, npair - 1));
+  // ---- prologue: each pipeline's first stage in LDS, its second in registers
+  gload(pipe);
+  lstore(pipe);
+  gload(pipe + 2);
   __syncthreads();
 
-  // A single loop exit keeps the compiler's wait analysis exact.
+  // Iteration pr: pipeline 0 computes stage 2pr, then stages 2pr + 2 and
+  // prefetches 2pr + 4; pipeline 1 stages 2pr + 3 and prefetches 2pr + 5,
+  // then computes 2pr + 1.  One barrier; a single loop exit keeps the
+  // compiler's wait analysis exact.
+  const int npair = (nkt + 1) >> 1;
   for (int pr = 0; pr < npair; ++pr) {
-    if (pr + 1 < npair) lstore(pr + 1);
-    gload(min(pr + 2, npair - 1));
     const int kt = 2 * pr + pipe;
+    if (pipe == 1) {
+      lstore(kt + 2);
+      gload(kt + 4);
+    }
     if (kt < nkt) compute(kt);
+    if (pipe == 0) {
+      lstore(kt + 2);
+      gload(kt + 4);
+    }
     __syncthreads();
   }
 
