@@ -1,8 +1,9 @@
 """MI355X (gfx950) matmul over MLX-style affine-quantized packed weights.
 
 The public calls mirror the C ABI of libmxq.so (``include/mxq.h``):
-``mxq_qmv`` (decode), ``mxq_qmm`` (prefill), ``mxq_dequant`` (bit-exact
-standalone dequant) and ``mxq_pack`` (host packer).
+``mxq_qmv`` (decode), ``mxq_qmv_grouped`` (several decode projections per
+launch), ``mxq_qmm`` (prefill), ``mxq_linear`` (either, plus an output bias),
+``mxq_dequant`` (bit-exact standalone dequant) and ``mxq_pack`` (host packer).
 """
 
 from ._lib import (  # noqa: F401
@@ -18,6 +19,7 @@ from ._lib import (  # noqa: F401
     load,
     mxq_dequant,
     mxq_describe,
+    mxq_linear,
     mxq_pack,
     mxq_qmm,
     mxq_qmv,

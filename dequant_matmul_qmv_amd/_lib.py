@@ -50,6 +50,8 @@ def _declare(lib):
     for name in ("mxq_qmv", "mxq_qmm"):
         f = getattr(lib, name)
         f.argtypes, f.restype = fused, c_int
+    lib.mxq_linear.argtypes = [vp, vp, vp, vp, vp, vp, c_i64, c_i64, c_i64, c_int, c_int, c_int, vp]
+    lib.mxq_linear.restype = c_int
     lib.mxq_qmv_grouped.argtypes = [ctypes.POINTER(QmvProblem), c_int, c_i64, c_int, c_int, c_int, vp]
     lib.mxq_qmv_grouped.restype = c_int
     lib.mxq_dequant.argtypes = [vp, vp, vp, vp, c_i64, c_i64, c_int, c_int, c_int, c_int, vp]
@@ -194,6 +196,28 @@ def mxq_qmv_grouped(problems, *, bits: int = 4, group_size: int = 64, stream=Non
 def mxq_qmm(x, w, scales, biases, y=None, *, bits: int = 4, group_size: int = 64, stream=None):
     """y = x @ dequant(w).T via the MFMA prefill kernel (any M; MFMA for M > 8)."""
     return _fused("mxq_qmm", x, w, scales, biases, y, bits, group_size, stream)
+
+
+def mxq_linear(x, w, scales, biases, bias=None, y=None, *, bits: int = 4, group_size: int = 64,
+               stream=None):
+    """y = x @ dequant(w).T + bias: a quantized linear layer with an optional
+    float16 output bias [N] (None: same result as mxq_qmm)."""
+    torch = _torch()
+    lib = load()
+    M, N, K = _check_packed(x, w, scales, biases, bits, group_size, "mxq_linear")
+    if bias is not None and (bias.dtype != torch.float16 or tuple(bias.shape) != (N,) or not bias.is_cuda
+                             or not bias.is_contiguous() or bias.device != x.device):
+        raise ValueError("mxq_linear: bias must be a contiguous float16 [N] tensor on x's device")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    elif y.dtype != torch.float16 or tuple(y.shape) != (M, N) or not y.is_contiguous() or y.device != x.device:
+        raise ValueError("mxq_linear: y must be a contiguous float16 [M, N] tensor on x's device")
+    with torch.cuda.device(x.device):
+        st = lib.mxq_linear(x.data_ptr(), w.data_ptr(), scales.data_ptr(), biases.data_ptr(),
+                            None if bias is None else bias.data_ptr(), y.data_ptr(), M, N, K, bits,
+                            group_size, _sb_code(scales), _stream_handle(x.device, stream))
+    _check(lib, st)
+    return y
 
 
 def mxq_dequant(w, scales, biases, out=None, *, bits: int = 4, group_size: int = 64,

@@ -59,8 +59,8 @@ mxq_status hip_fail(const char* who, hipError_t e) {
 
 // M-sliced qmv over the whole M range.
 mxq_status run_qmv(const char* who, const void* x, const uint32_t* w, const void* scales,
-                   const void* biases, void* y, int64_t M, int64_t N, int64_t K, int bits,
-                   int group_size, mxq_dtype sb_dtype, void* stream) {
+                   const void* biases, const void* out_bias, void* y, int64_t M, int64_t N, int64_t K,
+                   int bits, int group_size, mxq_dtype sb_dtype, void* stream) {
   mxq::DeviceInfo dev;
   hipError_t e = mxq::device_info(&dev);
   if (e != hipSuccess) return hip_fail(who, e);
@@ -72,6 +72,7 @@ mxq_status run_qmv(const char* who, const void* x, const uint32_t* w, const void
   a.w = w;
   a.s = static_cast<const uint16_t*>(scales);
   a.b = static_cast<const uint16_t*>(biases);
+  a.ob = static_cast<const uint16_t*>(out_bias);
   a.N = N;
   a.K = K;
   a.bits = bits;
@@ -112,7 +113,7 @@ mxq_status run_qmv_grouped(const char* who, const mxq_qmv_problem* pr, int count
         chunk[i] = mxq::QmvProblem{static_cast<const uint16_t*>(q.x) + m0 * q.K, q.w,
                                    static_cast<const uint16_t*>(q.scales),
                                    static_cast<const uint16_t*>(q.biases),
-                                   static_cast<uint16_t*>(q.y) + m0 * q.N, q.N, q.K};
+                                   static_cast<uint16_t*>(q.y) + m0 * q.N, nullptr, q.N, q.K};
       }
       e = mxq::launch_qmv_group(chunk, n, bits, log2_group(group_size), sb_dtype == MXQ_BF16, dev, mt,
                                 static_cast<hipStream_t>(stream));
@@ -120,6 +121,40 @@ mxq_status run_qmv_grouped(const char* who, const mxq_qmv_problem* pr, int count
     }
   }
   return MXQ_OK;
+}
+
+// Validated fused call with M, N > 0: qmv kernel for small M (or shapes the
+// MFMA kernel does not take), MFMA kernel otherwise; out_bias may be null.
+mxq_status run_matmul(const char* who, const void* x, const uint32_t* w, const void* scales,
+                      const void* biases, const void* out_bias, void* y, int64_t M, int64_t N, int64_t K,
+                      int bits, int group_size, mxq_dtype sb_dtype, void* stream) {
+  if (K == 0) {
+    hipError_t e = mxq::launch_fill_rows(static_cast<uint16_t*>(y), static_cast<const uint16_t*>(out_bias), M, N,
+                                         static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MXQ_OK : hip_fail(who, e);
+  }
+  // The MFMA kernel stages x with 16-byte loads and walks K in stages of 64.
+  if (!mxq::qmm_mfma_shape(M, K) || !aligned(x, 16))
+    return run_qmv(who, x, w, scales, biases, out_bias, y, M, N, K, bits, group_size, sb_dtype, stream);
+  mxq::DeviceInfo dev;
+  hipError_t e = mxq::device_info(&dev);
+  if (e != hipSuccess) return hip_fail(who, e);
+  mxq::QmmArgs a{};
+  a.x = static_cast<const uint16_t*>(x);
+  a.w = w;
+  a.s = static_cast<const uint16_t*>(scales);
+  a.b = static_cast<const uint16_t*>(biases);
+  a.y = static_cast<uint16_t*>(y);
+  a.ob = static_cast<const uint16_t*>(out_bias);
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.bits = bits;
+  a.group_size = group_size;
+  a.sb_bf16 = sb_dtype == MXQ_BF16;
+  a.stream = static_cast<hipStream_t>(stream);
+  e = mxq::launch_qmm(a, dev);
+  return e == hipSuccess ? MXQ_OK : hip_fail(who, e);
 }
 
 }  // namespace
@@ -195,7 +230,7 @@ mxq_status mxq_qmv(const void* x, const uint32_t* w, const void* scales, const v
     hipError_t e = mxq::launch_zero_fill(static_cast<uint16_t*>(y), M * N, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? MXQ_OK : hip_fail("mxq_qmv", e);
   }
-  return run_qmv("mxq_qmv", x, w, scales, biases, y, M, N, K, bits, group_size, sb_dtype, stream);
+  return run_qmv("mxq_qmv", x, w, scales, biases, nullptr, y, M, N, K, bits, group_size, sb_dtype, stream);
 }
 
 mxq_status mxq_qmv_grouped(const mxq_qmv_problem* problems, int count, int64_t M, int bits,
@@ -232,31 +267,19 @@ mxq_status mxq_qmm(const void* x, const uint32_t* w, const void* scales, const v
   g_last_error.clear();
   mxq_status st = check_fused("mxq_qmm", x, w, scales, biases, y, M, N, K, bits, group_size, sb_dtype);
   if (st != MXQ_OK || M == 0 || N == 0) return st;
-  if (K == 0) {
-    hipError_t e = mxq::launch_zero_fill(static_cast<uint16_t*>(y), M * N, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? MXQ_OK : hip_fail("mxq_qmm", e);
-  }
-  // The MFMA kernel stages x with 16-byte loads and walks K in stages of 64.
-  if (!mxq::qmm_mfma_shape(M, K) || !aligned(x, 16))
-    return run_qmv("mxq_qmm", x, w, scales, biases, y, M, N, K, bits, group_size, sb_dtype, stream);
-  mxq::DeviceInfo dev;
-  hipError_t e = mxq::device_info(&dev);
-  if (e != hipSuccess) return hip_fail("mxq_qmm", e);
-  mxq::QmmArgs a{};
-  a.x = static_cast<const uint16_t*>(x);
-  a.w = w;
-  a.s = static_cast<const uint16_t*>(scales);
-  a.b = static_cast<const uint16_t*>(biases);
-  a.y = static_cast<uint16_t*>(y);
-  a.M = M;
-  a.N = N;
-  a.K = K;
-  a.bits = bits;
-  a.group_size = group_size;
-  a.sb_bf16 = sb_dtype == MXQ_BF16;
-  a.stream = static_cast<hipStream_t>(stream);
-  e = mxq::launch_qmm(a, dev);
-  return e == hipSuccess ? MXQ_OK : hip_fail("mxq_qmm", e);
+  return run_matmul("mxq_qmm", x, w, scales, biases, nullptr, y, M, N, K, bits, group_size, sb_dtype, stream);
+}
+
+mxq_status mxq_linear(const void* x, const uint32_t* w, const void* scales, const void* biases,
+                      const void* out_bias, void* y, int64_t M, int64_t N, int64_t K, int bits,
+                      int group_size, mxq_dtype sb_dtype, void* stream) {
+  g_last_error.clear();
+  mxq_status st = check_fused("mxq_linear", x, w, scales, biases, y, M, N, K, bits, group_size, sb_dtype);
+  if (st != MXQ_OK || M == 0 || N == 0) return st;
+  if (out_bias && !aligned(out_bias, 2))
+    return fail(MXQ_ERR_MISALIGNED, "mxq_linear: out_bias must be 2-byte aligned");
+  return run_matmul("mxq_linear", x, w, scales, biases, out_bias, y, M, N, K, bits, group_size, sb_dtype,
+                    stream);
 }
 
 mxq_status mxq_dequant(const uint32_t* w, const void* scales, const void* biases, void* out,

@@ -95,6 +95,21 @@ __global__ void zero_fill_kernel(uint16_t* __restrict__ y, int64_t count) {
     y[i] = 0;
 }
 
+__global__ void fill_rows_kernel(uint16_t* __restrict__ y, const uint16_t* __restrict__ ob, int64_t M, int64_t N) {
+  const int64_t count = M * N;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < count; i += stride)
+    y[i] = ob[i % N];
+}
+
+hipError_t launch_fill_rows(uint16_t* y, const uint16_t* ob, int64_t M, int64_t N, hipStream_t stream) {
+  if (!ob) return launch_zero_fill(y, M * N, stream);
+  int64_t blocks = (M * N + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(fill_rows_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, y, ob, M, N);
+  return hipGetLastError();
+}
+
 hipError_t launch_zero_fill(uint16_t* y, int64_t count, hipStream_t stream) {
   int64_t blocks = (count + 255) / 256;
   if (blocks > 4096) blocks = 4096;

@@ -30,6 +30,7 @@ struct QmvBatch {
   const uint16_t* s[kMaxGroup];
   const uint16_t* b[kMaxGroup];
   uint16_t* y[kMaxGroup];
+  const uint16_t* ob[kMaxGroup];  // f16 output bias [N] or null
   int N[kMaxGroup];
   int K[kMaxGroup];
   int xvec[kMaxGroup];
@@ -44,6 +45,7 @@ struct QmvProblem {
   const uint16_t* s;
   const uint16_t* b;
   uint16_t* y;         // f16 bits [M, N] of this slice
+  const uint16_t* ob;  // f16 bits [N], added to every row of y, or null
   int64_t N, K;
 };
 
@@ -53,6 +55,7 @@ struct QmvArgs {
   const uint16_t* s;
   const uint16_t* b;
   uint16_t* y;         // f16 bits [M, N] of this slice
+  const uint16_t* ob;  // f16 bits [N], added to every row of y, or null
   int64_t N, K;
   int bits;
   int glog2;           // log2(group_size)
@@ -87,6 +90,7 @@ struct QmmArgs {
   const uint16_t* s;
   const uint16_t* b;
   uint16_t* y;
+  const uint16_t* ob;  // f16 bits [N], added to every row of y, or null
   int64_t M, N, K;
   int bits;
   int group_size;
@@ -121,6 +125,8 @@ struct DequantArgs {
 hipError_t launch_dequant(const DequantArgs& a, const DeviceInfo& dev);
 
 // y[0 .. count) = +0 (f16 bits), used for K == 0.
+// y[m, n] = ob[n] (ob non-null) or +0, for m < M, n < N.
+hipError_t launch_fill_rows(uint16_t* y, const uint16_t* ob, int64_t M, int64_t N, hipStream_t stream);
 hipError_t launch_zero_fill(uint16_t* y, int64_t count, hipStream_t stream);
 
 }  // namespace mxq

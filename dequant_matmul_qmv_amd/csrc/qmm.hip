@@ -180,8 +180,8 @@ __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x
                                                   const uint32_t* __restrict__ W,
                                                   const uint16_t* __restrict__ S,
                                                   const uint16_t* __restrict__ B,
-                                                  uint16_t* __restrict__ y, int M, int N, int K,
-                                                  int tiles_m, int tiles_n) {
+                                                  uint16_t* __restrict__ y, const uint16_t* __restrict__ ob,
+                                                  int M, int N, int K, int tiles_m, int tiles_n) {
   using C = QmmCfg<BITS, GS, MB, NB>;
   constexpr int BM = C::BM, BN = C::BN, TWM = C::TWM, TWN = C::TWN, PT = C::PT;
   constexpr int XCH = C::XCH, WCH = C::WCH, U4R = C::U4R, WPS = C::WPS, RPS = C::RPS;
@@ -444,9 +444,10 @@ __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       const int n = n0 + bcol + j * 32;
+      const float o = ob != nullptr ? sb_to_f32<false>(ob[min(n, N - 1)]) : 0.0f;  // output bias of column n
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float v = acc[i][j][r] + red[((q * MB * NB + i * NB + j) * 16 + r) * 64 + lane];
+        const float v = acc[i][j][r] + red[((q * MB * NB + i * NB + j) * 16 + r) * 64 + lane] + o;
         const int m = m0 + wm * TWM + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
         if (m < M && n < N) y[static_cast<size_t>(m) * N + n] = f32_to_f16_bits(v);
       }
@@ -463,7 +464,7 @@ static hipError_t launch_qmm_cfg(const QmmArgs& a) {
   const int tiles_n = static_cast<int>((a.N + C::BN - 1) / C::BN);
   const int M = static_cast<int>(a.M), N = static_cast<int>(a.N), K = static_cast<int>(a.K);
   hipLaunchKernelGGL((qmm_kernel<BITS, SB_BF16, GS, MB, NB>), dim3(tiles_m * tiles_n), dim3(C::NT), C::lds_bytes,
-                     a.stream, a.x, a.w, a.s, a.b, a.y, M, N, K, tiles_m, tiles_n);
+                     a.stream, a.x, a.w, a.s, a.b, a.y, a.ob, M, N, K, tiles_m, tiles_n);
   return hipGetLastError();
 }
 

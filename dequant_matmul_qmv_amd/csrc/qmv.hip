@@ -55,6 +55,7 @@ template <int R>
 struct QmvItem {
   u4 w[R];
   uint16_t s[R], b[R];
+  uint16_t ob;  // output bias of the row this lane stores (when there is one)
 };
 
 template <int BITS, bool SB_BF16, int MT, int R, bool XD>
@@ -70,6 +71,8 @@ __global__ __launch_bounds__(256) void qmv_kernel(const QmvBatch batch) {
   const uint16_t* __restrict__ S = batch.s[p];
   const uint16_t* __restrict__ B = batch.b[p];
   uint16_t* __restrict__ y = batch.y[p];
+  const uint16_t* __restrict__ ob = batch.ob[p];
+  const bool has_ob = ob != nullptr;
   const int N = batch.N[p], K = batch.K[p], x_vec = batch.xvec[p], glog2 = batch.glog2;
   constexpr int CPS = SegTraits<BITS>::kChunksPerSeg;
   constexpr int CODES = SegTraits<BITS>::kCodesPerSeg;
@@ -86,6 +89,15 @@ __global__ __launch_bounds__(256) void qmv_kernel(const QmvBatch batch) {
   float* xsum = reinterpret_cast<float*>(smem + static_cast<size_t>(MT) * CPS * nseg * 16);  // [MT][nseg]
 
   const int lane = threadIdx.x & (kWave - 1);
+  // Output this lane stores after the wave reduction (see the butterfly in
+  // step): its value index, and from it the row offset within a row block.
+  int my_idx = 0;
+#pragma unroll
+  for (int s = 0; s < 6; ++s) {
+    const int live = VP >> s;
+    if (live >= 2 && (lane & (32 >> s))) my_idx += live / 2;
+  }
+  const int my_r = min(my_idx, V - 1) / MT;
   // wave-uniform values live in scalar registers: all row addressing is scalar,
   // and each load adds one 32-bit per-lane offset to a scalar base (the caller
   // guarantees W, S and B are each below 4 GiB)
@@ -125,6 +137,11 @@ __global__ __launch_bounds__(256) void qmv_kernel(const QmvBatch batch) {
       it.s[r] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(sbase + (row * sbrow_bytes + sl)));
       it.b[r] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(bbase + (row * sbrow_bytes + sl)));
     }
+    // the stored row's output bias, fetched with every item of the row block
+    // (so the one the block ends with has it); without a bias, a harmless
+    // read of x[0] whose value is never used
+    const uint32_t orow = dummy ? 0u : static_cast<uint32_t>(min(rbl * R + my_r, N - 1));
+    it.ob = *reinterpret_cast<const uint16_t*>(has_ob ? reinterpret_cast<const char*>(ob) + orow * 2u : Xb);
   };
 
   // The first item's loads go out before the x staging, to overlap the two.
@@ -337,7 +354,8 @@ __global__ __launch_bounds__(256) void qmv_kernel(const QmvBatch batch) {
         const int r = idx / MT;
         const int m = idx - r * MT;
         const int row = rbl * R + r;
-        if (row < N) y[static_cast<size_t>(m) * N + row] = f32_to_f16_bits(v[0]);
+        const float o = has_ob ? sb_to_f32<false>(it.ob) : 0.0f;
+        if (row < N) y[static_cast<size_t>(m) * N + row] = f32_to_f16_bits(v[0] + o);
       }
     }
 #pragma unroll
@@ -542,6 +560,7 @@ hipError_t launch_qmv_group(const QmvProblem* probs, int count, int bits, int gl
     batch.s[i] = probs[i].s;
     batch.b[i] = probs[i].b;
     batch.y[i] = probs[i].y;
+    batch.ob[i] = probs[i].ob;
     batch.N[i] = static_cast<int>(probs[i].N);
     batch.K[i] = static_cast<int>(probs[i].K);
     batch.xvec[i] = (reinterpret_cast<uintptr_t>(probs[i].x) & 15u) == 0 ? 1 : 0;
@@ -554,7 +573,7 @@ hipError_t launch_qmv_group(const QmvProblem* probs, int count, int bits, int gl
 }
 
 hipError_t launch_qmv_slice(const QmvArgs& a, const DeviceInfo& dev, int mt) {
-  QmvProblem pr{a.x, a.w, a.s, a.b, a.y, a.N, a.K};
+  QmvProblem pr{a.x, a.w, a.s, a.b, a.y, a.ob, a.N, a.K};
   return launch_qmv_group(&pr, 1, a.bits, a.glog2, a.sb_bf16, dev, mt, a.stream);
 }
 

@@ -135,6 +135,23 @@ mxq_status mxq_qmm(const void* x, const uint32_t* w, const void* scales, const v
                    mxq_dtype sb_dtype, void* stream);
 
 /*
+ * mxq_linear -- a quantized linear layer with an output bias:
+ *   y[m, n] = RNE_f16( sum_k x[m, k] * (q[n, k] * s + b) + out_bias[n] ).
+ *
+ * The "linear with bias" case of the 4-bit linear op whose Metal kernel
+ * ExecuTorch PR #17187 ("Metal backend: import qmv_impl from MLX") imports
+ * (its stack: "enable linear with bias", "test 4-bit linear with bias").
+ * out_bias is an f16 device vector [N], 2-byte aligned, added in f32 before
+ * the single f16 rounding; a null out_bias gives exactly the mxq_qmm result.
+ * Other arguments, routing (qmv kernel for M <= 8, MFMA kernel above),
+ * accuracy and determinism as mxq_qmm; K = 0 gives y[m, n] = out_bias[n]
+ * (or +0).  Errors as mxq_qmv, plus MXQ_ERR_MISALIGNED for out_bias.
+ */
+mxq_status mxq_linear(const void* x, const uint32_t* w, const void* scales, const void* biases,
+                      const void* out_bias, void* y, int64_t M, int64_t N, int64_t K, int bits,
+                      int group_size, mxq_dtype sb_dtype, void* stream);
+
+/*
  * mxq_dequant -- standalone dequantization: out[n, k] = q * s + b.
  *
  * The reconstruction mlxcel #574 ("What is already in-tree") requires to be

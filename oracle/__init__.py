@@ -16,6 +16,7 @@ from .qmv_oracle import (  # noqa: F401
     dequant_f64,
     matmul_ref,
     matmul_ref_rows,
+    linear_ref,
     dequant_ref_out,
     f32_to_bf16_bits,
 )

@@ -15,13 +15,15 @@ What the method computes (sources are the four pages of the reference):
   result of dequant followed by the matmul, without writing the f32 weight out.
 * ExecuTorch PR #17187 "Metal backend: import qmv_impl from MLX",
   "Description": the operation is a linear layer with floating-point
-  activations and 4-bit weights, including M = 1 with N not a multiple of 4.
+  activations and 4-bit weights, including M = 1 with N not a multiple of 4;
+  the PR's stack lists the same linear "with bias".
 
 Readings where the pages are silent:
 
 * Codes are packed LSB-first: code i of a word occupies bits [b*i, b*i + b).
 * ``W`` is ``[N, K*b/32]`` uint32 (out-features x in-features), so
   ``y = x @ dequant(W).T``; scales and biases are ``[N, K/group_size]``.
+* "Linear with bias" adds an f16 output bias ``[N]`` to every row of ``y``.
 * The fused output is compared against the f64 value before any rounding; the
   standalone dequant output is the f32 value ``RN_f32(q*s + b)``, and f16 or
   bf16 outputs are round-to-nearest-even of that f32 value (two steps).
@@ -40,6 +42,7 @@ __all__ = [
     "widen_sb",
     "dequant_f64",
     "matmul_ref",
+    "linear_ref",
     "matmul_ref_rows",
     "dequant_ref_out",
     "f32_to_bf16_bits",
@@ -127,6 +130,21 @@ def matmul_ref_rows(x, w_words, scales, biases, rows, K: int, bits: int,
     rows = np.asarray(rows, dtype=np.int64)
     return matmul_ref(x, np.asarray(w_words)[rows], np.asarray(scales)[rows],
                       np.asarray(biases)[rows], K, bits, group_size, sb_dtype)
+
+
+def linear_ref(x, w_words, scales, biases, out_bias_bits, K: int, bits: int, group_size: int,
+               sb_dtype: str) -> np.ndarray:
+    """Float64 ``y = x @ dequant(W).T + out_bias`` (before any output rounding).
+
+    The "linear with bias" entry of the ExecuTorch PR #17187 stack: the layer's
+    f16 output bias ``[N]`` (uint16 bit patterns, or None for no bias) is added
+    to every row of the linear layer's result.
+    """
+    y = matmul_ref(x, w_words, scales, biases, K, bits, group_size, sb_dtype)
+    if out_bias_bits is None:
+        return y
+    ob = np.asarray(out_bias_bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+    return y + ob[None, :]
 
 
 def f32_to_bf16_bits(v32: np.ndarray) -> np.ndarray:

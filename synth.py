@@ -97,6 +97,12 @@ def make_x(M: int, K: int, rng: np.random.Generator | None = None,
     return rng.standard_normal((M, K)).astype(np.float16)
 
 
+def make_out_bias(N: int, seed: int) -> np.ndarray:
+    """A linear layer's f16 output bias [N] as uint16 bit patterns: N(0, 0.5^2)."""
+    rng = np.random.default_rng(seed)
+    return (0.5 * rng.standard_normal(N)).astype(np.float16).view(np.uint16)
+
+
 def make_problem(M: int, N: int, K: int, bits: int = 4, group_size: int = 64,
                  sb_dtype: str = "f16", seed: int = 0) -> Problem:
     rng = np.random.default_rng(seed)

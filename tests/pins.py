@@ -304,9 +304,31 @@ def pin_bf16_rounding(O):
     assert (int(nan) & 0x7F80) == 0x7F80 and (int(nan) & 0x7F) != 0
 
 
+def pin_linear_bias_hand(O):
+    """Linear with an output bias on a hand-derived case (M=2, N=3, K=32, 4-bit, g32).
+
+    Row n of W holds the code n+1 everywhere (word (n+1) * 0x11111111), scale
+    2^-4 (f16 0x2C00), bias 0; x row 0 is all ones, row 1 alternates +1 / -1;
+    out_bias = (0.5, -1.25, 3.0).  Row 0: 32 * (n+1) / 16 + out_bias[n] =
+    (2.5, 2.75, 9.0); row 1: the x sum is 0, so y is out_bias itself.  M != N,
+    so a bias added along the wrong axis cannot broadcast.
+    """
+    w = np.array([[(n + 1) * 0x11111111] * 4 for n in range(3)], dtype=np.uint32)
+    s = np.full((3, 1), 0x2C00, dtype=np.uint16)
+    b = np.zeros((3, 1), dtype=np.uint16)
+    x = np.zeros((2, 32), dtype=np.uint16)
+    x[0, :] = 0x3C00
+    x[1, 0::2], x[1, 1::2] = 0x3C00, 0xBC00
+    ob = np.array([0x3800, 0xBD00, 0x4200], dtype=np.uint16)
+    y = O.linear_ref(x.view(np.float16), w, s, b, ob, 32, 4, 32, "f16")
+    assert np.array_equal(y, np.array([[2.5, 2.75, 9.0], [0.5, -1.25, 3.0]])), y
+    y0 = O.linear_ref(x.view(np.float16), w, s, b, None, 32, 4, 32, "f16")
+    assert np.array_equal(y0, np.array([[2.0, 4.0, 6.0], [0.0, 0.0, 0.0]])), y0
+
+
 ALL_PINS = [
     pin_unpack_hand_words, pin_unpack_every_value_every_slot, pin_unpack_bitstrings,
     pin_widen, pin_dequant_hand_values, pin_group_indexing, pin_bruteforce_tiny,
     pin_one_hot, pin_integer_case, pin_all_ones_closed_form, pin_linearity,
-    pin_rows_subset, pin_bf16_rounding,
+    pin_rows_subset, pin_bf16_rounding, pin_linear_bias_hand,
 ]

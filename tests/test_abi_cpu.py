@@ -93,14 +93,21 @@ def _call(name, *args):
     return st, lib.mxq_last_error().decode()
 
 
-@pytest.mark.parametrize("name", ["mxq_qmv", "mxq_qmm"])
+@pytest.mark.parametrize("name", ["mxq_qmv", "mxq_qmm", "mxq_linear"])
 def test_fused_validation(name):
     P = FAKE
     ok = dict(M=1, N=4, K=64, bits=4, gs=64, sb=mxq.MXQ_F16)
 
     def call(x=P, w=P, s=P, b=P, y=P, **kw):
         a = dict(ok, **kw)
+        if name == "mxq_linear":   # the output bias goes between biases and y
+            return _call(name, x, w, s, b, a.get("ob", None), y, a["M"], a["N"], a["K"], a["bits"], a["gs"],
+                         a["sb"], None)
         return _call(name, x, w, s, b, y, a["M"], a["N"], a["K"], a["bits"], a["gs"], a["sb"], None)
+
+    if name == "mxq_linear":
+        st, msg = call(ob=P + 1)
+        assert st == mxq.MXQ_ERR_MISALIGNED and "out_bias" in msg
 
     assert call(bits=3)[0] == mxq.MXQ_ERR_UNSUPPORTED
     assert call(bits=2)[0] == mxq.MXQ_ERR_UNSUPPORTED

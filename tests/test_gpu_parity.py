@@ -293,3 +293,58 @@ def test_grouped_qmv_empty_and_k_zero():
     torch.cuda.synchronize()
     assert_close(ys[0].cpu().numpy(), _ref(p), "grouped K>0")
     assert torch.equal(y0.cpu(), torch.zeros((2, 4), dtype=torch.float16))
+
+
+# ------------------------------------------------------ linear with bias ---
+LINEAR = [
+    (1, 1000, 2048, 4, 64, "f16"), (3, 130, 2048, 8, 32, "bf16"), (8, 2049, 4096, 4, 128, "f16"),
+    (5, 1, 64, 4, 64, "f16"), (64, 256, 1024, 8, 64, "bf16"), (200, 333, 2048, 4, 64, "f16"),
+    (130, 32768, 256, 4, 64, "f16"), (96, 100, 640, 4, 32, "bf16"),
+]
+
+
+def _bias_dev(ob):
+    return torch.from_numpy(ob.view(np.int16)).view(torch.float16).cuda()
+
+
+@pytest.mark.parametrize("case", LINEAR, ids=str)
+def test_linear_bias(case):
+    M, N, K, bits, gs, sb = case
+    p = synth.make_problem(M, N, K, bits, gs, sb, seed=M + 3 * N + K)
+    ob = synth.make_out_bias(N, seed=N + 17)
+    note(f"linear {case}")
+    x, w, s, b = to_dev(p)
+    y = y_host(mxq.mxq_linear(x, w, s, b, _bias_dev(ob), bits=bits, group_size=gs))
+    ref = oracle.linear_ref(p.x, p.w, p.scales, p.biases, ob, K, bits, gs, sb)
+    assert_close(y, ref, f"linear {case}")
+    # without a bias the call is mxq_qmm, bit for bit
+    y0 = mxq.mxq_linear(x, w, s, b, None, bits=bits, group_size=gs)
+    yq = mxq.mxq_qmm(x, w, s, b, bits=bits, group_size=gs)
+    assert torch.equal(y0.view(torch.int16), yq.view(torch.int16)), case
+
+
+@pytest.mark.parametrize("M", [1, 7, 64, 300])
+def test_linear_bias_exact_with_zero_weights(M):
+    """Scales and biases 0: the weights contribute exact zeros, so y = out_bias bit for bit."""
+    N, K = 1027, 512
+    p = synth.make_problem(M, N, K, 4, 64, "f16", seed=M)
+    ob = synth.make_out_bias(N, seed=5)
+    note(f"linear zero weights M={M}")
+    x, w, s, b = to_dev(p)
+    s.zero_()
+    b.zero_()
+    y = mxq.mxq_linear(x, w, s, b, _bias_dev(ob), bits=4, group_size=64)
+    want = torch.from_numpy(np.broadcast_to(ob.view(np.int16), (M, N)).copy()).cuda()
+    assert torch.equal(y.view(torch.int16), want), M
+
+
+def test_linear_k0_is_bias():
+    M, N = 9, 77
+    ob = synth.make_out_bias(N, seed=3)
+    note("linear K=0")
+    x = torch.empty((M, 0), dtype=torch.float16, device="cuda")
+    w = torch.empty((N, 0), dtype=torch.int32, device="cuda")
+    s = torch.empty((N, 0), dtype=torch.float16, device="cuda")
+    y = mxq.mxq_linear(x, w, s, s, _bias_dev(ob), bits=4, group_size=64)
+    want = torch.from_numpy(np.broadcast_to(ob.view(np.int16), (M, N)).copy()).cuda()
+    assert torch.equal(y.view(torch.int16), want)

@@ -17,7 +17,7 @@ from tests import pins
 def _namespace(**over):
     ns = types.SimpleNamespace(
         unpack_codes=Q.unpack_codes, widen_sb=Q.widen_sb, dequant_f64=Q.dequant_f64,
-        matmul_ref=Q.matmul_ref, matmul_ref_rows=Q.matmul_ref_rows,
+        matmul_ref=Q.matmul_ref, matmul_ref_rows=Q.matmul_ref_rows, linear_ref=Q.linear_ref,
         dequant_ref_out=Q.dequant_ref_out, f32_to_bf16_bits=Q.f32_to_bf16_bits)
     for k, v in over.items():
         setattr(ns, k, v)
@@ -40,6 +40,14 @@ def _namespace(**over):
         return ns.matmul_ref(x, np.asarray(w)[rows], np.asarray(s)[rows], np.asarray(b)[rows],
                              K, bits, gs, sb)
 
+    def linear_ref(x, w, s, b, ob, K, bits, gs, sb):
+        y = ns.matmul_ref(x, w, s, b, K, bits, gs, sb)
+        if "linear_bias" in over:
+            return over["linear_bias"](y, ob)
+        if ob is None:
+            return y
+        return y + np.asarray(ob, np.uint16).view(np.float16).astype(np.float64)[None, :]
+
     def dequant_ref_out(w, s, b, K, bits, gs, sb, out):
         w64 = ns.dequant_f64(w, s, b, K, bits, gs, sb)
         if "out_cast" in over:
@@ -53,6 +61,7 @@ def _namespace(**over):
 
     ns.dequant_f64, ns.matmul_ref = dequant_f64, matmul_ref
     ns.matmul_ref_rows, ns.dequant_ref_out = matmul_ref_rows, dequant_ref_out
+    ns.linear_ref = linear_ref
     return ns
 
 
@@ -131,7 +140,15 @@ def _f16_direct_from_f64(w64, out, ns):
     return w32 if out == "f32" else ns.f32_to_bf16_bits(w32)
 
 
+def _ob(ob):
+    return np.asarray(ob, np.uint16).view(np.float16).astype(np.float64)
+
+
 MUTANTS = {
+    "out_bias_dropped": dict(linear_bias=lambda y, ob: y),
+    "out_bias_negated": dict(linear_bias=lambda y, ob: y if ob is None else y - _ob(ob)[None, :]),
+    "out_bias_wrong_axis": dict(linear_bias=lambda y, ob: y if ob is None else y + _ob(ob)[:, None]),
+    "out_bias_without_bias_arg": dict(linear_bias=lambda y, ob: y + 1.0 if ob is None else y + _ob(ob)[None, :]),
     "msb_first": dict(unpack_codes=_msb_first),
     "shift_off_by_one": dict(unpack_codes=_shift_off_by_one),
     "mask_too_narrow": dict(unpack_codes=_mask_too_narrow),
