@@ -338,12 +338,13 @@ const char* mxq_describe(const char* op, int64_t M, int64_t N, int64_t K, int bi
   const char* sb = sb_dtype == MXQ_BF16 ? "bf16" : "f16";
   const bool mfma = o == "qmm" && mxq::qmm_mfma_shape(M, K);
   if (mfma) {
-    const mxq::QmmTile tl = mxq::qmm_pick_tile(M, N, dev);
+    const mxq::QmmTile tl = mxq::qmm_pick_tile(M, N, K, dev);
     const int64_t bm = 64 * tl.mb, bn = 64 * tl.nb;
     const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
     desc = "qmm_kernel<bits=" + std::to_string(bits) + ",sb=" + sb + ",gs=" + std::to_string(group_size) +
-           ",tile=" + std::to_string(bm) + "x" + std::to_string(bn) + "> grid=" + std::to_string(tiles) +
-           " block=512";
+           ",tile=" + std::to_string(bm) + "x" + std::to_string(bn) +
+           (tl.splits > 1 ? ",ksplit=" + std::to_string(tl.splits) : std::string()) +
+           "> grid=" + std::to_string(tiles * tl.splits) + " block=512";
     return desc.c_str();
   }
   int mt_max = 8;

@@ -91,6 +91,8 @@ struct QmmArgs {
   const uint16_t* b;
   uint16_t* y;
   const uint16_t* ob;  // f16 bits [N], added to every row of y, or null
+  float* part;         // split-K workspace [splits, M, N] (set by launch_qmm)
+  int splits;
   int64_t M, N, K;
   int bits;
   int group_size;
@@ -99,11 +101,12 @@ struct QmmArgs {
 };
 
 hipError_t launch_qmm(const QmmArgs& a, const DeviceInfo& dev);
-// MFMA blocks (32 x 32) per wave along M and N; the tile is (64*mb) x (64*nb).
+// MFMA blocks (32 x 32) per wave along M and N (the tile is (64*mb) x (64*nb))
+// and the number of K splits.
 struct QmmTile {
-  int mb, nb;
+  int mb, nb, splits;
 };
-QmmTile qmm_pick_tile(int64_t M, int64_t N, const DeviceInfo& dev);
+QmmTile qmm_pick_tile(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev);
 // Shapes the MFMA kernel takes: M > 8 (smaller M runs the qmv kernel), K a
 // multiple of its 64-code stage, and K < 2^24 so that every per-lane offset
 // within a tile (at most 128 rows of x, W, scales) fits in 32 bits.

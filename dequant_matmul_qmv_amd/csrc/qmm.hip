@@ -181,7 +181,8 @@ __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x
                                                   const uint16_t* __restrict__ S,
                                                   const uint16_t* __restrict__ B,
                                                   uint16_t* __restrict__ y, const uint16_t* __restrict__ ob,
-                                                  int M, int N, int K, int tiles_m, int tiles_n) {
+                                                  float* __restrict__ part, int M, int N, int K, int tiles_m,
+                                                  int tiles_n, int splits, int nks) {
   using C = QmmCfg<BITS, GS, MB, NB>;
   constexpr int BM = C::BM, BN = C::BN, TWM = C::TWM, TWN = C::TWN, PT = C::PT;
   constexpr int XCH = C::XCH, WCH = C::WCH, U4R = C::U4R, WPS = C::WPS, RPS = C::RPS;
@@ -195,9 +196,14 @@ __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x
   uint16_t* bq = sq + BN * SBS;                                  // [BN][SBS]: biases, ring of groups
 
   // ---- tile assignment (XCD-aware when the tile count allows it) ---------
+  // A unit is (K split, tile); with splits > 1 each unit covers nks stages and
+  // writes its f32 partial tile to part[split] for a fixed-order reduction.
   const int T = tiles_m * tiles_n;
-  int tile = blockIdx.x;
-  if ((T & 7) == 0) tile = (blockIdx.x & 7) * (T >> 3) + (blockIdx.x >> 3);
+  const int units = T * splits;
+  int unit = blockIdx.x;
+  if ((units & 7) == 0) unit = (blockIdx.x & 7) * (units >> 3) + (blockIdx.x >> 3);
+  const int split = unit / T;
+  const int tile = unit - split * T;
   const int tn = tile / tiles_m;
   const int tm = tile - tn * tiles_m;
   const int m0 = tm * BM, n0 = tn * BN;
@@ -211,8 +217,9 @@ __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x
   const int hi = lane >> 5;               // k half of this lane in the 32x32 MFMA operands
   const int G = K / GS;
   const int kw = K * BITS / 32;
-  const int nkt = K / KT;
-  const int GR = nkt * RPS;               // ring groups
+  const int kt0 = split * nks;                 // first stage of this unit
+  const int nkt = min(nks, K / KT - kt0);      // stages of this unit (>= 1)
+  const int GR = nkt * RPS;                    // ring groups of this unit
 
   Unpack4 up4;
   up4.magic = kMagic;
@@ -252,7 +259,7 @@ __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x
   u4 wr[WCH];
   uint16_t sv, bv;
   auto gload = [&](int kt) __attribute__((always_inline)) {
-    kt = min(kt, nkt - 1);  // the tail re-reads the last stage; it is never stored where it is read
+    kt = kt0 + min(kt, nkt - 1);  // global stage; the tail re-reads the last one, never stored where it is read
 #pragma unroll
     for (int i = 0; i < XCH; ++i)
       xr[i] = *reinterpret_cast<const u4*>(xbase + static_cast<size_t>(kt) * (KT * 2) + xoff[i]);
@@ -439,19 +446,40 @@ __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x
   __syncthreads();
   if (pipe == 1) return;
   // lane holds column n, rows 8*(r/4) + 4*(lane/32) + r%4 of each 32x32 block
+  float* pout = part != nullptr ? part + static_cast<size_t>(split) * M * N : nullptr;
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       const int n = n0 + bcol + j * 32;
-      const float o = ob != nullptr ? sb_to_f32<false>(ob[min(n, N - 1)]) : 0.0f;  // output bias of column n
+      const float o = (ob != nullptr && pout == nullptr) ? sb_to_f32<false>(ob[min(n, N - 1)]) : 0.0f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float v = acc[i][j][r] + red[((q * MB * NB + i * NB + j) * 16 + r) * 64 + lane] + o;
         const int m = m0 + wm * TWM + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-        if (m < M && n < N) y[static_cast<size_t>(m) * N + n] = f32_to_f16_bits(v);
+        if (m < M && n < N) {
+          if (pout != nullptr) {
+            pout[static_cast<size_t>(m) * N + n] = v;
+          } else {
+            y[static_cast<size_t>(m) * N + n] = f32_to_f16_bits(v);
+          }
+        }
       }
     }
+}
+
+// y = RNE_f16(sum over splits of part[split] (in split order) + out_bias).
+__global__ __launch_bounds__(256) void qmm_split_reduce_kernel(const float* __restrict__ part,
+                                                               const uint16_t* __restrict__ ob,
+                                                               uint16_t* __restrict__ y, int64_t MN, int N,
+                                                               int splits) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < MN; i += stride) {
+    float v = part[i];
+    for (int sp = 1; sp < splits; ++sp) v += part[static_cast<size_t>(sp) * MN + i];
+    if (ob != nullptr) v += sb_to_f32<false>(ob[i % N]);
+    y[i] = f32_to_f16_bits(v);
+  }
 }
 
 template <int BITS, bool SB_BF16, int GS, int MB, int NB>
@@ -463,8 +491,20 @@ static hipError_t launch_qmm_cfg(const QmmArgs& a) {
   const int tiles_m = static_cast<int>((a.M + C::BM - 1) / C::BM);
   const int tiles_n = static_cast<int>((a.N + C::BN - 1) / C::BN);
   const int M = static_cast<int>(a.M), N = static_cast<int>(a.N), K = static_cast<int>(a.K);
-  hipLaunchKernelGGL((qmm_kernel<BITS, SB_BF16, GS, MB, NB>), dim3(tiles_m * tiles_n), dim3(C::NT), C::lds_bytes,
-                     a.stream, a.x, a.w, a.s, a.b, a.y, a.ob, M, N, K, tiles_m, tiles_n);
+  const int nkt = K / KT;
+  int splits = a.part != nullptr ? a.splits : 1;  // the workspace holds a.splits partial tiles
+  const int nks = (nkt + splits - 1) / splits;    // stages per split
+  splits = (nkt + nks - 1) / nks;                 // every split non-empty, never more than a.splits
+  hipLaunchKernelGGL((qmm_kernel<BITS, SB_BF16, GS, MB, NB>), dim3(tiles_m * tiles_n * splits), dim3(C::NT),
+                     C::lds_bytes, a.stream, a.x, a.w, a.s, a.b, a.y, a.ob, a.part, M, N, K, tiles_m, tiles_n,
+                     splits, nks);
+  e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  const int64_t MN = a.M * a.N;
+  int64_t blocks = (MN + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(qmm_split_reduce_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, a.stream,
+                     a.part, a.ob, a.y, MN, N, splits);
   return hipGetLastError();
 }
 
@@ -488,16 +528,43 @@ static hipError_t launch_qmm_shape(const QmmArgs& a) {
 }
 
 // Tile policy: 128 x 128 tiles (64 x 64 per wave) when they alone give every
-// CU a tile, else 64 x 64 tiles, which quadruple the tile count.
-QmmTile qmm_pick_tile(int64_t M, int64_t N, const DeviceInfo& dev) {
+// CU a tile; else, for long K, the same tiles with K split so that tiles x
+// splits fills the CUs (each split at least 8 stages), the partial sums going
+// through a workspace and a fixed-order reduction; else 64 x 64 tiles.
+QmmTile qmm_pick_tile(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) {
   const int64_t big = ((M + 127) / 128) * ((N + 127) / 128);
-  return big >= dev.num_cu ? QmmTile{2, 2} : QmmTile{1, 1};
+  if (big >= dev.num_cu) return QmmTile{2, 2, 1};
+  const int64_t nkt = K / 64;
+  int64_t splits = (dev.num_cu + big - 1) / big;
+  if (splits > nkt / 8) splits = nkt / 8;
+  if (splits >= 2) {
+    const int64_t nks = (nkt + splits - 1) / splits;
+    return QmmTile{2, 2, static_cast<int>((nkt + nks - 1) / nks)};  // no empty split
+  }
+  return QmmTile{1, 1, 1};
 }
 
-hipError_t launch_qmm(const QmmArgs& a, const DeviceInfo& dev) {
-  const QmmTile tl = qmm_pick_tile(a.M, a.N, dev);
-  if (tl.mb == 2 && tl.nb == 2) return launch_qmm_shape<2, 2>(a);
-  return launch_qmm_shape<1, 1>(a);
+hipError_t launch_qmm(const QmmArgs& a0, const DeviceInfo& dev) {
+  const QmmTile tl = qmm_pick_tile(a0.M, a0.N, a0.K, dev);
+  QmmArgs a = a0;
+  a.part = nullptr;
+  a.splits = 1;
+  if (tl.mb == 1) return launch_qmm_shape<1, 1>(a);
+  if (tl.splits == 1) return launch_qmm_shape<2, 2>(a);
+  // split K: an f32 workspace [splits, M, N] from the stream-ordered pool,
+  // released in stream order after the reduction
+  void* ws = nullptr;
+  const size_t bytes = static_cast<size_t>(tl.splits) * static_cast<size_t>(a.M) * static_cast<size_t>(a.N) * 4;
+  hipError_t e = hipMallocAsync(&ws, bytes, a.stream);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return launch_qmm_shape<1, 1>(a);  // no workspace: the unsplit small-tile kernel
+  }
+  a.part = static_cast<float*>(ws);
+  a.splits = tl.splits;
+  e = launch_qmm_shape<2, 2>(a);
+  const hipError_t ef = hipFreeAsync(ws, a.stream);
+  return e != hipSuccess ? e : ef;
 }
 
 }  // namespace mxq

@@ -71,5 +71,7 @@ def test_describe_on_device():
     d = mxq.mxq_describe("qmm", 512, 8192, 2048, 4, 64, "f16")
     assert d.startswith("qmm_kernel<bits=4,sb=f16,gs=64,tile=128x128> grid=256 block=512"), d
     d = mxq.mxq_describe("qmm", 512, 2048, 8192, 4, 64, "f16")
-    assert d.startswith("qmm_kernel<bits=4,sb=f16,gs=64,tile=64x64> grid=256 block=512"), d
+    assert d.startswith("qmm_kernel<bits=4,sb=f16,gs=64,tile=128x128,ksplit=4> grid=256 block=512"), d
+    d = mxq.mxq_describe("qmm", 64, 256, 256, 4, 64, "f16")   # too few stages to split
+    assert d.startswith("qmm_kernel<bits=4,sb=f16,gs=64,tile=64x64> grid=4 block=512"), d
     assert mxq.mxq_describe("qmm", 4, 100, 2048, 4, 64, "f16").startswith("qmv_kernel")
