@@ -475,11 +475,21 @@ def main():
                                   torch.from_numpy(b.view(np.int16)).view(sbt).to(dev),
                                   torch.empty((512, N), dtype=torch.float16, device=dev),
                                   512, N, K, 4, 64, 0 if sb == "f16" else 1, name))
-            t = per_launch_times(torch, [calls], reps=30)
+            # back-to-back calls per projection (a prefill runs them in a row):
+            # one event pair around 20 calls after warm-up
+            st = cur_stream(torch)
             entry = {}
             tot_flop, tot_ms = 0, 0.0
             for c in calls:
-                ms = float(np.median(t[c.name]))
+                for _ in range(5):
+                    c(st)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(20):
+                    c(st)
+                e1.record()
+                torch.cuda.synchronize()
+                ms = e0.elapsed_time(e1) / 20
                 flop = 2 * c.M * c.N * c.K
                 entry[c.name] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(flop / (ms / 1e3) / 1e12, 1)}
                 tot_flop += flop

@@ -36,6 +36,8 @@
 // the compiler's load counters exact.  Tiles are assigned so that consecutive
 // tiles on one XCD (dispatch is round-robin over the 8 XCDs) share a slice
 // of W, for L2 reuse.
+#include <atomic>
+#include <cstdint>
 #include <type_traits>
 
 #include "mxq_device.h"
@@ -468,17 +470,29 @@ __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x
     }
 }
 
-// y = RNE_f16(sum over splits of part[split] (in split order) + out_bias).
+// y = RNE_f16(sum over splits of part[split] (in split order) + out_bias);
+// four consecutive elements per thread (the workspace is 256-byte aligned and
+// MN is a multiple of 4 on this path, checked by the host).
 __global__ __launch_bounds__(256) void qmm_split_reduce_kernel(const float* __restrict__ part,
                                                                const uint16_t* __restrict__ ob,
                                                                uint16_t* __restrict__ y, int64_t MN, int N,
                                                                int splits) {
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < MN; i += stride) {
-    float v = part[i];
-    for (int sp = 1; sp < splits; ++sp) v += part[static_cast<size_t>(sp) * MN + i];
-    if (ob != nullptr) v += sb_to_f32<false>(ob[i % N]);
-    y[i] = f32_to_f16_bits(v);
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x * 4;
+  for (int64_t i = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 4; i < MN; i += stride) {
+    float4 v = *reinterpret_cast<const float4*>(part + i);
+    for (int sp = 1; sp < splits; ++sp) {
+      const float4 u = *reinterpret_cast<const float4*>(part + static_cast<size_t>(sp) * MN + i);
+      v.x += u.x;
+      v.y += u.y;
+      v.z += u.z;
+      v.w += u.w;
+    }
+    float o[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (ob != nullptr) o[e] += sb_to_f32<false>(ob[(i + e) % N]);
+      y[i + e] = f32_to_f16_bits(o[e]);
+    }
   }
 }
 
@@ -501,7 +515,7 @@ static hipError_t launch_qmm_cfg(const QmmArgs& a) {
   e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   const int64_t MN = a.M * a.N;
-  int64_t blocks = (MN + 255) / 256;
+  int64_t blocks = (MN / 4 + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   hipLaunchKernelGGL(qmm_split_reduce_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, a.stream,
                      a.part, a.ob, a.y, MN, N, splits);
@@ -544,6 +558,20 @@ QmmTile qmm_pick_tile(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) {
   return QmmTile{1, 1, 1};
 }
 
+// Raise the default memory pool's release threshold once per device so that
+// memory freed back to the pool stays mapped for the next call.
+static void keep_pool_memory(int device) {
+  static std::atomic<uint64_t> done{0};
+  if (device < 0 || device >= 64 || (done.load() >> device) & 1u) return;
+  hipMemPool_t pool = nullptr;
+  if (hipDeviceGetDefaultMemPool(&pool, device) == hipSuccess && pool != nullptr) {
+    uint64_t threshold = UINT64_MAX;
+    (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &threshold);
+  }
+  (void)hipGetLastError();
+  done.fetch_or(uint64_t{1} << device);
+}
+
 hipError_t launch_qmm(const QmmArgs& a0, const DeviceInfo& dev) {
   const QmmTile tl = qmm_pick_tile(a0.M, a0.N, a0.K, dev);
   QmmArgs a = a0;
@@ -551,8 +579,11 @@ hipError_t launch_qmm(const QmmArgs& a0, const DeviceInfo& dev) {
   a.splits = 1;
   if (tl.mb == 1) return launch_qmm_shape<1, 1>(a);
   if (tl.splits == 1) return launch_qmm_shape<2, 2>(a);
+  if ((a.M * a.N) % 4 != 0) return launch_qmm_shape<1, 1>(a);  // the reduction works in fours
   // split K: an f32 workspace [splits, M, N] from the stream-ordered pool,
-  // released in stream order after the reduction
+  // released in stream order after the reduction.  The pool is told once per
+  // device to keep freed memory (so steady-state calls reuse it).
+  keep_pool_memory(dev.device);
   void* ws = nullptr;
   const size_t bytes = static_cast<size_t>(tl.splits) * static_cast<size_t>(a.M) * static_cast<size_t>(a.N) * 4;
   hipError_t e = hipMallocAsync(&ws, bytes, a.stream);
