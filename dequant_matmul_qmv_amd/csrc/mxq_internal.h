@@ -24,19 +24,26 @@ hipError_t ensure_dynamic_lds(const void* kernel, size_t bytes);
 // size, scale dtype and the activation row count are common).  Passed by value
 // as the kernel argument: no device allocation, safe under graph capture.
 constexpr int kMaxGroup = 16;
+// One problem of a grouped launch: 64 bytes, so a workgroup fetches all of its
+// fields with one scalar load once it knows its problem.
+struct QmvSlot {
+  const uint16_t* x;
+  const uint32_t* w;
+  const uint16_t* s;
+  const uint16_t* b;
+  uint16_t* y;
+  const uint16_t* ob;  // f16 output bias [N] or null
+  int N;
+  int K;
+  int block_begin;     // first block of the grid that works on this problem
+  int nblk;            // blocks working on it
+};
+static_assert(sizeof(QmvSlot) == 64, "one 64-byte scalar load per problem");
 struct QmvBatch {
-  const uint16_t* x[kMaxGroup];
-  const uint32_t* w[kMaxGroup];
-  const uint16_t* s[kMaxGroup];
-  const uint16_t* b[kMaxGroup];
-  uint16_t* y[kMaxGroup];
-  const uint16_t* ob[kMaxGroup];  // f16 output bias [N] or null
-  int N[kMaxGroup];
-  int K[kMaxGroup];
-  int xvec[kMaxGroup];
-  int block_begin[kMaxGroup + 1];
-  int count;
+  int block_end[kMaxGroup];  // one past the last block of problem p; INT_MAX past count
   int glog2;
+  int pad[3];
+  QmvSlot prob[kMaxGroup];
 };
 
 struct QmvProblem {

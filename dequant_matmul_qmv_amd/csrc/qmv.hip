@@ -23,11 +23,19 @@
 //    16-byte reads hit consecutive addresses (no bank conflicts), together
 //    with the per-segment sums of x.
 //  * Partial sums of the R*M outputs are reduced across the wave with a
-//    "transpose" butterfly: each stage halves the number of live values per
-//    lane, so R*M values need (R*M - 1) + (6 - log2(R*M)) exchanges instead of
-//    6*R*M.  Everything is in a fixed order: results are deterministic.
+//    "transpose" butterfly: each cross-lane exchange stage halves the number
+//    of live values per lane (R*M - 1 exchanges instead of 6*R*M), after which
+//    each value's partial sums lie in an aligned group of 64/(R*M) lanes and
+//    are summed with DPP row moves (no LDS round trips, which dominate the
+//    latency of the small launches).  Everything is in a fixed order: results
+//    are deterministic.
+//  * The kernel argument holds one 64-byte record per problem of a grouped
+//    launch; a workgroup finds its problem from the block ranges with scalar
+//    selects and fetches the record with one scalar load, so two dependent
+//    scalar round trips precede the first weight load.
 //  * Workgroups are persistent (grid-stride over row blocks) so the x staging
 //    is paid once per workgroup, not once per row block.
+#include <climits>
 #include <map>
 #include <mutex>
 #include <tuple>
@@ -50,6 +58,28 @@ __host__ __device__ constexpr size_t qmv_lds_bytes(int MT, int K) {
          (SegTraits<BITS>::kChunksPerSeg * 16 + 4);
 }
 
+constexpr int kQmvBlock = 256;  // threads per workgroup (the host always launches this many)
+
+// Sum of v over each aligned group of L lanes (L a power of two <= 64), left
+// in the group's last lane (for L <= 16 in every lane of the group), through
+// DPP moves: two quad swaps, the half-row and row mirrors, then the row
+// broadcasts of lane 15 into the next row and of lane 31 into rows 2 and 3
+// (rows the broadcast does not write add zero).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f32(float u) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(u), CTRL, ROW_MASK, 0xF, false));
+}
+template <int L>
+__device__ __forceinline__ float group_sum_to_last(float v) {
+  if constexpr (L >= 2) v += dpp_f32<0xB1, 0xF>(v);   // quad_perm 1,0,3,2
+  if constexpr (L >= 4) v += dpp_f32<0x4E, 0xF>(v);   // quad_perm 2,3,0,1
+  if constexpr (L >= 8) v += dpp_f32<0x141, 0xF>(v);  // row_half_mirror
+  if constexpr (L >= 16) v += dpp_f32<0x140, 0xF>(v); // row_mirror
+  if constexpr (L >= 32) v += dpp_f32<0x142, 0xA>(v); // row_bcast:15 into rows 1 and 3
+  if constexpr (L >= 64) v += dpp_f32<0x143, 0xC>(v); // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
 // Loads of one work item: R rows x one 16-byte segment, plus their scales and biases.
 template <int R>
 struct QmvItem {
@@ -59,21 +89,25 @@ struct QmvItem {
 };
 
 template <int BITS, bool SB_BF16, int MT, int R, bool XD>
-__global__ __launch_bounds__(256) void qmv_kernel(const QmvBatch batch) {
-  // This workgroup's problem: blocks [block_begin[p], block_begin[p+1]) of the
-  // grid belong to problem p (wave-uniform scalar search over <= 16 entries).
+__global__ __launch_bounds__(kQmvBlock) void qmv_kernel(const QmvBatch batch) {
+  // This workgroup's problem: the number of problems whose block range ends
+  // at or before this block (every block_end is read in one go, so the problem
+  // fields follow after a single dependent scalar load).
   int p = 0;
-  while (p + 1 < batch.count && static_cast<int>(blockIdx.x) >= batch.block_begin[p + 1]) ++p;
-  const int blk = static_cast<int>(blockIdx.x) - batch.block_begin[p];
-  const int nblk = batch.block_begin[p + 1] - batch.block_begin[p];
-  const uint16_t* __restrict__ x = batch.x[p];
-  const uint32_t* __restrict__ W = batch.w[p];
-  const uint16_t* __restrict__ S = batch.s[p];
-  const uint16_t* __restrict__ B = batch.b[p];
-  uint16_t* __restrict__ y = batch.y[p];
-  const uint16_t* __restrict__ ob = batch.ob[p];
+#pragma unroll
+  for (int i = 0; i + 1 < kMaxGroup; ++i) p = static_cast<int>(blockIdx.x) >= batch.block_end[i] ? i + 1 : p;
+  const QmvSlot& pb = batch.prob[p];
+  const int blk = static_cast<int>(blockIdx.x) - pb.block_begin;
+  const int nblk = pb.nblk;
+  const uint16_t* __restrict__ x = pb.x;
+  const uint32_t* __restrict__ W = pb.w;
+  const uint16_t* __restrict__ S = pb.s;
+  const uint16_t* __restrict__ B = pb.b;
+  uint16_t* __restrict__ y = pb.y;
+  const uint16_t* __restrict__ ob = pb.ob;
   const bool has_ob = ob != nullptr;
-  const int N = batch.N[p], K = batch.K[p], x_vec = batch.xvec[p], glog2 = batch.glog2;
+  const int N = pb.N, K = pb.K, glog2 = batch.glog2;
+  const bool x_vec = (reinterpret_cast<uintptr_t>(x) & 15u) == 0;
   constexpr int CPS = SegTraits<BITS>::kChunksPerSeg;
   constexpr int CODES = SegTraits<BITS>::kCodesPerSeg;
   constexpr int NP = (BITS == 4) ? 16 : 8;  // f16 code pairs per segment
@@ -102,7 +136,7 @@ __global__ __launch_bounds__(256) void qmv_kernel(const QmvBatch batch) {
   // and each load adds one 32-bit per-lane offset to a scalar base (the caller
   // guarantees W, S and B are each below 4 GiB)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int waves_per_block = blockDim.x >> 6;
+  constexpr int waves_per_block = kQmvBlock / kWave;
   const int nrb = (N + R - 1) / R;
   const int jn = (nseg + kWave - 1) / kWave;
   const int stride = nblk * waves_per_block;
@@ -194,7 +228,7 @@ __global__ __launch_bounds__(256) void qmv_kernel(const QmvBatch batch) {
     }
     if (rb >= nrb) return;
   } else {
-    for (int u = threadIdx.x; u < MT * nseg; u += blockDim.x) {
+    for (int u = threadIdx.x; u < MT * nseg; u += kQmvBlock) {
       const int m = u / nseg;
       const int seg = u - m * nseg;
       u4 v[CPS];
@@ -320,6 +354,9 @@ __global__ __launch_bounds__(256) void qmv_kernel(const QmvBatch batch) {
     if (!block_done) return;
 
     // ---- transpose butterfly over the 64 lanes -------------------------
+    // While several values are live per lane, each stage swaps halves with
+    // the lane `off` away; then each value's partial sums sit in an aligned
+    // group of kLow lanes and are summed within the group with DPP moves.
     float v[VP];
 #pragma unroll
     for (int i = 0; i < VP; ++i) v[i] = (i < V) ? acc[i / MT][i % MT] : 0.0f;
@@ -336,13 +373,13 @@ __global__ __launch_bounds__(256) void qmv_kernel(const QmvBatch batch) {
           const float keep = upper ? v[i + h] : v[i];
           v[i] = keep + __shfl_xor(send, off, kWave);
         }
-      } else {
-        v[0] += __shfl_xor(v[0], off, kWave);
       }
     }
-    // lane holds value index idx = sum over halving stages of bit(lane, off) * h
     constexpr int kLow = kWave / VP;  // lanes sharing one value index
-    if ((lane & (kLow - 1)) == 0) {
+    v[0] = group_sum_to_last<kLow>(v[0]);
+    // the group's last lane holds the total; its value index is the sum over
+    // the exchange stages of bit(lane, off) * h (bits above the group)
+    if ((lane & (kLow - 1)) == kLow - 1) {
       int idx = 0;
 #pragma unroll
       for (int s = 0; s < 6; ++s) {
@@ -479,7 +516,7 @@ int blocks_per_cu(const DeviceInfo& dev, const void* kern, size_t lds) {
     if (it != g_occ.end()) return it->second;
   }
   int nb = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, 256, lds) != hipSuccess || nb < 1) {
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, kQmvBlock, lds) != hipSuccess || nb < 1) {
     (void)hipGetLastError();
     nb = 1;
   }
@@ -551,25 +588,26 @@ hipError_t launch_qmv_group(const QmvProblem* probs, int count, int bits, int gl
     if (e != hipSuccess) return e;
   }
   QmvBatch batch{};
-  batch.count = count;
   batch.glog2 = glog2;
   int begin = 0;
+  for (int i = 0; i < kMaxGroup; ++i) batch.block_end[i] = INT_MAX;
   for (int i = 0; i < count; ++i) {
-    batch.x[i] = probs[i].x;
-    batch.w[i] = probs[i].w;
-    batch.s[i] = probs[i].s;
-    batch.b[i] = probs[i].b;
-    batch.y[i] = probs[i].y;
-    batch.ob[i] = probs[i].ob;
-    batch.N[i] = static_cast<int>(probs[i].N);
-    batch.K[i] = static_cast<int>(probs[i].K);
-    batch.xvec[i] = (reinterpret_cast<uintptr_t>(probs[i].x) & 15u) == 0 ? 1 : 0;
-    batch.block_begin[i] = begin;
+    QmvSlot& q = batch.prob[i];
+    q.x = probs[i].x;
+    q.w = probs[i].w;
+    q.s = probs[i].s;
+    q.b = probs[i].b;
+    q.y = probs[i].y;
+    q.ob = probs[i].ob;
+    q.N = static_cast<int>(probs[i].N);
+    q.K = static_cast<int>(probs[i].K);
+    q.block_begin = begin;
+    q.nblk = grids[i];
     begin += grids[i];
+    batch.block_end[i] = begin;
   }
-  batch.block_begin[count] = begin;
   void* args[] = {&batch};
-  return hipLaunchKernel(p.kernel, dim3(begin), dim3(256), args, p.lds, stream);
+  return hipLaunchKernel(p.kernel, dim3(begin), dim3(kQmvBlock), args, p.lds, stream);
 }
 
 hipError_t launch_qmv_slice(const QmvArgs& a, const DeviceInfo& dev, int mt) {
