@@ -39,11 +39,14 @@ struct QmvSlot {
   int nblk;            // blocks working on it
 };
 static_assert(sizeof(QmvSlot) == 64, "one 64-byte scalar load per problem");
+// Problem 0 sits next to the block ranges, so single-problem launches (and
+// the blocks of a group's first problem) read everything in one round trip.
 struct QmvBatch {
   int block_end[kMaxGroup];  // one past the last block of problem p; INT_MAX past count
+  QmvSlot first;             // problem 0
   int glog2;
-  int pad[3];
-  QmvSlot prob[kMaxGroup];
+  int pad[15];
+  QmvSlot rest[kMaxGroup - 1];  // problems 1 ..
 };
 
 struct QmvProblem {

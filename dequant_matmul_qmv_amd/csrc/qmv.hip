@@ -31,8 +31,9 @@
 //    are deterministic.
 //  * The kernel argument holds one 64-byte record per problem of a grouped
 //    launch; a workgroup finds its problem from the block ranges with scalar
-//    selects and fetches the record with one scalar load, so two dependent
-//    scalar round trips precede the first weight load.
+//    selects and fetches the record with one scalar load.  The first
+//    problem's record is read with the block ranges, so single-problem
+//    launches wait for one scalar round trip before the first weight load.
 //  * Workgroups are persistent (grid-stride over row blocks) so the x staging
 //    is paid once per workgroup, not once per row block.
 #include <climits>
@@ -91,12 +92,23 @@ struct QmvItem {
 template <int BITS, bool SB_BF16, int MT, int R, bool XD>
 __global__ __launch_bounds__(kQmvBlock) void qmv_kernel(const QmvBatch batch) {
   // This workgroup's problem: the number of problems whose block range ends
-  // at or before this block (every block_end is read in one go, so the problem
-  // fields follow after a single dependent scalar load).
+  // at or before this block.  The block ranges, problem 0's record and the
+  // group size are read in one batch of scalar loads (an empty asm use of all
+  // of them keeps the compiler from spreading them over several round trips);
+  // blocks of the other problems then fetch their record with one more.
+  QmvSlot pb = batch.first;
+  const int glog2 = batch.glog2;
+  int ends[kMaxGroup - 1];
+#pragma unroll
+  for (int i = 0; i + 1 < kMaxGroup; ++i) ends[i] = batch.block_end[i];
+  asm volatile("" ::"s"(pb.x), "s"(pb.w), "s"(pb.s), "s"(pb.b), "s"(pb.y), "s"(pb.ob), "s"(pb.N), "s"(pb.K),
+               "s"(pb.block_begin), "s"(pb.nblk), "s"(glog2), "s"(ends[0]), "s"(ends[1]), "s"(ends[2]),
+               "s"(ends[3]), "s"(ends[4]), "s"(ends[5]), "s"(ends[6]), "s"(ends[7]), "s"(ends[8]), "s"(ends[9]),
+               "s"(ends[10]), "s"(ends[11]), "s"(ends[12]), "s"(ends[13]), "s"(ends[14]));
   int p = 0;
 #pragma unroll
-  for (int i = 0; i + 1 < kMaxGroup; ++i) p = static_cast<int>(blockIdx.x) >= batch.block_end[i] ? i + 1 : p;
-  const QmvSlot& pb = batch.prob[p];
+  for (int i = 0; i + 1 < kMaxGroup; ++i) p = static_cast<int>(blockIdx.x) >= ends[i] ? i + 1 : p;
+  if (p != 0) pb = batch.rest[p - 1];
   const int blk = static_cast<int>(blockIdx.x) - pb.block_begin;
   const int nblk = pb.nblk;
   const uint16_t* __restrict__ x = pb.x;
@@ -106,7 +118,7 @@ __global__ __launch_bounds__(kQmvBlock) void qmv_kernel(const QmvBatch batch) {
   uint16_t* __restrict__ y = pb.y;
   const uint16_t* __restrict__ ob = pb.ob;
   const bool has_ob = ob != nullptr;
-  const int N = pb.N, K = pb.K, glog2 = batch.glog2;
+  const int N = pb.N, K = pb.K;
   const bool x_vec = (reinterpret_cast<uintptr_t>(x) & 15u) == 0;
   constexpr int CPS = SegTraits<BITS>::kChunksPerSeg;
   constexpr int CODES = SegTraits<BITS>::kCodesPerSeg;
@@ -592,7 +604,7 @@ hipError_t launch_qmv_group(const QmvProblem* probs, int count, int bits, int gl
   int begin = 0;
   for (int i = 0; i < kMaxGroup; ++i) batch.block_end[i] = INT_MAX;
   for (int i = 0; i < count; ++i) {
-    QmvSlot& q = batch.prob[i];
+    QmvSlot& q = i == 0 ? batch.first : batch.rest[i - 1];
     q.x = probs[i].x;
     q.w = probs[i].w;
     q.s = probs[i].s;
