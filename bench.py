@@ -7,8 +7,8 @@ gate/up 8192x2048, down 2048x8192, lm_head 128256x2048; N x K, g64, f16
 scales/biases, f16 x ~ N(0,1)).  One step = every projection once, launched
 as a decoder layer allows: projections reading the same activation share one
 mxq_qmv_grouped launch -- {q,k,v}, {o}, {gate,up}, {down}, {lm_head}, 5
-launches (the 8-launch and 1-launch plans are reported too).  The projection set is replicated REPLICAS times with distinct
-seeded weights (~1.1 GB in total) and the steps cycle through the replicas,
+launches (the 8-launch and 1-launch plans are reported too).  The projection
+set is replicated REPLICAS times with distinct seeded weights (~1.1 GB in total) and the steps cycle through the replicas,
 so every step streams its weights from HBM, not from the 256 MB Infinity
 Cache.  value = algorithmic bytes per step / time per step.
 
@@ -18,11 +18,13 @@ Extra objects on the same line:
                 against the 8 TB/s HBM peak;  traffic from committed rocprofv3
                 PMC counters when they match the current kernel source;
   cpu_baseline  the f64 CPU oracle on a bounded sample, single BLAS thread;
-  decode_step   16 layers x {q,k,v,o,gate,up,down} + lm_head (113 launches,
-                ~697 MB of distinct weights): bytes/step, GB/s, steps/s;
+  decode_step   16 layers x {q,k,v,o,gate,up,down} + lm_head, ~697 MB of
+                distinct weights, as 113 separate launches and as 65 grouped
+                launches (eager and graph replay): bytes/step, GB/s, steps/s;
   qmm           M=512 prefill on gate/up (8192x2048) and down (2048x8192),
-                f16 and bf16 scales: TFLOP/s and MFMA utilisation (of the
-                2.5 PFLOP/s dense f16 peak);
+                f16 and bf16 scales, 20 calls back to back per projection:
+                TFLOP/s and MFMA utilisation (of the 2.5 PFLOP/s dense f16
+                peak);
   dequant       standalone dequant of the lm_head weights to f32, GB/s.
 """
 

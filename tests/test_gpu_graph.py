@@ -20,15 +20,23 @@ def test_graph_replay_matches_eager():
     dev = "cuda:0"
     pv = synth.make_problem(1, 3000, 2048, 4, 64, "f16", seed=61)
     pm = synth.make_problem(80, 500, 1024, 8, 64, "bf16", seed=62)
+    # 1 x 4 tiles of 128 x 128 and 64 stages: the split-K path, whose workspace
+    # comes from the stream-ordered pool inside the captured graph
+    ps = synth.make_problem(128, 512, 4096, 4, 64, "f16", seed=63)
+    assert mxq.mxq_describe("qmm", 128, 512, 4096, 4, 64, "f16").startswith(
+        "qmm_kernel<bits=4,sb=f16,gs=64,tile=128x128,ksplit=")
     xv, wv, sv, bv = to_dev(pv)
     xm, wm, sm, bm = to_dev(pm)
+    xs, ws, ss, bs = to_dev(ps)
     yv = torch.empty((1, 3000), dtype=torch.float16, device=dev)
     ym = torch.empty((80, 500), dtype=torch.float16, device=dev)
+    ys = torch.empty((128, 512), dtype=torch.float16, device=dev)
     dq = torch.empty((500, 1024), dtype=torch.float32, device=dev)
 
     def work():
         mxq.mxq_qmv(xv, wv, sv, bv, yv, bits=4)
         mxq.mxq_qmm(xm, wm, sm, bm, ym, bits=8)
+        mxq.mxq_qmm(xs, ws, ss, bs, ys, bits=4)
         mxq.mxq_dequant(wm, sm, bm, dq, bits=8)
 
     s = torch.cuda.Stream()
@@ -47,19 +55,23 @@ def test_graph_replay_matches_eager():
     for rep in range(4):
         new_xv = torch.from_numpy(rng.standard_normal((1, 2048)).astype(np.float16)).to(dev)
         new_xm = torch.from_numpy(rng.standard_normal((80, 1024)).astype(np.float16)).to(dev)
+        new_xs = torch.from_numpy(rng.standard_normal((128, 4096)).astype(np.float16)).to(dev)
         xv.copy_(new_xv)
         xm.copy_(new_xm)
+        xs.copy_(new_xs)
         torch.cuda.synchronize()
         note(f"graph replay {rep}")
         g.replay()
         torch.cuda.synchronize()
-        got_v, got_m, got_d = yv.clone(), ym.clone(), dq.clone()
+        got_v, got_m, got_s, got_d = yv.clone(), ym.clone(), ys.clone(), dq.clone()
         ev = mxq.mxq_qmv(new_xv, wv, sv, bv, bits=4)
         em = mxq.mxq_qmm(new_xm, wm, sm, bm, bits=8)
+        es = mxq.mxq_qmm(new_xs, ws, ss, bs, bits=4)
         ed = mxq.mxq_dequant(wm, sm, bm, bits=8)
         torch.cuda.synchronize()
         assert torch.equal(got_v.view(torch.int16), ev.view(torch.int16)), rep
         assert torch.equal(got_m.view(torch.int16), em.view(torch.int16)), rep
+        assert torch.equal(got_s.view(torch.int16), es.view(torch.int16)), rep
         assert torch.equal(got_d.view(torch.int32), ed.view(torch.int32)), rep
 
 
