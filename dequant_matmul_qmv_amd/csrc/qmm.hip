@@ -36,9 +36,11 @@
 // the compiler's load counters exact.  Tiles are assigned so that consecutive
 // tiles on one XCD (dispatch is round-robin over the 8 XCDs) share a slice
 // of W, for L2 reuse.
-#include <atomic>
 #include <cstdint>
+#include <map>
+#include <mutex>
 #include <type_traits>
+#include <utility>
 
 #include "mxq_device.h"
 #include "mxq_internal.h"
@@ -419,17 +421,24 @@ __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x
   // prefetches 2pr + 4; pipeline 1 stages 2pr + 3 and prefetches 2pr + 5,
   // then computes 2pr + 1.  One barrier; a single loop exit keeps the
   // compiler's wait analysis exact.
+  // The staging work (the longer dependent chain of the two) runs at a raised
+  // wave priority, so on each SIMD it wins issue slots over the other wave's
+  // scale FMAs and LDS reads while that wave's MFMAs run (measured 2-6 %).
   const int npair = (nkt + 1) >> 1;
   for (int pr = 0; pr < npair; ++pr) {
     const int kt = 2 * pr + pipe;
     if (pipe == 1) {
+      __builtin_amdgcn_s_setprio(1);
       lstore(kt + 2);
       gload(kt + 4);
+      __builtin_amdgcn_s_setprio(0);
     }
     if (kt < nkt) compute(kt);
     if (pipe == 0) {
+      __builtin_amdgcn_s_setprio(1);
       lstore(kt + 2);
       gload(kt + 4);
+      __builtin_amdgcn_s_setprio(0);
     }
     __syncthreads();
   }
@@ -558,19 +567,35 @@ QmmTile qmm_pick_tile(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) {
   return QmmTile{1, 1, 1};
 }
 
-// Raise the default memory pool's release threshold once per device so that
-// memory freed back to the pool stays mapped for the next call.
-static void keep_pool_memory(int device) {
-  static std::atomic<uint64_t> done{0};
-  if (device < 0 || device >= 64 || (done.load() >> device) & 1u) return;
-  hipMemPool_t pool = nullptr;
-  if (hipDeviceGetDefaultMemPool(&pool, device) == hipSuccess && pool != nullptr) {
-    uint64_t threshold = UINT64_MAX;
-    (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &threshold);
+// Split-K workspace, one per (device, stream): grown on demand with a
+// stream-ordered allocation (the old buffer is released in stream order, after
+// the work that used it) and kept until the process ends.  Calls on one stream
+// are ordered, so they may share it; calls on different streams use different
+// buffers.  A stream being captured into a graph never uses the cache: its
+// workspace is allocated and freed inside the graph (graph-owned memory is only
+// valid during replays).  An allocation and free per call cost ~4 us of stream
+// time at M = 512, which is why the cache exists.
+namespace {
+std::mutex g_ws_mu;
+std::map<std::pair<int, hipStream_t>, std::pair<void*, size_t>> g_ws;
+
+// Called with g_ws_mu held, which the caller keeps until its kernels are
+// enqueued: another thread growing the same stream's buffer then frees it only
+// after those kernels in stream order.
+void* cached_workspace(int device, hipStream_t stream, size_t bytes) {
+  auto& e = g_ws[std::make_pair(device, stream)];
+  if (e.first != nullptr && e.second >= bytes) return e.first;
+  if (e.first != nullptr) (void)hipFreeAsync(e.first, stream);
+  e = std::make_pair(nullptr, size_t{0});
+  void* p = nullptr;
+  if (hipMallocAsync(&p, bytes, stream) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
   }
-  (void)hipGetLastError();
-  done.fetch_or(uint64_t{1} << device);
+  e = std::make_pair(p, bytes);
+  return p;
 }
+}  // namespace
 
 hipError_t launch_qmm(const QmmArgs& a0, const DeviceInfo& dev) {
   const QmmTile tl = qmm_pick_tile(a0.M, a0.N, a0.K, dev);
@@ -580,19 +605,32 @@ hipError_t launch_qmm(const QmmArgs& a0, const DeviceInfo& dev) {
   if (tl.mb == 1) return launch_qmm_shape<1, 1>(a);
   if (tl.splits == 1) return launch_qmm_shape<2, 2>(a);
   if ((a.M * a.N) % 4 != 0) return launch_qmm_shape<1, 1>(a);  // the reduction works in fours
-  // split K: an f32 workspace [splits, M, N] from the stream-ordered pool,
-  // released in stream order after the reduction.  The pool is told once per
-  // device to keep freed memory (so steady-state calls reuse it).
-  keep_pool_memory(dev.device);
-  void* ws = nullptr;
+  // split K: an f32 workspace [splits, M, N], the stream's cached one, or
+  // under graph capture one allocated and freed inside the graph
   const size_t bytes = static_cast<size_t>(tl.splits) * static_cast<size_t>(a.M) * static_cast<size_t>(a.N) * 4;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(a.stream, &cap) != hipSuccess) {
+    (void)hipGetLastError();
+    cap = hipStreamCaptureStatusNone;
+  }
+  a.splits = tl.splits;
+  if (cap == hipStreamCaptureStatusNone) {
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    a.part = static_cast<float*>(cached_workspace(dev.device, a.stream, bytes));
+    if (a.part == nullptr) {
+      a.splits = 1;
+      return launch_qmm_shape<1, 1>(a);  // no workspace: the unsplit small-tile kernel
+    }
+    return launch_qmm_shape<2, 2>(a);
+  }
+  void* ws = nullptr;
   hipError_t e = hipMallocAsync(&ws, bytes, a.stream);
   if (e != hipSuccess) {
     (void)hipGetLastError();
-    return launch_qmm_shape<1, 1>(a);  // no workspace: the unsplit small-tile kernel
+    a.splits = 1;
+    return launch_qmm_shape<1, 1>(a);
   }
   a.part = static_cast<float*>(ws);
-  a.splits = tl.splits;
   e = launch_qmm_shape<2, 2>(a);
   const hipError_t ef = hipFreeAsync(ws, a.stream);
   return e != hipSuccess ? e : ef;

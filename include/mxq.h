@@ -30,17 +30,16 @@
  * dequant output `out` must be 16-byte aligned.
  *
  * Ownership and threading: every pointer is owned by the caller and must stay
- * valid until the enqueued work has finished.  The library keeps only a
- * per-device cache of device properties, and allocates device memory on one
- * path only: an MFMA call (mxq_qmm / mxq_linear with M > 8) whose 128 x 128
- * output tiles are too few to occupy every compute unit and whose K is long
- * splits K and takes an f32 workspace of splits * M * N floats from the
- * device's default stream-ordered memory pool (hipMallocAsync on `stream`,
- * returned with hipFreeAsync after the fixed-order reduction, so the call
- * stays asynchronous and can be captured in a graph).  On first use the
- * library raises that pool's release threshold so freed workspace stays
- * mapped for the next call.  If the allocation fails, the call runs the
- * unsplit kernel instead.  Calls are thread-safe.
+ * valid until the enqueued work has finished.  The library keeps a per-device
+ * cache of device properties and allocates device memory on one path only: an
+ * MFMA call (mxq_qmm / mxq_linear with M > 8) whose 128 x 128 output tiles are
+ * too few to occupy every compute unit and whose K is long splits K and needs
+ * an f32 workspace of splits * M * N floats.  It uses one workspace per
+ * (device, stream), allocated stream-ordered (hipMallocAsync on `stream`),
+ * grown the same way when a call needs more, and kept until the process ends
+ * (16 MiB for a 512 x 2048 x 8192 call).  On a stream being captured into a
+ * graph the workspace is instead allocated and freed inside the graph.  If the
+ * allocation fails, the call runs the unsplit kernel.  Calls are thread-safe.
  *
  * Asynchrony: a call validates its arguments synchronously, enqueues its
  * kernel(s) on `stream` (a hipStream_t; NULL means the null stream) and
