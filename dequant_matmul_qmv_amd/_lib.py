@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(HERE, "libmxq.so")
 
 MXQ_OK, MXQ_ERR_INVALID_ARG, MXQ_ERR_UNSUPPORTED, MXQ_ERR_MISALIGNED, MXQ_ERR_HIP = range(5)
 MXQ_F16, MXQ_BF16, MXQ_F32 = 0, 1, 2
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 _lock = threading.Lock()
 _lib = None
@@ -52,6 +52,8 @@ def _declare(lib):
         f.argtypes, f.restype = fused, c_int
     lib.mxq_linear.argtypes = [vp, vp, vp, vp, vp, vp, c_i64, c_i64, c_i64, c_int, c_int, c_int, vp]
     lib.mxq_linear.restype = c_int
+    lib.mxq_linear_act.argtypes = [vp, vp, vp, vp, vp, vp, c_i64, c_i64, c_i64, c_int, c_int, c_int, c_int, vp]
+    lib.mxq_linear_act.restype = c_int
     lib.mxq_qmv_grouped.argtypes = [ctypes.POINTER(QmvProblem), c_int, c_i64, c_int, c_int, c_int, vp]
     lib.mxq_qmv_grouped.restype = c_int
     lib.mxq_dequant.argtypes = [vp, vp, vp, vp, c_i64, c_i64, c_int, c_int, c_int, c_int, vp]
@@ -112,12 +114,14 @@ def _stream_handle(dev, stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _check_packed(x, w, scales, biases, bits, group_size, who):
+def _check_packed(x, w, scales, biases, bits, group_size, who, act_dtypes=None):
     torch = _torch()
     if bits not in (4, 8):
         raise ValueError(f"{who}: bits must be 4 or 8")
-    if x.dtype != torch.float16 or x.dim() != 2:
-        raise TypeError(f"{who}: x must be a 2-D float16 tensor")
+    act_dtypes = (torch.float16,) if act_dtypes is None else act_dtypes
+    if x.dtype not in act_dtypes or x.dim() != 2:
+        names = " or ".join(str(d).replace("torch.", "") for d in act_dtypes)
+        raise TypeError(f"{who}: x must be a 2-D {names} tensor")
     if w.dtype not in (torch.int32, torch.uint32) or w.dim() != 2:
         raise TypeError(f"{who}: w must be a 2-D int32/uint32 tensor of packed words")
     if scales.dtype != biases.dtype or scales.shape != biases.shape or scales.dim() != 2:
@@ -216,6 +220,30 @@ def mxq_linear(x, w, scales, biases, bias=None, y=None, *, bits: int = 4, group_
         st = lib.mxq_linear(x.data_ptr(), w.data_ptr(), scales.data_ptr(), biases.data_ptr(),
                             None if bias is None else bias.data_ptr(), y.data_ptr(), M, N, K, bits,
                             group_size, _sb_code(scales), _stream_handle(x.device, stream))
+    _check(lib, st)
+    return y
+
+
+def mxq_linear_act(x, w, scales, biases, bias=None, y=None, *, bits: int = 4, group_size: int = 64,
+                   stream=None):
+    """mxq_linear for float16 or bfloat16 activations: x, the optional output
+    bias [N] and y share x's dtype (float16 gives exactly mxq_linear's result)."""
+    torch = _torch()
+    lib = load()
+    M, N, K = _check_packed(x, w, scales, biases, bits, group_size, "mxq_linear_act",
+                            (torch.float16, torch.bfloat16))
+    act = MXQ_BF16 if x.dtype == torch.bfloat16 else MXQ_F16
+    if bias is not None and (bias.dtype != x.dtype or tuple(bias.shape) != (N,) or not bias.is_cuda
+                             or not bias.is_contiguous() or bias.device != x.device):
+        raise ValueError("mxq_linear_act: bias must be a contiguous [N] tensor of x's dtype on x's device")
+    if y is None:
+        y = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    elif y.dtype != x.dtype or tuple(y.shape) != (M, N) or not y.is_contiguous() or y.device != x.device:
+        raise ValueError("mxq_linear_act: y must be a contiguous [M, N] tensor of x's dtype on x's device")
+    with torch.cuda.device(x.device):
+        st = lib.mxq_linear_act(x.data_ptr(), w.data_ptr(), scales.data_ptr(), biases.data_ptr(),
+                                None if bias is None else bias.data_ptr(), y.data_ptr(), M, N, K, bits,
+                                group_size, _sb_code(scales), act, _stream_handle(x.device, stream))
     _check(lib, st)
     return y
 

@@ -122,6 +122,87 @@ __device__ __forceinline__ float sum8_f32(u4 v) {
   return s;
 }
 
+// ---------------------------------------------------------------------------
+// bf16 activations.  bf16 keeps 7 mantissa bits, so the f16 tricks above change:
+//  * 4-bit codes are injected under the exponent of 128 (bits 0x4300): each
+//    half holds 128 + c exactly.  The offset is not subtracted per code; the
+//    caller folds it into the bias term (sum x*(128 + c) = sum x*c + 128 sum x).
+//    One shift per nibble position, pairs (c0, c4) (c1, c5) (c2, c6) (c3, c7)
+//    as in unpack_w4, so the same activation reorder (perm_x_w4) applies.
+//  * 8-bit codes (up to 255, beyond what the mantissa can hold under a power
+//    of two) are converted exactly: v_cvt_f32_ubyte then a packed f32 -> bf16
+//    conversion, pairs in natural order (c0, c1) (c2, c3).
+// ---------------------------------------------------------------------------
+typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+constexpr uint32_t kMagicB = 0x43004300u;
+
+__device__ __forceinline__ b2 as_b2(uint32_t u) { return __builtin_bit_cast(b2, u); }
+
+// 4-bit word -> (128 + c0, 128 + c4), (128 + c1, 128 + c5), ... as bf16 pairs.
+__device__ __forceinline__ void unpack_w4_bf16_off(uint32_t w, uint32_t magic, uint32_t (&q)[4]) {
+  q[0] = and_or(w, 0x000F000Fu, magic);
+  q[1] = and_or(w >> 4, 0x000F000Fu, magic);
+  q[2] = and_or(w >> 8, 0x000F000Fu, magic);
+  q[3] = and_or(w >> 12, 0x000F000Fu, magic);
+}
+
+// Byte i of w as an f32 integer (v_cvt_f32_ubyte<i>).
+template <int I>
+__device__ __forceinline__ float ubyte_f32(uint32_t w) {
+  return static_cast<float>((w >> (8 * I)) & 0xFFu);
+}
+
+// Two f32 values -> packed bf16 pair (a low, b high), round to nearest even
+// (exact for the small integers it is used on).
+__device__ __forceinline__ uint32_t pack_bf16_pair(float a, float b) {
+  const b2 v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// 8-bit word -> exact bf16 codes (c0, c1), (c2, c3).
+__device__ __forceinline__ void unpack_w8_bf16(uint32_t w, uint32_t (&q)[2]) {
+  q[0] = pack_bf16_pair(ubyte_f32<0>(w), ubyte_f32<1>(w));
+  q[1] = pack_bf16_pair(ubyte_f32<2>(w), ubyte_f32<3>(w));
+}
+
+// 4-bit word -> exact bf16 codes in natural order (c0, c1), (c2, c3), (c4, c5), (c6, c7).
+__device__ __forceinline__ u4 unpack4_bf16_natural(uint32_t w) {
+  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+  return u4{pack_bf16_pair(ubyte_f32<0>(lo), ubyte_f32<0>(hi)),
+            pack_bf16_pair(ubyte_f32<1>(lo), ubyte_f32<1>(hi)),
+            pack_bf16_pair(ubyte_f32<2>(lo), ubyte_f32<2>(hi)),
+            pack_bf16_pair(ubyte_f32<3>(lo), ubyte_f32<3>(hi))};
+}
+
+// 8-bit words w0 (codes 0..3), w1 (codes 4..7) -> exact bf16 codes in natural order.
+__device__ __forceinline__ u4 unpack8_bf16_natural(uint32_t w0, uint32_t w1) {
+  uint32_t a[2], b[2];
+  unpack_w8_bf16(w0, a);
+  unpack_w8_bf16(w1, b);
+  return u4{a[0], a[1], b[0], b[1]};
+}
+
+// Sum of 8 bf16 values held as 4 dwords, in f32, fixed order.
+__device__ __forceinline__ float sum8_f32_bf16(u4 v) {
+  const b2 one = as_b2(0x3F803F80u);
+  float s = __builtin_amdgcn_fdot2_f32_bf16(as_b2(v.x), one, 0.0f, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(as_b2(v.y), one, s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(as_b2(v.z), one, s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(as_b2(v.w), one, s, false);
+  return s;
+}
+
+// Sum of 8 activations of either type (XB: bf16), in f32.
+template <bool XB>
+__device__ __forceinline__ float sum8_act(u4 v) {
+  if constexpr (XB) {
+    return sum8_f32_bf16(v);
+  } else {
+    return sum8_f32(v);
+  }
+}
+
 // Round-to-nearest-even f32 -> f16 bits, of the f32 value itself.  The empty
 // asm makes v opaque: without it the compiler folds a preceding f32 add/fma
 // and this conversion into one v_fma_mixlo_f16, which rounds the exact sum
@@ -138,6 +219,16 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float v) {
   if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
   u += 0x7FFFu + ((u >> 16) & 1u);
   return static_cast<uint16_t>(u >> 16);
+}
+
+// f32 -> stored activation-type bits (XB: bf16, else f16), round to nearest even.
+template <bool XB>
+__device__ __forceinline__ uint16_t f32_to_act_bits(float v) {
+  if constexpr (XB) {
+    return f32_to_bf16_bits(v);
+  } else {
+    return f32_to_f16_bits(v);
+  }
 }
 
 }  // namespace mxq

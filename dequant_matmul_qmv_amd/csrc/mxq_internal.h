@@ -50,26 +50,27 @@ struct QmvBatch {
 };
 
 struct QmvProblem {
-  const uint16_t* x;   // f16 bits [M, K] of this slice
+  const uint16_t* x;   // activation bits (f16 or bf16) [M, K] of this slice
   const uint32_t* w;
   const uint16_t* s;
   const uint16_t* b;
-  uint16_t* y;         // f16 bits [M, N] of this slice
-  const uint16_t* ob;  // f16 bits [N], added to every row of y, or null
+  uint16_t* y;         // activation bits [M, N] of this slice
+  const uint16_t* ob;  // activation bits [N], added to every row of y, or null
   int64_t N, K;
 };
 
 struct QmvArgs {
-  const uint16_t* x;   // f16 bits [M, K] of this slice
+  const uint16_t* x;   // activation bits (f16 or bf16) [M, K] of this slice
   const uint32_t* w;
   const uint16_t* s;
   const uint16_t* b;
-  uint16_t* y;         // f16 bits [M, N] of this slice
-  const uint16_t* ob;  // f16 bits [N], added to every row of y, or null
+  uint16_t* y;         // activation bits [M, N] of this slice
+  const uint16_t* ob;  // activation bits [N], added to every row of y, or null
   int64_t N, K;
   int bits;
   int glog2;           // log2(group_size)
   bool sb_bf16;
+  bool x_bf16;         // activations (x, y, output bias) are bf16, else f16
   int x_vec;           // x is 16-byte aligned
   int rows_per_wave;   // 0 = pick automatically
   hipStream_t stream;
@@ -85,14 +86,13 @@ struct QmvPlan {
   size_t lds;
   const void* kernel;
 };
-QmvPlan qmv_plan(const DeviceInfo& dev, int64_t N, int64_t K, int bits, bool sb_bf16, int mt,
-                 int rows_override);
+QmvPlan qmv_plan(const DeviceInfo& dev, int64_t N, int64_t K, int bits, bool sb_bf16, bool x_bf16, int mt);
 QmvPlan qmv_plan_group(const DeviceInfo& dev, const int64_t* Ns, const int64_t* Ks, int count, int bits,
-                       bool sb_bf16, int mt, int* grids);
+                       bool sb_bf16, bool x_bf16, int mt, int* grids);
 hipError_t launch_qmv_slice(const QmvArgs& a, const DeviceInfo& dev, int mt);
 // One launch for `count` (<= kMaxGroup) problems with a common mt (rows of x).
 hipError_t launch_qmv_group(const QmvProblem* probs, int count, int bits, int glog2, bool sb_bf16,
-                            const DeviceInfo& dev, int mt, hipStream_t stream);
+                            bool x_bf16, const DeviceInfo& dev, int mt, hipStream_t stream);
 
 struct QmmArgs {
   const uint16_t* x;
@@ -100,13 +100,14 @@ struct QmmArgs {
   const uint16_t* s;
   const uint16_t* b;
   uint16_t* y;
-  const uint16_t* ob;  // f16 bits [N], added to every row of y, or null
+  const uint16_t* ob;  // activation bits [N], added to every row of y, or null
   float* part;         // split-K workspace [splits, M, N] (set by launch_qmm)
   int splits;
   int64_t M, N, K;
   int bits;
   int group_size;
   bool sb_bf16;
+  bool x_bf16;         // activations (x, y, output bias) are bf16, else f16
   hipStream_t stream;
 };
 

@@ -179,7 +179,9 @@ struct QmmCfg {
 // iteration pipeline 0 computes and then stages, pipeline 1 stages and then
 // computes, so on every SIMD one wave's MFMAs run against the other wave's
 // unpack / load / LDS work; one barrier per iteration.
-template <int BITS, bool SB_BF16, int GS, int MB, int NB>
+// XB: activations (x, y, output bias) are bf16; codes are then staged as exact
+// bf16 integers and contracted with bf16 MFMAs.
+template <int BITS, bool SB_BF16, int GS, int MB, int NB, bool XB>
 __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x,
                                                   const uint32_t* __restrict__ W,
                                                   const uint16_t* __restrict__ S,
@@ -288,7 +290,7 @@ __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x
       *reinterpret_cast<u4*>(&xs[row * LDK + swz(row, ch)]) = xr[i];
       // x sums over each ring group, over the 8 (32-code groups: 4) lanes that
       // hold one row; every lane of the group writes the same value
-      const float gsum = lane_group_sum<C::RGC == 32 ? 4 : 8>(sum8_f32(xr[i]));
+      const float gsum = lane_group_sum<C::RGC == 32 ? 4 : 8>(sum8_act<XB>(xr[i]));
       xg[row * XGS + (kt * RPS + (RPS == 2 ? (ch >> 2) : 0)) % RING] = gsum;
     }
 #pragma unroll
@@ -300,11 +302,12 @@ __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x
       if constexpr (BITS == 4) {
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-          *reinterpret_cast<u4*>(dst + swz(row, c0 + k)) = unpack4_natural(wv[k], up4);
+          *reinterpret_cast<u4*>(dst + swz(row, c0 + k)) = XB ? unpack4_bf16_natural(wv[k]) : unpack4_natural(wv[k], up4);
       } else {
 #pragma unroll
         for (int k = 0; k < 2; ++k)
-          *reinterpret_cast<u4*>(dst + swz(row, c0 + k)) = unpack8_natural(wv[2 * k], wv[2 * k + 1], up4.magic);
+          *reinterpret_cast<u4*>(dst + swz(row, c0 + k)) =
+              XB ? unpack8_bf16_natural(wv[2 * k], wv[2 * k + 1]) : unpack8_natural(wv[2 * k], wv[2 * k + 1], up4.magic);
       }
     }
     const int slot = (kt * RPS + sb_e) % RING;
@@ -380,19 +383,20 @@ __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const bool first = kk % C::KSPR == 0;
-      h8 a[MB], b[NB];
+      u4 a[MB], b[NB];
 #pragma unroll
       for (int i = 0; i < MB; ++i)
-        a[i] = *reinterpret_cast<const h8*>(&xs[(arow + i * 32) * LDK + swz(arow, 2 * kk + hi)]);
+        a[i] = *reinterpret_cast<const u4*>(&xs[(arow + i * 32) * LDK + swz(arow, 2 * kk + hi)]);
 #pragma unroll
       for (int j = 0; j < NB; ++j)
-        b[j] = *reinterpret_cast<const h8*>(&qs[(bcol + j * 32) * LDK + swz(bcol, 2 * kk + hi)]);
+        b[j] = *reinterpret_cast<const u4*>(&qs[(bcol + j * 32) * LDK + swz(bcol, 2 * kk + hi)]);
       const f16x zero = {};
 #pragma unroll
       for (int i = 0; i < MB; ++i)
 #pragma unroll
         for (int j = 0; j < NB; ++j)
-          P[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], first ? zero : P[i][j], 0, 0, 0);
+          P[i][j] = XB ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(a[i]), as_bf8(b[j]), first ? zero : P[i][j], 0, 0, 0)
+                       : __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(a[i]), as_h8(b[j]), first ? zero : P[i][j], 0, 0, 0);
       if (kk % C::KSPR == C::KSPR - 1) {
         const int rg = kt * RPS + kk / C::KSPR;
 #pragma unroll
@@ -463,7 +467,7 @@ __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       const int n = n0 + bcol + j * 32;
-      const float o = (ob != nullptr && pout == nullptr) ? sb_to_f32<false>(ob[min(n, N - 1)]) : 0.0f;
+      const float o = (ob != nullptr && pout == nullptr) ? sb_to_f32<XB>(ob[min(n, N - 1)]) : 0.0f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float v = acc[i][j][r] + red[((q * MB * NB + i * NB + j) * 16 + r) * 64 + lane] + o;
@@ -472,7 +476,7 @@ __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x
           if (pout != nullptr) {
             pout[static_cast<size_t>(m) * N + n] = v;
           } else {
-            y[static_cast<size_t>(m) * N + n] = f32_to_f16_bits(v);
+            y[static_cast<size_t>(m) * N + n] = f32_to_act_bits<XB>(v);
           }
         }
       }
@@ -482,6 +486,7 @@ __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x
 // y = RNE_f16(sum over splits of part[split] (in split order) + out_bias);
 // four consecutive elements per thread (the workspace is 256-byte aligned and
 // MN is a multiple of 4 on this path, checked by the host).
+template <bool XB>
 __global__ __launch_bounds__(256) void qmm_split_reduce_kernel(const float* __restrict__ part,
                                                                const uint16_t* __restrict__ ob,
                                                                uint16_t* __restrict__ y, int64_t MN, int N,
@@ -499,16 +504,16 @@ __global__ __launch_bounds__(256) void qmm_split_reduce_kernel(const float* __re
     float o[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      if (ob != nullptr) o[e] += sb_to_f32<false>(ob[(i + e) % N]);
-      y[i + e] = f32_to_f16_bits(o[e]);
+      if (ob != nullptr) o[e] += sb_to_f32<XB>(ob[(i + e) % N]);
+      y[i + e] = f32_to_act_bits<XB>(o[e]);
     }
   }
 }
 
-template <int BITS, bool SB_BF16, int GS, int MB, int NB>
+template <int BITS, bool SB_BF16, int GS, int MB, int NB, bool XB>
 static hipError_t launch_qmm_cfg(const QmmArgs& a) {
   using C = QmmCfg<BITS, GS, MB, NB>;
-  const void* kern = reinterpret_cast<const void*>(&qmm_kernel<BITS, SB_BF16, GS, MB, NB>);
+  const void* kern = reinterpret_cast<const void*>(&qmm_kernel<BITS, SB_BF16, GS, MB, NB, XB>);
   hipError_t e = ensure_dynamic_lds(kern, C::lds_bytes);
   if (e != hipSuccess) return e;
   const int tiles_m = static_cast<int>((a.M + C::BM - 1) / C::BM);
@@ -518,7 +523,7 @@ static hipError_t launch_qmm_cfg(const QmmArgs& a) {
   int splits = a.part != nullptr ? a.splits : 1;  // the workspace holds a.splits partial tiles
   const int nks = (nkt + splits - 1) / splits;    // stages per split
   splits = (nkt + nks - 1) / nks;                 // every split non-empty, never more than a.splits
-  hipLaunchKernelGGL((qmm_kernel<BITS, SB_BF16, GS, MB, NB>), dim3(tiles_m * tiles_n * splits), dim3(C::NT),
+  hipLaunchKernelGGL((qmm_kernel<BITS, SB_BF16, GS, MB, NB, XB>), dim3(tiles_m * tiles_n * splits), dim3(C::NT),
                      C::lds_bytes, a.stream, a.x, a.w, a.s, a.b, a.y, a.ob, a.part, M, N, K, tiles_m, tiles_n,
                      splits, nks);
   e = hipGetLastError();
@@ -526,28 +531,33 @@ static hipError_t launch_qmm_cfg(const QmmArgs& a) {
   const int64_t MN = a.M * a.N;
   int64_t blocks = (MN / 4 + 255) / 256;
   if (blocks > 8192) blocks = 8192;
-  hipLaunchKernelGGL(qmm_split_reduce_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, a.stream,
+  hipLaunchKernelGGL(qmm_split_reduce_kernel<XB>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, a.stream,
                      a.part, a.ob, a.y, MN, N, splits);
   return hipGetLastError();
 }
 
-template <int MB, int NB>
-static hipError_t launch_qmm_shape(const QmmArgs& a) {
+template <int MB, int NB, bool XB>
+static hipError_t launch_qmm_shape_x(const QmmArgs& a) {
   const int gs = a.group_size;
   if (a.bits == 4) {
     if (a.sb_bf16) {
-      return gs == 32 ? launch_qmm_cfg<4, true, 32, MB, NB>(a)
-                      : gs == 64 ? launch_qmm_cfg<4, true, 64, MB, NB>(a) : launch_qmm_cfg<4, true, 128, MB, NB>(a);
+      return gs == 32 ? launch_qmm_cfg<4, true, 32, MB, NB, XB>(a)
+                      : gs == 64 ? launch_qmm_cfg<4, true, 64, MB, NB, XB>(a) : launch_qmm_cfg<4, true, 128, MB, NB, XB>(a);
     }
-    return gs == 32 ? launch_qmm_cfg<4, false, 32, MB, NB>(a)
-                    : gs == 64 ? launch_qmm_cfg<4, false, 64, MB, NB>(a) : launch_qmm_cfg<4, false, 128, MB, NB>(a);
+    return gs == 32 ? launch_qmm_cfg<4, false, 32, MB, NB, XB>(a)
+                    : gs == 64 ? launch_qmm_cfg<4, false, 64, MB, NB, XB>(a) : launch_qmm_cfg<4, false, 128, MB, NB, XB>(a);
   }
   if (a.sb_bf16) {
-    return gs == 32 ? launch_qmm_cfg<8, true, 32, MB, NB>(a)
-                    : gs == 64 ? launch_qmm_cfg<8, true, 64, MB, NB>(a) : launch_qmm_cfg<8, true, 128, MB, NB>(a);
+    return gs == 32 ? launch_qmm_cfg<8, true, 32, MB, NB, XB>(a)
+                    : gs == 64 ? launch_qmm_cfg<8, true, 64, MB, NB, XB>(a) : launch_qmm_cfg<8, true, 128, MB, NB, XB>(a);
   }
-  return gs == 32 ? launch_qmm_cfg<8, false, 32, MB, NB>(a)
-                  : gs == 64 ? launch_qmm_cfg<8, false, 64, MB, NB>(a) : launch_qmm_cfg<8, false, 128, MB, NB>(a);
+  return gs == 32 ? launch_qmm_cfg<8, false, 32, MB, NB, XB>(a)
+                  : gs == 64 ? launch_qmm_cfg<8, false, 64, MB, NB, XB>(a) : launch_qmm_cfg<8, false, 128, MB, NB, XB>(a);
+}
+
+template <int MB, int NB>
+static hipError_t launch_qmm_shape(const QmmArgs& a) {
+  return a.x_bf16 ? launch_qmm_shape_x<MB, NB, true>(a) : launch_qmm_shape_x<MB, NB, false>(a);
 }
 
 // Tile policy: 128 x 128 tiles (64 x 64 per wave) when they alone give every

@@ -89,7 +89,22 @@ struct QmvItem {
   uint16_t ob;  // output bias of the row this lane stores (when there is one)
 };
 
-template <int BITS, bool SB_BF16, int MT, int R, bool XD>
+// Activation pair order of the unpack for one 16-byte chunk (8 activations):
+// 4-bit codes pair (c0, c4) (c1, c5) ..., f16 8-bit codes (c0, c2) (c1, c3),
+// bf16 8-bit codes in natural order.
+template <int BITS, bool XB>
+__device__ __forceinline__ u4 perm_x(u4 v) {
+  if constexpr (BITS == 4) {
+    return perm_x_w4(v);
+  } else if constexpr (XB) {
+    return v;
+  } else {
+    return perm_x_w8(v);
+  }
+}
+
+// XB: activations (x and y) are bf16 instead of f16.
+template <int BITS, bool SB_BF16, int MT, int R, bool XD, bool XB>
 __global__ __launch_bounds__(kQmvBlock) void qmv_kernel(const QmvBatch batch) {
   // This workgroup's problem: the number of problems whose block range ends
   // at or before this block.  The block ranges, problem 0's record and the
@@ -229,8 +244,8 @@ __global__ __launch_bounds__(kQmvBlock) void qmv_kernel(const QmvBatch batch) {
       float sum = 0.0f;
 #pragma unroll
       for (int c = 0; c < CPS; ++c) {
-        sum += sum8_f32(v[c]);
-        const u4 p = (BITS == 4) ? perm_x_w4(v[c]) : perm_x_w8(v[c]);
+        sum += sum8_act<XB>(v[c]);
+        const u4 p = perm_x<BITS, XB>(v[c]);
         xreg[m][4 * c] = p.x;
         xreg[m][4 * c + 1] = p.y;
         xreg[m][4 * c + 2] = p.z;
@@ -248,8 +263,8 @@ __global__ __launch_bounds__(kQmvBlock) void qmv_kernel(const QmvBatch batch) {
       float sum = 0.0f;
 #pragma unroll
       for (int c = 0; c < CPS; ++c) {
-        sum += sum8_f32(v[c]);
-        xs[(m * CPS + c) * nseg + seg] = (BITS == 4) ? perm_x_w4(v[c]) : perm_x_w8(v[c]);
+        sum += sum8_act<XB>(v[c]);
+        xs[(m * CPS + c) * nseg + seg] = perm_x<BITS, XB>(v[c]);
       }
       xsum[m * nseg + seg] = sum;
     }
@@ -257,7 +272,17 @@ __global__ __launch_bounds__(kQmvBlock) void qmv_kernel(const QmvBatch batch) {
     if (rb >= nrb) return;  // no block-level barrier follows
   }
 
-  const uint32_t magic = kMagic;
+  const uint32_t magic = XB ? kMagicB : kMagic;
+  // the per-segment bias factor: b, or b - 128 s when the codes carry +128
+  // (bf16 4-bit), which is exact in f32 for the scale and bias ranges in use
+  auto bias_term = [&](uint16_t bbits, float sc) {
+    const float b = sb_to_f32<SB_BF16>(bbits);
+    if constexpr (XB && BITS == 4) {
+      return __builtin_fmaf(-128.0f, sc, b);
+    } else {
+      return b;
+    }
+  };
   float acc[R][MT];
 #pragma unroll
   for (int r = 0; r < R; ++r)
@@ -265,37 +290,56 @@ __global__ __launch_bounds__(kQmvBlock) void qmv_kernel(const QmvBatch batch) {
     for (int m = 0; m < MT; ++m) acc[r][m] = 0.0f;
 
   // segment dot product of one row's codes with one activation row's pairs
-  auto seg_dot = [&](const h2 (&q)[NP], const uint32_t (&xp)[NP]) {
-    if constexpr (BITS == 4) {
+  // (bf16 4-bit codes carry +128 each; the bias term takes the 128 * sum(x) back)
+  auto seg_dot = [&](const uint32_t (&q)[NP], const uint32_t (&xp)[NP]) {
+    if constexpr (XB) {
+      float d0 = 0.0f, d1 = 0.0f;
+#pragma unroll
+      for (int p = 0; p < NP; p += 2) {
+        d0 = __builtin_amdgcn_fdot2_f32_bf16(as_b2(q[p]), as_b2(xp[p]), d0, false);
+        d1 = __builtin_amdgcn_fdot2_f32_bf16(as_b2(q[p + 1]), as_b2(xp[p + 1]), d1, false);
+      }
+      return d0 + d1;
+    } else if constexpr (BITS == 4) {
       // even pairs carry codes, odd pairs 16 x codes (see unpack_w4_x16)
       float de = 0.0f, dd = 0.0f;
 #pragma unroll
       for (int p = 0; p < NP; p += 2) {
-        de = __builtin_amdgcn_fdot2(q[p], as_h2(xp[p]), de, false);
-        dd = __builtin_amdgcn_fdot2(q[p + 1], as_h2(xp[p + 1]), dd, false);
+        de = __builtin_amdgcn_fdot2(as_h2(q[p]), as_h2(xp[p]), de, false);
+        dd = __builtin_amdgcn_fdot2(as_h2(q[p + 1]), as_h2(xp[p + 1]), dd, false);
       }
       return __builtin_fmaf(dd, 0.0625f, de);
     } else {
       float d = 0.0f;
 #pragma unroll
-      for (int p = 0; p < NP; ++p) d = __builtin_amdgcn_fdot2(q[p], as_h2(xp[p]), d, false);
+      for (int p = 0; p < NP; ++p) d = __builtin_amdgcn_fdot2(as_h2(q[p]), as_h2(xp[p]), d, false);
       return d;
     }
   };
-  auto unpack_row = [&](const u4& wv, h2 (&q)[NP]) {
+  auto unpack_row = [&](const u4& wv, uint32_t (&q)[NP]) {
     const uint32_t wr[4] = {wv.x, wv.y, wv.z, wv.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      if constexpr (BITS == 4) {
+      if constexpr (XB && BITS == 4) {
+        uint32_t t[4];
+        unpack_w4_bf16_off(wr[i], magic, t);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) q[4 * i + p] = t[p];
+      } else if constexpr (XB) {
+        uint32_t t[2];
+        unpack_w8_bf16(wr[i], t);
+        q[2 * i] = t[0];
+        q[2 * i + 1] = t[1];
+      } else if constexpr (BITS == 4) {
         h2 t[4];
         unpack_w4_x16(wr[i], magic, t);
 #pragma unroll
-        for (int p = 0; p < 4; ++p) q[4 * i + p] = t[p];
+        for (int p = 0; p < 4; ++p) q[4 * i + p] = as_u32(t[p]);
       } else {
         h2 t[2];
         unpack_w8_ao(wr[i], magic, t);
-        q[2 * i] = t[0];
-        q[2 * i + 1] = t[1];
+        q[2 * i] = as_u32(t[0]);
+        q[2 * i + 1] = as_u32(t[1]);
       }
     }
   };
@@ -335,10 +379,10 @@ __global__ __launch_bounds__(kQmvBlock) void qmv_kernel(const QmvBatch batch) {
       }
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        h2 q[NP];
+        uint32_t q[NP];
         unpack_row(it.w[r], q);
         const float sc = sb_to_f32<SB_BF16>(it.s[r]);
-        const float bi = sb_to_f32<SB_BF16>(it.b[r]);
+        const float bi = bias_term(it.b[r], sc);
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           const float t = __builtin_fmaf(bi, xsm[m], __builtin_fmaf(sc, seg_dot(q, xp[m]), acc[r][m]));
@@ -347,7 +391,7 @@ __global__ __launch_bounds__(kQmvBlock) void qmv_kernel(const QmvBatch batch) {
       }
     } else {
       // many activation rows: unpack all R rows once, stream x rows from LDS
-      h2 q[R][NP];
+      uint32_t q[R][NP];
 #pragma unroll
       for (int r = 0; r < R; ++r) unpack_row(it.w[r], q[r]);
 #pragma unroll
@@ -357,8 +401,8 @@ __global__ __launch_bounds__(kQmvBlock) void qmv_kernel(const QmvBatch batch) {
         const float xsm = XD ? xsreg[XD ? m : 0] : xsum[m * nseg + seg];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-          const float t = __builtin_fmaf(sb_to_f32<SB_BF16>(it.b[r]), xsm,
-                                         __builtin_fmaf(sb_to_f32<SB_BF16>(it.s[r]), seg_dot(q[r], xp), acc[r][m]));
+          const float sc = sb_to_f32<SB_BF16>(it.s[r]);
+          const float t = __builtin_fmaf(bias_term(it.b[r], sc), xsm, __builtin_fmaf(sc, seg_dot(q[r], xp), acc[r][m]));
           acc[r][m] = active ? t : acc[r][m];
         }
       }
@@ -403,8 +447,8 @@ __global__ __launch_bounds__(kQmvBlock) void qmv_kernel(const QmvBatch batch) {
         const int r = idx / MT;
         const int m = idx - r * MT;
         const int row = rbl * R + r;
-        const float o = has_ob ? sb_to_f32<false>(it.ob) : 0.0f;
-        if (row < N) y[static_cast<size_t>(m) * N + row] = f32_to_f16_bits(v[0] + o);
+        const float o = has_ob ? sb_to_f32<XB>(it.ob) : 0.0f;
+        if (row < N) y[static_cast<size_t>(m) * N + row] = f32_to_act_bits<XB>(v[0] + o);
       }
     }
 #pragma unroll
@@ -452,34 +496,39 @@ __global__ __launch_bounds__(kQmvBlock) void qmv_kernel(const QmvBatch batch) {
 // ---------------------------------------------------------------------------
 namespace {
 
-template <int BITS, bool SB_BF16, int R>
+template <int BITS, bool SB_BF16, int R, bool XB>
 const void* qmv_ptr_mt(int mt, bool xd) {
   if (xd) {
-    if (mt == 1) return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 1, R, true>);
-    return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 2, R, true>);
+    if (mt == 1) return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 1, R, true, XB>);
+    return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 2, R, true, XB>);
   }
   switch (mt) {
-    case 1: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 1, R, false>);
-    case 2: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 2, R, false>);
-    case 3: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 3, R, false>);
-    case 4: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 4, R, false>);
-    case 5: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 5, R, false>);
-    case 6: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 6, R, false>);
-    case 7: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 7, R, false>);
-    default: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 8, R, false>);
+    case 1: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 1, R, false, XB>);
+    case 2: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 2, R, false, XB>);
+    case 3: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 3, R, false, XB>);
+    case 4: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 4, R, false, XB>);
+    case 5: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 5, R, false, XB>);
+    case 6: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 6, R, false, XB>);
+    case 7: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 7, R, false, XB>);
+    default: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 8, R, false, XB>);
   }
 }
 
-template <int BITS, bool SB_BF16>
+template <int BITS, bool SB_BF16, bool XB>
 const void* qmv_ptr_r(int mt, int R, bool xd) {
-  if (R == 4) return qmv_ptr_mt<BITS, SB_BF16, 4>(mt, xd);
-  if (R == 2) return qmv_ptr_mt<BITS, SB_BF16, 2>(mt, xd);
-  return qmv_ptr_mt<BITS, SB_BF16, 1>(mt, xd);
+  if (R == 4) return qmv_ptr_mt<BITS, SB_BF16, 4, XB>(mt, xd);
+  if (R == 2) return qmv_ptr_mt<BITS, SB_BF16, 2, XB>(mt, xd);
+  return qmv_ptr_mt<BITS, SB_BF16, 1, XB>(mt, xd);
 }
 
-const void* qmv_kernel_ptr(int bits, bool bf16, int mt, int R, bool xd) {
-  if (bits == 4) return bf16 ? qmv_ptr_r<4, true>(mt, R, xd) : qmv_ptr_r<4, false>(mt, R, xd);
-  return bf16 ? qmv_ptr_r<8, true>(mt, R, xd) : qmv_ptr_r<8, false>(mt, R, xd);
+template <bool XB>
+const void* qmv_ptr_x(int bits, bool bf16, int mt, int R, bool xd) {
+  if (bits == 4) return bf16 ? qmv_ptr_r<4, true, XB>(mt, R, xd) : qmv_ptr_r<4, false, XB>(mt, R, xd);
+  return bf16 ? qmv_ptr_r<8, true, XB>(mt, R, xd) : qmv_ptr_r<8, false, XB>(mt, R, xd);
+}
+
+const void* qmv_kernel_ptr(int bits, bool bf16, bool xb, int mt, int R, bool xd) {
+  return xb ? qmv_ptr_x<true>(bits, bf16, mt, R, xd) : qmv_ptr_x<false>(bits, bf16, mt, R, xd);
 }
 
 // Rows of W per wave step and the grid, by size class of N (measured on
@@ -549,7 +598,7 @@ size_t qmv_lds_need(int bits, int mt, int64_t K) {
 // segment step, LDS sized for the largest K.  Each problem gets its own block
 // range, sized as it would be alone.
 QmvPlan qmv_plan_group(const DeviceInfo& dev, const int64_t* Ns, const int64_t* Ks, int count, int bits,
-                       bool sb_bf16, int mt, int* grids) {
+                       bool sb_bf16, bool x_bf16, int mt, int* grids) {
   QmvPlan p{};
   p.mt = mt;
   int big = 0;
@@ -564,7 +613,7 @@ QmvPlan qmv_plan_group(const DeviceInfo& dev, const int64_t* Ns, const int64_t* 
   p.rows = qmv_pick_rows(dev, Ns[big], Ks[big], bits, mt);
   p.xdirect = xd;
   p.lds = xd ? 0 : lds;
-  p.kernel = qmv_kernel_ptr(bits, sb_bf16, mt, p.rows, p.xdirect);
+  p.kernel = qmv_kernel_ptr(bits, sb_bf16, x_bf16, mt, p.rows, p.xdirect);
   if (p.lds > 65536 && ensure_dynamic_lds(p.kernel, p.lds) != hipSuccess) (void)hipGetLastError();
   const int occ = blocks_per_cu(dev, p.kernel, p.lds);
   p.grid = 0;
@@ -580,21 +629,19 @@ QmvPlan qmv_plan_group(const DeviceInfo& dev, const int64_t* Ns, const int64_t* 
   return p;
 }
 
-QmvPlan qmv_plan(const DeviceInfo& dev, int64_t N, int64_t K, int bits, bool sb_bf16, int mt,
-                 int rows_override) {
-  (void)rows_override;
-  return qmv_plan_group(dev, &N, &K, 1, bits, sb_bf16, mt, nullptr);
+QmvPlan qmv_plan(const DeviceInfo& dev, int64_t N, int64_t K, int bits, bool sb_bf16, bool x_bf16, int mt) {
+  return qmv_plan_group(dev, &N, &K, 1, bits, sb_bf16, x_bf16, mt, nullptr);
 }
 
 hipError_t launch_qmv_group(const QmvProblem* probs, int count, int bits, int glog2, bool sb_bf16,
-                            const DeviceInfo& dev, int mt, hipStream_t stream) {
+                            bool x_bf16, const DeviceInfo& dev, int mt, hipStream_t stream) {
   int64_t Ns[kMaxGroup], Ks[kMaxGroup];
   int grids[kMaxGroup];
   for (int i = 0; i < count; ++i) {
     Ns[i] = probs[i].N;
     Ks[i] = probs[i].K;
   }
-  const QmvPlan p = qmv_plan_group(dev, Ns, Ks, count, bits, sb_bf16, mt, grids);
+  const QmvPlan p = qmv_plan_group(dev, Ns, Ks, count, bits, sb_bf16, x_bf16, mt, grids);
   if (p.lds > 65536) {
     hipError_t e = ensure_dynamic_lds(p.kernel, p.lds);
     if (e != hipSuccess) return e;
@@ -624,7 +671,7 @@ hipError_t launch_qmv_group(const QmvProblem* probs, int count, int bits, int gl
 
 hipError_t launch_qmv_slice(const QmvArgs& a, const DeviceInfo& dev, int mt) {
   QmvProblem pr{a.x, a.w, a.s, a.b, a.y, a.ob, a.N, a.K};
-  return launch_qmv_group(&pr, 1, a.bits, a.glog2, a.sb_bf16, dev, mt, a.stream);
+  return launch_qmv_group(&pr, 1, a.bits, a.glog2, a.sb_bf16, a.x_bf16, dev, mt, a.stream);
 }
 
 }  // namespace mxq

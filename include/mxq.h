@@ -74,7 +74,7 @@ typedef enum mxq_dtype {
 } mxq_dtype;
 
 /* Bumped whenever a signature in this header changes. */
-#define MXQ_ABI_VERSION 1
+#define MXQ_ABI_VERSION 2
 int mxq_abi_version(void);
 
 /*
@@ -157,6 +157,22 @@ mxq_status mxq_qmm(const void* x, const uint32_t* w, const void* scales, const v
 mxq_status mxq_linear(const void* x, const uint32_t* w, const void* scales, const void* biases,
                       const void* out_bias, void* y, int64_t M, int64_t N, int64_t K, int bits,
                       int group_size, mxq_dtype sb_dtype, void* stream);
+
+/*
+ * mxq_linear_act -- mxq_linear with the activation type as an argument:
+ * act_dtype MXQ_F16 (the same result as mxq_linear, bit for bit) or MXQ_BF16,
+ * in which case x, y and out_bias are bf16 (the other activation format of
+ * MLX checkpoints).  With bf16 activations the decode kernel feeds 4-bit codes
+ * to v_dot2 as bf16 integers 128 + c (exact) and takes the 128 * sum(x) back
+ * through the bias term; 8-bit codes, and the codes of the MFMA kernel, are
+ * converted exactly to bf16, and the MFMA kernel contracts with bf16 MFMAs.
+ * Accumulation stays f32; y is the round-to-nearest-even bf16 of the f32
+ * result (tolerance as mxq_qmv).  Other arguments, routing and errors as
+ * mxq_linear, plus MXQ_ERR_UNSUPPORTED for another act_dtype.
+ */
+mxq_status mxq_linear_act(const void* x, const uint32_t* w, const void* scales, const void* biases,
+                          const void* out_bias, void* y, int64_t M, int64_t N, int64_t K, int bits,
+                          int group_size, mxq_dtype sb_dtype, mxq_dtype act_dtype, void* stream);
 
 /*
  * mxq_dequant -- standalone dequantization: out[n, k] = q * s + b.

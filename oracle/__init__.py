@@ -13,6 +13,7 @@ inputs, closed forms and special cases).  No function is "parity unpinned".
 from .qmv_oracle import (  # noqa: F401
     unpack_codes,
     widen_sb,
+    widen_act,
     dequant_f64,
     matmul_ref,
     matmul_ref_rows,

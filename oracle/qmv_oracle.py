@@ -23,7 +23,10 @@ Readings where the pages are silent:
 * Codes are packed LSB-first: code i of a word occupies bits [b*i, b*i + b).
 * ``W`` is ``[N, K*b/32]`` uint32 (out-features x in-features), so
   ``y = x @ dequant(W).T``; scales and biases are ``[N, K/group_size]``.
-* "Linear with bias" adds an f16 output bias ``[N]`` to every row of ``y``.
+* "Linear with bias" adds an output bias ``[N]`` (of the activation type) to
+  every row of ``y``.
+* Activations are f16, or bf16 (MLX's other activation format; the pages name
+  only "floating-point activations"); either is widened exactly to f64.
 * The fused output is compared against the f64 value before any rounding; the
   standalone dequant output is the f32 value ``RN_f32(q*s + b)``, and f16 or
   bf16 outputs are round-to-nearest-even of that f32 value (two steps).
@@ -40,6 +43,7 @@ import torch
 __all__ = [
     "unpack_codes",
     "widen_sb",
+    "widen_act",
     "dequant_f64",
     "matmul_ref",
     "linear_ref",
@@ -105,22 +109,32 @@ def dequant_f64(w_words, scales, biases, K: int, bits: int, group_size: int,
     return q * s[:, g_of_k] + b[:, g_of_k]
 
 
+def widen_act(x, act_dtype: str = "f16") -> np.ndarray:
+    """Widen activations exactly to float64: float16 values (``"f16"``), or
+    bf16 bit patterns held as uint16 (``"bf16"``, decoded like a bf16 scale)."""
+    if act_dtype == "f16":
+        return np.asarray(x, dtype=np.float16).astype(np.float64)
+    if act_dtype == "bf16":
+        return widen_sb(np.asarray(x, dtype=np.uint16), "bf16")
+    raise ValueError(f"unknown activation dtype {act_dtype!r}")
+
+
 def matmul_ref(x, w_words, scales, biases, K: int, bits: int, group_size: int,
-               sb_dtype: str) -> np.ndarray:
+               sb_dtype: str, act_dtype: str = "f16") -> np.ndarray:
     """Float64 ``y = x @ dequant(W).T`` (before any output rounding).
 
     The fused kernel is defined (mlxcel #574 "The blocker"; epic #570 "The
     measured fusion gate") as giving the result of dequant followed by the
-    matmul.  ``x`` is ``[M, K]`` f16 activations (ExecuTorch #17187
-    "Description": floating-point activations), widened exactly to f64.
+    matmul.  ``x`` is ``[M, K]`` activations (ExecuTorch #17187 "Description":
+    floating-point activations), f16 or bf16, widened exactly to f64.
     """
-    xf = np.asarray(x, dtype=np.float16).astype(np.float64)
+    xf = widen_act(x, act_dtype)
     w = dequant_f64(w_words, scales, biases, K, bits, group_size, sb_dtype)
     return xf @ w.T
 
 
 def matmul_ref_rows(x, w_words, scales, biases, rows, K: int, bits: int,
-                    group_size: int, sb_dtype: str) -> np.ndarray:
+                    group_size: int, sb_dtype: str, act_dtype: str = "f16") -> np.ndarray:
     """``matmul_ref`` restricted to output columns ``rows`` (rows of W).
 
     Output column ``n`` depends only on row ``n`` of W, its scales and biases,
@@ -129,21 +143,22 @@ def matmul_ref_rows(x, w_words, scales, biases, rows, K: int, bits: int,
     """
     rows = np.asarray(rows, dtype=np.int64)
     return matmul_ref(x, np.asarray(w_words)[rows], np.asarray(scales)[rows],
-                      np.asarray(biases)[rows], K, bits, group_size, sb_dtype)
+                      np.asarray(biases)[rows], K, bits, group_size, sb_dtype, act_dtype)
 
 
 def linear_ref(x, w_words, scales, biases, out_bias_bits, K: int, bits: int, group_size: int,
-               sb_dtype: str) -> np.ndarray:
+               sb_dtype: str, act_dtype: str = "f16") -> np.ndarray:
     """Float64 ``y = x @ dequant(W).T + out_bias`` (before any output rounding).
 
     The "linear with bias" entry of the ExecuTorch PR #17187 stack: the layer's
-    f16 output bias ``[N]`` (uint16 bit patterns, or None for no bias) is added
-    to every row of the linear layer's result.
+    output bias ``[N]`` (uint16 bit patterns of the activation type, or None for
+    no bias) is added to every row of the linear layer's result.
     """
-    y = matmul_ref(x, w_words, scales, biases, K, bits, group_size, sb_dtype)
+    y = matmul_ref(x, w_words, scales, biases, K, bits, group_size, sb_dtype, act_dtype)
     if out_bias_bits is None:
         return y
-    ob = np.asarray(out_bias_bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+    ob_bits = np.asarray(out_bias_bits, dtype=np.uint16)
+    ob = widen_act(ob_bits.view(np.float16), "f16") if act_dtype == "f16" else widen_act(ob_bits, act_dtype)
     return y + ob[None, :]
 
 

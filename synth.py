@@ -48,7 +48,7 @@ LLAMA_1B_LAYERS = 16
 class Problem:
     """One synthetic quantized-linear problem; arrays are host numpy."""
 
-    x: np.ndarray          # float16 [M, K]
+    x: np.ndarray          # float16 [M, K], or bf16 bit patterns (uint16) when act_dtype is "bf16"
     w: np.ndarray          # uint32 [N, K*bits/32]
     scales: np.ndarray     # uint16 bit patterns [N, K/group_size]
     biases: np.ndarray     # uint16 bit patterns [N, K/group_size]
@@ -58,6 +58,7 @@ class Problem:
     bits: int
     group_size: int
     sb_dtype: str          # "f16" or "bf16"
+    act_dtype: str = "f16"  # activations: "f16" or "bf16"
 
 
 def _round_sb(v64: np.ndarray, sb_dtype: str) -> np.ndarray:
@@ -91,25 +92,28 @@ def make_weights(N: int, K: int, bits: int = 4, group_size: int = 64,
 
 
 def make_x(M: int, K: int, rng: np.random.Generator | None = None,
-           seed: int | None = None) -> np.ndarray:
+           seed: int | None = None, act_dtype: str = "f16") -> np.ndarray:
+    """Activations N(0, 1): float16 values, or bf16 bit patterns (uint16)."""
     if rng is None:
         rng = np.random.default_rng(seed)
-    return rng.standard_normal((M, K)).astype(np.float16)
+    v = rng.standard_normal((M, K))
+    return v.astype(np.float16) if act_dtype == "f16" else _round_sb(v, act_dtype)
 
 
-def make_out_bias(N: int, seed: int) -> np.ndarray:
-    """A linear layer's f16 output bias [N] as uint16 bit patterns: N(0, 0.5^2)."""
+def make_out_bias(N: int, seed: int, act_dtype: str = "f16") -> np.ndarray:
+    """A linear layer's output bias [N] as uint16 bit patterns of the
+    activation type: N(0, 0.5^2)."""
     rng = np.random.default_rng(seed)
-    return (0.5 * rng.standard_normal(N)).astype(np.float16).view(np.uint16)
+    return _round_sb(0.5 * rng.standard_normal(N), act_dtype)
 
 
 def make_problem(M: int, N: int, K: int, bits: int = 4, group_size: int = 64,
-                 sb_dtype: str = "f16", seed: int = 0) -> Problem:
+                 sb_dtype: str = "f16", seed: int = 0, act_dtype: str = "f16") -> Problem:
     rng = np.random.default_rng(seed)
     w, s, b = make_weights(N, K, bits, group_size, sb_dtype, rng=rng)
-    x = make_x(M, K, rng=rng)
+    x = make_x(M, K, rng=rng, act_dtype=act_dtype)
     return Problem(x=x, w=w, scales=s, biases=b, M=M, N=N, K=K, bits=bits,
-                   group_size=group_size, sb_dtype=sb_dtype)
+                   group_size=group_size, sb_dtype=sb_dtype, act_dtype=act_dtype)
 
 
 def proj_seed(config: int, layer: int, proj_idx: int) -> int:

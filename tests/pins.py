@@ -326,9 +326,34 @@ def pin_linear_bias_hand(O):
     assert np.array_equal(y0, np.array([[2.0, 4.0, 6.0], [0.0, 0.0, 0.0]])), y0
 
 
+def pin_act_bf16_hand(O):
+    """bf16 activations (and a bf16 output bias) on a hand-derived case
+    (M=2, N=2, K=32, 4-bit, g32, f16 scale 1.0, bias 0).
+
+    Row 0 of W holds code 1 everywhere (word 0x11111111), row 1 code 3
+    (0x33333333).  x row 0: sixteen bf16 0x3F80 (1.0) then sixteen 0xC000
+    (-2.0), sum -16; x row 1: all 0x3E80 (0.25), sum 8.  So y = x-sum times the
+    code: [[-16, -48], [8, 24]].  With the bf16 output bias (0x4040 = 3.0,
+    0xBF00 = -0.5): [[-13, -48.5], [11, 23.5]].  Read as f16, 0x3F80 is 1.875
+    and 0x3E80 is 1.625, so a bf16 pattern decoded as f16 cannot pass.
+    """
+    w = np.array([[0x11111111] * 4, [0x33333333] * 4], dtype=np.uint32)
+    s = np.full((2, 1), 0x3C00, dtype=np.uint16)
+    b = np.zeros((2, 1), dtype=np.uint16)
+    x = np.zeros((2, 32), dtype=np.uint16)
+    x[0, :16], x[0, 16:] = 0x3F80, 0xC000
+    x[1, :] = 0x3E80
+    assert np.array_equal(O.widen_act(x[:, :1], "bf16"), np.array([[1.0], [0.25]]))
+    y = O.matmul_ref(x, w, s, b, 32, 4, 32, "f16", "bf16")
+    assert np.array_equal(y, np.array([[-16.0, -48.0], [8.0, 24.0]])), y
+    ob = np.array([0x4040, 0xBF00], dtype=np.uint16)
+    yb = O.linear_ref(x, w, s, b, ob, 32, 4, 32, "f16", "bf16")
+    assert np.array_equal(yb, np.array([[-13.0, -48.5], [11.0, 23.5]])), yb
+
+
 ALL_PINS = [
     pin_unpack_hand_words, pin_unpack_every_value_every_slot, pin_unpack_bitstrings,
     pin_widen, pin_dequant_hand_values, pin_group_indexing, pin_bruteforce_tiny,
     pin_one_hot, pin_integer_case, pin_all_ones_closed_form, pin_linearity,
-    pin_rows_subset, pin_bf16_rounding, pin_linear_bias_hand,
+    pin_rows_subset, pin_bf16_rounding, pin_linear_bias_hand, pin_act_bf16_hand,
 ]

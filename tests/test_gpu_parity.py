@@ -13,7 +13,7 @@ import dequant_matmul_qmv_amd as mxq
 import oracle
 import synth
 from tests import pins
-from tests.gpu_util import assert_close, note, to_dev, y_host
+from tests.gpu_util import assert_close, assert_close_act, note, to_dev, to_dev_act, y_host
 
 pytestmark = pytest.mark.gpu
 
@@ -398,3 +398,100 @@ def test_split_k_workspace_reuse_and_streams():
     torch.cuda.synchronize()
     assert torch.equal(yc.view(torch.int16), yc2.view(torch.int16))
     assert torch.equal(ya1.view(torch.int16), ya3.view(torch.int16))
+
+
+
+# bf16 activations (x, y and the output bias in bf16) through mxq_linear_act:
+# the decode kernel for M <= 8, the MFMA kernel above (split K included).
+ACT_BF16 = [
+    # M, N, K, bits, gs, sb
+    (1, 1, 32, 4, 32, "f16"), (1, 2049, 2048, 4, 64, "f16"), (1, 513, 2048, 8, 64, "bf16"),
+    (2, 1023, 8192, 4, 64, "f16"), (3, 130, 2048, 4, 64, "bf16"), (4, 2050, 8192, 8, 64, "bf16"),
+    (5, 66, 4096, 8, 64, "f16"), (8, 1000, 2048, 4, 128, "f16"), (17, 33, 256, 8, 32, "bf16"),
+    (64, 128, 64, 4, 64, "f16"), (100, 130, 512, 4, 32, "f16"), (200, 333, 2048, 4, 64, "bf16"),
+    (129, 64, 8192, 8, 64, "f16"), (128, 512, 4096, 4, 64, "f16"), (130, 32768, 256, 4, 64, "f16"),
+    (256, 16400, 512, 8, 128, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", ACT_BF16, ids=str)
+def test_bf16_activations(case):
+    M, N, K, bits, gs, sb = case
+    p = synth.make_problem(M, N, K, bits, gs, sb, seed=M * 3 + N + K + 17, act_dtype="bf16")
+    x, w, s, b = to_dev_act(p)
+    note(f"bf16 activations {case}")
+    y = mxq.mxq_linear_act(x, w, s, b, bits=bits, group_size=gs)
+    assert y.dtype == torch.bfloat16
+    ref = oracle.matmul_ref(p.x, p.w, p.scales, p.biases, K, bits, gs, sb, "bf16")
+    assert_close_act(y, ref, f"bf16 act {case}")
+
+
+@pytest.mark.parametrize("M", [1, 5, 96])
+@pytest.mark.parametrize("bits", [4, 8])
+def test_bf16_activations_with_bias(M, bits):
+    N, K = 300, 1024
+    p = synth.make_problem(M, N, K, bits, 64, "f16", seed=900 + M + bits, act_dtype="bf16")
+    ob = synth.make_out_bias(N, seed=901 + M, act_dtype="bf16")
+    x, w, s, b = to_dev_act(p)
+    obt = torch.from_numpy(ob.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+    note(f"bf16 activations with bias M={M} bits={bits}")
+    y = mxq.mxq_linear_act(x, w, s, b, obt, bits=bits)
+    ref = oracle.linear_ref(p.x, p.w, p.scales, p.biases, ob, K, bits, 64, "f16", "bf16")
+    assert_close_act(y, ref, f"bf16 act + bias M={M} bits={bits}")
+
+
+@pytest.mark.parametrize("M", [1, 3, 64])
+@pytest.mark.parametrize("bits", [4, 8])
+def test_bf16_activations_integer_case_bitexact(M, bits):
+    """Scale 1, bias 0, x in {-1, 0, 1}: every product and partial sum is an
+    integer exact in f32, so y must be the round-to-nearest-even bf16 of the
+    exact integer result, bit for bit (results span well past 256, where bf16
+    starts rounding)."""
+    N, K = 200, 512
+    rng = np.random.default_rng(40 + M + bits)
+    w = rng.integers(0, 2 ** 32, size=(N, K * bits // 32), dtype=np.uint32)
+    s = np.full((N, K // 64), 0x3C00, dtype=np.uint16)
+    b = np.zeros((N, K // 64), dtype=np.uint16)
+    xv = rng.integers(-1, 2, size=(M, K)).astype(np.float64)
+    xb = oracle.f32_to_bf16_bits(xv.astype(np.float32))
+    p = synth.Problem(x=xb, w=w, scales=s, biases=b, M=M, N=N, K=K, bits=bits, group_size=64,
+                      sb_dtype="f16", act_dtype="bf16")
+    x, wt, st, bt = to_dev_act(p)
+    note(f"bf16 activations integer case M={M} bits={bits}")
+    y = mxq.mxq_linear_act(x, wt, st, bt, bits=bits)
+    ref = oracle.matmul_ref(xb, w, s, b, K, bits, 64, "f16", "bf16")
+    assert np.array_equal(ref, np.round(ref))
+    want = oracle.f32_to_bf16_bits(ref.astype(np.float32))
+    torch.cuda.synchronize()
+    got = y.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, want), int((got != want).sum())
+
+
+@pytest.mark.parametrize("M", [1, 7, 80])
+def test_act_f16_matches_linear(M):
+    """act_dtype f16 is mxq_linear exactly (same kernels)."""
+    p = synth.make_problem(M, 260, 1024, 4, 64, "bf16", seed=950 + M)
+    x, w, s, b = to_dev(p)
+    ob = torch.from_numpy(synth.make_out_bias(260, seed=951).view(np.int16)).view(torch.float16).to("cuda:0")
+    note(f"act f16 vs mxq_linear M={M}")
+    y1 = mxq.mxq_linear(x, w, s, b, ob, bits=4)
+    y2 = mxq.mxq_linear_act(x, w, s, b, ob, bits=4)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+def test_bf16_activations_k0_and_empty():
+    dev = "cuda:0"
+    w = torch.zeros((5, 0), dtype=torch.int32, device=dev)
+    s = torch.zeros((5, 0), dtype=torch.float16, device=dev)
+    x = torch.zeros((3, 0), dtype=torch.bfloat16, device=dev)
+    ob = torch.tensor([1.5, -2.0, 0.25, 3.0, -0.5], dtype=torch.bfloat16, device=dev)
+    note("bf16 activations K=0")
+    y = mxq.mxq_linear_act(x, w, s, s, ob)
+    torch.cuda.synchronize()
+    assert torch.equal(y.float().cpu(), ob.float().cpu()[None, :].expand(3, 5))
+    y0 = mxq.mxq_linear_act(torch.zeros((0, 64), dtype=torch.bfloat16, device=dev),
+                            torch.zeros((5, 8), dtype=torch.int32, device=dev),
+                            torch.zeros((5, 1), dtype=torch.float16, device=dev),
+                            torch.zeros((5, 1), dtype=torch.float16, device=dev))
+    assert tuple(y0.shape) == (0, 5)

@@ -16,7 +16,7 @@ from tests import pins
 
 def _namespace(**over):
     ns = types.SimpleNamespace(
-        unpack_codes=Q.unpack_codes, widen_sb=Q.widen_sb, dequant_f64=Q.dequant_f64,
+        unpack_codes=Q.unpack_codes, widen_sb=Q.widen_sb, widen_act=Q.widen_act, dequant_f64=Q.dequant_f64,
         matmul_ref=Q.matmul_ref, matmul_ref_rows=Q.matmul_ref_rows, linear_ref=Q.linear_ref,
         dequant_ref_out=Q.dequant_ref_out, f32_to_bf16_bits=Q.f32_to_bf16_bits)
     for k, v in over.items():
@@ -30,23 +30,25 @@ def _namespace(**over):
         g = np.arange(K) // gs
         return q * sv[:, g] + bv[:, g]
 
-    def matmul_ref(x, w, s, b, K, bits, gs, sb):
+    def matmul_ref(x, w, s, b, K, bits, gs, sb, act="f16"):
         if "matmul_ref" in over:
             return over["matmul_ref"](x, w, s, b, K, bits, gs, sb, ns)
-        return np.asarray(x, np.float16).astype(np.float64) @ ns.dequant_f64(w, s, b, K, bits, gs, sb).T
+        return ns.widen_act(x, act) @ ns.dequant_f64(w, s, b, K, bits, gs, sb).T
 
-    def matmul_ref_rows(x, w, s, b, rows, K, bits, gs, sb):
+    def matmul_ref_rows(x, w, s, b, rows, K, bits, gs, sb, act="f16"):
         rows = np.asarray(rows)
         return ns.matmul_ref(x, np.asarray(w)[rows], np.asarray(s)[rows], np.asarray(b)[rows],
-                             K, bits, gs, sb)
+                             K, bits, gs, sb, act)
 
-    def linear_ref(x, w, s, b, ob, K, bits, gs, sb):
-        y = ns.matmul_ref(x, w, s, b, K, bits, gs, sb)
+    def linear_ref(x, w, s, b, ob, K, bits, gs, sb, act="f16"):
+        y = ns.matmul_ref(x, w, s, b, K, bits, gs, sb, act)
         if "linear_bias" in over:
             return over["linear_bias"](y, ob)
         if ob is None:
             return y
-        return y + np.asarray(ob, np.uint16).view(np.float16).astype(np.float64)[None, :]
+        obits = np.asarray(ob, np.uint16)
+        obv = ns.widen_act(obits.view(np.float16), "f16") if act == "f16" else ns.widen_act(obits, act)
+        return y + obv[None, :]
 
     def dequant_ref_out(w, s, b, K, bits, gs, sb, out):
         w64 = ns.dequant_f64(w, s, b, K, bits, gs, sb)
@@ -162,6 +164,9 @@ MUTANTS = {
     "x_k_reversed": dict(matmul_ref=_x_reversed),
     "tiny_relative_error": dict(matmul_ref=_rows_from_x),
     "f16_out_direct": dict(out_cast=_f16_direct_from_f64),
+    "x_bf16_read_as_f16": dict(widen_act=lambda x, act: Q.widen_act(np.asarray(x, np.uint16).view(np.float16), "f16")
+                               if act == "bf16" else Q.widen_act(x, act)),
+    "out_bias_always_f16": dict(linear_bias=lambda y, ob: y if ob is None else y + _ob(ob)[None, :]),
 }
 
 
