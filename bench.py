@@ -25,6 +25,8 @@ Extra objects on the same line:
                 f16 and bf16 scales, 20 calls back to back per projection:
                 TFLOP/s and MFMA utilisation (of the 2.5 PFLOP/s dense f16
                 peak);
+  bf16_activations  the lm_head decode launch (GB/s) and the M=512 prefill
+                projections (TFLOP/s) with bf16 x and y;
   dequant       standalone dequant of the lm_head weights to f32, GB/s.
 """
 
@@ -99,6 +101,22 @@ class GroupCall:
         st = self.fn(self.arr, len(self.calls), 1, 4, 64, 0, stream_handle)
         if st != 0:
             raise RuntimeError(f"grouped launch: libmxq status {st}")
+
+
+class ActCall:
+    """One pre-marshalled mxq_linear_act launch with bf16 activations (no output bias)."""
+
+    def __init__(self, lib, x, w, s, b, y, M, N, K, name, bits=4, gs=64):
+        self.fn = lib.mxq_linear_act
+        self.tensors = (x, w, s, b, y)  # keep alive
+        self.args = (x.data_ptr(), w.data_ptr(), s.data_ptr(), b.data_ptr(), None, y.data_ptr(),
+                     M, N, K, bits, gs, 0, 1)
+        self.name = name
+
+    def __call__(self, stream_handle):
+        st = self.fn(*self.args, stream_handle)
+        if st != 0:
+            raise RuntimeError(f"{self.name}: libmxq status {st}")
 
 
 def make_qmv_set(mxq, lib, synth, torch, config, replica, shapes, dev, sb="f16"):
@@ -502,6 +520,62 @@ def main():
             entry["kernel"] = mxq.mxq_describe("qmm", 512, 8192, 2048, 4, 64, sb)
             qmm[sb] = entry
         result["qmm"] = qmm
+
+        # bf16 activations (x and y bf16) through mxq_linear_act: the lm_head
+        # decode launch (two weight sets alternating, 296 MB > the 256 MB
+        # Infinity Cache) and the M=512 prefill projections, f16 scales.
+        log("bf16 activations ...")
+        act = {}
+        lm_sets = []
+        for r in range(2):
+            w, s, b = synth.make_weights(128256, 2048, 4, 64, "f16", seed=synth.proj_seed(1, r, 7))
+            xb = synth.make_x(1, 2048, seed=synth.proj_seed(1, r, 7) + 500, act_dtype="bf16")
+            lm_sets.append(ActCall(lib, torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev),
+                                   torch.from_numpy(w.view(np.int32)).to(dev),
+                                   torch.from_numpy(s.view(np.int16)).view(torch.float16).to(dev),
+                                   torch.from_numpy(b.view(np.int16)).view(torch.float16).to(dev),
+                                   torch.empty((1, 128256), dtype=torch.bfloat16, device=dev),
+                                   1, 128256, 2048, "lm_head"))
+        st = cur_stream(torch)
+        for i in range(6):
+            lm_sets[i % 2](st)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(20):
+            lm_sets[i % 2](st)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 20
+        act["lm_head_decode"] = {"us": round(ms * 1e3, 2),
+                                 "GB/s": round(call_bytes(1, 128256, 2048) / (ms / 1e3) / 1e9, 1)}
+        del lm_sets
+        torch.cuda.empty_cache()
+        tot_flop, tot_ms = 0, 0.0
+        prefill = {}
+        for idx, (name, N, K) in enumerate([("gate", 8192, 2048), ("up", 8192, 2048), ("down", 2048, 8192)]):
+            w, s, b = synth.make_weights(N, K, 4, 64, "f16", seed=synth.proj_seed(4, 0, idx))
+            xb = synth.make_x(512, K, seed=synth.proj_seed(4, 0, idx) + 500, act_dtype="bf16")
+            c = ActCall(lib, torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev),
+                        torch.from_numpy(w.view(np.int32)).to(dev),
+                        torch.from_numpy(s.view(np.int16)).view(torch.float16).to(dev),
+                        torch.from_numpy(b.view(np.int16)).view(torch.float16).to(dev),
+                        torch.empty((512, N), dtype=torch.bfloat16, device=dev), 512, N, K, name)
+            for _ in range(5):
+                c(st)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(20):
+                c(st)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / 20
+            flop = 2 * 512 * N * K
+            prefill[name] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(flop / (ms / 1e3) / 1e12, 1)}
+            tot_flop += flop
+            tot_ms += ms
+        prefill["TFLOP/s"] = round(tot_flop / (tot_ms / 1e3) / 1e12, 1)
+        act["qmm_m512"] = prefill
+        result["bf16_activations"] = act
 
         log("dequant ...")
         w, s, b = synth.make_weights(128256, 2048, 4, 64, "f16", seed=7)
