@@ -18,6 +18,8 @@ from .qmv_oracle import (  # noqa: F401
     matmul_ref,
     matmul_ref_rows,
     linear_ref,
+    quantize_act_i8,
+    matmul_ref_a8,
     dequant_ref_out,
     f32_to_bf16_bits,
 )

@@ -27,6 +27,15 @@ Readings where the pages are silent:
   every row of ``y``.
 * Activations are f16, or bf16 (MLX's other activation format; the pages name
   only "floating-point activations"); either is widened exactly to f64.
+* The native-int8 route (mlxcel #574 "Next actionable step" and "Upstream
+  status refresh": a quantized dot lowered to the hardware's int8 path, dp4a /
+  integer MMA, instead of scalar widening) needs int8 activations; the pages
+  define no scheme, so the reading here is dynamic per-row (per-token)
+  symmetric quantization: amax = max_k |x[m, k]| (f32), r = 127 / amax and
+  sx = amax / 127 (f32 divisions), xq = clamp(rint(x * r), -127, 127) with the
+  product and the rounding to nearest even in f32; a row with amax = 0 gives
+  xq = 0, sx = 0.  The int8 path then computes exactly the dequant-matmul of
+  x_hat = sx * xq.
 * The fused output is compared against the f64 value before any rounding; the
   standalone dequant output is the f32 value ``RN_f32(q*s + b)``, and f16 or
   bf16 outputs are round-to-nearest-even of that f32 value (two steps).
@@ -47,6 +56,8 @@ __all__ = [
     "dequant_f64",
     "matmul_ref",
     "linear_ref",
+    "quantize_act_i8",
+    "matmul_ref_a8",
     "matmul_ref_rows",
     "dequant_ref_out",
     "f32_to_bf16_bits",
@@ -160,6 +171,38 @@ def linear_ref(x, w_words, scales, biases, out_bias_bits, K: int, bits: int, gro
     ob_bits = np.asarray(out_bias_bits, dtype=np.uint16)
     ob = widen_act(ob_bits.view(np.float16), "f16") if act_dtype == "f16" else widen_act(ob_bits, act_dtype)
     return y + ob[None, :]
+
+
+def quantize_act_i8(x):
+    """Per-row symmetric int8 quantization of f16 activations ``[M, K]``.
+
+    Returns ``(xq, sx)``: int8 codes ``[M, K]`` and the f32 row scales ``[M]``,
+    following the steps of the reading in the module docstring, every step in
+    float32 (the decisions that pick each integer are taken in f32, as in the
+    kernel).
+    """
+    xf = np.asarray(x, dtype=np.float16).astype(np.float32)
+    amax = np.max(np.abs(xf), axis=1) if xf.shape[1] else np.zeros(xf.shape[0], np.float32)
+    amax = amax.astype(np.float32)
+    zero = amax == 0
+    safe = np.where(zero, np.float32(1), amax).astype(np.float32)
+    r = (np.float32(127) / safe).astype(np.float32)
+    sx = (safe / np.float32(127)).astype(np.float32)
+    prod = (xf * r[:, None]).astype(np.float32)
+    xq = np.clip(np.rint(prod), -127, 127)
+    xq = np.where(zero[:, None], 0, xq).astype(np.int8)
+    sx = np.where(zero, np.float32(0), sx).astype(np.float32)
+    return xq, sx
+
+
+def matmul_ref_a8(x, w_words, scales, biases, K: int, bits: int, group_size: int,
+                  sb_dtype: str) -> np.ndarray:
+    """Float64 result of the int8-activation path: ``(sx * xq) @ dequant(W).T``
+    with ``(xq, sx) = quantize_act_i8(x)`` (before any output rounding)."""
+    xq, sx = quantize_act_i8(x)
+    xhat = xq.astype(np.float64) * sx.astype(np.float64)[:, None]
+    w = dequant_f64(w_words, scales, biases, K, bits, group_size, sb_dtype)
+    return xhat @ w.T
 
 
 def f32_to_bf16_bits(v32: np.ndarray) -> np.ndarray:

@@ -351,9 +351,48 @@ def pin_act_bf16_hand(O):
     assert np.array_equal(yb, np.array([[-13.0, -48.5], [11.0, 23.5]])), yb
 
 
+def pin_act_i8_hand(O):
+    """int8 activations (per-row symmetric, the reading in the oracle) on a
+    hand-derived case, K = 32 (x beyond column 7 is zero), 4-bit, g32, scale 1,
+    bias 0; W row 0 holds code 1 everywhere, row 1 code 3.
+
+    Row 0: x = (1, -2, 0.5, 4, -3.75, 2^-6, 0, 0), amax 4, r = 127/4 = 31.75
+    (exact), products 31.75, -63.5, 15.875, 127, -119.0625, 0.49609375 ->
+    rint (ties to even) 32, -64, 16, 127, -119, 0; sum -8.  Row 1 is all zero:
+    xq = 0 and sx = 0.  Row 2: x = (-1/4, 1/4, 1/8, -1/8, 0, 0, 0, 1/16),
+    amax 1/4, r = 508, products -127, 127, 63.5, -63.5, 0, 0, 0, 31.75 ->
+    -127, 127, 64, -64, 0, 0, 0, 32; sum 32.  Row 3: amax 127/64, so r = 64 and
+    sx = 2^-6 exactly; x = (127/64, 5/128, 1/128, -3/128) gives 127, 2.5, 0.5,
+    -1.5 -> 127, 2, 0, -2 (ties to even; ties away from zero would give 3 and
+    1); sum 127.  sx is the f32 quotient amax/127, and
+    y[m, n] = sx[m] * code_n * sum(xq[m]).
+    """
+    x = np.zeros((4, 32), dtype=np.float16)
+    x[0, :6] = [1, -2, 0.5, 4, -3.75, 2.0 ** -6]
+    x[2, :8] = [-0.25, 0.25, 0.125, -0.125, 0, 0, 0, 0.0625]
+    x[3, :4] = [127 / 64, 5 / 128, 1 / 128, -3 / 128]
+    xq, sx = O.quantize_act_i8(x)
+    want = np.zeros((4, 32), dtype=np.int8)
+    want[0, :6] = [32, -64, 16, 127, -119, 0]
+    want[2, :8] = [-127, 127, 64, -64, 0, 0, 0, 32]
+    want[3, :4] = [127, 2, 0, -2]
+    assert np.array_equal(xq, want), xq
+    want_sx = np.array([np.float32(4) / np.float32(127), 0, np.float32(0.25) / np.float32(127), 2.0 ** -6],
+                       dtype=np.float32)
+    assert sx.dtype == np.float32 and np.array_equal(sx, want_sx), sx
+    w = np.array([[0x11111111] * 4, [0x33333333] * 4], dtype=np.uint32)
+    s = np.full((2, 1), 0x3C00, dtype=np.uint16)
+    b = np.zeros((2, 1), dtype=np.uint16)
+    y = O.matmul_ref_a8(x, w, s, b, 32, 4, 32, "f16")
+    sxd = want_sx.astype(np.float64)
+    want_y = np.array([[sxd[0] * -8, sxd[0] * -24], [0, 0], [sxd[2] * 32, sxd[2] * 96],
+                       [sxd[3] * 127, sxd[3] * 381]])
+    assert np.array_equal(y, want_y), y
+
+
 ALL_PINS = [
     pin_unpack_hand_words, pin_unpack_every_value_every_slot, pin_unpack_bitstrings,
     pin_widen, pin_dequant_hand_values, pin_group_indexing, pin_bruteforce_tiny,
     pin_one_hot, pin_integer_case, pin_all_ones_closed_form, pin_linearity,
-    pin_rows_subset, pin_bf16_rounding, pin_linear_bias_hand, pin_act_bf16_hand,
+    pin_rows_subset, pin_bf16_rounding, pin_linear_bias_hand, pin_act_bf16_hand, pin_act_i8_hand,
 ]

@@ -18,7 +18,8 @@ def _namespace(**over):
     ns = types.SimpleNamespace(
         unpack_codes=Q.unpack_codes, widen_sb=Q.widen_sb, widen_act=Q.widen_act, dequant_f64=Q.dequant_f64,
         matmul_ref=Q.matmul_ref, matmul_ref_rows=Q.matmul_ref_rows, linear_ref=Q.linear_ref,
-        dequant_ref_out=Q.dequant_ref_out, f32_to_bf16_bits=Q.f32_to_bf16_bits)
+        dequant_ref_out=Q.dequant_ref_out, f32_to_bf16_bits=Q.f32_to_bf16_bits,
+        quantize_act_i8=Q.quantize_act_i8)
     for k, v in over.items():
         setattr(ns, k, v)
     # re-bind the composite functions so they call the (possibly mutated) parts
@@ -63,7 +64,13 @@ def _namespace(**over):
 
     ns.dequant_f64, ns.matmul_ref = dequant_f64, matmul_ref
     ns.matmul_ref_rows, ns.dequant_ref_out = matmul_ref_rows, dequant_ref_out
+    def matmul_ref_a8(x, w, s, b, K, bits, gs, sb):
+        xq, sx = ns.quantize_act_i8(x)
+        xhat = xq.astype(np.float64) * sx.astype(np.float64)[:, None]
+        return xhat @ ns.dequant_f64(w, s, b, K, bits, gs, sb).T
+
     ns.linear_ref = linear_ref
+    ns.matmul_ref_a8 = matmul_ref_a8
     return ns
 
 
@@ -142,6 +149,22 @@ def _f16_direct_from_f64(w64, out, ns):
     return w32 if out == "f32" else ns.f32_to_bf16_bits(w32)
 
 
+def _quant_i8(x, rounding=np.rint, qmax=127, per_row=True, zero_guard=True):
+    xf = np.asarray(x, np.float16).astype(np.float32)
+    amax = np.max(np.abs(xf), axis=1).astype(np.float32)
+    if not per_row:
+        amax = np.full_like(amax, np.max(amax))
+    with np.errstate(divide="ignore", invalid="ignore"):
+        safe = np.where(amax == 0, np.float32(1), amax).astype(np.float32) if zero_guard else amax
+        r = (np.float32(qmax) / safe).astype(np.float32)
+        sx = (safe / np.float32(qmax)).astype(np.float32)
+        q = np.clip(rounding((xf * r[:, None]).astype(np.float32)), -127, 127)
+    if zero_guard:
+        q = np.where((amax == 0)[:, None], 0, q)
+        sx = np.where(amax == 0, np.float32(0), sx).astype(np.float32)
+    return np.nan_to_num(q, nan=-128).astype(np.int8), sx
+
+
 def _ob(ob):
     return np.asarray(ob, np.uint16).view(np.float16).astype(np.float64)
 
@@ -167,6 +190,11 @@ MUTANTS = {
     "x_bf16_read_as_f16": dict(widen_act=lambda x, act: Q.widen_act(np.asarray(x, np.uint16).view(np.float16), "f16")
                                if act == "bf16" else Q.widen_act(x, act)),
     "out_bias_always_f16": dict(linear_bias=lambda y, ob: y if ob is None else y + _ob(ob)[None, :]),
+    "i8_truncates": dict(quantize_act_i8=lambda x: _quant_i8(x, rounding=np.trunc)),
+    "i8_ties_away": dict(quantize_act_i8=lambda x: _quant_i8(x, rounding=lambda v: np.sign(v) * np.floor(np.abs(v) + 0.5))),
+    "i8_scale_128": dict(quantize_act_i8=lambda x: _quant_i8(x, qmax=128)),
+    "i8_per_tensor": dict(quantize_act_i8=lambda x: _quant_i8(x, per_row=False)),
+    "i8_zero_row_unguarded": dict(quantize_act_i8=lambda x: _quant_i8(x, zero_guard=False)),
 }
 
 
