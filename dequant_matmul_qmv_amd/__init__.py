@@ -4,6 +4,7 @@ The public calls mirror the C ABI of libmxq.so (``include/mxq.h``):
 ``mxq_qmv`` (decode), ``mxq_qmv_grouped`` (several decode projections per
 launch), ``mxq_qmm`` (prefill), ``mxq_linear`` (either, plus an output bias),
 ``mxq_linear_act`` (the same for float16 or bfloat16 activations),
+``mxq_linear_a8`` (int8 activations, quantized per row in the kernel),
 ``mxq_dequant`` (bit-exact standalone dequant) and ``mxq_pack`` (host packer).
 """
 
@@ -21,6 +22,7 @@ from ._lib import (  # noqa: F401
     mxq_dequant,
     mxq_describe,
     mxq_linear,
+    mxq_linear_a8,
     mxq_linear_act,
     mxq_pack,
     mxq_qmm,

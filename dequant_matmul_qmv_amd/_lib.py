@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(HERE, "libmxq.so")
 
 MXQ_OK, MXQ_ERR_INVALID_ARG, MXQ_ERR_UNSUPPORTED, MXQ_ERR_MISALIGNED, MXQ_ERR_HIP = range(5)
 MXQ_F16, MXQ_BF16, MXQ_F32 = 0, 1, 2
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 _lock = threading.Lock()
 _lib = None
@@ -54,6 +54,8 @@ def _declare(lib):
     lib.mxq_linear.restype = c_int
     lib.mxq_linear_act.argtypes = [vp, vp, vp, vp, vp, vp, c_i64, c_i64, c_i64, c_int, c_int, c_int, c_int, vp]
     lib.mxq_linear_act.restype = c_int
+    lib.mxq_linear_a8.argtypes = [vp, vp, vp, vp, vp, vp, c_i64, c_i64, c_i64, c_int, c_int, c_int, vp]
+    lib.mxq_linear_a8.restype = c_int
     lib.mxq_qmv_grouped.argtypes = [ctypes.POINTER(QmvProblem), c_int, c_i64, c_int, c_int, c_int, vp]
     lib.mxq_qmv_grouped.restype = c_int
     lib.mxq_dequant.argtypes = [vp, vp, vp, vp, c_i64, c_i64, c_int, c_int, c_int, c_int, vp]
@@ -244,6 +246,29 @@ def mxq_linear_act(x, w, scales, biases, bias=None, y=None, *, bits: int = 4, gr
         st = lib.mxq_linear_act(x.data_ptr(), w.data_ptr(), scales.data_ptr(), biases.data_ptr(),
                                 None if bias is None else bias.data_ptr(), y.data_ptr(), M, N, K, bits,
                                 group_size, _sb_code(scales), act, _stream_handle(x.device, stream))
+    _check(lib, st)
+    return y
+
+
+def mxq_linear_a8(x, w, scales, biases, bias=None, y=None, *, bits: int = 4, group_size: int = 64,
+                  stream=None):
+    """mxq_linear on the native int8 path: float16 x quantized per row to int8
+    inside the kernel (the scheme is stated in include/mxq.h), v_dot4 products;
+    optional float16 output bias [N]; float16 y."""
+    torch = _torch()
+    lib = load()
+    M, N, K = _check_packed(x, w, scales, biases, bits, group_size, "mxq_linear_a8")
+    if bias is not None and (bias.dtype != torch.float16 or tuple(bias.shape) != (N,) or not bias.is_cuda
+                             or not bias.is_contiguous() or bias.device != x.device):
+        raise ValueError("mxq_linear_a8: bias must be a contiguous float16 [N] tensor on x's device")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    elif y.dtype != torch.float16 or tuple(y.shape) != (M, N) or not y.is_contiguous() or y.device != x.device:
+        raise ValueError("mxq_linear_a8: y must be a contiguous float16 [M, N] tensor on x's device")
+    with torch.cuda.device(x.device):
+        st = lib.mxq_linear_a8(x.data_ptr(), w.data_ptr(), scales.data_ptr(), biases.data_ptr(),
+                               None if bias is None else bias.data_ptr(), y.data_ptr(), M, N, K, bits,
+                               group_size, _sb_code(scales), _stream_handle(x.device, stream))
     _check(lib, st)
     return y
 

@@ -24,6 +24,9 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 int log2_group(int g) { return g == 32 ? 5 : g == 64 ? 6 : g == 128 ? 7 : -1; }
 
+// activation modes of the decode kernel (mxq::QmvArgs::act)
+constexpr int kActF16 = 0, kActBF16 = 1, kActI8 = 2;
+
 constexpr int kMaxDevices = 64;
 std::mutex g_mu;
 mxq::DeviceInfo g_dev[kMaxDevices];
@@ -60,7 +63,7 @@ mxq_status hip_fail(const char* who, hipError_t e) {
 // M-sliced qmv over the whole M range.
 mxq_status run_qmv(const char* who, const void* x, const uint32_t* w, const void* scales,
                    const void* biases, const void* out_bias, void* y, int64_t M, int64_t N, int64_t K,
-                   int bits, int group_size, mxq_dtype sb_dtype, bool x_bf16, void* stream) {
+                   int bits, int group_size, mxq_dtype sb_dtype, int act, void* stream) {
   mxq::DeviceInfo dev;
   hipError_t e = mxq::device_info(&dev);
   if (e != hipSuccess) return hip_fail(who, e);
@@ -78,7 +81,7 @@ mxq_status run_qmv(const char* who, const void* x, const uint32_t* w, const void
   a.bits = bits;
   a.glog2 = log2_group(group_size);
   a.sb_bf16 = sb_dtype == MXQ_BF16;
-  a.x_bf16 = x_bf16;
+  a.act = act;
   a.rows_per_wave = 0;
   a.stream = static_cast<hipStream_t>(stream);
   for (int64_t m0 = 0; m0 < M; m0 += mt_max) {
@@ -116,7 +119,7 @@ mxq_status run_qmv_grouped(const char* who, const mxq_qmv_problem* pr, int count
                                    static_cast<const uint16_t*>(q.biases),
                                    static_cast<uint16_t*>(q.y) + m0 * q.N, nullptr, q.N, q.K};
       }
-      e = mxq::launch_qmv_group(chunk, n, bits, log2_group(group_size), sb_dtype == MXQ_BF16, false, dev, mt,
+      e = mxq::launch_qmv_group(chunk, n, bits, log2_group(group_size), sb_dtype == MXQ_BF16, kActF16, dev, mt,
                                 static_cast<hipStream_t>(stream));
       if (e != hipSuccess) return hip_fail(who, e);
     }
@@ -128,15 +131,16 @@ mxq_status run_qmv_grouped(const char* who, const mxq_qmv_problem* pr, int count
 // MFMA kernel does not take), MFMA kernel otherwise; out_bias may be null.
 mxq_status run_matmul(const char* who, const void* x, const uint32_t* w, const void* scales,
                       const void* biases, const void* out_bias, void* y, int64_t M, int64_t N, int64_t K,
-                      int bits, int group_size, mxq_dtype sb_dtype, bool x_bf16, void* stream) {
+                      int bits, int group_size, mxq_dtype sb_dtype, int act, void* stream) {
   if (K == 0) {
     hipError_t e = mxq::launch_fill_rows(static_cast<uint16_t*>(y), static_cast<const uint16_t*>(out_bias), M, N,
                                          static_cast<hipStream_t>(stream));
     return e == hipSuccess ? MXQ_OK : hip_fail(who, e);
   }
-  // The MFMA kernel stages x with 16-byte loads and walks K in stages of 64.
-  if (!mxq::qmm_mfma_shape(M, K) || !aligned(x, 16))
-    return run_qmv(who, x, w, scales, biases, out_bias, y, M, N, K, bits, group_size, sb_dtype, x_bf16, stream);
+  // The MFMA kernel stages x with 16-byte loads and walks K in stages of 64;
+  // int8 activations run on the decode kernel's v_dot4 path at every M.
+  if (act == kActI8 || !mxq::qmm_mfma_shape(M, K) || !aligned(x, 16))
+    return run_qmv(who, x, w, scales, biases, out_bias, y, M, N, K, bits, group_size, sb_dtype, act, stream);
   mxq::DeviceInfo dev;
   hipError_t e = mxq::device_info(&dev);
   if (e != hipSuccess) return hip_fail(who, e);
@@ -153,7 +157,7 @@ mxq_status run_matmul(const char* who, const void* x, const uint32_t* w, const v
   a.bits = bits;
   a.group_size = group_size;
   a.sb_bf16 = sb_dtype == MXQ_BF16;
-  a.x_bf16 = x_bf16;
+  a.x_bf16 = act == kActBF16;
   a.stream = static_cast<hipStream_t>(stream);
   e = mxq::launch_qmm(a, dev);
   return e == hipSuccess ? MXQ_OK : hip_fail(who, e);
@@ -232,7 +236,7 @@ mxq_status mxq_qmv(const void* x, const uint32_t* w, const void* scales, const v
     hipError_t e = mxq::launch_zero_fill(static_cast<uint16_t*>(y), M * N, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? MXQ_OK : hip_fail("mxq_qmv", e);
   }
-  return run_qmv("mxq_qmv", x, w, scales, biases, nullptr, y, M, N, K, bits, group_size, sb_dtype, false, stream);
+  return run_qmv("mxq_qmv", x, w, scales, biases, nullptr, y, M, N, K, bits, group_size, sb_dtype, kActF16, stream);
 }
 
 mxq_status mxq_qmv_grouped(const mxq_qmv_problem* problems, int count, int64_t M, int bits,
@@ -269,7 +273,7 @@ mxq_status mxq_qmm(const void* x, const uint32_t* w, const void* scales, const v
   g_last_error.clear();
   mxq_status st = check_fused("mxq_qmm", x, w, scales, biases, y, M, N, K, bits, group_size, sb_dtype);
   if (st != MXQ_OK || M == 0 || N == 0) return st;
-  return run_matmul("mxq_qmm", x, w, scales, biases, nullptr, y, M, N, K, bits, group_size, sb_dtype, false,
+  return run_matmul("mxq_qmm", x, w, scales, biases, nullptr, y, M, N, K, bits, group_size, sb_dtype, kActF16,
                     stream);
 }
 
@@ -282,7 +286,7 @@ mxq_status mxq_linear(const void* x, const uint32_t* w, const void* scales, cons
   if (out_bias && !aligned(out_bias, 2))
     return fail(MXQ_ERR_MISALIGNED, "mxq_linear: out_bias must be 2-byte aligned");
   return run_matmul("mxq_linear", x, w, scales, biases, out_bias, y, M, N, K, bits, group_size, sb_dtype,
-                    false, stream);
+                    kActF16, stream);
 }
 
 mxq_status mxq_linear_act(const void* x, const uint32_t* w, const void* scales, const void* biases,
@@ -297,7 +301,19 @@ mxq_status mxq_linear_act(const void* x, const uint32_t* w, const void* scales, 
   if (out_bias && !aligned(out_bias, 2))
     return fail(MXQ_ERR_MISALIGNED, "mxq_linear_act: out_bias must be 2-byte aligned");
   return run_matmul("mxq_linear_act", x, w, scales, biases, out_bias, y, M, N, K, bits, group_size, sb_dtype,
-                    act_dtype == MXQ_BF16, stream);
+                    act_dtype == MXQ_BF16 ? kActBF16 : kActF16, stream);
+}
+
+mxq_status mxq_linear_a8(const void* x, const uint32_t* w, const void* scales, const void* biases,
+                         const void* out_bias, void* y, int64_t M, int64_t N, int64_t K, int bits,
+                         int group_size, mxq_dtype sb_dtype, void* stream) {
+  g_last_error.clear();
+  mxq_status st = check_fused("mxq_linear_a8", x, w, scales, biases, y, M, N, K, bits, group_size, sb_dtype);
+  if (st != MXQ_OK || M == 0 || N == 0) return st;
+  if (out_bias && !aligned(out_bias, 2))
+    return fail(MXQ_ERR_MISALIGNED, "mxq_linear_a8: out_bias must be 2-byte aligned");
+  return run_matmul("mxq_linear_a8", x, w, scales, biases, out_bias, y, M, N, K, bits, group_size, sb_dtype,
+                    kActI8, stream);
 }
 
 mxq_status mxq_dequant(const uint32_t* w, const void* scales, const void* biases, void* out,
@@ -370,7 +386,7 @@ const char* mxq_describe(const char* op, int64_t M, int64_t N, int64_t K, int bi
   desc.clear();
   for (int64_t m0 = 0; m0 < M; m0 += mt_max) {
     const int mt = static_cast<int>((M - m0) < mt_max ? (M - m0) : mt_max);
-    const mxq::QmvPlan p = mxq::qmv_plan(dev, N, K, bits, sb_dtype == MXQ_BF16, false, mt);
+    const mxq::QmvPlan p = mxq::qmv_plan(dev, N, K, bits, sb_dtype == MXQ_BF16, kActF16, mt);
     if (!desc.empty()) desc += "; ";
     desc += "qmv_kernel<bits=" + std::to_string(bits) + ",sb=" + sb + ",mt=" + std::to_string(mt) +
             ",rows=" + std::to_string(p.rows) + (p.xdirect ? ",xreg" : "") + "> grid=" + std::to_string(p.grid) +

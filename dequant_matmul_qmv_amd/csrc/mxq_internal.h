@@ -70,7 +70,7 @@ struct QmvArgs {
   int bits;
   int glog2;           // log2(group_size)
   bool sb_bf16;
-  bool x_bf16;         // activations (x, y, output bias) are bf16, else f16
+  int act;             // activations: 0 f16, 1 bf16 (x, y, output bias), 2 f16 quantized to int8 per row
   int x_vec;           // x is 16-byte aligned
   int rows_per_wave;   // 0 = pick automatically
   hipStream_t stream;
@@ -86,13 +86,14 @@ struct QmvPlan {
   size_t lds;
   const void* kernel;
 };
-QmvPlan qmv_plan(const DeviceInfo& dev, int64_t N, int64_t K, int bits, bool sb_bf16, bool x_bf16, int mt);
+// act: activation mode, 0 f16, 1 bf16, 2 int8 (f16 x quantized per row inside the kernel)
+QmvPlan qmv_plan(const DeviceInfo& dev, int64_t N, int64_t K, int bits, bool sb_bf16, int act, int mt);
 QmvPlan qmv_plan_group(const DeviceInfo& dev, const int64_t* Ns, const int64_t* Ks, int count, int bits,
-                       bool sb_bf16, bool x_bf16, int mt, int* grids);
+                       bool sb_bf16, int act, int mt, int* grids);
 hipError_t launch_qmv_slice(const QmvArgs& a, const DeviceInfo& dev, int mt);
 // One launch for `count` (<= kMaxGroup) problems with a common mt (rows of x).
 hipError_t launch_qmv_group(const QmvProblem* probs, int count, int bits, int glog2, bool sb_bf16,
-                            bool x_bf16, const DeviceInfo& dev, int mt, hipStream_t stream);
+                            int act, const DeviceInfo& dev, int mt, hipStream_t stream);
 
 struct QmmArgs {
   const uint16_t* x;

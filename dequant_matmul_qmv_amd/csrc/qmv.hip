@@ -56,7 +56,7 @@ struct SegTraits {
 template <int BITS>
 __host__ __device__ constexpr size_t qmv_lds_bytes(int MT, int K) {
   return static_cast<size_t>(MT) * (K * BITS / 128) *
-         (SegTraits<BITS>::kChunksPerSeg * 16 + 4);
+         (SegTraits<BITS>::kChunksPerSeg * 16 + 4) + static_cast<size_t>(MT) * 4;  // + int8 mode's row maxima
 }
 
 constexpr int kQmvBlock = 256;  // threads per workgroup (the host always launches this many)
@@ -103,9 +103,77 @@ __device__ __forceinline__ u4 perm_x(u4 v) {
   }
 }
 
-// XB: activations (x and y) are bf16 instead of f16.
-template <int BITS, bool SB_BF16, int MT, int R, bool XD, bool XB>
+// Activation modes of the decode kernel.
+constexpr int kActF16 = 0;   // x, y f16
+constexpr int kActBF16 = 1;  // x, y bf16
+constexpr int kActI8 = 2;    // x f16, quantized per row to int8 inside the kernel; y f16
+
+// Largest |x| over 8 f16 activations (4 dwords), in f32.
+__device__ __forceinline__ float absmax8_f16(u4 v) {
+  const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const h2 h = as_h2(d[i]);
+    m = fmaxf(m, fmaxf(fabsf(static_cast<float>(h.x)), fabsf(static_cast<float>(h.y))));
+  }
+  return m;
+}
+
+// int8 code of one activation: clamp(rint(x * r), -127, 127), product and
+// rounding (to nearest, ties to even) in f32.
+__device__ __forceinline__ int quant_i8(float x, float r) {
+  const float p = __builtin_rintf(x * r);
+  return static_cast<int>(fminf(fmaxf(p, -127.0f), 127.0f));
+}
+
+__device__ __forceinline__ uint32_t pack_i8x4(int a, int b, int c, int d) {
+  return (static_cast<uint32_t>(a) & 0xFFu) | ((static_cast<uint32_t>(b) & 0xFFu) << 8) |
+         ((static_cast<uint32_t>(c) & 0xFFu) << 16) | ((static_cast<uint32_t>(d) & 0xFFu) << 24);
+}
+
+// Quantize one 16-byte chunk (8 f16 activations x0..x7) into two dwords of
+// int8 codes in the byte order of the code unpack: 4-bit words split into
+// even codes (x0, x2, x4, x6) and odd codes (x1, x3, x5, x7); 8-bit words hold
+// four codes in natural order (x0..x3 | x4..x7).  Adds the codes to `sum`.
+template <int BITS>
+__device__ __forceinline__ void quant_chunk_i8(u4 v, float r, uint32_t& a, uint32_t& b, int& sum) {
+  const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+  int q[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const h2 h = as_h2(d[i]);
+    q[2 * i] = quant_i8(static_cast<float>(h.x), r);
+    q[2 * i + 1] = quant_i8(static_cast<float>(h.y), r);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sum += q[i];
+  if constexpr (BITS == 4) {
+    a = pack_i8x4(q[0], q[2], q[4], q[6]);
+    b = pack_i8x4(q[1], q[3], q[5], q[7]);
+  } else {
+    a = pack_i8x4(q[0], q[1], q[2], q[3]);
+    b = pack_i8x4(q[4], q[5], q[6], q[7]);
+  }
+}
+
+// Largest value over the wave (non-negative inputs), in every lane: DPP moves
+// fold it into lane 63, which is then read as a wave-uniform value.
+__device__ __forceinline__ float wave_max_nonneg(float v) {
+  v = fmaxf(v, dpp_f32<0xB1, 0xF>(v));
+  v = fmaxf(v, dpp_f32<0x4E, 0xF>(v));
+  v = fmaxf(v, dpp_f32<0x141, 0xF>(v));
+  v = fmaxf(v, dpp_f32<0x140, 0xF>(v));
+  v = fmaxf(v, dpp_f32<0x142, 0xA>(v));
+  v = fmaxf(v, dpp_f32<0x143, 0xC>(v));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// ACT: activation mode (kActF16, kActBF16, kActI8).
+template <int BITS, bool SB_BF16, int MT, int R, bool XD, int ACT>
 __global__ __launch_bounds__(kQmvBlock) void qmv_kernel(const QmvBatch batch) {
+  constexpr bool XB = ACT == kActBF16;
+  constexpr bool XI = ACT == kActI8;
   // This workgroup's problem: the number of problems whose block range ends
   // at or before this block.  The block ranges, problem 0's record and the
   // group size are read in one batch of scalar loads (an empty asm use of all
@@ -235,25 +303,90 @@ __global__ __launch_bounds__(kQmvBlock) void qmv_kernel(const QmvBatch batch) {
   constexpr int NPX = (BITS == 4) ? 16 : 8;
   uint32_t xreg[XD ? MT : 1][NPX];
   float xsreg[XD ? MT : 1];
+  // int8 mode: per-row scale sx = amax / 127 and factor r = 127 / amax (both
+  // f32 quotients; a zero row gives r = 0, sx = 0, so its codes are 0)
+  float sxm[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) sxm[m] = 1.0f;
+  auto row_scales = [&](float amax, float& r, float& sx) {
+    const bool z = !(amax > 0.0f);
+    r = z ? 0.0f : 127.0f / amax;
+    sx = z ? 0.0f : amax / 127.0f;
+  };
   if constexpr (XD) {
     const int seg = min(lane, nseg - 1);
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       u4 v[CPS];
       load_x_global(m, seg, v);
-      float sum = 0.0f;
+      if constexpr (XI) {
+        // the row lies within this wave's lanes (one segment step), so the
+        // wave finds its largest |x| itself
+        float am = 0.0f;
 #pragma unroll
-      for (int c = 0; c < CPS; ++c) {
-        sum += sum8_act<XB>(v[c]);
-        const u4 p = perm_x<BITS, XB>(v[c]);
-        xreg[m][4 * c] = p.x;
-        xreg[m][4 * c + 1] = p.y;
-        xreg[m][4 * c + 2] = p.z;
-        xreg[m][4 * c + 3] = p.w;
+        for (int c = 0; c < CPS; ++c) am = fmaxf(am, absmax8_f16(v[c]));
+        float r;
+        row_scales(wave_max_nonneg(am), r, sxm[m]);
+        int sum = 0;
+#pragma unroll
+        for (int c = 0; c < CPS; ++c) quant_chunk_i8<BITS>(v[c], r, xreg[m][2 * c], xreg[m][2 * c + 1], sum);
+        xsreg[m] = static_cast<float>(sum);
+      } else {
+        float sum = 0.0f;
+#pragma unroll
+        for (int c = 0; c < CPS; ++c) {
+          sum += sum8_act<XB>(v[c]);
+          const u4 p = perm_x<BITS, XB>(v[c]);
+          xreg[m][4 * c] = p.x;
+          xreg[m][4 * c + 1] = p.y;
+          xreg[m][4 * c + 2] = p.z;
+          xreg[m][4 * c + 3] = p.w;
+        }
+        xsreg[m] = sum;
       }
-      xsreg[m] = sum;
     }
     if (rb >= nrb) return;
+  } else if constexpr (XI) {
+    // int8 mode, staged: pass 1 finds each row's largest |x| (LDS atomic max
+    // on the f32 bits, which order like unsigned integers for values >= 0),
+    // pass 2 quantizes into LDS with the row's factor
+    uint32_t* amax_s = reinterpret_cast<uint32_t*>(xsum + MT * nseg);
+    if (threadIdx.x < MT) amax_s[threadIdx.x] = 0u;
+    __syncthreads();
+    for (int u = threadIdx.x; u < MT * nseg; u += kQmvBlock) {
+      const int m = u / nseg;
+      const int seg = u - m * nseg;
+      u4 v[CPS];
+      load_x_global(m, seg, v);
+      float am = 0.0f;
+#pragma unroll
+      for (int c = 0; c < CPS; ++c) am = fmaxf(am, absmax8_f16(v[c]));
+      atomicMax(&amax_s[m], __float_as_uint(am));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      float r;
+      row_scales(__uint_as_float(amax_s[m]), r, sxm[m]);
+    }
+    for (int u = threadIdx.x; u < MT * nseg; u += kQmvBlock) {
+      const int m = u / nseg;
+      const int seg = u - m * nseg;
+      float r, sx;
+      row_scales(__uint_as_float(amax_s[m]), r, sx);
+      u4 v[CPS];
+      load_x_global(m, seg, v);
+      int sum = 0;
+      uint32_t d[2 * CPS];
+#pragma unroll
+      for (int c = 0; c < CPS; ++c) quant_chunk_i8<BITS>(v[c], r, d[2 * c], d[2 * c + 1], sum);
+#pragma unroll
+      for (int c = 0; c < CPS / 2; ++c)
+        xs[(m * CPS + c) * nseg + seg] = u4{d[4 * c], d[4 * c + 1], d[4 * c + 2], d[4 * c + 3]};
+      xsum[m * nseg + seg] = static_cast<float>(sum);
+    }
+    __syncthreads();
+    if (rb >= nrb) return;  // no block-level barrier follows
   } else {
     for (int u = threadIdx.x; u < MT * nseg; u += kQmvBlock) {
       const int m = u / nseg;
@@ -274,11 +407,14 @@ __global__ __launch_bounds__(kQmvBlock) void qmv_kernel(const QmvBatch batch) {
 
   const uint32_t magic = XB ? kMagicB : kMagic;
   // the per-segment bias factor: b, or b - 128 s when the codes carry +128
-  // (bf16 4-bit), which is exact in f32 for the scale and bias ranges in use
+  // (bf16 4-bit), or b + 128 s when they carry -128 (int8 mode, 8-bit codes
+  // as signed bytes c - 128); exact in f32 for the scale and bias ranges in use
   auto bias_term = [&](uint16_t bbits, float sc) {
     const float b = sb_to_f32<SB_BF16>(bbits);
     if constexpr (XB && BITS == 4) {
       return __builtin_fmaf(-128.0f, sc, b);
+    } else if constexpr (XI && BITS == 8) {
+      return __builtin_fmaf(128.0f, sc, b);
     } else {
       return b;
     }
@@ -292,7 +428,17 @@ __global__ __launch_bounds__(kQmvBlock) void qmv_kernel(const QmvBatch batch) {
   // segment dot product of one row's codes with one activation row's pairs
   // (bf16 4-bit codes carry +128 each; the bias term takes the 128 * sum(x) back)
   auto seg_dot = [&](const uint32_t (&q)[NP], const uint32_t (&xp)[NP]) {
-    if constexpr (XB) {
+    if constexpr (XI) {
+      // int8 codes against int8 activations, four products per v_dot4, exact
+      constexpr int NQ = 2 * CPS;
+      int d0 = 0, d1 = 0;
+#pragma unroll
+      for (int p = 0; p < NQ; p += 2) {
+        d0 = __builtin_amdgcn_sdot4(static_cast<int>(q[p]), static_cast<int>(xp[p]), d0, false);
+        d1 = __builtin_amdgcn_sdot4(static_cast<int>(q[p + 1]), static_cast<int>(xp[p + 1]), d1, false);
+      }
+      return static_cast<float>(d0 + d1);
+    } else if constexpr (XB) {
       float d0 = 0.0f, d1 = 0.0f;
 #pragma unroll
       for (int p = 0; p < NP; p += 2) {
@@ -320,7 +466,13 @@ __global__ __launch_bounds__(kQmvBlock) void qmv_kernel(const QmvBatch batch) {
     const uint32_t wr[4] = {wv.x, wv.y, wv.z, wv.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      if constexpr (XB && BITS == 4) {
+      if constexpr (XI && BITS == 4) {
+        // nibbles to bytes: even codes (0, 2, 4, 6) and odd codes (1, 3, 5, 7)
+        q[2 * i] = wr[i] & 0x0F0F0F0Fu;
+        q[2 * i + 1] = (wr[i] >> 4) & 0x0F0F0F0Fu;
+      } else if constexpr (XI) {
+        q[i] = wr[i] ^ 0x80808080u;  // c - 128 as a signed byte
+      } else if constexpr (XB && BITS == 4) {
         uint32_t t[4];
         unpack_w4_bf16_off(wr[i], magic, t);
 #pragma unroll
@@ -349,8 +501,9 @@ __global__ __launch_bounds__(kQmvBlock) void qmv_kernel(const QmvBatch batch) {
       for (int p = 0; p < NP; ++p) xp[p] = xreg[m][p];
       return;
     }
+    constexpr int XC = XI ? CPS / 2 : CPS;  // 16-byte chunks of one segment's activations
 #pragma unroll
-    for (int c = 0; c < CPS; ++c) {
+    for (int c = 0; c < XC; ++c) {
       const u4 xv = xs[(m * CPS + c) * nseg + seg];
       xp[4 * c] = xv.x;
       xp[4 * c + 1] = xv.y;
@@ -415,7 +568,7 @@ __global__ __launch_bounds__(kQmvBlock) void qmv_kernel(const QmvBatch batch) {
     // group of kLow lanes and are summed within the group with DPP moves.
     float v[VP];
 #pragma unroll
-    for (int i = 0; i < VP; ++i) v[i] = (i < V) ? acc[i / MT][i % MT] : 0.0f;
+    for (int i = 0; i < VP; ++i) v[i] = (i < V) ? acc[i / MT][i % MT] * (XI ? sxm[i % MT] : 1.0f) : 0.0f;
 #pragma unroll
     for (int s = 0; s < 6; ++s) {
       const int off = 32 >> s;
@@ -496,39 +649,40 @@ __global__ __launch_bounds__(kQmvBlock) void qmv_kernel(const QmvBatch batch) {
 // ---------------------------------------------------------------------------
 namespace {
 
-template <int BITS, bool SB_BF16, int R, bool XB>
+template <int BITS, bool SB_BF16, int R, int ACT>
 const void* qmv_ptr_mt(int mt, bool xd) {
   if (xd) {
-    if (mt == 1) return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 1, R, true, XB>);
-    return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 2, R, true, XB>);
+    if (mt == 1) return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 1, R, true, ACT>);
+    return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 2, R, true, ACT>);
   }
   switch (mt) {
-    case 1: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 1, R, false, XB>);
-    case 2: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 2, R, false, XB>);
-    case 3: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 3, R, false, XB>);
-    case 4: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 4, R, false, XB>);
-    case 5: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 5, R, false, XB>);
-    case 6: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 6, R, false, XB>);
-    case 7: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 7, R, false, XB>);
-    default: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 8, R, false, XB>);
+    case 1: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 1, R, false, ACT>);
+    case 2: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 2, R, false, ACT>);
+    case 3: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 3, R, false, ACT>);
+    case 4: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 4, R, false, ACT>);
+    case 5: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 5, R, false, ACT>);
+    case 6: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 6, R, false, ACT>);
+    case 7: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 7, R, false, ACT>);
+    default: return reinterpret_cast<const void*>(&qmv_kernel<BITS, SB_BF16, 8, R, false, ACT>);
   }
 }
 
-template <int BITS, bool SB_BF16, bool XB>
+template <int BITS, bool SB_BF16, int ACT>
 const void* qmv_ptr_r(int mt, int R, bool xd) {
-  if (R == 4) return qmv_ptr_mt<BITS, SB_BF16, 4, XB>(mt, xd);
-  if (R == 2) return qmv_ptr_mt<BITS, SB_BF16, 2, XB>(mt, xd);
-  return qmv_ptr_mt<BITS, SB_BF16, 1, XB>(mt, xd);
+  if (R == 4) return qmv_ptr_mt<BITS, SB_BF16, 4, ACT>(mt, xd);
+  if (R == 2) return qmv_ptr_mt<BITS, SB_BF16, 2, ACT>(mt, xd);
+  return qmv_ptr_mt<BITS, SB_BF16, 1, ACT>(mt, xd);
 }
 
-template <bool XB>
+template <int ACT>
 const void* qmv_ptr_x(int bits, bool bf16, int mt, int R, bool xd) {
-  if (bits == 4) return bf16 ? qmv_ptr_r<4, true, XB>(mt, R, xd) : qmv_ptr_r<4, false, XB>(mt, R, xd);
-  return bf16 ? qmv_ptr_r<8, true, XB>(mt, R, xd) : qmv_ptr_r<8, false, XB>(mt, R, xd);
+  if (bits == 4) return bf16 ? qmv_ptr_r<4, true, ACT>(mt, R, xd) : qmv_ptr_r<4, false, ACT>(mt, R, xd);
+  return bf16 ? qmv_ptr_r<8, true, ACT>(mt, R, xd) : qmv_ptr_r<8, false, ACT>(mt, R, xd);
 }
 
-const void* qmv_kernel_ptr(int bits, bool bf16, bool xb, int mt, int R, bool xd) {
-  return xb ? qmv_ptr_x<true>(bits, bf16, mt, R, xd) : qmv_ptr_x<false>(bits, bf16, mt, R, xd);
+const void* qmv_kernel_ptr(int bits, bool bf16, int act, int mt, int R, bool xd) {
+  if (act == kActI8) return qmv_ptr_x<kActI8>(bits, bf16, mt, R, xd);
+  return act == kActBF16 ? qmv_ptr_x<kActBF16>(bits, bf16, mt, R, xd) : qmv_ptr_x<kActF16>(bits, bf16, mt, R, xd);
 }
 
 // Rows of W per wave step and the grid, by size class of N (measured on
@@ -598,7 +752,7 @@ size_t qmv_lds_need(int bits, int mt, int64_t K) {
 // segment step, LDS sized for the largest K.  Each problem gets its own block
 // range, sized as it would be alone.
 QmvPlan qmv_plan_group(const DeviceInfo& dev, const int64_t* Ns, const int64_t* Ks, int count, int bits,
-                       bool sb_bf16, bool x_bf16, int mt, int* grids) {
+                       bool sb_bf16, int act, int mt, int* grids) {
   QmvPlan p{};
   p.mt = mt;
   int big = 0;
@@ -613,7 +767,7 @@ QmvPlan qmv_plan_group(const DeviceInfo& dev, const int64_t* Ns, const int64_t* 
   p.rows = qmv_pick_rows(dev, Ns[big], Ks[big], bits, mt);
   p.xdirect = xd;
   p.lds = xd ? 0 : lds;
-  p.kernel = qmv_kernel_ptr(bits, sb_bf16, x_bf16, mt, p.rows, p.xdirect);
+  p.kernel = qmv_kernel_ptr(bits, sb_bf16, act, mt, p.rows, p.xdirect);
   if (p.lds > 65536 && ensure_dynamic_lds(p.kernel, p.lds) != hipSuccess) (void)hipGetLastError();
   const int occ = blocks_per_cu(dev, p.kernel, p.lds);
   p.grid = 0;
@@ -629,19 +783,19 @@ QmvPlan qmv_plan_group(const DeviceInfo& dev, const int64_t* Ns, const int64_t* 
   return p;
 }
 
-QmvPlan qmv_plan(const DeviceInfo& dev, int64_t N, int64_t K, int bits, bool sb_bf16, bool x_bf16, int mt) {
-  return qmv_plan_group(dev, &N, &K, 1, bits, sb_bf16, x_bf16, mt, nullptr);
+QmvPlan qmv_plan(const DeviceInfo& dev, int64_t N, int64_t K, int bits, bool sb_bf16, int act, int mt) {
+  return qmv_plan_group(dev, &N, &K, 1, bits, sb_bf16, act, mt, nullptr);
 }
 
 hipError_t launch_qmv_group(const QmvProblem* probs, int count, int bits, int glog2, bool sb_bf16,
-                            bool x_bf16, const DeviceInfo& dev, int mt, hipStream_t stream) {
+                            int act, const DeviceInfo& dev, int mt, hipStream_t stream) {
   int64_t Ns[kMaxGroup], Ks[kMaxGroup];
   int grids[kMaxGroup];
   for (int i = 0; i < count; ++i) {
     Ns[i] = probs[i].N;
     Ks[i] = probs[i].K;
   }
-  const QmvPlan p = qmv_plan_group(dev, Ns, Ks, count, bits, sb_bf16, x_bf16, mt, grids);
+  const QmvPlan p = qmv_plan_group(dev, Ns, Ks, count, bits, sb_bf16, act, mt, grids);
   if (p.lds > 65536) {
     hipError_t e = ensure_dynamic_lds(p.kernel, p.lds);
     if (e != hipSuccess) return e;
@@ -671,7 +825,7 @@ hipError_t launch_qmv_group(const QmvProblem* probs, int count, int bits, int gl
 
 hipError_t launch_qmv_slice(const QmvArgs& a, const DeviceInfo& dev, int mt) {
   QmvProblem pr{a.x, a.w, a.s, a.b, a.y, a.ob, a.N, a.K};
-  return launch_qmv_group(&pr, 1, a.bits, a.glog2, a.sb_bf16, a.x_bf16, dev, mt, a.stream);
+  return launch_qmv_group(&pr, 1, a.bits, a.glog2, a.sb_bf16, a.act, dev, mt, a.stream);
 }
 
 }  // namespace mxq

@@ -74,7 +74,7 @@ typedef enum mxq_dtype {
 } mxq_dtype;
 
 /* Bumped whenever a signature in this header changes. */
-#define MXQ_ABI_VERSION 2
+#define MXQ_ABI_VERSION 3
 int mxq_abi_version(void);
 
 /*
@@ -173,6 +173,28 @@ mxq_status mxq_linear(const void* x, const uint32_t* w, const void* scales, cons
 mxq_status mxq_linear_act(const void* x, const uint32_t* w, const void* scales, const void* biases,
                           const void* out_bias, void* y, int64_t M, int64_t N, int64_t K, int bits,
                           int group_size, mxq_dtype sb_dtype, mxq_dtype act_dtype, void* stream);
+
+/*
+ * mxq_linear_a8 -- mxq_linear on the native int8 path: f16 activations are
+ * quantized per row to int8 inside the decode kernel and contracted with the
+ * 4-bit or 8-bit codes by v_dot4_i32_i8 (four exact integer products per
+ * instruction) -- the "quantized dot lowered to the hardware's int8 path"
+ * route of mlxcel #574 ("Upstream status refresh", "Next actionable step").
+ * The pages define no activation scheme; the one used, dynamic per-row
+ * symmetric quantization, is part of the result:
+ *   amax[m] = max_k |x[m, k]|, r = 127 / amax, sx = amax / 127 (f32 quotients),
+ *   xq[m, k] = clamp(rint(x[m, k] * r), -127, 127) (f32 product, ties to even),
+ *   a row with amax = 0 gives xq = 0;
+ *   y[m, n] = RNE_f16( sx[m] * sum_k xq[m, k] * (q[n, k] * s + b) + out_bias[n] ).
+ * So y differs from mxq_linear's by the activation rounding (about 0.4 % of
+ * a row's largest |x| per element); it matches the int8 method itself to the
+ * tolerance of mxq_qmv.  x must be finite.  Every M runs the decode kernel
+ * (in slices of 8 rows).  Arguments, layouts, out_bias and errors as
+ * mxq_linear.
+ */
+mxq_status mxq_linear_a8(const void* x, const uint32_t* w, const void* scales, const void* biases,
+                         const void* out_bias, void* y, int64_t M, int64_t N, int64_t K, int bits,
+                         int group_size, mxq_dtype sb_dtype, void* stream);
 
 /*
  * mxq_dequant -- standalone dequantization: out[n, k] = q * s + b.

@@ -30,7 +30,7 @@ def test_header_symbols_exported():
             "mxq_last_error", "mxq_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.mxq_abi_version() == 2
+    assert lib.mxq_abi_version() == 3
 
 
 def test_describe_without_device_or_with_bad_args():
@@ -93,14 +93,14 @@ def _call(name, *args):
     return st, lib.mxq_last_error().decode()
 
 
-@pytest.mark.parametrize("name", ["mxq_qmv", "mxq_qmm", "mxq_linear", "mxq_linear_act"])
+@pytest.mark.parametrize("name", ["mxq_qmv", "mxq_qmm", "mxq_linear", "mxq_linear_act", "mxq_linear_a8"])
 def test_fused_validation(name):
     P = FAKE
     ok = dict(M=1, N=4, K=64, bits=4, gs=64, sb=mxq.MXQ_F16, act=mxq.MXQ_BF16)
 
     def call(x=P, w=P, s=P, b=P, y=P, **kw):
         a = dict(ok, **kw)
-        if name == "mxq_linear":   # the output bias goes between biases and y
+        if name in ("mxq_linear", "mxq_linear_a8"):   # the output bias goes between biases and y
             return _call(name, x, w, s, b, a.get("ob", None), y, a["M"], a["N"], a["K"], a["bits"], a["gs"],
                          a["sb"], None)
         if name == "mxq_linear_act":   # ... and the activation dtype follows the scale dtype
@@ -108,7 +108,7 @@ def test_fused_validation(name):
                          a["sb"], a["act"], None)
         return _call(name, x, w, s, b, y, a["M"], a["N"], a["K"], a["bits"], a["gs"], a["sb"], None)
 
-    if name in ("mxq_linear", "mxq_linear_act"):
+    if name in ("mxq_linear", "mxq_linear_act", "mxq_linear_a8"):
         st, msg = call(ob=P + 1)
         assert st == mxq.MXQ_ERR_MISALIGNED and "out_bias" in msg
     if name == "mxq_linear_act":

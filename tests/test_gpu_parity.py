@@ -495,3 +495,79 @@ def test_bf16_activations_k0_and_empty():
                             torch.zeros((5, 1), dtype=torch.float16, device=dev),
                             torch.zeros((5, 1), dtype=torch.float16, device=dev))
     assert tuple(y0.shape) == (0, 5)
+
+
+
+# int8 activations (mxq_linear_a8): f16 x quantized per row inside the decode
+# kernel, v_dot4 products; compared with the oracle of the same method
+# (oracle.matmul_ref_a8: the same f32 quantization decisions, then f64).
+A8 = [
+    # M, N, K, bits, gs, sb
+    (1, 1, 32, 4, 32, "f16"), (1, 2049, 2048, 4, 64, "f16"), (1, 513, 2048, 8, 64, "bf16"),
+    (2, 1023, 8192, 4, 64, "f16"), (3, 130, 2048, 4, 64, "bf16"), (4, 2050, 8192, 8, 64, "bf16"),
+    (5, 66, 4096, 8, 64, "f16"), (8, 1000, 2048, 4, 128, "f16"), (17, 33, 256, 8, 32, "bf16"),
+    (64, 300, 1024, 4, 64, "f16"), (1, 64, 6144, 4, 64, "f16"), (2, 40, 512, 4, 32, "f16"),
+]
+
+
+@pytest.mark.parametrize("case", A8, ids=str)
+def test_int8_activations(case):
+    M, N, K, bits, gs, sb = case
+    p = synth.make_problem(M, N, K, bits, gs, sb, seed=M * 11 + N + K + 23)
+    x, w, s, b = to_dev(p)
+    note(f"int8 activations {case}")
+    y = y_host(mxq.mxq_linear_a8(x, w, s, b, bits=bits, group_size=gs))
+    assert_close(y, oracle.matmul_ref_a8(p.x, p.w, p.scales, p.biases, K, bits, gs, sb), f"a8 {case}")
+
+
+@pytest.mark.parametrize("M", [1, 2, 9])
+@pytest.mark.parametrize("K", [2048, 8192])
+def test_int8_activations_zero_rows_and_bias(M, K):
+    """Rows of x that are all zero quantize to zero (y = output bias); a row
+    whose largest |x| is 127/64 has the exact factor 64, and exact ties."""
+    N = 130
+    p = synth.make_problem(M, N, K, 4, 64, "f16", seed=500 + M + K)
+    x = p.x.copy()
+    x[0, :] = 0
+    if M > 1:
+        x[1, :] = np.float16(0)
+        x[1, :4] = np.array([127 / 64, 5 / 128, 1 / 128, -3 / 128], dtype=np.float16)
+    ob = synth.make_out_bias(N, seed=501)
+    xt = torch.from_numpy(x).to("cuda:0")
+    _, w, s, b = to_dev(p)
+    obt = torch.from_numpy(ob.view(np.int16)).view(torch.float16).to("cuda:0")
+    note(f"int8 activations zero rows M={M} K={K}")
+    y = y_host(mxq.mxq_linear_a8(xt, w, s, b, obt, bits=4))
+    ref = oracle.matmul_ref_a8(x, p.w, p.scales, p.biases, K, 4, 64, "f16") + ob.view(np.float16).astype(np.float64)
+    assert_close(y, ref, f"a8 zero rows M={M} K={K}")
+    assert np.array_equal(y[0], ob.view(np.float16)), "a zero row must give the output bias exactly"
+
+
+@pytest.mark.parametrize("M", [1, 4])
+def test_int8_activations_integer_case(M):
+    """x in {-1, 0, 1} with a 1 in every row: amax 1, r = 127, xq = 127 x and
+    sx = f32(1/127); with scale 1 and bias 0 every integer product and sum is
+    exact, so only the row scale and the f16 store round."""
+    N, K = 96, 512
+    rng = np.random.default_rng(70 + M)
+    w = rng.integers(0, 2 ** 32, size=(N, K // 8), dtype=np.uint32)
+    s = np.full((N, K // 64), 0x3C00, dtype=np.uint16)
+    b = np.zeros((N, K // 64), dtype=np.uint16)
+    xv = rng.integers(-1, 2, size=(M, K)).astype(np.float16)
+    xv[:, 0] = 1
+    p = synth.Problem(x=xv, w=w, scales=s, biases=b, M=M, N=N, K=K, bits=4, group_size=64, sb_dtype="f16")
+    x, wt, st, bt = to_dev(p)
+    note(f"int8 activations integer case M={M}")
+    y = y_host(mxq.mxq_linear_a8(x, wt, st, bt, bits=4))
+    ref = oracle.matmul_ref_a8(xv, w, s, b, K, 4, 64, "f16")
+    assert_close(y, ref, f"a8 integer M={M}")
+
+
+def test_int8_activations_deterministic():
+    p = synth.make_problem(3, 4000, 2048, 4, 64, "f16", seed=77)
+    x, w, s, b = to_dev(p)
+    note("int8 activations determinism")
+    y1 = mxq.mxq_linear_a8(x, w, s, b)
+    y2 = mxq.mxq_linear_a8(x, w, s, b)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
