@@ -27,6 +27,8 @@ Extra objects on the same line:
                 peak);
   bf16_activations  the lm_head decode launch (GB/s) and the M=512 prefill
                 projections (TFLOP/s) with bf16 x and y;
+  int8_activations  the lm_head launch at M=1 and M=8, f16 path against the
+                int8-activation path (mxq_linear_a8), GB/s;
   dequant       standalone dequant of the lm_head weights to f32, GB/s.
 """
 
@@ -576,6 +578,48 @@ def main():
         prefill["TFLOP/s"] = round(tot_flop / (tot_ms / 1e3) / 1e12, 1)
         act["qmm_m512"] = prefill
         result["bf16_activations"] = act
+
+        # int8 activations (mxq_linear_a8) against the f16 path on the lm_head
+        # shape at M = 1 and M = 8, two weight sets alternating, 20 launches
+        # back to back per figure
+        log("int8 activations ...")
+        i8 = {}
+        wsets = []
+        for r in range(2):
+            w, s, b = synth.make_weights(128256, 2048, 4, 64, "f16", seed=synth.proj_seed(1, r, 7))
+            wsets.append((torch.from_numpy(w.view(np.int32)).to(dev),
+                          torch.from_numpy(s.view(np.int16)).view(torch.float16).to(dev),
+                          torch.from_numpy(b.view(np.int16)).view(torch.float16).to(dev)))
+        for M in (1, 8):
+            x8 = torch.from_numpy(synth.make_x(M, 2048, seed=91 + M)).to(dev)
+            y8 = torch.empty((M, 128256), dtype=torch.float16, device=dev)
+            row = {}
+            for label, fn in (("f16", lib.mxq_qmv), ("int8", lib.mxq_linear_a8)):
+                def launch(i, fn=fn, label=label):
+                    tw, ts, tb = wsets[i % 2]
+                    if label == "f16":
+                        st_ = fn(x8.data_ptr(), tw.data_ptr(), ts.data_ptr(), tb.data_ptr(), y8.data_ptr(),
+                                 M, 128256, 2048, 4, 64, 0, cur_stream(torch))
+                    else:
+                        st_ = fn(x8.data_ptr(), tw.data_ptr(), ts.data_ptr(), tb.data_ptr(), None, y8.data_ptr(),
+                                 M, 128256, 2048, 4, 64, 0, cur_stream(torch))
+                    if st_ != 0:
+                        raise RuntimeError(f"{label} lm_head M={M}: libmxq status {st_}")
+                for i in range(6):
+                    launch(i)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for i in range(20):
+                    launch(i)
+                e1.record()
+                torch.cuda.synchronize()
+                ms = e0.elapsed_time(e1) / 20
+                row[label] = {"us": round(ms * 1e3, 2),
+                              "GB/s": round(call_bytes(M, 128256, 2048) / (ms / 1e3) / 1e9, 1)}
+            i8[f"lm_head_M{M}"] = row
+        del wsets
+        torch.cuda.empty_cache()
+        result["int8_activations"] = i8
 
         log("dequant ...")
         w, s, b = synth.make_weights(128256, 2048, 4, 64, "f16", seed=7)
