@@ -27,8 +27,9 @@ Extra objects on the same line:
                 peak);
   bf16_activations  the lm_head decode launch (GB/s) and the M=512 prefill
                 projections (TFLOP/s) with bf16 x and y;
-  int8_activations  the lm_head launch at M=1 and M=8, f16 path against the
-                int8-activation path (mxq_linear_a8), GB/s;
+  int8_activations  the lm_head launch at M=1, 8 and 16, f16 path (the
+                few-row matrix-core kernel at 16) against the int8-activation
+                path (mxq_linear_a8), GB/s;
   dequant       standalone dequant of the lm_head weights to f32, GB/s.
 """
 
@@ -590,7 +591,7 @@ def main():
             wsets.append((torch.from_numpy(w.view(np.int32)).to(dev),
                           torch.from_numpy(s.view(np.int16)).view(torch.float16).to(dev),
                           torch.from_numpy(b.view(np.int16)).view(torch.float16).to(dev)))
-        for M in (1, 8):
+        for M in (1, 8, 16):
             x8 = torch.from_numpy(synth.make_x(M, 2048, seed=91 + M)).to(dev)
             y8 = torch.empty((M, 128256), dtype=torch.float16, device=dev)
             row = {}

@@ -84,6 +84,16 @@ mxq_status run_qmv(const char* who, const void* x, const uint32_t* w, const void
   a.act = act;
   a.rows_per_wave = 0;
   a.stream = static_cast<hipStream_t>(stream);
+  // 9..16 rows of f16 activations: the few-row matrix-core kernel (one launch
+  // instead of two 8-row decode launches), when the shape fills the GPU (its x
+  // staging uses 16-byte loads)
+  if (act == kActF16 && aligned(x, 16) && mxq::qsm_shape(M, N, K, bits, group_size, dev)) {
+    a.x = static_cast<const uint16_t*>(x);
+    a.y = static_cast<uint16_t*>(y);
+    a.x_vec = 1;
+    e = mxq::launch_qsm(a, static_cast<int>(M), dev);
+    return e == hipSuccess ? MXQ_OK : hip_fail(who, e);
+  }
   for (int64_t m0 = 0; m0 < M; m0 += mt_max) {
     const int mt = static_cast<int>((M - m0) < mt_max ? (M - m0) : mt_max);
     a.x = static_cast<const uint16_t*>(x) + m0 * K;
@@ -379,6 +389,12 @@ const char* mxq_describe(const char* op, int64_t M, int64_t N, int64_t K, int bi
            ",tile=" + std::to_string(bm) + "x" + std::to_string(bn) +
            (tl.splits > 1 ? ",ksplit=" + std::to_string(tl.splits) : std::string()) +
            "> grid=" + std::to_string(tiles * tl.splits) + " block=512";
+    return desc.c_str();
+  }
+  if (mxq::qsm_shape(M, N, K, bits, group_size, dev)) {
+    desc = "qsm_kernel<bits=" + std::to_string(bits) + ",sb=" + sb + ",m=" + std::to_string(M) + "> grid=" +
+           std::to_string((N + 255) / 256) + " block=256 lds=" +
+           std::to_string(mxq::qsm_lds_bytes(static_cast<int>(M), static_cast<int>(K)));
     return desc.c_str();
   }
   int mt_max = 8;

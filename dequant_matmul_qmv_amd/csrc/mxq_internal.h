@@ -95,6 +95,13 @@ hipError_t launch_qmv_slice(const QmvArgs& a, const DeviceInfo& dev, int mt);
 hipError_t launch_qmv_group(const QmvProblem* probs, int count, int bits, int glog2, bool sb_bf16,
                             int act, const DeviceInfo& dev, int mt, hipStream_t stream);
 
+// Few-row kernel on the matrix cores (9 <= M <= 16 activation rows, f16
+// activations, group size 64 or 128, N large enough to occupy the GPU).
+bool qsm_shape(int64_t M, int64_t N, int64_t K, int bits, int group_size, const DeviceInfo& dev);
+size_t qsm_lds_bytes(int M, int K);
+// All M rows in one launch; a.x must be 16-byte aligned.
+hipError_t launch_qsm(const QmvArgs& a, int M, const DeviceInfo& dev);
+
 struct QmmArgs {
   const uint16_t* x;
   const uint32_t* w;

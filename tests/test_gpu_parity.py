@@ -571,3 +571,46 @@ def test_int8_activations_deterministic():
     y2 = mxq.mxq_linear_a8(x, w, s, b)
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+# Few activation rows (9..16) with N large enough to fill the GPU: the
+# matrix-core few-row kernel (qsm).  Sampled output columns against the oracle,
+# including the ragged tail.
+QSM = [
+    (9, 65600, 2048, 4, 64, "f16"), (10, 66000, 1024, 8, 64, "bf16"), (16, 65536, 2048, 4, 128, "f16"),
+    (13, 70001, 512, 4, 64, "bf16"), (12, 65540, 4096, 8, 128, "f16"), (16, 128256, 2048, 4, 64, "f16"),
+]
+
+
+def _sampled_cols(N, seed):
+    return np.unique(np.concatenate([[0, 1, N - 2, N - 1], np.arange(N - 300, N - 250),
+                                     np.random.default_rng(seed).integers(0, N, 150)]))
+
+
+@pytest.mark.parametrize("case", QSM, ids=str)
+def test_few_rows_mfma(case):
+    M, N, K, bits, gs, sb = case
+    assert mxq.mxq_describe("qmv", M, N, K, bits, gs, sb).startswith("qsm_kernel"), case
+    assert not mxq.mxq_describe("qmv", 8, N, K, bits, gs, sb).startswith("qsm_kernel"), case
+    p = synth.make_problem(M, N, K, bits, gs, sb, seed=M + N + K + 31)
+    x, w, s, b = to_dev(p)
+    note(f"few-row mfma {case}")
+    y = y_host(mxq.mxq_qmv(x, w, s, b, bits=bits, group_size=gs))
+    cols = _sampled_cols(N, M)
+    ref = oracle.matmul_ref_rows(p.x, p.w, p.scales, p.biases, cols, K, bits, gs, sb)
+    assert_close(y[:, cols], ref, f"qsm {case}")
+
+
+@pytest.mark.parametrize("M", list(range(9, 17)))
+def test_few_rows_mfma_every_m(M):
+    """Every row count the few-row kernel takes, 4-bit, with an output bias."""
+    N, K = 65792, 1024
+    p = synth.make_problem(M, N, K, 4, 64, "f16", seed=1200 + M)
+    ob = synth.make_out_bias(N, seed=1201)
+    x, w, s, b = to_dev(p)
+    obt = torch.from_numpy(ob.view(np.int16)).view(torch.float16).to("cuda:0")
+    note(f"few-row mfma M={M}")
+    y = y_host(mxq.mxq_linear(x, w, s, b, obt, bits=4))
+    cols = _sampled_cols(N, 100 + M)
+    ref = oracle.linear_ref(p.x, p.w[cols], p.scales[cols], p.biases[cols], ob[cols], K, 4, 64, "f16")
+    assert_close(y[:, cols], ref, f"qsm M={M}")
