@@ -105,34 +105,6 @@ __device__ __forceinline__ void split2_f16_to_bf16(const u4& v, u4& hi, u4& lo) 
 }
 }  // namespace
 
-// Codes in natural k order for the MFMA B operand (the x tile is then used as
-// stored, with no reordering).  A byte-select puts byte i of the word, twice,
-// under the f16 exponent of 1024 (the selector's byte 5 is magic's 0x64); the
-// mask keeps the low nibble in the low half (1024 + c) and the high nibble in
-// the high half (1024 + 16 c); one packed f16 fma, exact, maps them to
-// (c_lo, c_hi).  8-bit words: bytes 2i and 2i + 1 under the exponent, then -1024.
-struct Unpack4 {
-  uint32_t magic;   // kMagic
-  h2 scale;         // (1, 1/16)
-};
-__device__ __forceinline__ u4 unpack4_natural(uint32_t w, const Unpack4& u) {
-  const h2 off = {static_cast<_Float16>(-1024.0f), static_cast<_Float16>(-64.0f)};
-  uint32_t p[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t sel = 0x05000500u | (static_cast<uint32_t>(i) << 16) | static_cast<uint32_t>(i);
-    const uint32_t t = __builtin_amdgcn_perm(u.magic, w, sel) & 0x64F0640Fu;
-    p[i] = as_u32(__builtin_elementwise_fma(as_h2(t), u.scale, off));
-  }
-  return u4{p[0], p[1], p[2], p[3]};
-}
-__device__ __forceinline__ u4 unpack8_natural(uint32_t w0, uint32_t w1, uint32_t magic) {
-  const uint32_t sel_lo = 0x05010500u, sel_hi = 0x05030502u;
-  const uint32_t p0 = __builtin_amdgcn_perm(magic, w0, sel_lo), p1 = __builtin_amdgcn_perm(magic, w0, sel_hi);
-  const uint32_t p2 = __builtin_amdgcn_perm(magic, w1, sel_lo), p3 = __builtin_amdgcn_perm(magic, w1, sel_hi);
-  return u4{as_u32(sub1024(p0)), as_u32(sub1024(p1)), as_u32(sub1024(p2)), as_u32(sub1024(p3))};
-}
-
 // Sum of v over aligned groups of 8 lanes (4 when GS == 32), in every lane of
 // the group, through DPP lane swizzles (no LDS traffic).
 template <int LANES>

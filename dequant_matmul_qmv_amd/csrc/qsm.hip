@@ -38,26 +38,6 @@ constexpr int kQsmNB = 4;                                // 16-row MFMA blocks p
 constexpr int kQsmRows = kQsmWaves * kQsmNB * 16;        // rows of W per workgroup
 constexpr int kQsmPad = 8;                               // halves of padding per staged x row
 
-// natural-order exact f16 codes of one word, as in the prefill kernel
-__device__ __forceinline__ u4 qsm_unpack4(uint32_t w, uint32_t magic) {
-  const h2 scale = {static_cast<_Float16>(1.0f), static_cast<_Float16>(0.0625f)};
-  const h2 off = {static_cast<_Float16>(-1024.0f), static_cast<_Float16>(-64.0f)};
-  uint32_t p[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t sel = 0x05000500u | (static_cast<uint32_t>(i) << 16) | static_cast<uint32_t>(i);
-    const uint32_t t = __builtin_amdgcn_perm(magic, w, sel) & 0x64F0640Fu;
-    p[i] = as_u32(__builtin_elementwise_fma(as_h2(t), scale, off));
-  }
-  return u4{p[0], p[1], p[2], p[3]};
-}
-__device__ __forceinline__ u4 qsm_unpack8(uint32_t w0, uint32_t w1, uint32_t magic) {
-  const uint32_t sel_lo = 0x05010500u, sel_hi = 0x05030502u;
-  return u4{as_u32(sub1024(__builtin_amdgcn_perm(magic, w0, sel_lo))),
-            as_u32(sub1024(__builtin_amdgcn_perm(magic, w0, sel_hi))),
-            as_u32(sub1024(__builtin_amdgcn_perm(magic, w1, sel_lo))),
-            as_u32(sub1024(__builtin_amdgcn_perm(magic, w1, sel_hi)))};
-}
 }  // namespace
 
 size_t qsm_lds_bytes(int M, int K) {
@@ -100,7 +80,9 @@ __global__ __launch_bounds__(256) void qsm_kernel(const uint16_t* __restrict__ x
   const int col = lane & 15;   // W row within a 16-row block; x row of the A operand
   const int lg = lane >> 4;    // lane group: codes [16 lg, 16 lg + 16) of each 64-code group
   const int row0 = blockIdx.x * kQsmRows + wave * kQsmNB * 16;
-  const uint32_t magic = kMagic;
+  Unpack4 up4;
+  up4.magic = kMagic;
+  up4.scale = h2{static_cast<_Float16>(1.0f), static_cast<_Float16>(0.0625f)};
   constexpr int WPG = 64 * BITS / 32;   // words per row per 64-code group: 8 or 16
   constexpr int WPL = WPG / 4;          // words per lane per group: 2 or 4
   const int kw = K * BITS / 32;
@@ -169,11 +151,11 @@ __global__ __launch_bounds__(256) void qsm_kernel(const uint16_t* __restrict__ x
       for (int j = 0; j < kQsmNB; ++j) {
         u4 b0, b1;
         if constexpr (BITS == 4) {
-          b0 = qsm_unpack4(d.w[q][j][0], magic);
-          b1 = qsm_unpack4(d.w[q][j][1], magic);
+          b0 = unpack4_natural(d.w[q][j][0], up4);
+          b1 = unpack4_natural(d.w[q][j][1], up4);
         } else {
-          b0 = qsm_unpack8(d.w[q][j][0], d.w[q][j][1], magic);
-          b1 = qsm_unpack8(d.w[q][j][2], d.w[q][j][3], magic);
+          b0 = unpack8_natural(d.w[q][j][0], d.w[q][j][1], up4.magic);
+          b1 = unpack8_natural(d.w[q][j][2], d.w[q][j][3], up4.magic);
         }
         f4 p = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, a0), __builtin_bit_cast(h8, b0), zero,
                                                        0, 0, 0);
