@@ -145,6 +145,49 @@ def test_qmm_mfma(case):
     assert_close(_run("qmm", p), _ref(p), f"qmm {case}")
 
 
+def _scale_regime_problem(M, N, K, gs, sb, regime, seed):
+    """4-bit problem whose scales sit in one magnitude regime, biases zero and
+    x rescaled by a power of two so that y stays well inside f16.
+    "big": |s| ~ U[1000, 4000], 2 % of (row, group) pairs in [4096, 30000];
+    "tiny": |s| ~ U[1e-5, 1e-4] (f16 subnormals below 2^-14), 5 % log-uniform
+    in [1e-8, 1e-5]; random signs."""
+    p = synth.make_problem(M, N, K, 4, gs, sb, seed=seed)
+    rng = np.random.default_rng(seed + 1)
+    G = K // gs
+    pick = rng.random((N, G)) < (0.02 if regime == "big" else 0.05)
+    if regime == "big":
+        s = rng.uniform(1000, 4000, (N, G))
+        s[pick] = rng.uniform(4096, 30000, int(pick.sum()))
+        xs = 2.0 ** -12
+    else:
+        s = rng.uniform(1e-5, 1e-4, (N, G))
+        s[pick] = 10 ** rng.uniform(-8, -5, int(pick.sum()))
+        xs = 2.0 ** 10
+    s *= np.where(rng.random((N, G)) < 0.5, -1.0, 1.0)
+    p.scales = synth._round_sb(s, sb)
+    p.biases = synth._round_sb(np.zeros((N, G)), sb)
+    p.x = (p.x.astype(np.float64) * xs).astype(np.float16)
+    return p
+
+
+@pytest.mark.parametrize("regime", ["big", "tiny"])
+@pytest.mark.parametrize("sb", ["f16", "bf16"])
+@pytest.mark.parametrize("shape", [(96, 330, 1024, 64), (70, 200, 1024, 32), (100, 260, 1536, 128),
+                                   (130, 32768, 512, 64)], ids=str)
+def test_qmm_scale_regimes(shape, sb, regime):
+    """Scales at both magnitude ends on the MFMA path (per-group f32 scale
+    FMAs; the bias block's bf16 splits of a zero bias): products of large
+    scales near the f16 range, f16 subnormal and zero scales, bf16 scales far
+    below f16's range, random signs, on 64 x 64 and 128 x 128 tiles and group
+    sizes 32, 64 and 128."""
+    M, N, K, gs = shape
+    p = _scale_regime_problem(M, N, K, gs, sb, regime, seed=M + N + gs)
+    note(f"qmm scale regime {shape} {sb} {regime}")
+    y = _run("qmm", p)
+    assert np.all(np.isfinite(y))
+    assert_close(y, _ref(p), f"qmm scale regime {shape} {sb} {regime}")
+
+
 @pytest.mark.parametrize("proj", ["gate", "down"])
 @pytest.mark.parametrize("sb", ["f16", "bf16"])
 def test_prefill_full_size_sampled(proj, sb):
@@ -174,7 +217,7 @@ def test_decode_projections_full_size(name, N, K):
 
 # ------------------------------------------------------- exact special cases ---
 @pytest.mark.parametrize("entry,M", [("qmv", 1), ("qmv", 8), ("qmm", 64), ("qmm", 128)])
-@pytest.mark.parametrize("bits,sb", [(4, "f16"), (8, "bf16")])
+@pytest.mark.parametrize("bits,sb", [(4, "f16"), (8, "bf16"), (4, "bf16")])
 def test_one_hot_bitexact(entry, M, bits, sb):
     """x rows one-hot at k_m: y[m, n] = f16(f32(w[n, k_m])) exactly."""
     K, N = 512, 70
