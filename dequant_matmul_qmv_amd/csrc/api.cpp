@@ -60,6 +60,9 @@ mxq_status hip_fail(const char* who, hipError_t e) {
   return fail(MXQ_ERR_HIP, std::string(who) + ": " + hipGetErrorName(e) + ": " + hipGetErrorString(e));
 }
 
+// Row counts the K-split few-row kernel takes (its shape test aside).
+bool qsmk_rows(int64_t M, int64_t K) { return M >= 3 || (M == 2 && K <= 2048); }
+
 // M-sliced qmv over the whole M range.
 mxq_status run_qmv(const char* who, const void* x, const uint32_t* w, const void* scales,
                    const void* biases, const void* out_bias, void* y, int64_t M, int64_t N, int64_t K,
@@ -84,9 +87,20 @@ mxq_status run_qmv(const char* who, const void* x, const uint32_t* w, const void
   a.act = act;
   a.rows_per_wave = 0;
   a.stream = static_cast<hipStream_t>(stream);
-  // 9..16 rows of f16 activations: the few-row matrix-core kernel (one launch
-  // instead of two 8-row decode launches), when the shape fills the GPU (its x
-  // staging uses 16-byte loads)
+  // A few rows of f16 activations go to the matrix cores when the shape fills
+  // the GPU: the K-split kernel (4-bit codes) from 3 rows, or from 2 when K <=
+  // 2048 (where the decode kernel's two-row variant is slower; measured), else
+  // the 16-row-block kernel for 9..16 rows (one launch instead of two 8-row
+  // decode launches).  Both read x, and the K-split kernel the scales and
+  // biases, with 16-byte loads.
+  if (act == kActF16 && aligned(x, 16) && aligned(scales, 16) && aligned(biases, 16) && qsmk_rows(M, K) &&
+      mxq::qsmk_shape(M, N, K, bits, group_size, dev)) {
+    a.x = static_cast<const uint16_t*>(x);
+    a.y = static_cast<uint16_t*>(y);
+    a.x_vec = 1;
+    e = mxq::launch_qsmk(a, static_cast<int>(M), dev);
+    return e == hipSuccess ? MXQ_OK : hip_fail(who, e);
+  }
   if (act == kActF16 && aligned(x, 16) && mxq::qsm_shape(M, N, K, bits, group_size, dev)) {
     a.x = static_cast<const uint16_t*>(x);
     a.y = static_cast<uint16_t*>(y);
@@ -148,12 +162,15 @@ mxq_status run_matmul(const char* who, const void* x, const uint32_t* w, const v
     return e == hipSuccess ? MXQ_OK : hip_fail(who, e);
   }
   // The MFMA kernel stages x with 16-byte loads and walks K in stages of 64;
-  // int8 activations run on the decode kernel's v_dot4 path at every M.
-  if (act == kActI8 || !mxq::qmm_mfma_shape(M, K) || !aligned(x, 16))
-    return run_qmv(who, x, w, scales, biases, out_bias, y, M, N, K, bits, group_size, sb_dtype, act, stream);
+  // int8 activations run on the decode kernel's v_dot4 path at every M, and
+  // up to 16 rows of f16 activations on the K-split few-row kernel where it
+  // applies (run_qmv routes them).
   mxq::DeviceInfo dev;
   hipError_t e = mxq::device_info(&dev);
   if (e != hipSuccess) return hip_fail(who, e);
+  const bool few = act == kActF16 && qsmk_rows(M, K) && mxq::qsmk_shape(M, N, K, bits, group_size, dev);
+  if (act == kActI8 || few || !mxq::qmm_mfma_shape(M, K) || !aligned(x, 16))
+    return run_qmv(who, x, w, scales, biases, out_bias, y, M, N, K, bits, group_size, sb_dtype, act, stream);
   mxq::QmmArgs a{};
   a.x = static_cast<const uint16_t*>(x);
   a.w = w;
@@ -380,6 +397,13 @@ const char* mxq_describe(const char* op, int64_t M, int64_t N, int64_t K, int bi
     return desc.c_str();
   }
   const char* sb = sb_dtype == MXQ_BF16 ? "bf16" : "f16";
+  if (qsmk_rows(M, K) && mxq::qsmk_shape(M, N, K, bits, group_size, dev)) {
+    const int64_t nw = K / 512;
+    desc = "qsmk_kernel<bits=4,sb=" + std::string(sb) + ",gs=" + std::to_string(group_size) + ",m=" +
+           std::to_string(M) + ",waves=" + std::to_string(nw) + "> block=" + std::to_string(64 * nw) +
+           " lds=" + std::to_string(mxq::qsmk_lds_bytes(static_cast<int>(nw)));
+    return desc.c_str();
+  }
   const bool mfma = o == "qmm" && mxq::qmm_mfma_shape(M, K);
   if (mfma) {
     const mxq::QmmTile tl = mxq::qmm_pick_tile(M, N, K, dev);

@@ -102,6 +102,14 @@ size_t qsm_lds_bytes(int M, int K);
 // All M rows in one launch; a.x must be 16-byte aligned.
 hipError_t launch_qsm(const QmvArgs& a, int M, const DeviceInfo& dev);
 
+// Few-row kernel with K split over the waves of a workgroup (2 <= M <= 16,
+// 4-bit codes, f16 activations, group size 64 or 128, K = 512, 1024, 2048 or
+// 4096, at least one 16-row block of W per compute unit); a.x and the scales
+// and biases 16-byte aligned.
+bool qsmk_shape(int64_t M, int64_t N, int64_t K, int bits, int group_size, const DeviceInfo& dev);
+size_t qsmk_lds_bytes(int waves);
+hipError_t launch_qsmk(const QmvArgs& a, int M, const DeviceInfo& dev);
+
 struct QmmArgs {
   const uint16_t* x;
   const uint32_t* w;

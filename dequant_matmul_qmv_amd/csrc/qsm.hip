@@ -199,6 +199,215 @@ __global__ __launch_bounds__(256) void qsm_kernel(const uint16_t* __restrict__ x
   }
 }
 
+// ---------------------------------------------------------------------------
+// qsmk: the same contraction with K split over the waves of a workgroup.
+//
+// Wave w of a workgroup owns codes [512 w, 512 w + 512) of every row (K =
+// 512 * waves, at most 8 waves).  Its activation fragments for that slice
+// (16 rows x 512 codes, rows at or past M zero) and their per-group sums stay
+// in registers for the whole kernel.  The workgroup walks blocks of 16 W rows
+// with a grid stride; for each block a wave
+//  * loads its slice of the 16 rows with whole-line reads: instruction i takes
+//    rows 4i .. 4i + 3, 16 lanes x 16 bytes per row (256 contiguous bytes),
+//  * passes them through its own LDS region to the MFMA B layout (lane l:
+//    W row l % 16, codes [16 (l / 16), +16) of each 64-code group, so the two
+//    k-steps of a group never mix groups),
+//  * runs two v_mfma_f32_16x16x32_f16 per group (codes exact in f16) and
+//    applies the group's scale and bias in f32 (s P + b X_g),
+// and the waves' partial 16 x 16 tiles are added in LDS in wave order (one
+// barrier per block; the buffer alternates between blocks).
+namespace {
+constexpr int kKsCodes = 512;                // codes per wave slice
+constexpr int kKsGroups = kKsCodes / 64;     // 64-code groups per slice
+constexpr int kKsRow = kKsCodes / 2 + 16;    // staged 4-bit row slice: 256 bytes + pad
+constexpr int kKsMaxWaves = 8;
+}  // namespace
+
+size_t qsmk_lds_bytes(int waves) {
+  return static_cast<size_t>(waves) * 16 * kKsRow + static_cast<size_t>(2 * waves) * 64 * 16;
+}
+
+template <bool SB_BF16, int GSH, int NW>
+__global__ __launch_bounds__(64 * NW) void qsmk_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ W,
+                                                   const uint16_t* __restrict__ S, const uint16_t* __restrict__ B,
+                                                   uint16_t* __restrict__ y, const uint16_t* __restrict__ ob, int M,
+                                                   int N, int K) {
+  constexpr int nw = NW;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c16 = lane & 15;  // A row (x row), B column (W row of the block), D column
+  const int kg = lane >> 4;   // k-slot group of the operands; D rows 4 kg .. 4 kg + 3
+  unsigned char* wst = smem + wave * 16 * kKsRow;                      // [16][kKsRow] this wave's codes
+  float* red = reinterpret_cast<float*>(smem + nw * 16 * kKsRow);     // [2][nw][64][4] partial tiles
+  const int ks0 = wave * kKsCodes;
+  const int kw = K / 8;
+  const int G = K >> (6 + GSH);
+  constexpr int SBN = kKsGroups >> GSH;  // real groups per slice: 8 (g64) or 4 (g128)
+
+  // ---- activations of this slice, in the A layout, and the group sums of
+  // the D rows this lane holds
+  u4 xa[kKsGroups][2];
+  float xs[kKsGroups][4];
+  {
+    const uint16_t* xp = x + static_cast<size_t>(min(c16, M - 1)) * K + ks0 + 16 * kg;
+    const u4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int g = 0; g < kKsGroups; ++g) {
+      const u4 v0 = *reinterpret_cast<const u4*>(xp + 64 * g);
+      const u4 v1 = *reinterpret_cast<const u4*>(xp + 64 * g + 8);
+      xa[g][0] = c16 < M ? v0 : z;
+      xa[g][1] = c16 < M ? v1 : z;
+    }
+#pragma unroll
+    for (int g = 0; g < kKsGroups; ++g) {
+      float p = sum8_f32(xa[g][0]) + sum8_f32(xa[g][1]);
+      p += __shfl_xor(p, 16);
+      p += __shfl_xor(p, 32);  // X_g of x row c16, in all four lane groups
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xs[g][i] = __shfl(p, 4 * kg + i);
+    }
+  }
+
+  Unpack4 up4;
+  up4.magic = kMagic;
+  up4.scale = h2{static_cast<_Float16>(1.0f), static_cast<_Float16>(0.0625f)};
+
+  // Loads of one block (indices clamped: branch-free; a block past the end
+  // re-reads the last one and is never stored).
+  struct Ld {
+    u4 w[4];
+    u4 s, b;     // SBN scales / biases of column c16 (g128: the low 8 bytes)
+    uint16_t o;  // output bias of column c16 (unused without one)
+  };
+  const int nrb = (N + 15) >> 4;
+  const uint32_t* wl = W + ks0 / 8 + 4 * c16;
+  const uint16_t* obs = ob != nullptr ? ob : S;  // without an output bias: any N readable halves
+  auto load = [&](Ld& d, int rb) __attribute__((always_inline)) {
+    rb = min(rb, nrb - 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = min(16 * rb + 4 * i + kg, N - 1);
+      d.w[i] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(wl + static_cast<size_t>(row) * kw));
+    }
+    const size_t so = static_cast<size_t>(min(16 * rb + c16, N - 1)) * G + wave * SBN;
+    if constexpr (GSH == 0) {
+      d.s = __builtin_nontemporal_load(reinterpret_cast<const u4*>(S + so));
+      d.b = __builtin_nontemporal_load(reinterpret_cast<const u4*>(B + so));
+    } else {
+      typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+      const u2 sv = __builtin_nontemporal_load(reinterpret_cast<const u2*>(S + so));
+      const u2 bv = __builtin_nontemporal_load(reinterpret_cast<const u2*>(B + so));
+      d.s = u4{sv.x, sv.y, 0u, 0u};
+      d.b = u4{bv.x, bv.y, 0u, 0u};
+    }
+    d.o = obs[min(16 * rb + c16, N - 1)];  // unconditional: a load under a branch would drain the prefetch
+  };
+
+  int par = 0;
+  auto step = [&](const Ld& d, int rb) __attribute__((always_inline)) {
+    // codes to this wave's LDS region (row 4i + kg, bytes 16 c16 .. of the slice)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u4*>(wst + (4 * i + kg) * kKsRow + 16 * c16) = d.w[i];
+    __builtin_amdgcn_wave_barrier();
+    const uint32_t sw[4] = {d.s.x, d.s.y, d.s.z, d.s.w};
+    const uint32_t bw[4] = {d.b.x, d.b.y, d.b.z, d.b.w};
+    const f4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    f4 acc = zero;
+#pragma unroll
+    for (int g = 0; g < kKsGroups; ++g) {
+      typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+      const u2 wv = *reinterpret_cast<const u2*>(wst + c16 * kKsRow + 32 * g + 8 * kg);
+      const u4 b0 = unpack4_natural(wv.x, up4);
+      const u4 b1 = unpack4_natural(wv.y, up4);
+      f4 p = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, xa[g][0]), __builtin_bit_cast(h8, b0),
+                                                     zero, 0, 0, 0);
+      p = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, xa[g][1]), __builtin_bit_cast(h8, b1), p, 0,
+                                                 0, 0);
+      const int r = g >> GSH;
+      const float sc = sb_to_f32<SB_BF16>(static_cast<uint16_t>(sw[r >> 1] >> (16 * (r & 1))));
+      const float bi = sb_to_f32<SB_BF16>(static_cast<uint16_t>(bw[r >> 1] >> (16 * (r & 1))));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(bi, xs[g][i], __builtin_fmaf(sc, p[i], acc[i]));
+    }
+    // add the waves' tiles: wave w finishes D rows 4 kg + i for i = w, w + nw, ...
+    *reinterpret_cast<f4*>(red + ((par * nw + wave) * 64 + lane) * 4) = acc;
+    __syncthreads();
+    const int n = 16 * rb + c16;
+    const float o = ob != nullptr ? sb_to_f32<false>(d.o) : 0.0f;
+    for (int i = wave; i < 4; i += nw) {
+      float v = red[((par * nw) * 64 + lane) * 4 + i];
+#pragma unroll
+      for (int w = 1; w < nw; ++w) v += red[((par * nw + w) * 64 + lane) * 4 + i];
+      const int m = 4 * kg + i;
+      if (m < M && n < N) y[static_cast<size_t>(m) * N + n] = f32_to_f16_bits(v + o);
+    }
+    par ^= 1;
+  };
+
+  // two register sets in ping-pong over this workgroup's blocks; a single
+  // loop exit keeps the load counters exact
+  const int stride = gridDim.x;
+  int rb = blockIdx.x;
+  Ld cur, alt;
+  load(cur, rb);
+  for (; rb + stride < nrb; rb += 2 * stride) {
+    load(alt, rb + stride);
+    __builtin_amdgcn_sched_barrier(0);
+    step(cur, rb);
+    load(cur, rb + 2 * stride);
+    __builtin_amdgcn_sched_barrier(0);
+    step(alt, rb + stride);
+  }
+  if (rb < nrb) step(cur, rb);
+}
+
+bool qsmk_shape(int64_t M, int64_t N, int64_t K, int bits, int group_size, const DeviceInfo& dev) {
+  if (bits != 4 || M < 2 || M > 16 || (group_size != 64 && group_size != 128)) return false;
+  const int64_t nw = K / kKsCodes;  // waves per workgroup: 1, 2, 4 or 8
+  if (K % kKsCodes != 0 || nw < 1 || nw > kKsMaxWaves || (nw & (nw - 1)) != 0) return false;
+  // at least one block of 16 rows per compute unit (smaller N stays on qmv)
+  return (N + 15) / 16 >= static_cast<int64_t>(dev.num_cu);
+}
+
+namespace {
+template <bool SB_BF16, int GSH>
+const void* qsmk_ptr(int nw) {
+  switch (nw) {
+    case 1: return reinterpret_cast<const void*>(&qsmk_kernel<SB_BF16, GSH, 1>);
+    case 2: return reinterpret_cast<const void*>(&qsmk_kernel<SB_BF16, GSH, 2>);
+    case 4: return reinterpret_cast<const void*>(&qsmk_kernel<SB_BF16, GSH, 4>);
+    default: return reinterpret_cast<const void*>(&qsmk_kernel<SB_BF16, GSH, 8>);
+  }
+}
+}  // namespace
+
+hipError_t launch_qsmk(const QmvArgs& a, int M, const DeviceInfo& dev) {
+  const int nw = static_cast<int>(a.K / kKsCodes);
+  const size_t lds = qsmk_lds_bytes(nw);
+  const bool g128 = a.glog2 == 7;
+  const void* kern = a.sb_bf16 ? (g128 ? qsmk_ptr<true, 1>(nw) : qsmk_ptr<true, 0>(nw))
+                               : (g128 ? qsmk_ptr<false, 1>(nw) : qsmk_ptr<false, 0>(nw));
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, 64 * nw, lds) != hipSuccess || occ < 1) {
+    (void)hipGetLastError();
+    occ = 1;
+  }
+  const int per_cu = occ < 2 ? occ : 2;
+  const int64_t nrb = (a.N + 15) / 16;
+  const int64_t cap = static_cast<int64_t>(dev.num_cu) * per_cu;
+  const unsigned grid = static_cast<unsigned>(nrb < cap ? nrb : cap);
+  const uint16_t* xp = a.x;
+  const uint32_t* wp = a.w;
+  const uint16_t* sp = a.s;
+  const uint16_t* bp = a.b;
+  uint16_t* yp = a.y;
+  const uint16_t* obp = a.ob;
+  int Mi = M, Ni = static_cast<int>(a.N), Ki = static_cast<int>(a.K);
+  void* args[] = {&xp, &wp, &sp, &bp, &yp, &obp, &Mi, &Ni, &Ki};
+  return hipLaunchKernel(kern, dim3(grid), dim3(64 * nw), args, lds, a.stream);
+}
+
 bool qsm_shape(int64_t M, int64_t N, int64_t K, int bits, int group_size, const DeviceInfo& dev) {
   (void)bits;
   if (M < 9 || M > 16 || K % 64 != 0 || K < 64 || (group_size != 64 && group_size != 128)) return false;

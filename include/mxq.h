@@ -78,16 +78,22 @@ typedef enum mxq_dtype {
 int mxq_abi_version(void);
 
 /*
- * mxq_qmv -- fused dequant + matmul tuned for decode (M = 1 .. 8).
+ * mxq_qmv -- fused dequant + matmul tuned for decode (M = 1 .. 16).
  *
  * Computes y[m, n] = RN_f16( sum_k x[m, k] * (q[n, k] * s[n, g(k)] + b[n, g(k)]) )
  * with g(k) = k / group_size, accumulating in f32 (the scale and bias are
  * applied per group to partial sums, which is the same value up to f32
  * rounding).  The sum of epic #570's "dequant -> matmul" without the weight
- * ever leaving registers.  Accepts any M >= 0; M > 8 is processed in
- * slices of at most 8 rows (each slice re-reads W).  N need not be a
- * multiple of anything (ExecuTorch PR #17187 "Description": M = 1 with N not
- * a multiple of 4).
+ * ever leaving registers.  Accepts any M >= 0.  Routing by shape: one row
+ * (and two at K > 2048) on the decode kernel; up to 16 rows on the matrix
+ * cores when the shape fits them -- 4-bit codes, group size 64 or 128, K of
+ * 512, 1024, 2048 or 4096 and at least 16 rows of W per compute unit (from 3
+ * rows, or 2 at K <= 2048), else 9..16 rows of any supported codes with at
+ * least 256 rows of W per compute unit -- both with x (and for the first, the
+ * scales and biases) 16-byte aligned; otherwise the decode kernel in slices
+ * of at most 8 rows (each slice re-reads W).  N need not be a multiple of
+ * anything (ExecuTorch PR #17187 "Description": M = 1 with N not a multiple
+ * of 4).
  * Results match the f64 definition within |y - y_ref| <= 2e-3 (1 + |y_ref|)
  * and are bit-identical from run to run.
  */
@@ -135,7 +141,8 @@ mxq_status mxq_qmv_grouped(const mxq_qmv_problem* problems, int count, int64_t M
  * group's f32 scale and the bias is added as bias * sum_{k in group} x
  * (the zero-point decomposition mlxcel #574 cites in "Upstream status
  * refresh").  Same arguments, layouts, accuracy and determinism as mxq_qmv;
- * calls with M <= 8 take the mxq_qmv kernel.
+ * calls with M <= 8, and with up to 16 rows where the mxq_qmv matrix-core
+ * route for a few rows fits, take mxq_qmv's routing.
  */
 mxq_status mxq_qmm(const void* x, const uint32_t* w, const void* scales, const void* biases,
                    void* y, int64_t M, int64_t N, int64_t K, int bits, int group_size,
@@ -150,7 +157,7 @@ mxq_status mxq_qmm(const void* x, const uint32_t* w, const void* scales, const v
  * (its stack: "enable linear with bias", "test 4-bit linear with bias").
  * out_bias is an f16 device vector [N], 2-byte aligned, added in f32 before
  * the single f16 rounding; a null out_bias gives exactly the mxq_qmm result.
- * Other arguments, routing (qmv kernel for M <= 8, MFMA kernel above),
+ * Other arguments, routing (mxq_qmv's for a few rows, MFMA kernel above),
  * accuracy and determinism as mxq_qmm; K = 0 gives y[m, n] = out_bias[n]
  * (or +0).  Errors as mxq_qmv, plus MXQ_ERR_MISALIGNED for out_bias.
  */

@@ -616,12 +616,13 @@ def test_int8_activations_deterministic():
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
 
 
-# Few activation rows (9..16) with N large enough to fill the GPU: the
-# matrix-core few-row kernel (qsm).  Sampled output columns against the oracle,
-# including the ragged tail.
+# Few activation rows (9..16) with N large enough to fill the GPU, on shapes
+# the K-split kernel does not take (8-bit codes, K not 512 * 2^j): the
+# 16-row-block matrix-core kernel (qsm).  Sampled output columns against the
+# oracle, including the ragged tail.
 QSM = [
-    (9, 65600, 2048, 4, 64, "f16"), (10, 66000, 1024, 8, 64, "bf16"), (16, 65536, 2048, 4, 128, "f16"),
-    (13, 70001, 512, 4, 64, "bf16"), (12, 65540, 4096, 8, 128, "f16"), (16, 128256, 2048, 4, 64, "f16"),
+    (9, 65600, 3072, 4, 64, "f16"), (10, 66000, 1024, 8, 64, "bf16"), (16, 65536, 1536, 4, 128, "f16"),
+    (13, 70001, 512, 8, 64, "bf16"), (12, 65540, 4096, 8, 128, "f16"), (16, 128256, 2048, 8, 64, "f16"),
 ]
 
 
@@ -634,7 +635,7 @@ def _sampled_cols(N, seed):
 def test_few_rows_mfma(case):
     M, N, K, bits, gs, sb = case
     assert mxq.mxq_describe("qmv", M, N, K, bits, gs, sb).startswith("qsm_kernel"), case
-    assert not mxq.mxq_describe("qmv", 8, N, K, bits, gs, sb).startswith("qsm_kernel"), case
+    assert not mxq.mxq_describe("qmv", 8, N, K, bits, gs, sb).startswith("qsm"), case
     p = synth.make_problem(M, N, K, bits, gs, sb, seed=M + N + K + 31)
     x, w, s, b = to_dev(p)
     note(f"few-row mfma {case}")
@@ -644,10 +645,77 @@ def test_few_rows_mfma(case):
     assert_close(y[:, cols], ref, f"qsm {case}")
 
 
-@pytest.mark.parametrize("M", list(range(9, 17)))
+# 2..16 rows, 4-bit codes, K = 512 * 2^j <= 4096, at least 16 W rows per
+# compute unit: the K-split few-row kernel (qsmk), for 1, 2, 4 and 8 waves per
+# workgroup, group sizes 64 and 128, both scale dtypes, ragged N.
+QSMK = [
+    (2, 128256, 2048, 64, "f16"), (3, 4100, 512, 64, "bf16"), (5, 8192, 1024, 128, "f16"),
+    (8, 8192, 2048, 64, "bf16"), (16, 16390, 4096, 64, "f16"), (11, 65537, 4096, 128, "bf16"),
+    (16, 128256, 2048, 64, "f16"), (4, 4111, 4096, 64, "f16"),
+]
+
+
+@pytest.mark.parametrize("entry", ["qmv", "qmm"])
+@pytest.mark.parametrize("case", QSMK, ids=str)
+def test_few_rows_ksplit(case, entry):
+    M, N, K, gs, sb = case
+    assert mxq.mxq_describe(entry, M, N, K, 4, gs, sb).startswith("qsmk_kernel"), case
+    p = synth.make_problem(M, N, K, 4, gs, sb, seed=M + N + K + 37)
+    x, w, s, b = to_dev(p)
+    note(f"few-row k-split {entry} {case}")
+    fn = mxq.mxq_qmv if entry == "qmv" else mxq.mxq_qmm
+    y = y_host(fn(x, w, s, b, bits=4, group_size=gs))
+    if N * K <= 8192 * 2048:
+        assert_close(y, _ref(p), f"qsmk {case}")
+    else:
+        cols = _sampled_cols(N, M)
+        ref = oracle.matmul_ref_rows(p.x, p.w, p.scales, p.biases, cols, K, 4, gs, sb)
+        assert_close(y[:, cols], ref, f"qsmk {case}")
+
+
+def test_few_rows_ksplit_routing():
+    """Shapes around the K-split kernel's bounds take the other kernels."""
+    d = mxq.mxq_describe
+    assert d("qmv", 2, 8192, 2048, 4, 64, "f16").startswith("qsmk")
+    assert not d("qmv", 2, 16384, 4096, 4, 64, "f16").startswith("qsmk")   # two rows at K > 2048: decode kernel
+    assert d("qmv", 3, 16384, 4096, 4, 64, "f16").startswith("qsmk")
+    assert not d("qmv", 1, 128256, 2048, 4, 64, "f16").startswith("qsmk")
+    assert not d("qmv", 17, 128256, 2048, 4, 64, "f16").startswith("qsmk")
+    assert not d("qmv", 8, 128256, 2048, 8, 64, "f16").startswith("qsmk")   # 8-bit codes
+    assert not d("qmv", 8, 128256, 2048, 4, 32, "f16").startswith("qsmk")   # group size 32
+    assert not d("qmv", 8, 128256, 1536, 4, 64, "f16").startswith("qsmk")   # K not 512 * 2^j
+    assert not d("qmv", 8, 128256, 8192, 4, 64, "f16").startswith("qsmk")   # K > 4096
+    assert not d("qmv", 8, 2048, 2048, 4, 64, "f16").startswith("qsmk")     # too few W rows per CU
+
+
+def test_few_rows_ksplit_misaligned_scales_and_determinism():
+    """Scales and biases only 2-byte aligned leave the K-split kernel (it reads
+    them with 16-byte loads) with the same result bar rounding order; its own
+    result is bit-identical from run to run."""
+    M, N, K = 6, 8192, 2048
+    p = synth.make_problem(M, N, K, 4, 64, "f16", seed=77)
+    x, w, s, b = to_dev(p)
+    y1 = y_host(mxq.mxq_qmv(x, w, s, b, bits=4))
+    y2 = y_host(mxq.mxq_qmv(x, w, s, b, bits=4))
+    assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16))
+    G = K // 64
+    s_off = torch.empty(N * G + 1, dtype=torch.float16, device="cuda:0")
+    b_off = torch.empty(N * G + 1, dtype=torch.float16, device="cuda:0")
+    s_off[1:].copy_(s.reshape(-1))
+    b_off[1:].copy_(b.reshape(-1))
+    note("few-row k-split misaligned scales")
+    y3 = y_host(mxq.mxq_qmv(x, w, s_off[1:].view(N, G), b_off[1:].view(N, G), bits=4))
+    ref = _ref(p)
+    assert_close(y1, ref, "qsmk aligned")
+    assert_close(y3, ref, "misaligned scales route")
+
+
+@pytest.mark.parametrize("M", list(range(2, 17)))
 def test_few_rows_mfma_every_m(M):
-    """Every row count the few-row kernel takes, 4-bit, with an output bias."""
+    """Every row count the K-split few-row kernel takes, through mxq_linear
+    (4-bit, with an output bias)."""
     N, K = 65792, 1024
+    assert mxq.mxq_describe("qmm", M, N, K, 4, 64, "f16").startswith("qsmk_kernel"), M
     p = synth.make_problem(M, N, K, 4, 64, "f16", seed=1200 + M)
     ob = synth.make_out_bias(N, seed=1201)
     x, w, s, b = to_dev(p)
