@@ -167,12 +167,27 @@ constexpr uint32_t kMagicB = 0x43004300u;
 
 __device__ __forceinline__ b2 as_b2(uint32_t u) { return __builtin_bit_cast(b2, u); }
 
-// 4-bit word -> (128 + c0, 128 + c4), (128 + c1, 128 + c5), ... as bf16 pairs.
-__device__ __forceinline__ void unpack_w4_bf16_off(uint32_t w, uint32_t magic, uint32_t (&q)[4]) {
+// 4-bit word -> (E + c0, E + c4), (E + c1, E + c5), (E + c2, E + c6),
+// (E + c3, E + c7), with E the power of two whose bit pattern is `magic` in
+// each half: 128 for kMagicB (bf16 pairs), 1024 for kMagic (f16 pairs).  The
+// offset is left in; callers remove E * sum(x) through the group's bias.
+__device__ __forceinline__ void unpack_w4_off(uint32_t w, uint32_t magic, uint32_t (&q)[4]) {
   q[0] = and_or(w, 0x000F000Fu, magic);
   q[1] = and_or(w >> 4, 0x000F000Fu, magic);
   q[2] = and_or(w >> 8, 0x000F000Fu, magic);
   q[3] = and_or(w >> 12, 0x000F000Fu, magic);
+}
+
+// The same pairs as unpack_w4_off in plain code, which the compiler turns
+// into one v_bfi_b32 per pair when `magic` is a value it cannot see (the
+// caller hides the constant behind an empty asm).  Use this form where the
+// pairs feed the matrix cores: the compiler inserts the wait states an MFMA
+// needs after a VALU write of its operand only for instructions it knows, not
+// for inline asm, whose result the MFMA could then read before it is written.
+__device__ __forceinline__ u4 unpack_w4_off_mfma(uint32_t w, uint32_t magic) {
+  constexpr uint32_t m = 0x000F000Fu;
+  return u4{(w & m) | (magic & ~m), ((w >> 4) & m) | (magic & ~m), ((w >> 8) & m) | (magic & ~m),
+            ((w >> 12) & m) | (magic & ~m)};
 }
 
 // Byte i of w as an f32 integer (v_cvt_f32_ubyte<i>).

@@ -474,7 +474,7 @@ __global__ __launch_bounds__(kQmvBlock) void qmv_kernel(const QmvBatch batch) {
         q[i] = wr[i] ^ 0x80808080u;  // c - 128 as a signed byte
       } else if constexpr (XB && BITS == 4) {
         uint32_t t[4];
-        unpack_w4_bf16_off(wr[i], magic, t);
+        unpack_w4_off(wr[i], magic, t);
 #pragma unroll
         for (int p = 0; p < 4; ++p) q[4 * i + p] = t[p];
       } else if constexpr (XB) {

@@ -212,8 +212,12 @@ __global__ __launch_bounds__(256) void qsm_kernel(const uint16_t* __restrict__ x
 //  * passes them through its own LDS region to the MFMA B layout (lane l:
 //    W row l % 16, codes [16 (l / 16), +16) of each 64-code group, so the two
 //    k-steps of a group never mix groups),
-//  * runs two v_mfma_f32_16x16x32_f16 per group (codes exact in f16) and
-//    applies the group's scale and bias in f32 (s P + b X_g),
+//  * unpacks codes two at a time (one v_bfi_b32 per pair) to the f16
+//    values 1024 + code
+//    (exact; the activation fragments are permuted once into the matching
+//    k order), runs two v_mfma_f32_16x16x32_f16 per group and applies the
+//    group's scale and bias in f32 as s P' + (b - 1024 s) X_g, where
+//    P' = P + 1024 X_g is what the offset codes give,
 // and the waves' partial 16 x 16 tiles are added in LDS in wave order (one
 // barrier per block; the buffer alternates between blocks).
 namespace {
@@ -228,7 +232,7 @@ size_t qsmk_lds_bytes(int waves) {
 }
 
 template <bool SB_BF16, int GSH, int NW>
-__global__ __launch_bounds__(64 * NW) void qsmk_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ W,
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void qsmk_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ W,
                                                    const uint16_t* __restrict__ S, const uint16_t* __restrict__ B,
                                                    uint16_t* __restrict__ y, const uint16_t* __restrict__ ob, int M,
                                                    int N, int K) {
@@ -256,8 +260,9 @@ __global__ __launch_bounds__(64 * NW) void qsmk_kernel(const uint16_t* __restric
     for (int g = 0; g < kKsGroups; ++g) {
       const u4 v0 = *reinterpret_cast<const u4*>(xp + 64 * g);
       const u4 v1 = *reinterpret_cast<const u4*>(xp + 64 * g + 8);
-      xa[g][0] = c16 < M ? v0 : z;
-      xa[g][1] = c16 < M ? v1 : z;
+      // k slots in the pair order of the offset unpack: (x0, x4) (x1, x5) ...
+      xa[g][0] = perm_x_w4(c16 < M ? v0 : z);
+      xa[g][1] = perm_x_w4(c16 < M ? v1 : z);
     }
 #pragma unroll
     for (int g = 0; g < kKsGroups; ++g) {
@@ -269,9 +274,8 @@ __global__ __launch_bounds__(64 * NW) void qsmk_kernel(const uint16_t* __restric
     }
   }
 
-  Unpack4 up4;
-  up4.magic = kMagic;
-  up4.scale = h2{static_cast<_Float16>(1.0f), static_cast<_Float16>(0.0625f)};
+  uint32_t magic = kMagic;
+  asm volatile("" : "+v"(magic));  // opaque to the compiler: the unpack becomes v_bfi_b32
 
   // Loads of one block (indices clamped: branch-free; a block past the end
   // re-reads the last one and is never stored).
@@ -313,22 +317,32 @@ __global__ __launch_bounds__(64 * NW) void qsmk_kernel(const uint16_t* __restric
     const uint32_t sw[4] = {d.s.x, d.s.y, d.s.z, d.s.w};
     const uint32_t bw[4] = {d.b.x, d.b.y, d.b.z, d.b.w};
     const f4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
-    f4 acc = zero;
+    // all groups' MFMAs first, each into its own registers, so that the
+    // matrix core runs them back to back while the codes of the next group
+    // are unpacked; then the scale and bias per group, in group order
+    f4 p[kKsGroups];
 #pragma unroll
     for (int g = 0; g < kKsGroups; ++g) {
       typedef uint32_t u2 __attribute__((ext_vector_type(2)));
       const u2 wv = *reinterpret_cast<const u2*>(wst + c16 * kKsRow + 32 * g + 8 * kg);
-      const u4 b0 = unpack4_natural(wv.x, up4);
-      const u4 b1 = unpack4_natural(wv.y, up4);
-      f4 p = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, xa[g][0]), __builtin_bit_cast(h8, b0),
-                                                     zero, 0, 0, 0);
-      p = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, xa[g][1]), __builtin_bit_cast(h8, b1), p, 0,
-                                                 0, 0);
+      const u4 b0 = unpack_w4_off_mfma(wv.x, magic);  // 1024 + code, exact f16
+      const u4 b1 = unpack_w4_off_mfma(wv.y, magic);
+      p[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, xa[g][0]), __builtin_bit_cast(h8, b0),
+                                                    zero, 0, 0, 0);
+      p[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, xa[g][1]), __builtin_bit_cast(h8, b1),
+                                                    p[g], 0, 0, 0);
+    }
+    f4 acc = zero;
+#pragma unroll
+    for (int g = 0; g < kKsGroups; ++g) {
       const int r = g >> GSH;
       const float sc = sb_to_f32<SB_BF16>(static_cast<uint16_t>(sw[r >> 1] >> (16 * (r & 1))));
-      const float bi = sb_to_f32<SB_BF16>(static_cast<uint16_t>(bw[r >> 1] >> (16 * (r & 1))));
+      // p holds P + 1024 X_g: the offset leaves through the bias factor
+      // b - 1024 s (1024 s is exact; its one rounding, like the f32 sum of
+      // the offset products, errs by about 2^-14 |s X_g| per group)
+      const float bi = __builtin_fmaf(-1024.0f, sc, sb_to_f32<SB_BF16>(static_cast<uint16_t>(bw[r >> 1] >> (16 * (r & 1)))));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(bi, xs[g][i], __builtin_fmaf(sc, p[i], acc[i]));
+      for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(bi, xs[g][i], __builtin_fmaf(sc, p[g][i], acc[i]));
     }
     // add the waves' tiles: wave w finishes D rows 4 kg + i for i = w, w + nw, ...
     *reinterpret_cast<f4*>(red + ((par * nw + wave) * 64 + lane) * 4) = acc;
