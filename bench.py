@@ -27,9 +27,10 @@ Extra objects on the same line:
                 peak);
   bf16_activations  the lm_head decode launch (GB/s) and the M=512 prefill
                 projections (TFLOP/s) with bf16 x and y;
-  int8_activations  the lm_head launch at M=1, 8 and 16, f16 path (the
-                few-row matrix-core kernel at 16) against the int8-activation
-                path (mxq_linear_a8), GB/s;
+  few_rows      the lm_head launch at M = 1, 2, 4, 8 and 16: the f16 route of
+                mxq_qmv (decode kernel at M = 1, the K-split matrix-core kernel
+                from M = 2; kernel named) against the int8-activation route
+                (mxq_linear_a8), GB/s;
   dequant       standalone dequant of the lm_head weights to f32, GB/s.
 """
 
@@ -600,24 +601,26 @@ def main():
         act["qmm_m512"] = prefill
         result["bf16_activations"] = act
 
-        # int8 activations (mxq_linear_a8) against the f16 path on the lm_head
-        # shape at M = 1 and M = 8, two weight sets alternating, 20 launches
-        # back to back per figure
-        log("int8 activations ...")
-        i8 = {}
+        # few activation rows on the lm_head shape: the f16 route mxq_qmv takes
+        # (decode kernel at M = 1, the K-split matrix-core kernel from M = 2)
+        # against the int8-activation route (mxq_linear_a8), three weight sets
+        # (444 MB, more than the Infinity Cache holds) rotating, 20 launches back
+        # to back per figure
+        log("few rows (f16 and int8 activations) ...")
+        few = {}
         wsets = []
-        for r in range(2):
+        for r in range(3):
             w, s, b = synth.make_weights(128256, 2048, 4, 64, "f16", seed=synth.proj_seed(1, r, 7))
             wsets.append((torch.from_numpy(w.view(np.int32)).to(dev),
                           torch.from_numpy(s.view(np.int16)).view(torch.float16).to(dev),
                           torch.from_numpy(b.view(np.int16)).view(torch.float16).to(dev)))
-        for M in (1, 8, 16):
+        for M in (1, 2, 4, 8, 16):
             x8 = torch.from_numpy(synth.make_x(M, 2048, seed=91 + M)).to(dev)
             y8 = torch.empty((M, 128256), dtype=torch.float16, device=dev)
             row = {}
             for label, fn in (("f16", lib.mxq_qmv), ("int8", lib.mxq_linear_a8)):
                 def launch(i, fn=fn, label=label):
-                    tw, ts, tb = wsets[i % 2]
+                    tw, ts, tb = wsets[i % 3]
                     if label == "f16":
                         st_ = fn(x8.data_ptr(), tw.data_ptr(), ts.data_ptr(), tb.data_ptr(), y8.data_ptr(),
                                  M, 128256, 2048, 4, 64, 0, cur_stream(torch))
@@ -637,10 +640,11 @@ def main():
                 ms = e0.elapsed_time(e1) / 20
                 row[label] = {"us": round(ms * 1e3, 2),
                               "GB/s": round(call_bytes(M, 128256, 2048) / (ms / 1e3) / 1e9, 1)}
-            i8[f"lm_head_M{M}"] = row
+            row["f16"]["kernel"] = mxq.mxq_describe("qmv", M, 128256, 2048)
+            few[f"lm_head_M{M}"] = row
         del wsets
         torch.cuda.empty_cache()
-        result["int8_activations"] = i8
+        result["few_rows"] = few
 
         log("dequant ...")
         w, s, b = synth.make_weights(128256, 2048, 4, 64, "f16", seed=7)
