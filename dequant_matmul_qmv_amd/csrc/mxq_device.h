@@ -178,16 +178,39 @@ __device__ __forceinline__ void unpack_w4_off(uint32_t w, uint32_t magic, uint32
   q[3] = and_or(w >> 12, 0x000F000Fu, magic);
 }
 
-// The same pairs as unpack_w4_off in plain code, which the compiler turns
-// into one v_bfi_b32 per pair when `magic` is a value it cannot see (the
-// caller hides the constant behind an empty asm).  Use this form where the
-// pairs feed the matrix cores: the compiler inserts the wait states an MFMA
-// needs after a VALU write of its operand only for instructions it knows, not
-// for inline asm, whose result the MFMA could then read before it is written.
-__device__ __forceinline__ u4 unpack_w4_off_mfma(uint32_t w, uint32_t magic) {
-  constexpr uint32_t m = 0x000F000Fu;
-  return u4{(w & m) | (magic & ~m), ((w >> 4) & m) | (magic & ~m), ((w >> 8) & m) | (magic & ~m),
-            ((w >> 12) & m) | (magic & ~m)};
+// 4-bit word -> four pairs of exact f16 codes for the matrix cores, in the
+// pair order (c0, c5) (c1, c4) (c2, c7) (c3, c6): one shift and four
+// (w & mask) | magic put each pair under the exponent of 1024, as 1024 + c in
+// one half and 1024 + 16 c' in the other (c' taken from bits 4..7 of its half);
+// one packed f16 fma per pair, exact, maps (1024 + c, 1024 + 16 c') to (c, c').
+// Plain code, which the compiler turns into v_and_or_b32 / v_bfi_b32 when
+// `magic` is a value it cannot see (the caller hides the constant behind an
+// empty asm): the compiler inserts the wait states an MFMA needs after a VALU
+// write of its operand only for instructions it knows, not for inline asm,
+// whose result the MFMA could then read before it is written.
+__device__ __forceinline__ u4 unpack_w4_mfma(uint32_t w, uint32_t magic) {
+  constexpr uint32_t m_a = 0x00F0000Fu, m_b = 0x000F00F0u;
+  const h2 sa = {static_cast<_Float16>(1.0f), static_cast<_Float16>(0.0625f)};
+  const h2 oa = {static_cast<_Float16>(-1024.0f), static_cast<_Float16>(-64.0f)};
+  const h2 sb = {static_cast<_Float16>(0.0625f), static_cast<_Float16>(1.0f)};
+  const h2 ob = {static_cast<_Float16>(-64.0f), static_cast<_Float16>(-1024.0f)};
+  const uint32_t h = w >> 8;
+  const uint32_t t0 = (w & m_a) | (magic & ~m_a), t1 = (w & m_b) | (magic & ~m_b);
+  const uint32_t t2 = (h & m_a) | (magic & ~m_a), t3 = (h & m_b) | (magic & ~m_b);
+  return u4{as_u32(__builtin_elementwise_fma(as_h2(t0), sa, oa)), as_u32(__builtin_elementwise_fma(as_h2(t1), sb, ob)),
+            as_u32(__builtin_elementwise_fma(as_h2(t2), sa, oa)), as_u32(__builtin_elementwise_fma(as_h2(t3), sb, ob))};
+}
+
+// Reorder 8 consecutive f16 activations x0..x7 (dwords (x0,x1) (x2,x3)
+// (x4,x5) (x6,x7)) into the pair order of unpack_w4_mfma: (x0,x5) (x1,x4)
+// (x2,x7) (x3,x6).
+__device__ __forceinline__ u4 perm_x_w4_mfma(u4 v) {
+  u4 o;
+  o.x = __builtin_amdgcn_perm(v.z, v.x, 0x07060100u);  // (x0 from v.x bytes 0-1, x5 from v.z bytes 2-3)
+  o.y = __builtin_amdgcn_perm(v.z, v.x, 0x05040302u);  // (x1, x4)
+  o.z = __builtin_amdgcn_perm(v.w, v.y, 0x07060100u);  // (x2, x7)
+  o.w = __builtin_amdgcn_perm(v.w, v.y, 0x05040302u);  // (x3, x6)
+  return o;
 }
 
 // Byte i of w as an f32 integer (v_cvt_f32_ubyte<i>).

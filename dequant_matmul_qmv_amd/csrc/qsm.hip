@@ -213,12 +213,11 @@ __global__ __launch_bounds__(256) void qsm_kernel(const uint16_t* __restrict__ x
 //  * passes them through its own LDS region to the MFMA B layout (lane l:
 //    W row l % 16, codes [16 (l / 16), +16) of each 64-code group, so the two
 //    k-steps of a group never mix groups),
-//  * unpacks codes two at a time (one v_bfi_b32 per pair) to the f16
-//    values 1024 + code
-//    (exact; the activation fragments are permuted once into the matching
-//    k order), runs two v_mfma_f32_16x16x32_f16 per group and applies the
-//    group's scale and bias in f32 as s P' + (b - 1024 s) X_g, where
-//    P' = P + 1024 X_g is what the offset codes give,
+//  * unpacks codes two at a time to exact f16 values (one v_and_or_b32 and
+//    one packed f16 fma per pair, one shift per word; the activation
+//    fragments are permuted once into the matching k order), runs the two
+//    v_mfma_f32_16x16x32_f16 of every group back to back and then applies
+//    each group's scale and bias in f32 (s P + b X_g),
 // and the waves' partial 16 x 16 tiles are added in LDS in wave order (one
 // barrier per block; the buffer alternates between blocks).
 namespace {
@@ -261,9 +260,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     for (int g = 0; g < kKsGroups; ++g) {
       const u4 v0 = *reinterpret_cast<const u4*>(xp + 64 * g);
       const u4 v1 = *reinterpret_cast<const u4*>(xp + 64 * g + 8);
-      // k slots in the pair order of the offset unpack: (x0, x4) (x1, x5) ...
-      xa[g][0] = perm_x_w4(c16 < M ? v0 : z);
-      xa[g][1] = perm_x_w4(c16 < M ? v1 : z);
+      // k slots in the pair order of the code unpack: (x0, x5) (x1, x4) ...
+      xa[g][0] = perm_x_w4_mfma(c16 < M ? v0 : z);
+      xa[g][1] = perm_x_w4_mfma(c16 < M ? v1 : z);
     }
 #pragma unroll
     for (int g = 0; g < kKsGroups; ++g) {
@@ -276,7 +275,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   }
 
   uint32_t magic = kMagic;
-  asm volatile("" : "+v"(magic));  // opaque to the compiler: the unpack becomes v_bfi_b32
+  asm volatile("" : "+v"(magic));  // opaque to the compiler: the unpack becomes v_and_or_b32 / v_bfi_b32
 
   // Loads of one block (indices clamped: branch-free; a block past the end
   // re-reads the last one and is never stored).
@@ -326,8 +325,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     for (int g = 0; g < kKsGroups; ++g) {
       typedef uint32_t u2 __attribute__((ext_vector_type(2)));
       const u2 wv = *reinterpret_cast<const u2*>(wst + c16 * kKsRow + 32 * g + 8 * kg);
-      const u4 b0 = unpack_w4_off_mfma(wv.x, magic);  // 1024 + code, exact f16
-      const u4 b1 = unpack_w4_off_mfma(wv.y, magic);
+      const u4 b0 = unpack_w4_mfma(wv.x, magic);  // exact f16 codes
+      const u4 b1 = unpack_w4_mfma(wv.y, magic);
       p[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, xa[g][0]), __builtin_bit_cast(h8, b0),
                                                     zero, 0, 0, 0);
       p[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, xa[g][1]), __builtin_bit_cast(h8, b1),
@@ -338,10 +337,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     for (int g = 0; g < kKsGroups; ++g) {
       const int r = g >> GSH;
       const float sc = sb_to_f32<SB_BF16>(static_cast<uint16_t>(sw[r >> 1] >> (16 * (r & 1))));
-      // p holds P + 1024 X_g: the offset leaves through the bias factor
-      // b - 1024 s (1024 s is exact; its one rounding, like the f32 sum of
-      // the offset products, errs by about 2^-14 |s X_g| per group)
-      const float bi = __builtin_fmaf(-1024.0f, sc, sb_to_f32<SB_BF16>(static_cast<uint16_t>(bw[r >> 1] >> (16 * (r & 1)))));
+      const float bi = sb_to_f32<SB_BF16>(static_cast<uint16_t>(bw[r >> 1] >> (16 * (r & 1))));
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(bi, xs[g][i], __builtin_fmaf(sc, p[g][i], acc[i]));
     }

@@ -75,6 +75,56 @@ def test_graph_replay_matches_eager():
         assert torch.equal(got_d.view(torch.int32), ed.view(torch.int32)), rep
 
 
+def test_graph_replay_few_rows_and_dequant_layouts():
+    """The K-split few-row kernel and the dequant kernel's f16 and f32 outputs
+    under graph replay, each replay equal to an eager call bit for bit."""
+    dev = "cuda:0"
+    pk = synth.make_problem(6, 8192, 2048, 4, 64, "f16", seed=64)
+    assert mxq.mxq_describe("qmv", 6, 8192, 2048, 4, 64, "f16").startswith("qsmk_kernel")
+    pd = synth.make_problem(1, 700, 2048, 4, 128, "bf16", seed=65)
+    xk, wk, sk, bk = to_dev(pk)
+    _, wd, sd, bd = to_dev(pd)
+    yk = torch.empty((6, 8192), dtype=torch.float16, device=dev)
+    d16 = torch.empty((700, 2048), dtype=torch.float16, device=dev)
+    d32 = torch.empty((700, 2048), dtype=torch.float32, device=dev)
+
+    def work():
+        mxq.mxq_qmv(xk, wk, sk, bk, yk, bits=4)
+        mxq.mxq_dequant(wd, sd, bd, d16, bits=4, group_size=128, out_dtype=torch.float16)
+        mxq.mxq_dequant(wd, sd, bd, d32, bits=4, group_size=128)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        work()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    note("graph capture of qsmk + dequant f16/f32")
+    with torch.cuda.graph(g):
+        work()
+    torch.cuda.synchronize()
+
+    rng = np.random.default_rng(6)
+    for rep in range(3):
+        new_x = torch.from_numpy(rng.standard_normal((6, 2048)).astype(np.float16)).to(dev)
+        xk.copy_(new_x)
+        d16.zero_()
+        d32.zero_()
+        torch.cuda.synchronize()
+        note(f"graph replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        got_k, got_16, got_32 = yk.clone(), d16.clone(), d32.clone()
+        ek = mxq.mxq_qmv(new_x, wk, sk, bk, bits=4)
+        e16 = mxq.mxq_dequant(wd, sd, bd, bits=4, group_size=128, out_dtype=torch.float16)
+        e32 = mxq.mxq_dequant(wd, sd, bd, bits=4, group_size=128)
+        torch.cuda.synchronize()
+        assert torch.equal(got_k.view(torch.int16), ek.view(torch.int16)), rep
+        assert torch.equal(got_16.view(torch.int16), e16.view(torch.int16)), rep
+        assert torch.equal(got_32.view(torch.int32), e32.view(torch.int32)), rep
+
+
 def test_describe_on_device():
     d = mxq.mxq_describe("qmv", 1, 128256, 2048, 4, 64, "f16")
     assert d.startswith("qmv_kernel<bits=4,sb=f16,mt=1,rows=4"), d

@@ -673,6 +673,22 @@ def test_few_rows_ksplit(case, entry):
         assert_close(y[:, cols], ref, f"qsmk {case}")
 
 
+@pytest.mark.parametrize("regime", ["big", "tiny"])
+@pytest.mark.parametrize("sb", ["f16", "bf16"])
+@pytest.mark.parametrize("shape", [(4, 4100, 2048, 64), (9, 8192, 1024, 128), (16, 4096, 4096, 64)], ids=str)
+def test_few_rows_ksplit_scale_regimes(shape, sb, regime):
+    """The K-split kernel's codes carry an offset of 1024 that leaves through
+    the bias factor b - 1024 s: scales near the f16 range, f16 subnormal and
+    zero scales and bf16 scales far below f16's range, random signs."""
+    M, N, K, gs = shape
+    assert mxq.mxq_describe("qmv", M, N, K, 4, gs, sb).startswith("qsmk_kernel"), shape
+    p = _scale_regime_problem(M, N, K, gs, sb, regime, seed=M + N + gs + 3)
+    note(f"qsmk scale regime {shape} {sb} {regime}")
+    y = _run("qmv", p)
+    assert np.all(np.isfinite(y))
+    assert_close(y, _ref(p), f"qsmk scale regime {shape} {sb} {regime}")
+
+
 def test_few_rows_ksplit_routing():
     """Shapes around the K-split kernel's bounds take the other kernels."""
     d = mxq.mxq_describe
