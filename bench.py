@@ -231,6 +231,30 @@ def traffic_pass():
     print(json.dumps(meta), flush=True)
 
 
+def qmm_pass():
+    """Workload for rocprofv3 --pmc passes over the prefill kernel: the M=512
+    gate (8192x2048) and down (2048x8192) projections, 4-bit g64, f16
+    scales, five calls each."""
+    import numpy as np
+    import torch
+
+    import dequant_matmul_qmv_amd as mxq
+    import synth
+    mxq.load()
+    dev = "cuda:0"
+    for N, K in ((8192, 2048), (2048, 8192)):
+        p = synth.make_problem(512, N, K, 4, 64, "f16", seed=3)
+        x = torch.from_numpy(p.x).to(dev)
+        w = torch.from_numpy(p.w.view(np.int32)).to(dev)
+        s = torch.from_numpy(p.scales.view(np.int16)).view(torch.float16).to(dev)
+        b = torch.from_numpy(p.biases.view(np.int16)).view(torch.float16).to(dev)
+        y = torch.empty((512, N), dtype=torch.float16, device=dev)
+        for _ in range(5):
+            mxq.mxq_qmm(x, w, s, b, y, bits=4)
+        torch.cuda.synchronize()
+        print(json.dumps({"kernel": mxq.mxq_describe("qmm", 512, N, K), "N": N, "K": K, "calls": 5}), flush=True)
+
+
 def write_traffic(fetch_csv: str, write_csv: str, meta_json: str):
     """Turn two rocprofv3 counter CSVs into profiles/qmv_traffic.json.
 
@@ -323,6 +347,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="skip decode_step, qmm and dequant legs")
     ap.add_argument("--traffic-pass", action="store_true",
                     help="only run the workload of the rocprofv3 --pmc traffic passes")
+    ap.add_argument("--qmm-pass", action="store_true",
+                    help="only run the M=512 prefill workload of the rocprofv3 --pmc counter passes")
     ap.add_argument("--write-traffic", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "META_JSON"),
                     help="write profiles/qmv_traffic.json from two rocprofv3 counter CSVs")
     args = ap.parse_args()
@@ -331,6 +357,9 @@ def main():
         return
     if args.traffic_pass:
         traffic_pass()
+        return
+    if args.qmm_pass:
+        qmm_pass()
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
