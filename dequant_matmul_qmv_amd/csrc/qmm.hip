@@ -242,12 +242,17 @@ __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x
   uint16_t sv, bv;
   auto gload = [&](int kt) __attribute__((always_inline)) {
     kt = kt0 + min(kt, nkt - 1);  // global stage; the tail re-reads the last one, never stored where it is read
+    // the stage's offsets are wave-uniform: kept in SGPRs (the empty asm stops
+    // the compiler from folding them into 64-bit per-lane pointers), so each
+    // load takes the SGPR-base + 32-bit lane-offset form with no VALU add
+    size_t xo = static_cast<size_t>(kt) * (KT * 2), wo = static_cast<size_t>(kt) * (WPS * 4);
+    asm volatile("" : "+s"(xo), "+s"(wo));
+    const char* xb = xbase + xo;
+    const char* wb = wbase + wo;
 #pragma unroll
-    for (int i = 0; i < XCH; ++i)
-      xr[i] = *reinterpret_cast<const u4*>(xbase + static_cast<size_t>(kt) * (KT * 2) + xoff[i]);
+    for (int i = 0; i < XCH; ++i) xr[i] = *reinterpret_cast<const u4*>(xb + xoff[i]);
 #pragma unroll
-    for (int i = 0; i < WCH; ++i)
-      wr[i] = *reinterpret_cast<const u4*>(wbase + static_cast<size_t>(kt) * (WPS * 4) + woff[i]);
+    for (int i = 0; i < WCH; ++i) wr[i] = *reinterpret_cast<const u4*>(wb + woff[i]);
     const size_t go = static_cast<size_t>(group_of(kt * RPS + sb_e)) * 2;
     sv = *reinterpret_cast<const uint16_t*>(sbase + go + sboff);
     bv = *reinterpret_cast<const uint16_t*>(bbase + go + sboff);
@@ -438,6 +443,30 @@ __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x
   if (pipe == 1) return;
   // lane holds column n, rows 8*(r/4) + 4*(lane/32) + r%4 of each 32x32 block
   float* pout = part != nullptr ? part + static_cast<size_t>(split) * M * N : nullptr;
+  if (m0 + BM <= M && n0 + BN <= N && N < (1 << 26)) {
+    // whole tile inside y: no bounds checks; each store takes a wave-uniform
+    // row base in SGPRs and the lane's fixed 32-bit offset (4*hi rows + column)
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int n = n0 + bcol + j * 32;
+        const uint32_t loff = static_cast<uint32_t>(4 * hi * N + n);  // elements; bytes below fit in 32 bits
+        const float o = (ob != nullptr && pout == nullptr) ? sb_to_f32<XB>(ob[n]) : 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float v = acc[i][j][r] + red[((q * MB * NB + i * NB + j) * 16 + r) * 64 + lane] + o;
+          size_t urow = static_cast<size_t>(m0 + wm * TWM + i * 32 + 8 * (r >> 2) + (r & 3)) * N;
+          asm volatile("" : "+s"(urow));
+          if (pout != nullptr) {
+            *reinterpret_cast<float*>(reinterpret_cast<char*>(pout + urow) + loff * 4u) = v;
+          } else {
+            *reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(y + urow) + loff * 2u) = f32_to_act_bits<XB>(v);
+          }
+        }
+      }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
