@@ -93,8 +93,13 @@ mxq_status run_qmv(const char* who, const void* x, const uint32_t* w, const void
   // the 16-row-block kernel for 9..16 rows (one launch instead of two 8-row
   // decode launches).  Both read x, and the K-split kernel the scales and
   // biases, with 16-byte loads.
-  if (act == kActF16 && aligned(x, 16) && aligned(scales, 16) && aligned(biases, 16) && qsmk_rows(M, K) &&
-      mxq::qsmk_shape(M, N, K, bits, group_size, dev)) {
+  // int8 activations take the K-split kernel's integer-MFMA variant from 3
+  // rows (the decode kernel's v_dot4 path is VALU-bound beyond a row or two;
+  // at two rows it is still faster than the kernel's per-row quantization of
+  // x in every workgroup; measured on lm_head: 28.3 against 31.2 us).
+  const bool few_i8 = act == kActI8 && M >= 3;
+  if ((act == kActF16 ? qsmk_rows(M, K) : few_i8) && aligned(x, 16) && aligned(scales, 16) &&
+      aligned(biases, 16) && mxq::qsmk_shape(M, N, K, bits, group_size, dev)) {
     a.x = static_cast<const uint16_t*>(x);
     a.y = static_cast<uint16_t*>(y);
     a.x_vec = 1;
@@ -386,7 +391,7 @@ const char* mxq_describe(const char* op, int64_t M, int64_t N, int64_t K, int bi
                          int group_size, mxq_dtype sb_dtype) {
   thread_local std::string desc;
   const std::string o = op ? op : "";
-  if ((o != "qmv" && o != "qmm") || M <= 0 || N <= 0 || K <= 0 || (bits != 4 && bits != 8) ||
+  if ((o != "qmv" && o != "qmm" && o != "a8") || M <= 0 || N <= 0 || K <= 0 || (bits != 4 && bits != 8) ||
       log2_group(group_size) < 0 || K % group_size != 0 || (sb_dtype != MXQ_F16 && sb_dtype != MXQ_BF16)) {
     desc = "invalid";
     return desc.c_str();
@@ -397,11 +402,12 @@ const char* mxq_describe(const char* op, int64_t M, int64_t N, int64_t K, int bi
     return desc.c_str();
   }
   const char* sb = sb_dtype == MXQ_BF16 ? "bf16" : "f16";
-  if (qsmk_rows(M, K) && mxq::qsmk_shape(M, N, K, bits, group_size, dev)) {
+  const bool a8 = o == "a8";
+  if ((a8 ? M >= 3 : qsmk_rows(M, K)) && mxq::qsmk_shape(M, N, K, bits, group_size, dev)) {
     const int64_t nw = K / 512;
     desc = "qsmk_kernel<bits=4,sb=" + std::string(sb) + ",gs=" + std::to_string(group_size) + ",m=" +
-           std::to_string(M) + ",waves=" + std::to_string(nw) + "> block=" + std::to_string(64 * nw) +
-           " lds=" + std::to_string(mxq::qsmk_lds_bytes(static_cast<int>(nw)));
+           std::to_string(M) + ",waves=" + std::to_string(nw) + (a8 ? ",act=i8" : "") + "> block=" +
+           std::to_string(64 * nw) + " lds=" + std::to_string(mxq::qsmk_lds_bytes(static_cast<int>(nw)));
     return desc.c_str();
   }
   const bool mfma = o == "qmm" && mxq::qmm_mfma_shape(M, K);
@@ -415,7 +421,7 @@ const char* mxq_describe(const char* op, int64_t M, int64_t N, int64_t K, int bi
            "> grid=" + std::to_string(tiles * tl.splits) + " block=512";
     return desc.c_str();
   }
-  if (mxq::qsm_shape(M, N, K, bits, group_size, dev)) {
+  if (!a8 && mxq::qsm_shape(M, N, K, bits, group_size, dev)) {
     desc = "qsm_kernel<bits=" + std::to_string(bits) + ",sb=" + sb + ",m=" + std::to_string(M) + "> grid=" +
            std::to_string((N + 255) / 256) + " block=256 lds=" +
            std::to_string(mxq::qsm_lds_bytes(static_cast<int>(M), static_cast<int>(K)));
@@ -426,10 +432,11 @@ const char* mxq_describe(const char* op, int64_t M, int64_t N, int64_t K, int bi
   desc.clear();
   for (int64_t m0 = 0; m0 < M; m0 += mt_max) {
     const int mt = static_cast<int>((M - m0) < mt_max ? (M - m0) : mt_max);
-    const mxq::QmvPlan p = mxq::qmv_plan(dev, N, K, bits, sb_dtype == MXQ_BF16, kActF16, mt);
+    const mxq::QmvPlan p = mxq::qmv_plan(dev, N, K, bits, sb_dtype == MXQ_BF16, a8 ? kActI8 : kActF16, mt);
     if (!desc.empty()) desc += "; ";
     desc += "qmv_kernel<bits=" + std::to_string(bits) + ",sb=" + sb + ",mt=" + std::to_string(mt) +
-            ",rows=" + std::to_string(p.rows) + (p.xdirect ? ",xreg" : "") + "> grid=" + std::to_string(p.grid) +
+            ",rows=" + std::to_string(p.rows) + (p.xdirect ? ",xreg" : "") + (a8 ? ",act=i8" : "") +
+            "> grid=" + std::to_string(p.grid) +
             " block=256 lds=" + std::to_string(p.lds);
   }
   return desc.c_str();

@@ -213,6 +213,60 @@ __device__ __forceinline__ u4 perm_x_w4_mfma(u4 v) {
   return o;
 }
 
+// ---------------------------------------------------------------------------
+// int8 activations: per-row symmetric quantization, taken in f32 (each integer
+// decision as the reference computation takes it): r = 127 / max|x| (0 for an
+// all-zero row), code = clamp(rint(x * r), -127, 127).
+// ---------------------------------------------------------------------------
+// Largest |x| over 8 f16 activations (4 dwords), in f32.
+__device__ __forceinline__ float absmax8_f16(u4 v) {
+  const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const h2 h = as_h2(d[i]);
+    m = fmaxf(m, fmaxf(fabsf(static_cast<float>(h.x)), fabsf(static_cast<float>(h.y))));
+  }
+  return m;
+}
+
+// int8 code of one activation: clamp(rint(x * r), -127, 127), product and
+// rounding (to nearest, ties to even) in f32.
+__device__ __forceinline__ int quant_i8(float x, float r) {
+  const float p = __builtin_rintf(x * r);
+  return static_cast<int>(fminf(fmaxf(p, -127.0f), 127.0f));
+}
+
+__device__ __forceinline__ uint32_t pack_i8x4(int a, int b, int c, int d) {
+  return (static_cast<uint32_t>(a) & 0xFFu) | ((static_cast<uint32_t>(b) & 0xFFu) << 8) |
+         ((static_cast<uint32_t>(c) & 0xFFu) << 16) | ((static_cast<uint32_t>(d) & 0xFFu) << 24);
+}
+
+// Quantize one 16-byte chunk (8 f16 activations x0..x7) into two dwords of
+// int8 codes in the byte order of the code unpack: 4-bit words split into
+// even codes (x0, x2, x4, x6) and odd codes (x1, x3, x5, x7); 8-bit words hold
+// four codes in natural order (x0..x3 | x4..x7).  Adds the codes to `sum`.
+template <int BITS>
+__device__ __forceinline__ void quant_chunk_i8(u4 v, float r, uint32_t& a, uint32_t& b, int& sum) {
+  const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+  int q[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const h2 h = as_h2(d[i]);
+    q[2 * i] = quant_i8(static_cast<float>(h.x), r);
+    q[2 * i + 1] = quant_i8(static_cast<float>(h.y), r);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sum += q[i];
+  if constexpr (BITS == 4) {
+    a = pack_i8x4(q[0], q[2], q[4], q[6]);
+    b = pack_i8x4(q[1], q[3], q[5], q[7]);
+  } else {
+    a = pack_i8x4(q[0], q[1], q[2], q[3]);
+    b = pack_i8x4(q[4], q[5], q[6], q[7]);
+  }
+}
+
 // Byte i of w as an f32 integer (v_cvt_f32_ubyte<i>).
 template <int I>
 __device__ __forceinline__ float ubyte_f32(uint32_t w) {

@@ -231,7 +231,10 @@ size_t qsmk_lds_bytes(int waves) {
   return static_cast<size_t>(waves) * 16 * kKsRow + static_cast<size_t>(2 * waves) * 64 * 16;
 }
 
-template <bool SB_BF16, int GSH, int NW>
+// XI: int8 activations -- each x row quantized in the kernel (per-row
+// symmetric, f32 decisions), codes as bytes, one v_mfma_i32_16x16x64_i8 per
+// 64-code group (exact integer dot products), the row scale applied at the end.
+template <bool SB_BF16, int GSH, int NW, bool XI>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void qsmk_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ W,
                                                    const uint16_t* __restrict__ S, const uint16_t* __restrict__ B,
                                                    uint16_t* __restrict__ y, const uint16_t* __restrict__ ob, int M,
@@ -253,7 +256,48 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   // the D rows this lane holds
   u4 xa[kKsGroups][2];
   float xs[kKsGroups][4];
-  {
+  float sxd[4] = {1.0f, 1.0f, 1.0f, 1.0f};  // row scales of the D rows (int8 activations)
+  if constexpr (XI) {
+    // the row's largest |x| over all slices (a cross-wave maximum through LDS),
+    // then r = 127 / max and the codes of this lane's 16 activations per group
+    // in the byte order of the code unpack: (x0, x2, x4, x6) (x1, x3, x5, x7) ...
+    const uint16_t* xp = x + static_cast<size_t>(min(c16, M - 1)) * K + ks0 + 16 * kg;
+    const u4 z = {0u, 0u, 0u, 0u};
+    u4 v[kKsGroups][2];
+    float am = 0.0f;
+#pragma unroll
+    for (int g = 0; g < kKsGroups; ++g) {
+      v[g][0] = c16 < M ? *reinterpret_cast<const u4*>(xp + 64 * g) : z;
+      v[g][1] = c16 < M ? *reinterpret_cast<const u4*>(xp + 64 * g + 8) : z;
+      am = fmaxf(am, fmaxf(absmax8_f16(v[g][0]), absmax8_f16(v[g][1])));
+    }
+    am = fmaxf(am, __shfl_xor(am, 16));
+    am = fmaxf(am, __shfl_xor(am, 32));
+    float* ams = red;  // [nw][16], free until the first block
+    if (kg == 0) ams[wave * 16 + c16] = am;
+    __syncthreads();
+    float amax = 0.0f;
+    for (int w = 0; w < nw; ++w) amax = fmaxf(amax, ams[w * 16 + c16]);
+    __syncthreads();
+    const bool zr = !(amax > 0.0f);
+    const float r = zr ? 0.0f : 127.0f / amax;
+    const float sx = zr ? 0.0f : amax / 127.0f;
+#pragma unroll
+    for (int g = 0; g < kKsGroups; ++g) {
+      uint32_t a0, b0, a1, b1;
+      int sum = 0;
+      quant_chunk_i8<4>(v[g][0], r, a0, b0, sum);
+      quant_chunk_i8<4>(v[g][1], r, a1, b1, sum);
+      xa[g][0] = u4{a0, b0, a1, b1};
+      float ps = static_cast<float>(sum);  // integer, exact
+      ps += __shfl_xor(ps, 16);
+      ps += __shfl_xor(ps, 32);  // sum of the codes of x row c16 over the group
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xs[g][i] = __shfl(ps, 4 * kg + i);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sxd[i] = __shfl(sx, 4 * kg + i);
+  } else {
     const uint16_t* xp = x + static_cast<size_t>(min(c16, M - 1)) * K + ks0 + 16 * kg;
     const u4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -325,12 +369,25 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     for (int g = 0; g < kKsGroups; ++g) {
       typedef uint32_t u2 __attribute__((ext_vector_type(2)));
       const u2 wv = *reinterpret_cast<const u2*>(wst + c16 * kKsRow + 32 * g + 8 * kg);
-      const u4 b0 = unpack_w4_mfma(wv.x, magic);  // exact f16 codes
-      const u4 b1 = unpack_w4_mfma(wv.y, magic);
-      p[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, xa[g][0]), __builtin_bit_cast(h8, b0),
-                                                    zero, 0, 0, 0);
-      p[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, xa[g][1]), __builtin_bit_cast(h8, b1),
-                                                    p[g], 0, 0, 0);
+      if constexpr (XI) {
+        // codes as bytes, even then odd nibbles of each word (the order of
+        // the activation codes); exact int32 dot products, at most 64 * 127 *
+        // 15 in magnitude, so exact in f32 as well
+        typedef int v4i __attribute__((ext_vector_type(4)));
+        const v4i b = {static_cast<int>(wv.x & 0x0F0F0F0Fu), static_cast<int>((wv.x >> 4) & 0x0F0F0F0Fu),
+                       static_cast<int>(wv.y & 0x0F0F0F0Fu), static_cast<int>((wv.y >> 4) & 0x0F0F0F0Fu)};
+        const v4i zi = {0, 0, 0, 0};
+        const v4i pi = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, xa[g][0]), b, zi, 0, 0, 0);
+        p[g] = f4{static_cast<float>(pi[0]), static_cast<float>(pi[1]), static_cast<float>(pi[2]),
+                  static_cast<float>(pi[3])};
+      } else {
+        const u4 b0 = unpack_w4_mfma(wv.x, magic);  // exact f16 codes
+        const u4 b1 = unpack_w4_mfma(wv.y, magic);
+        p[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, xa[g][0]), __builtin_bit_cast(h8, b0),
+                                                      zero, 0, 0, 0);
+        p[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, xa[g][1]), __builtin_bit_cast(h8, b1),
+                                                      p[g], 0, 0, 0);
+      }
     }
     f4 acc = zero;
 #pragma unroll
@@ -351,7 +408,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
       for (int w = 1; w < nw; ++w) v += red[((par * nw + w) * 64 + lane) * 4 + i];
       const int m = 4 * kg + i;
-      if (m < M && n < N) y[static_cast<size_t>(m) * N + n] = f32_to_f16_bits(v + o);
+      if (m < M && n < N) y[static_cast<size_t>(m) * N + n] = f32_to_f16_bits((XI ? v * sxd[i] : v) + o);
     }
     par ^= 1;
   };
@@ -382,14 +439,18 @@ bool qsmk_shape(int64_t M, int64_t N, int64_t K, int bits, int group_size, const
 }
 
 namespace {
-template <bool SB_BF16, int GSH>
-const void* qsmk_ptr(int nw) {
+template <bool SB_BF16, int GSH, bool XI>
+const void* qsmk_ptr_x(int nw) {
   switch (nw) {
-    case 1: return reinterpret_cast<const void*>(&qsmk_kernel<SB_BF16, GSH, 1>);
-    case 2: return reinterpret_cast<const void*>(&qsmk_kernel<SB_BF16, GSH, 2>);
-    case 4: return reinterpret_cast<const void*>(&qsmk_kernel<SB_BF16, GSH, 4>);
-    default: return reinterpret_cast<const void*>(&qsmk_kernel<SB_BF16, GSH, 8>);
+    case 1: return reinterpret_cast<const void*>(&qsmk_kernel<SB_BF16, GSH, 1, XI>);
+    case 2: return reinterpret_cast<const void*>(&qsmk_kernel<SB_BF16, GSH, 2, XI>);
+    case 4: return reinterpret_cast<const void*>(&qsmk_kernel<SB_BF16, GSH, 4, XI>);
+    default: return reinterpret_cast<const void*>(&qsmk_kernel<SB_BF16, GSH, 8, XI>);
   }
+}
+template <bool SB_BF16, int GSH>
+const void* qsmk_ptr(int nw, bool xi) {
+  return xi ? qsmk_ptr_x<SB_BF16, GSH, true>(nw) : qsmk_ptr_x<SB_BF16, GSH, false>(nw);
 }
 }  // namespace
 
@@ -397,8 +458,9 @@ hipError_t launch_qsmk(const QmvArgs& a, int M, const DeviceInfo& dev) {
   const int nw = static_cast<int>(a.K / kKsCodes);
   const size_t lds = qsmk_lds_bytes(nw);
   const bool g128 = a.glog2 == 7;
-  const void* kern = a.sb_bf16 ? (g128 ? qsmk_ptr<true, 1>(nw) : qsmk_ptr<true, 0>(nw))
-                               : (g128 ? qsmk_ptr<false, 1>(nw) : qsmk_ptr<false, 0>(nw));
+  const bool xi = a.act == 2;  // int8 activations (quantized in the kernel)
+  const void* kern = a.sb_bf16 ? (g128 ? qsmk_ptr<true, 1>(nw, xi) : qsmk_ptr<true, 0>(nw, xi))
+                               : (g128 ? qsmk_ptr<false, 1>(nw, xi) : qsmk_ptr<false, 0>(nw, xi));
   int occ = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, 64 * nw, lds) != hipSuccess || occ < 1) {
     (void)hipGetLastError();

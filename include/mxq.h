@@ -183,8 +183,12 @@ mxq_status mxq_linear_act(const void* x, const uint32_t* w, const void* scales, 
 
 /*
  * mxq_linear_a8 -- mxq_linear on the native int8 path: f16 activations are
- * quantized per row to int8 inside the decode kernel and contracted with the
- * 4-bit or 8-bit codes by v_dot4_i32_i8 (four exact integer products per
+ * quantized per row to int8 inside the kernel and contracted with the 4-bit
+ * or 8-bit codes in exact integer arithmetic -- by v_dot4_i32_i8 (four
+ * products per instruction) in the decode kernel, or, for 3..16 rows of
+ * 4-bit codes on the shapes the K-split few-row kernel takes (group 64 or 128,
+ * K = 512 * 2^j <= 4096, at least 16 rows of W per compute unit, x, scales and
+ * biases 16-byte aligned), by v_mfma_i32_16x16x64_i8 (one 64-code group per
  * instruction) -- the "quantized dot lowered to the hardware's int8 path"
  * route of mlxcel #574 ("Upstream status refresh", "Next actionable step").
  * The pages define no activation scheme; the one used, dynamic per-row
@@ -195,8 +199,8 @@ mxq_status mxq_linear_act(const void* x, const uint32_t* w, const void* scales, 
  *   y[m, n] = RNE_f16( sx[m] * sum_k xq[m, k] * (q[n, k] * s + b) + out_bias[n] ).
  * So y differs from mxq_linear's by the activation rounding (about 0.4 % of
  * a row's largest |x| per element); it matches the int8 method itself to the
- * tolerance of mxq_qmv.  x must be finite.  Every M runs the decode kernel
- * (in slices of 8 rows).  Arguments, layouts, out_bias and errors as
+ * tolerance of mxq_qmv.  x must be finite.  Other shapes run the decode
+ * kernel in slices of 8 rows.  Arguments, layouts, out_bias and errors as
  * mxq_linear.
  */
 mxq_status mxq_linear_a8(const void* x, const uint32_t* w, const void* scales, const void* biases,
@@ -228,8 +232,8 @@ mxq_status mxq_pack(const uint8_t* codes, uint32_t* w, int64_t N, int64_t K, int
 
 /*
  * mxq_describe -- diagnostic: the kernel instantiation(s) and launch shape
- * that mxq_qmv (op "qmv") or mxq_qmm (op "qmm") would use for these sizes on
- * the current device, e.g. "qmv_kernel<bits=4,sb=f16,mt=1,rows=4> grid=2048
+ * that mxq_qmv (op "qmv"), mxq_qmm (op "qmm") or mxq_linear_a8 (op "a8")
+ * would use for these sizes on the current device, e.g. "qmv_kernel<bits=4,sb=f16,mt=1,rows=4> grid=2048
  * block=256 lds=4352".  Returns a thread-local string, valid until the next
  * call on the thread; "invalid" for unsupported arguments and "no device"
  * without a GPU.  Enqueues nothing.

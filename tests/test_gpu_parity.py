@@ -616,6 +616,77 @@ def test_int8_activations_deterministic():
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
 
 
+# 3..16 rows of int8 activations on shapes the K-split kernel takes (4-bit,
+# K = 512 * 2^j <= 4096, N >= 16 rows per CU): its integer-MFMA variant
+# (rows quantized in the kernel, v_mfma_i32_16x16x64_i8 per 64-code group),
+# against the same oracle; ragged N, both group sizes and scale dtypes.
+A8_FEW = [
+    (3, 8192, 2048, 64, "f16"), (3, 4100, 1024, 128, "bf16"), (5, 8192, 512, 64, "f16"),
+    (8, 16390, 4096, 64, "bf16"), (16, 65537, 4096, 128, "f16"), (11, 128256, 2048, 64, "f16"),
+    (4, 4111, 4096, 64, "f16"),
+]
+
+
+@pytest.mark.parametrize("case", A8_FEW, ids=str)
+def test_int8_few_rows_ksplit(case):
+    M, N, K, gs, sb = case
+    assert mxq.mxq_describe("a8", M, N, K, 4, gs, sb).startswith("qsmk_kernel"), case
+    p = synth.make_problem(M, N, K, 4, gs, sb, seed=M + N + K + 41)
+    x, w, s, b = to_dev(p)
+    note(f"int8 few rows k-split {case}")
+    y = y_host(mxq.mxq_linear_a8(x, w, s, b, bits=4, group_size=gs))
+    if N * K <= 8192 * 2048:
+        assert_close(y, oracle.matmul_ref_a8(p.x, p.w, p.scales, p.biases, K, 4, gs, sb), f"a8 qsmk {case}")
+    else:
+        cols = _sampled_cols(N, M)
+        ref = oracle.matmul_ref_a8(p.x, p.w[cols], p.scales[cols], p.biases[cols], K, 4, gs, sb)
+        assert_close(y[:, cols], ref, f"a8 qsmk {case}")
+
+
+@pytest.mark.parametrize("M", [3, 9])
+def test_int8_few_rows_zero_rows_ties_and_bias(M):
+    """On the integer-MFMA kernel: an all-zero row gives the output bias
+    exactly; a row whose largest |x| is 127/64 has the exact factor 64 and
+    exact rounding ties."""
+    N, K = 8192, 2048
+    assert mxq.mxq_describe("a8", M, N, K, 4, 64, "f16").startswith("qsmk_kernel")
+    p = synth.make_problem(M, N, K, 4, 64, "f16", seed=600 + M)
+    x = p.x.copy()
+    x[0, :] = 0
+    x[1, :] = np.float16(0)
+    x[1, :4] = np.array([127 / 64, 5 / 128, 1 / 128, -3 / 128], dtype=np.float16)
+    ob = synth.make_out_bias(N, seed=601)
+    xt = torch.from_numpy(x).to("cuda:0")
+    _, w, s, b = to_dev(p)
+    obt = torch.from_numpy(ob.view(np.int16)).view(torch.float16).to("cuda:0")
+    note(f"int8 few rows zero rows M={M}")
+    y = y_host(mxq.mxq_linear_a8(xt, w, s, b, obt, bits=4))
+    ref = oracle.matmul_ref_a8(x, p.w, p.scales, p.biases, K, 4, 64, "f16") + ob.view(np.float16).astype(np.float64)
+    assert_close(y, ref, f"a8 qsmk zero rows M={M}")
+    assert np.array_equal(y[0], ob.view(np.float16)), "a zero row must give the output bias exactly"
+
+
+def test_int8_few_rows_integer_case_and_determinism():
+    """x in {-1, 0, 1}, scale 1, bias 0 on the integer-MFMA kernel: every
+    product and sum is an exact integer, only the row scale and the f16 store
+    round; two runs are bit-identical."""
+    M, N, K = 4, 4096, 1024
+    assert mxq.mxq_describe("a8", M, N, K, 4, 64, "f16").startswith("qsmk_kernel")
+    rng = np.random.default_rng(71)
+    w = rng.integers(0, 2 ** 32, size=(N, K // 8), dtype=np.uint32)
+    s = np.full((N, K // 64), 0x3C00, dtype=np.uint16)
+    b = np.zeros((N, K // 64), dtype=np.uint16)
+    xv = rng.integers(-1, 2, size=(M, K)).astype(np.float16)
+    xv[:, 0] = 1
+    p = synth.Problem(x=xv, w=w, scales=s, biases=b, M=M, N=N, K=K, bits=4, group_size=64, sb_dtype="f16")
+    x, wt, st, bt = to_dev(p)
+    note("int8 few rows integer case")
+    y1 = y_host(mxq.mxq_linear_a8(x, wt, st, bt, bits=4))
+    y2 = y_host(mxq.mxq_linear_a8(x, wt, st, bt, bits=4))
+    assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16))
+    assert_close(y1, oracle.matmul_ref_a8(xv, w, s, b, K, 4, 64, "f16"), "a8 qsmk integer")
+
+
 # Few activation rows (9..16) with N large enough to fill the GPU, on shapes
 # the K-split kernel does not take (8-bit codes, K not 512 * 2^j): the
 # 16-row-block matrix-core kernel (qsm).  Sampled output columns against the
@@ -692,6 +763,9 @@ def test_few_rows_ksplit_scale_regimes(shape, sb, regime):
 def test_few_rows_ksplit_routing():
     """Shapes around the K-split kernel's bounds take the other kernels."""
     d = mxq.mxq_describe
+    assert d("a8", 3, 8192, 2048, 4, 64, "f16").startswith("qsmk_kernel<bits=4,sb=f16,gs=64,m=3,waves=4,act=i8>")
+    assert d("a8", 2, 8192, 2048, 4, 64, "f16").startswith("qmv_kernel")       # two int8 rows: decode kernel
+    assert d("a8", 12, 8192, 2048, 8, 64, "f16").startswith("qmv_kernel")      # 8-bit codes: decode kernel
     assert d("qmv", 2, 8192, 2048, 4, 64, "f16").startswith("qsmk")
     assert not d("qmv", 2, 16384, 4096, 4, 64, "f16").startswith("qsmk")   # two rows at K > 2048: decode kernel
     assert d("qmv", 3, 16384, 4096, 4, 64, "f16").startswith("qsmk")
