@@ -37,6 +37,11 @@ def test_describe_without_device_or_with_bad_args():
     lib = mxq.load()
     assert lib.mxq_describe(b"qmv", 1, 4, 48, 4, 64, 0) == b"invalid"
     assert lib.mxq_describe(b"nope", 1, 4, 64, 4, 64, 0) == b"invalid"
+    assert lib.mxq_describe(b"a8", 3, 4, 48, 4, 64, 0) == b"invalid"   # K not a multiple of the group
+    # valid arguments for every op, no GPU in this process: no device
+    for op in (b"qmv", b"qmm", b"a8"):
+        d = lib.mxq_describe(op, 3, 8192, 2048, 4, 64, 0)
+        assert d in (b"no device",) or d.startswith((b"q", b"qsmk")), (op, d)
 
 
 def test_status_strings():
