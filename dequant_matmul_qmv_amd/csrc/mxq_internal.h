@@ -107,7 +107,7 @@ hipError_t launch_qsm(const QmvArgs& a, int M, const DeviceInfo& dev);
 // 4096, at least one 16-row block of W per compute unit); a.x and the scales
 // and biases 16-byte aligned.
 bool qsmk_shape(int64_t M, int64_t N, int64_t K, int bits, int group_size, const DeviceInfo& dev);
-size_t qsmk_lds_bytes(int waves);
+size_t qsmk_lds_bytes(int waves, int bits);
 hipError_t launch_qsmk(const QmvArgs& a, int M, const DeviceInfo& dev);
 
 struct QmmArgs {

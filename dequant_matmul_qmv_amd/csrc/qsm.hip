@@ -223,23 +223,27 @@ __global__ __launch_bounds__(256) void qsm_kernel(const uint16_t* __restrict__ x
 namespace {
 constexpr int kKsCodes = 512;                // codes per wave slice
 constexpr int kKsGroups = kKsCodes / 64;     // 64-code groups per slice
-constexpr int kKsRow = kKsCodes / 2 + 16;    // staged 4-bit row slice: 256 bytes + pad
 constexpr int kKsMaxWaves = 8;
+// staged row slice: 256 (4-bit) or 512 (8-bit) bytes + 16 bytes of pad
+__host__ __device__ constexpr int ks_row_bytes(int bits) { return kKsCodes * bits / 8 + 16; }
 }  // namespace
 
-size_t qsmk_lds_bytes(int waves) {
-  return static_cast<size_t>(waves) * 16 * kKsRow + static_cast<size_t>(2 * waves) * 64 * 16;
+size_t qsmk_lds_bytes(int waves, int bits) {
+  return static_cast<size_t>(waves) * 16 * ks_row_bytes(bits) + static_cast<size_t>(2 * waves) * 64 * 16;
 }
 
 // XI: int8 activations -- each x row quantized in the kernel (per-row
 // symmetric, f32 decisions), codes as bytes, one v_mfma_i32_16x16x64_i8 per
 // 64-code group (exact integer dot products), the row scale applied at the end.
-template <bool SB_BF16, int GSH, int NW, bool XI>
+template <int BITS, bool SB_BF16, int GSH, int NW, bool XI>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void qsmk_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ W,
                                                    const uint16_t* __restrict__ S, const uint16_t* __restrict__ B,
                                                    uint16_t* __restrict__ y, const uint16_t* __restrict__ ob, int M,
                                                    int N, int K) {
   constexpr int nw = NW;
+  constexpr int kKsRow = ks_row_bytes(BITS);
+  constexpr int NLD = BITS;  // 16-byte loads per lane and block: 4 (4-bit) or 8 (8-bit)
+  static_assert(!XI || BITS == 4, "int8 activations with 4-bit codes");
   extern __shared__ __align__(16) unsigned char smem[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -248,7 +252,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   unsigned char* wst = smem + wave * 16 * kKsRow;                      // [16][kKsRow] this wave's codes
   float* red = reinterpret_cast<float*>(smem + nw * 16 * kKsRow);     // [2][nw][64][4] partial tiles
   const int ks0 = wave * kKsCodes;
-  const int kw = K / 8;
+  const int kw = K * BITS / 32;
   const int G = K >> (6 + GSH);
   constexpr int SBN = kKsGroups >> GSH;  // real groups per slice: 8 (g64) or 4 (g128)
 
@@ -304,9 +308,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     for (int g = 0; g < kKsGroups; ++g) {
       const u4 v0 = *reinterpret_cast<const u4*>(xp + 64 * g);
       const u4 v1 = *reinterpret_cast<const u4*>(xp + 64 * g + 8);
-      // k slots in the pair order of the code unpack: (x0, x5) (x1, x4) ...
-      xa[g][0] = perm_x_w4_mfma(c16 < M ? v0 : z);
-      xa[g][1] = perm_x_w4_mfma(c16 < M ? v1 : z);
+      // k slots in the order of the code unpack: 4-bit pairs (x0, x5)
+      // (x1, x4) ..., 8-bit natural order
+      xa[g][0] = BITS == 4 ? perm_x_w4_mfma(c16 < M ? v0 : z) : (c16 < M ? v0 : z);
+      xa[g][1] = BITS == 4 ? perm_x_w4_mfma(c16 < M ? v1 : z) : (c16 < M ? v1 : z);
     }
 #pragma unroll
     for (int g = 0; g < kKsGroups; ++g) {
@@ -324,19 +329,21 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   // Loads of one block (indices clamped: branch-free; a block past the end
   // re-reads the last one and is never stored).
   struct Ld {
-    u4 w[4];
+    u4 w[NLD];
     u4 s, b;     // SBN scales / biases of column c16 (g128: the low 8 bytes)
     uint16_t o;  // output bias of column c16 (unused without one)
   };
   const int nrb = (N + 15) >> 4;
-  const uint32_t* wl = W + ks0 / 8 + 4 * c16;
+  const uint32_t* wl = W + ks0 * BITS / 32 + 4 * c16;
   const uint16_t* obs = ob != nullptr ? ob : S;  // without an output bias: any N readable halves
   auto load = [&](Ld& d, int rb) __attribute__((always_inline)) {
     rb = min(rb, nrb - 1);
+    // instruction i: rows 4 (i % 4) + kg, the (i / 4)-th 256 bytes of the slice
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = min(16 * rb + 4 * i + kg, N - 1);
-      d.w[i] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(wl + static_cast<size_t>(row) * kw));
+    for (int i = 0; i < NLD; ++i) {
+      const int row = min(16 * rb + 4 * (i % 4) + kg, N - 1);
+      d.w[i] = __builtin_nontemporal_load(
+          reinterpret_cast<const u4*>(wl + static_cast<size_t>(row) * kw + 64 * (i / 4)));
     }
     const size_t so = static_cast<size_t>(min(16 * rb + c16, N - 1)) * G + wave * SBN;
     if constexpr (GSH == 0) {
@@ -354,9 +361,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 
   int par = 0;
   auto step = [&](const Ld& d, int rb) __attribute__((always_inline)) {
-    // codes to this wave's LDS region (row 4i + kg, bytes 16 c16 .. of the slice)
+    // codes to this wave's LDS region (row 4 (i % 4) + kg, bytes 256 (i / 4) +
+    // 16 c16 .. of the slice)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<u4*>(wst + (4 * i + kg) * kKsRow + 16 * c16) = d.w[i];
+    for (int i = 0; i < NLD; ++i)
+      *reinterpret_cast<u4*>(wst + (4 * (i % 4) + kg) * kKsRow + 256 * (i / 4) + 16 * c16) = d.w[i];
     __builtin_amdgcn_wave_barrier();
     const uint32_t sw[4] = {d.s.x, d.s.y, d.s.z, d.s.w};
     const uint32_t bw[4] = {d.b.x, d.b.y, d.b.z, d.b.w};
@@ -368,6 +377,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
     for (int g = 0; g < kKsGroups; ++g) {
       typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+      if constexpr (BITS == 8) {
+        // codes [16 kg, 16 kg + 16) of the group: 16 bytes, natural order,
+        // each byte under the f16 exponent of 1024 then 1024 subtracted (exact)
+        const u4 wv = *reinterpret_cast<const u4*>(wst + c16 * kKsRow + 64 * g + 16 * kg);
+        const u4 b0 = unpack8_natural(wv.x, wv.y, magic);
+        const u4 b1 = unpack8_natural(wv.z, wv.w, magic);
+        p[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, xa[g][0]), __builtin_bit_cast(h8, b0),
+                                                      zero, 0, 0, 0);
+        p[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, xa[g][1]), __builtin_bit_cast(h8, b1),
+                                                      p[g], 0, 0, 0);
+        continue;
+      }
       const u2 wv = *reinterpret_cast<const u2*>(wst + c16 * kKsRow + 32 * g + 8 * kg);
       if constexpr (XI) {
         // codes as bytes, even then odd nibbles of each word (the order of
@@ -431,7 +452,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 }
 
 bool qsmk_shape(int64_t M, int64_t N, int64_t K, int bits, int group_size, const DeviceInfo& dev) {
-  if (bits != 4 || M < 2 || M > 16 || (group_size != 64 && group_size != 128)) return false;
+  if ((bits != 4 && bits != 8) || M < 2 || M > 16 || (group_size != 64 && group_size != 128)) return false;
   const int64_t nw = K / kKsCodes;  // waves per workgroup: 1, 2, 4 or 8
   if (K % kKsCodes != 0 || nw < 1 || nw > kKsMaxWaves || (nw & (nw - 1)) != 0) return false;
   // at least one block of 16 rows per compute unit (smaller N stays on qmv)
@@ -439,28 +460,33 @@ bool qsmk_shape(int64_t M, int64_t N, int64_t K, int bits, int group_size, const
 }
 
 namespace {
-template <bool SB_BF16, int GSH, bool XI>
+template <int BITS, bool SB_BF16, int GSH, bool XI>
 const void* qsmk_ptr_x(int nw) {
   switch (nw) {
-    case 1: return reinterpret_cast<const void*>(&qsmk_kernel<SB_BF16, GSH, 1, XI>);
-    case 2: return reinterpret_cast<const void*>(&qsmk_kernel<SB_BF16, GSH, 2, XI>);
-    case 4: return reinterpret_cast<const void*>(&qsmk_kernel<SB_BF16, GSH, 4, XI>);
-    default: return reinterpret_cast<const void*>(&qsmk_kernel<SB_BF16, GSH, 8, XI>);
+    case 1: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 1, XI>);
+    case 2: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 2, XI>);
+    case 4: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 4, XI>);
+    default: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 8, XI>);
   }
 }
 template <bool SB_BF16, int GSH>
-const void* qsmk_ptr(int nw, bool xi) {
-  return xi ? qsmk_ptr_x<SB_BF16, GSH, true>(nw) : qsmk_ptr_x<SB_BF16, GSH, false>(nw);
+const void* qsmk_ptr(int nw, int bits, bool xi) {
+  if (bits == 8) return qsmk_ptr_x<8, SB_BF16, GSH, false>(nw);  // int8 activations take 4-bit codes only
+  return xi ? qsmk_ptr_x<4, SB_BF16, GSH, true>(nw) : qsmk_ptr_x<4, SB_BF16, GSH, false>(nw);
 }
 }  // namespace
 
 hipError_t launch_qsmk(const QmvArgs& a, int M, const DeviceInfo& dev) {
   const int nw = static_cast<int>(a.K / kKsCodes);
-  const size_t lds = qsmk_lds_bytes(nw);
+  const size_t lds = qsmk_lds_bytes(nw, a.bits);
   const bool g128 = a.glog2 == 7;
   const bool xi = a.act == 2;  // int8 activations (quantized in the kernel)
-  const void* kern = a.sb_bf16 ? (g128 ? qsmk_ptr<true, 1>(nw, xi) : qsmk_ptr<true, 0>(nw, xi))
-                               : (g128 ? qsmk_ptr<false, 1>(nw, xi) : qsmk_ptr<false, 0>(nw, xi));
+  const void* kern = a.sb_bf16 ? (g128 ? qsmk_ptr<true, 1>(nw, a.bits, xi) : qsmk_ptr<true, 0>(nw, a.bits, xi))
+                               : (g128 ? qsmk_ptr<false, 1>(nw, a.bits, xi) : qsmk_ptr<false, 0>(nw, a.bits, xi));
+  if (lds > 65536) {  // 8 waves of 8-bit slices
+    const hipError_t e = ensure_dynamic_lds(kern, lds);
+    if (e != hipSuccess) return e;
+  }
   int occ = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, 64 * nw, lds) != hipSuccess || occ < 1) {
     (void)hipGetLastError();

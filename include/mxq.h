@@ -86,8 +86,8 @@ int mxq_abi_version(void);
  * rounding).  The sum of epic #570's "dequant -> matmul" without the weight
  * ever leaving registers.  Accepts any M >= 0.  Routing by shape: one row
  * (and two at K > 2048) on the decode kernel; up to 16 rows on the matrix
- * cores when the shape fits them -- 4-bit codes, group size 64 or 128, K of
- * 512, 1024, 2048 or 4096 and at least 16 rows of W per compute unit (from 3
+ * cores when the shape fits them -- 4- or 8-bit codes, group size 64 or 128,
+ * K of 512, 1024, 2048 or 4096 and at least 16 rows of W per compute unit (from 3
  * rows, or 2 at K <= 2048), else 9..16 rows of any supported codes with at
  * least 256 rows of W per compute unit -- both with x (and for the first, the
  * scales and biases) 16-byte aligned; otherwise the decode kernel in slices

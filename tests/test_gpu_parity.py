@@ -692,8 +692,8 @@ def test_int8_few_rows_integer_case_and_determinism():
 # 16-row-block matrix-core kernel (qsm).  Sampled output columns against the
 # oracle, including the ragged tail.
 QSM = [
-    (9, 65600, 3072, 4, 64, "f16"), (10, 66000, 1024, 8, 64, "bf16"), (16, 65536, 1536, 4, 128, "f16"),
-    (13, 70001, 512, 8, 64, "bf16"), (12, 65540, 4096, 8, 128, "f16"), (16, 128256, 2048, 8, 64, "f16"),
+    (9, 65600, 3072, 4, 64, "f16"), (10, 66000, 1536, 8, 64, "bf16"), (16, 65536, 1536, 4, 128, "f16"),
+    (13, 70001, 3072, 8, 64, "bf16"), (12, 65540, 6144, 8, 128, "f16"), (16, 128256, 1536, 8, 64, "f16"),
 ]
 
 
@@ -724,6 +724,31 @@ QSMK = [
     (8, 8192, 2048, 64, "bf16"), (16, 16390, 4096, 64, "f16"), (11, 65537, 4096, 128, "bf16"),
     (16, 128256, 2048, 64, "f16"), (4, 4111, 4096, 64, "f16"),
 ]
+
+
+# 8-bit codes on the K-split kernel (natural-order byte unpack, 512-byte row
+# slices per wave), including shapes the 16-row-block kernel used to take.
+QSMK8 = [
+    (2, 8192, 2048, 64, "f16"), (4, 4100, 512, 64, "bf16"), (10, 66000, 1024, 64, "bf16"),
+    (13, 70001, 512, 64, "bf16"), (12, 65540, 4096, 128, "f16"), (16, 128256, 2048, 64, "f16"),
+    (7, 8192, 4096, 64, "f16"),
+]
+
+
+@pytest.mark.parametrize("case", QSMK8, ids=str)
+def test_few_rows_ksplit_8bit(case):
+    M, N, K, gs, sb = case
+    assert mxq.mxq_describe("qmv", M, N, K, 8, gs, sb).startswith("qsmk_kernel<bits=8"), case
+    p = synth.make_problem(M, N, K, 8, gs, sb, seed=M + N + K + 43)
+    x, w, s, b = to_dev(p)
+    note(f"few-row k-split 8-bit {case}")
+    y = y_host(mxq.mxq_qmv(x, w, s, b, bits=8, group_size=gs))
+    if N * K <= 8192 * 2048:
+        assert_close(y, _ref(p), f"qsmk 8-bit {case}")
+    else:
+        cols = _sampled_cols(N, M)
+        ref = oracle.matmul_ref_rows(p.x, p.w, p.scales, p.biases, cols, K, 8, gs, sb)
+        assert_close(y[:, cols], ref, f"qsmk 8-bit {case}")
 
 
 @pytest.mark.parametrize("entry", ["qmv", "qmm"])
@@ -771,7 +796,8 @@ def test_few_rows_ksplit_routing():
     assert d("qmv", 3, 16384, 4096, 4, 64, "f16").startswith("qsmk")
     assert not d("qmv", 1, 128256, 2048, 4, 64, "f16").startswith("qsmk")
     assert not d("qmv", 17, 128256, 2048, 4, 64, "f16").startswith("qsmk")
-    assert not d("qmv", 8, 128256, 2048, 8, 64, "f16").startswith("qsmk")   # 8-bit codes
+    assert d("qmv", 8, 128256, 2048, 8, 64, "f16").startswith("qsmk_kernel<bits=8")   # 8-bit codes
+    assert d("a8", 8, 128256, 2048, 8, 64, "f16").startswith("qmv_kernel")         # int8 x with 8-bit codes
     assert not d("qmv", 8, 128256, 2048, 4, 32, "f16").startswith("qsmk")   # group size 32
     assert not d("qmv", 8, 128256, 1536, 4, 64, "f16").startswith("qsmk")   # K not 512 * 2^j
     assert not d("qmv", 8, 128256, 8192, 4, 64, "f16").startswith("qsmk")   # K > 4096
