@@ -17,7 +17,8 @@
 // algorithmic bytes fetched.  The decode kernel is faster up to 8 rows (one
 // launch per 8 rows, 23 us at M = 3, 52 us at M = 8) and slower beyond (two
 // launches: 96 us at M = 16), so this kernel takes 9..16 rows where the
-// K-split kernel below (qsmk: 4-bit codes, K = 512 * 2^j up to 4096) does not.
+// K-split kernel below (qsmk: 4- and 8-bit codes, K = 512 * 2^j up to 4096)
+// does not.
 //
 // Mapping: a workgroup of 4 waves owns 256 rows of W; a wave owns 64 of them
 // as four 16-column MFMA blocks.  Lane l works on W row (l % 16) of each block
