@@ -97,7 +97,7 @@ mxq_status run_qmv(const char* who, const void* x, const uint32_t* w, const void
   // rows (the decode kernel's v_dot4 path is VALU-bound beyond a row or two;
   // at two rows it is still faster than the kernel's per-row quantization of
   // x in every workgroup; measured on lm_head: 28.3 against 31.2 us).
-  const bool few_i8 = act == kActI8 && M >= 3 && bits == 4;
+  const bool few_i8 = act == kActI8 && M >= 3;
   if ((act == kActF16 ? qsmk_rows(M, K) : few_i8) && aligned(x, 16) && aligned(scales, 16) &&
       aligned(biases, 16) && mxq::qsmk_shape(M, N, K, bits, group_size, dev)) {
     a.x = static_cast<const uint16_t*>(x);
@@ -403,7 +403,7 @@ const char* mxq_describe(const char* op, int64_t M, int64_t N, int64_t K, int bi
   }
   const char* sb = sb_dtype == MXQ_BF16 ? "bf16" : "f16";
   const bool a8 = o == "a8";
-  if ((a8 ? M >= 3 && bits == 4 : qsmk_rows(M, K)) && mxq::qsmk_shape(M, N, K, bits, group_size, dev)) {
+  if ((a8 ? M >= 3 : qsmk_rows(M, K)) && mxq::qsmk_shape(M, N, K, bits, group_size, dev)) {
     const int64_t nw = K / 512;
     desc = "qsmk_kernel<bits=" + std::to_string(bits) + ",sb=" + std::string(sb) + ",gs=" +
            std::to_string(group_size) + ",m=" + std::to_string(M) + ",waves=" + std::to_string(nw) +

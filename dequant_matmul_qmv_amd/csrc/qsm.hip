@@ -244,7 +244,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   constexpr int nw = NW;
   constexpr int kKsRow = ks_row_bytes(BITS);
   constexpr int NLD = BITS;  // 16-byte loads per lane and block: 4 (4-bit) or 8 (8-bit)
-  static_assert(!XI || BITS == 4, "int8 activations with 4-bit codes");
   extern __shared__ __align__(16) unsigned char smem[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -291,8 +290,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     for (int g = 0; g < kKsGroups; ++g) {
       uint32_t a0, b0, a1, b1;
       int sum = 0;
-      quant_chunk_i8<4>(v[g][0], r, a0, b0, sum);
-      quant_chunk_i8<4>(v[g][1], r, a1, b1, sum);
+      quant_chunk_i8<BITS>(v[g][0], r, a0, b0, sum);
+      quant_chunk_i8<BITS>(v[g][1], r, a1, b1, sum);
       xa[g][0] = u4{a0, b0, a1, b1};
       float ps = static_cast<float>(sum);  // integer, exact
       ps += __shfl_xor(ps, 16);
@@ -378,7 +377,20 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
     for (int g = 0; g < kKsGroups; ++g) {
       typedef uint32_t u2 __attribute__((ext_vector_type(2)));
-      if constexpr (BITS == 8) {
+      if constexpr (BITS == 8 && XI) {
+        // codes [16 kg, 16 kg + 16) of the group as signed bytes c - 128 (one
+        // XOR per word; the offset returns through the bias factor b + 128 s),
+        // natural order, as the activation codes
+        typedef int v4i __attribute__((ext_vector_type(4)));
+        const u4 wv = *reinterpret_cast<const u4*>(wst + c16 * kKsRow + 64 * g + 16 * kg);
+        const v4i b = {static_cast<int>(wv.x ^ 0x80808080u), static_cast<int>(wv.y ^ 0x80808080u),
+                       static_cast<int>(wv.z ^ 0x80808080u), static_cast<int>(wv.w ^ 0x80808080u)};
+        const v4i zi = {0, 0, 0, 0};
+        const v4i pi = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, xa[g][0]), b, zi, 0, 0, 0);
+        p[g] = f4{static_cast<float>(pi[0]), static_cast<float>(pi[1]), static_cast<float>(pi[2]),
+                  static_cast<float>(pi[3])};
+        continue;
+      } else if constexpr (BITS == 8) {
         // codes [16 kg, 16 kg + 16) of the group: 16 bytes, natural order,
         // each byte under the f16 exponent of 1024 then 1024 subtracted (exact)
         const u4 wv = *reinterpret_cast<const u4*>(wst + c16 * kKsRow + 64 * g + 16 * kg);
@@ -416,7 +428,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     for (int g = 0; g < kKsGroups; ++g) {
       const int r = g >> GSH;
       const float sc = sb_to_f32<SB_BF16>(static_cast<uint16_t>(sw[r >> 1] >> (16 * (r & 1))));
-      const float bi = sb_to_f32<SB_BF16>(static_cast<uint16_t>(bw[r >> 1] >> (16 * (r & 1))));
+      float bi = sb_to_f32<SB_BF16>(static_cast<uint16_t>(bw[r >> 1] >> (16 * (r & 1))));
+      if constexpr (XI && BITS == 8) bi = __builtin_fmaf(128.0f, sc, bi);  // signed codes c - 128
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(bi, xs[g][i], __builtin_fmaf(sc, p[g][i], acc[i]));
     }
@@ -472,7 +485,7 @@ const void* qsmk_ptr_x(int nw) {
 }
 template <bool SB_BF16, int GSH>
 const void* qsmk_ptr(int nw, int bits, bool xi) {
-  if (bits == 8) return qsmk_ptr_x<8, SB_BF16, GSH, false>(nw);  // int8 activations take 4-bit codes only
+  if (bits == 8) return xi ? qsmk_ptr_x<8, SB_BF16, GSH, true>(nw) : qsmk_ptr_x<8, SB_BF16, GSH, false>(nw);
   return xi ? qsmk_ptr_x<4, SB_BF16, GSH, true>(nw) : qsmk_ptr_x<4, SB_BF16, GSH, false>(nw);
 }
 }  // namespace

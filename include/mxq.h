@@ -186,7 +186,7 @@ mxq_status mxq_linear_act(const void* x, const uint32_t* w, const void* scales, 
  * quantized per row to int8 inside the kernel and contracted with the 4-bit
  * or 8-bit codes in exact integer arithmetic -- by v_dot4_i32_i8 (four
  * products per instruction) in the decode kernel, or, for 3..16 rows of
- * 4-bit codes on the shapes the K-split few-row kernel takes (group 64 or 128,
+ * 4- or 8-bit codes on the shapes the K-split few-row kernel takes (group 64 or 128,
  * K = 512 * 2^j <= 4096, at least 16 rows of W per compute unit, x, scales and
  * biases 16-byte aligned), by v_mfma_i32_16x16x64_i8 (one 64-code group per
  * instruction) -- the "quantized dot lowered to the hardware's int8 path"

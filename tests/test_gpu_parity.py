@@ -643,6 +643,27 @@ def test_int8_few_rows_ksplit(case):
         assert_close(y[:, cols], ref, f"a8 qsmk {case}")
 
 
+# int8 activations with 8-bit codes on the integer-MFMA kernel: codes as
+# signed bytes c - 128, the offset folded into the bias factor b + 128 s.
+A8_FEW8 = [(3, 8192, 2048, 64, "f16"), (9, 4100, 1024, 128, "bf16"), (16, 65537, 4096, 64, "f16")]
+
+
+@pytest.mark.parametrize("case", A8_FEW8, ids=str)
+def test_int8_few_rows_ksplit_8bit(case):
+    M, N, K, gs, sb = case
+    assert mxq.mxq_describe("a8", M, N, K, 8, gs, sb).startswith("qsmk_kernel<bits=8"), case
+    p = synth.make_problem(M, N, K, 8, gs, sb, seed=M + N + K + 47)
+    x, w, s, b = to_dev(p)
+    note(f"int8 few rows k-split 8-bit {case}")
+    y = y_host(mxq.mxq_linear_a8(x, w, s, b, bits=8, group_size=gs))
+    if N * K <= 8192 * 2048:
+        assert_close(y, oracle.matmul_ref_a8(p.x, p.w, p.scales, p.biases, K, 8, gs, sb), f"a8 qsmk 8-bit {case}")
+    else:
+        cols = _sampled_cols(N, M)
+        ref = oracle.matmul_ref_a8(p.x, p.w[cols], p.scales[cols], p.biases[cols], K, 8, gs, sb)
+        assert_close(y[:, cols], ref, f"a8 qsmk 8-bit {case}")
+
+
 @pytest.mark.parametrize("M", [3, 9])
 def test_int8_few_rows_zero_rows_ties_and_bias(M):
     """On the integer-MFMA kernel: an all-zero row gives the output bias
@@ -790,14 +811,15 @@ def test_few_rows_ksplit_routing():
     d = mxq.mxq_describe
     assert d("a8", 3, 8192, 2048, 4, 64, "f16").startswith("qsmk_kernel<bits=4,sb=f16,gs=64,m=3,waves=4,act=i8>")
     assert d("a8", 2, 8192, 2048, 4, 64, "f16").startswith("qmv_kernel")       # two int8 rows: decode kernel
-    assert d("a8", 12, 8192, 2048, 8, 64, "f16").startswith("qmv_kernel")      # 8-bit codes: decode kernel
+    assert d("a8", 12, 8192, 2048, 8, 64, "f16").startswith("qsmk_kernel<bits=8,sb=f16,gs=64,m=12,waves=4,act=i8>")
     assert d("qmv", 2, 8192, 2048, 4, 64, "f16").startswith("qsmk")
     assert not d("qmv", 2, 16384, 4096, 4, 64, "f16").startswith("qsmk")   # two rows at K > 2048: decode kernel
     assert d("qmv", 3, 16384, 4096, 4, 64, "f16").startswith("qsmk")
     assert not d("qmv", 1, 128256, 2048, 4, 64, "f16").startswith("qsmk")
     assert not d("qmv", 17, 128256, 2048, 4, 64, "f16").startswith("qsmk")
     assert d("qmv", 8, 128256, 2048, 8, 64, "f16").startswith("qsmk_kernel<bits=8")   # 8-bit codes
-    assert d("a8", 8, 128256, 2048, 8, 64, "f16").startswith("qmv_kernel")         # int8 x with 8-bit codes
+    assert d("a8", 8, 128256, 2048, 8, 64, "f16").startswith("qsmk_kernel<bits=8")  # int8 x with 8-bit codes
+    assert d("a8", 8, 128256, 1536, 8, 64, "f16").startswith("qmv_kernel")         # K not 512 * 2^j
     assert not d("qmv", 8, 128256, 2048, 4, 32, "f16").startswith("qsmk")   # group size 32
     assert not d("qmv", 8, 128256, 1536, 4, 64, "f16").startswith("qsmk")   # K not 512 * 2^j
     assert not d("qmv", 8, 128256, 8192, 4, 64, "f16").startswith("qsmk")   # K > 4096
