@@ -209,16 +209,18 @@ __global__ __launch_bounds__(256) void qsm_kernel(const uint16_t* __restrict__ x
 // (16 rows x 512 codes, rows at or past M zero) and their per-group sums stay
 // in registers for the whole kernel.  The workgroup walks blocks of 16 W rows
 // with a grid stride; for each block a wave
-//  * loads its slice of the 16 rows with whole-line reads: instruction i takes
-//    rows 4i .. 4i + 3, 16 lanes x 16 bytes per row (256 contiguous bytes),
+//  * loads its slice of the 16 rows with whole-line reads: each instruction
+//    takes 4 rows, 16 lanes x 16 bytes per row (256 contiguous bytes); a
+//    slice row is 256 bytes of 4-bit or 512 bytes of 8-bit codes,
 //  * passes them through its own LDS region to the MFMA B layout (lane l:
 //    W row l % 16, codes [16 (l / 16), +16) of each 64-code group, so the two
 //    k-steps of a group never mix groups),
-//  * unpacks codes two at a time to exact f16 values (one v_and_or_b32 and
-//    one packed f16 fma per pair, one shift per word; the activation
-//    fragments are permuted once into the matching k order), runs the two
-//    v_mfma_f32_16x16x32_f16 of every group back to back and then applies
-//    each group's scale and bias in f32 (s P + b X_g),
+//  * unpacks the codes to exact f16 values -- 4-bit: one v_and_or_b32 and one
+//    packed f16 fma per pair, one shift per word, the activation fragments
+//    permuted once into the matching k order; 8-bit: a byte select under the
+//    exponent of 1024 and an exact subtraction per pair, natural order --
+//    runs the two v_mfma_f32_16x16x32_f16 of every group back to back and then
+//    applies each group's scale and bias in f32 (s P + b X_g),
 // and the waves' partial 16 x 16 tiles are added in LDS in wave order (one
 // barrier per block; the buffer alternates between blocks).
 namespace {
@@ -234,8 +236,10 @@ size_t qsmk_lds_bytes(int waves, int bits) {
 }
 
 // XI: int8 activations -- each x row quantized in the kernel (per-row
-// symmetric, f32 decisions), codes as bytes, one v_mfma_i32_16x16x64_i8 per
-// 64-code group (exact integer dot products), the row scale applied at the end.
+// symmetric, f32 decisions), codes as bytes (4-bit: even then odd nibbles of
+// each word; 8-bit: signed c - 128, the offset folded into the bias factor
+// b + 128 s), one v_mfma_i32_16x16x64_i8 per 64-code group (exact integer dot
+// products), the row scale applied at the end.
 template <int BITS, bool SB_BF16, int GSH, int NW, bool XI>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void qsmk_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ W,
                                                    const uint16_t* __restrict__ S, const uint16_t* __restrict__ B,
@@ -264,7 +268,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   if constexpr (XI) {
     // the row's largest |x| over all slices (a cross-wave maximum through LDS),
     // then r = 127 / max and the codes of this lane's 16 activations per group
-    // in the byte order of the code unpack: (x0, x2, x4, x6) (x1, x3, x5, x7) ...
+    // in the byte order of the codes: (x0, x2, x4, x6) (x1, x3, x5, x7) ... for
+    // 4-bit codes, natural for 8-bit
     const uint16_t* xp = x + static_cast<size_t>(min(c16, M - 1)) * K + ks0 + 16 * kg;
     const u4 z = {0u, 0u, 0u, 0u};
     u4 v[kKsGroups][2];
