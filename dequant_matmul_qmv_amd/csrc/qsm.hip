@@ -17,8 +17,8 @@
 // algorithmic bytes fetched.  The decode kernel is faster up to 8 rows (one
 // launch per 8 rows, 23 us at M = 3, 52 us at M = 8) and slower beyond (two
 // launches: 96 us at M = 16), so this kernel takes 9..16 rows where the
-// K-split kernel below (qsmk: 4- and 8-bit codes, K = 512 * 2^j up to 4096)
-// does not.
+// K-split kernel below (qsmk: 4- and 8-bit codes, K a multiple of 512 up to
+// 4096) does not.
 //
 // Mapping: a workgroup of 4 waves owns 256 rows of W; a wave owns 64 of them
 // as four 16-column MFMA blocks.  Lane l works on W row (l % 16) of each block
@@ -205,7 +205,7 @@ __global__ __launch_bounds__(256) void qsm_kernel(const uint16_t* __restrict__ x
 // qsmk: the same contraction with K split over the waves of a workgroup.
 //
 // Wave w of a workgroup owns codes [512 w, 512 w + 512) of every row (K =
-// 512 * waves, at most 8 waves).  Its activation fragments for that slice
+// 512 * waves, 1 to 8 waves).  Its activation fragments for that slice
 // (16 rows x 512 codes, rows at or past M zero) and their per-group sums stay
 // in registers for the whole kernel.  The workgroup walks blocks of 16 W rows
 // with a grid stride; for each block a wave
@@ -472,8 +472,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 
 bool qsmk_shape(int64_t M, int64_t N, int64_t K, int bits, int group_size, const DeviceInfo& dev) {
   if ((bits != 4 && bits != 8) || M < 2 || M > 16 || (group_size != 64 && group_size != 128)) return false;
-  const int64_t nw = K / kKsCodes;  // waves per workgroup: 1, 2, 4 or 8
-  if (K % kKsCodes != 0 || nw < 1 || nw > kKsMaxWaves || (nw & (nw - 1)) != 0) return false;
+  const int64_t nw = K / kKsCodes;  // waves per workgroup: 1 .. 8
+  if (K % kKsCodes != 0 || nw < 1 || nw > kKsMaxWaves) return false;
   // at least one block of 16 rows per compute unit (smaller N stays on qmv)
   return (N + 15) / 16 >= static_cast<int64_t>(dev.num_cu);
 }
@@ -484,7 +484,11 @@ const void* qsmk_ptr_x(int nw) {
   switch (nw) {
     case 1: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 1, XI>);
     case 2: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 2, XI>);
+    case 3: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 3, XI>);
     case 4: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 4, XI>);
+    case 5: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 5, XI>);
+    case 6: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 6, XI>);
+    case 7: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 7, XI>);
     default: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 8, XI>);
   }
 }

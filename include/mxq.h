@@ -87,7 +87,7 @@ int mxq_abi_version(void);
  * ever leaving registers.  Accepts any M >= 0.  Routing by shape: one row
  * (and two at K > 2048) on the decode kernel; up to 16 rows on the matrix
  * cores when the shape fits them -- 4- or 8-bit codes, group size 64 or 128,
- * K of 512, 1024, 2048 or 4096 and at least 16 rows of W per compute unit (from 3
+ * K a multiple of 512 up to 4096 and at least 16 rows of W per compute unit (from 3
  * rows, or 2 at K <= 2048), else 9..16 rows of any supported codes with at
  * least 256 rows of W per compute unit -- both with x (and for the first, the
  * scales and biases) 16-byte aligned; otherwise the decode kernel in slices
@@ -187,7 +187,7 @@ mxq_status mxq_linear_act(const void* x, const uint32_t* w, const void* scales, 
  * or 8-bit codes in exact integer arithmetic -- by v_dot4_i32_i8 (four
  * products per instruction) in the decode kernel, or, for 3..16 rows of
  * 4- or 8-bit codes on the shapes the K-split few-row kernel takes (group 64 or 128,
- * K = 512 * 2^j <= 4096, at least 16 rows of W per compute unit, x, scales and
+ * K a multiple of 512 up to 4096, at least 16 rows of W per compute unit, x, scales and
  * biases 16-byte aligned), by v_mfma_i32_16x16x64_i8 (one 64-code group per
  * instruction) -- the "quantized dot lowered to the hardware's int8 path"
  * route of mlxcel #574 ("Upstream status refresh", "Next actionable step").

@@ -617,7 +617,7 @@ def test_int8_activations_deterministic():
 
 
 # 3..16 rows of int8 activations on shapes the K-split kernel takes (4-bit,
-# K = 512 * 2^j <= 4096, N >= 16 rows per CU): its integer-MFMA variant
+# K a multiple of 512 up to 4096, N >= 16 rows per CU): its integer-MFMA variant
 # (rows quantized in the kernel, v_mfma_i32_16x16x64_i8 per 64-code group),
 # against the same oracle; ragged N, both group sizes and scale dtypes.
 A8_FEW = [
@@ -709,12 +709,12 @@ def test_int8_few_rows_integer_case_and_determinism():
 
 
 # Few activation rows (9..16) with N large enough to fill the GPU, on shapes
-# the K-split kernel does not take (8-bit codes, K not 512 * 2^j): the
+# the K-split kernel does not take (K not a multiple of 512, or above 4096): the
 # 16-row-block matrix-core kernel (qsm).  Sampled output columns against the
 # oracle, including the ragged tail.
 QSM = [
-    (9, 65600, 3072, 4, 64, "f16"), (10, 66000, 1536, 8, 64, "bf16"), (16, 65536, 1536, 4, 128, "f16"),
-    (13, 70001, 3072, 8, 64, "bf16"), (12, 65540, 6144, 8, 128, "f16"), (16, 128256, 1536, 8, 64, "f16"),
+    (9, 65600, 2112, 4, 64, "f16"), (10, 66000, 576, 8, 64, "bf16"), (16, 65536, 4352, 4, 128, "f16"),
+    (13, 70001, 2624, 8, 64, "bf16"), (12, 65540, 6144, 8, 128, "f16"), (16, 128256, 1088, 8, 64, "f16"),
 ]
 
 
@@ -737,20 +737,21 @@ def test_few_rows_mfma(case):
     assert_close(y[:, cols], ref, f"qsm {case}")
 
 
-# 2..16 rows, 4-bit codes, K = 512 * 2^j <= 4096, at least 16 W rows per
+# 2..16 rows, 4-bit codes, K a multiple of 512 up to 4096, at least 16 W rows per
 # compute unit: the K-split few-row kernel (qsmk), for 1, 2, 4 and 8 waves per
 # workgroup, group sizes 64 and 128, both scale dtypes, ragged N.
 QSMK = [
     (2, 128256, 2048, 64, "f16"), (3, 4100, 512, 64, "bf16"), (5, 8192, 1024, 128, "f16"),
     (8, 8192, 2048, 64, "bf16"), (16, 16390, 4096, 64, "f16"), (11, 65537, 4096, 128, "bf16"),
-    (16, 128256, 2048, 64, "f16"), (4, 4111, 4096, 64, "f16"),
+    (16, 128256, 2048, 64, "f16"), (4, 4111, 4096, 64, "f16"), (6, 8192, 3072, 64, "bf16"),
+    (9, 4300, 2560, 128, "f16"), (3, 8192, 3584, 64, "f16"),
 ]
 
 
 # 8-bit codes on the K-split kernel (natural-order byte unpack, 512-byte row
 # slices per wave), including shapes the 16-row-block kernel used to take.
 QSMK8 = [
-    (2, 8192, 2048, 64, "f16"), (4, 4100, 512, 64, "bf16"), (10, 66000, 1024, 64, "bf16"),
+    (2, 8192, 2048, 64, "f16"), (4, 4100, 1536, 64, "bf16"), (10, 66000, 1024, 64, "bf16"),
     (13, 70001, 512, 64, "bf16"), (12, 65540, 4096, 128, "f16"), (16, 128256, 2048, 64, "f16"),
     (7, 8192, 4096, 64, "f16"),
 ]
@@ -819,9 +820,11 @@ def test_few_rows_ksplit_routing():
     assert not d("qmv", 17, 128256, 2048, 4, 64, "f16").startswith("qsmk")
     assert d("qmv", 8, 128256, 2048, 8, 64, "f16").startswith("qsmk_kernel<bits=8")   # 8-bit codes
     assert d("a8", 8, 128256, 2048, 8, 64, "f16").startswith("qsmk_kernel<bits=8")  # int8 x with 8-bit codes
-    assert d("a8", 8, 128256, 1536, 8, 64, "f16").startswith("qmv_kernel")         # K not 512 * 2^j
+    assert d("a8", 8, 128256, 1536, 8, 64, "f16").startswith("qsmk_kernel<bits=8")  # K = 3 x 512: 3 waves
+    assert d("a8", 8, 128256, 2112, 8, 64, "f16").startswith("qmv_kernel")         # K not a multiple of 512
     assert not d("qmv", 8, 128256, 2048, 4, 32, "f16").startswith("qsmk")   # group size 32
-    assert not d("qmv", 8, 128256, 1536, 4, 64, "f16").startswith("qsmk")   # K not 512 * 2^j
+    assert d("qmv", 8, 128256, 1536, 4, 64, "f16").startswith("qsmk_kernel<bits=4,sb=f16,gs=64,m=8,waves=3>")
+    assert not d("qmv", 8, 128256, 2112, 4, 64, "f16").startswith("qsmk")   # K not a multiple of 512
     assert not d("qmv", 8, 128256, 8192, 4, 64, "f16").startswith("qsmk")   # K > 4096
     assert not d("qmv", 8, 2048, 2048, 4, 64, "f16").startswith("qsmk")     # too few W rows per CU
 
