@@ -264,7 +264,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   // the D rows this lane holds
   u4 xa[kKsGroups][2];
   float xs[kKsGroups][4];
-  float sxd[4] = {1.0f, 1.0f, 1.0f, 1.0f};  // row scales of the D rows (int8 activations)
+  float sxl = 1.0f;  // row scale of x row c16 (int8 activations)
   if constexpr (XI) {
     // the row's largest |x| over all slices (a cross-wave maximum through LDS),
     // then r = 127 / max and the codes of this lane's 16 activations per group
@@ -304,8 +304,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
       for (int i = 0; i < 4; ++i) xs[g][i] = __shfl(ps, 4 * kg + i);
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sxd[i] = __shfl(sx, 4 * kg + i);
+    sxl = sx;
   } else {
     const uint16_t* xp = x + static_cast<size_t>(min(c16, M - 1)) * K + ks0 + 16 * kg;
     const u4 z = {0u, 0u, 0u, 0u};
@@ -378,7 +377,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     // all groups' MFMAs first, each into its own registers, so that the
     // matrix core runs them back to back while the codes of the next group
     // are unpacked; then the scale and bias per group, in group order
+    typedef int v4i __attribute__((ext_vector_type(4)));
     f4 p[kKsGroups];
+    v4i pq[kKsGroups];  // int8 activations: the exact integer tiles, converted after the last MFMA
 #pragma unroll
     for (int g = 0; g < kKsGroups; ++g) {
       typedef uint32_t u2 __attribute__((ext_vector_type(2)));
@@ -386,14 +387,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
         // codes [16 kg, 16 kg + 16) of the group as signed bytes c - 128 (one
         // XOR per word; the offset returns through the bias factor b + 128 s),
         // natural order, as the activation codes
-        typedef int v4i __attribute__((ext_vector_type(4)));
         const u4 wv = *reinterpret_cast<const u4*>(wst + c16 * kKsRow + 64 * g + 16 * kg);
         const v4i b = {static_cast<int>(wv.x ^ 0x80808080u), static_cast<int>(wv.y ^ 0x80808080u),
                        static_cast<int>(wv.z ^ 0x80808080u), static_cast<int>(wv.w ^ 0x80808080u)};
         const v4i zi = {0, 0, 0, 0};
-        const v4i pi = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, xa[g][0]), b, zi, 0, 0, 0);
-        p[g] = f4{static_cast<float>(pi[0]), static_cast<float>(pi[1]), static_cast<float>(pi[2]),
-                  static_cast<float>(pi[3])};
+        pq[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, xa[g][0]), b, zi, 0, 0, 0);
         continue;
       } else if constexpr (BITS == 8) {
         // codes [16 kg, 16 kg + 16) of the group: 16 bytes, natural order,
@@ -412,13 +410,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
         // codes as bytes, even then odd nibbles of each word (the order of
         // the activation codes); exact int32 dot products, at most 64 * 127 *
         // 15 in magnitude, so exact in f32 as well
-        typedef int v4i __attribute__((ext_vector_type(4)));
         const v4i b = {static_cast<int>(wv.x & 0x0F0F0F0Fu), static_cast<int>((wv.x >> 4) & 0x0F0F0F0Fu),
                        static_cast<int>(wv.y & 0x0F0F0F0Fu), static_cast<int>((wv.y >> 4) & 0x0F0F0F0Fu)};
         const v4i zi = {0, 0, 0, 0};
-        const v4i pi = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, xa[g][0]), b, zi, 0, 0, 0);
-        p[g] = f4{static_cast<float>(pi[0]), static_cast<float>(pi[1]), static_cast<float>(pi[2]),
-                  static_cast<float>(pi[3])};
+        pq[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, xa[g][0]), b, zi, 0, 0, 0);
       } else {
         const u4 b0 = unpack_w4_mfma(wv.x, magic);  // exact f16 codes
         const u4 b1 = unpack_w4_mfma(wv.y, magic);
@@ -435,6 +430,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       const float sc = sb_to_f32<SB_BF16>(static_cast<uint16_t>(sw[r >> 1] >> (16 * (r & 1))));
       float bi = sb_to_f32<SB_BF16>(static_cast<uint16_t>(bw[r >> 1] >> (16 * (r & 1))));
       if constexpr (XI && BITS == 8) bi = __builtin_fmaf(128.0f, sc, bi);  // signed codes c - 128
+      if constexpr (XI)
+        p[g] = f4{static_cast<float>(pq[g][0]), static_cast<float>(pq[g][1]), static_cast<float>(pq[g][2]),
+                  static_cast<float>(pq[g][3])};
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(bi, xs[g][i], __builtin_fmaf(sc, p[g][i], acc[i]));
     }
@@ -448,7 +446,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
       for (int w = 1; w < nw; ++w) v += red[((par * nw + w) * 64 + lane) * 4 + i];
       const int m = 4 * kg + i;
-      if (m < M && n < N) y[static_cast<size_t>(m) * N + n] = f32_to_f16_bits((XI ? v * sxd[i] : v) + o);
+      // the row scale of D row m from lane m (i is wave-uniform but not a
+      // constant: an array indexed by it would live in scratch memory)
+      const float sxi = XI ? __shfl(sxl, m) : 1.0f;
+      if (m < M && n < N) y[static_cast<size_t>(m) * N + n] = f32_to_f16_bits((XI ? v * sxi : v) + o);
     }
     par ^= 1;
   };
