@@ -56,16 +56,20 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t c
   return d;
 }
 
-// 4-bit word -> four f16 pairs with one shift: (c0, c4), (16*c1, 16*c5),
-// (c2, c6), (16*c3, 16*c7).  The odd codes stay in mantissa bits 4..7 (value
-// 1024 + 16*c), so they come out scaled by 16; callers accumulate their dot
-// products separately and fold the 1/16 back with one exact f32 multiply-add.
-__device__ __forceinline__ void unpack_w4_x16(uint32_t w, uint32_t magic, h2 (&q)[4]) {
-  const uint32_t hi = w >> 8;
-  q[0] = sub1024(and_or(w, 0x000F000Fu, magic));
-  q[1] = sub1024(and_or(w, 0x00F000F0u, magic));
-  q[2] = sub1024(and_or(hi, 0x000F000Fu, magic));
-  q[3] = sub1024(and_or(hi, 0x00F000F0u, magic));
+// f16 pattern of 64 in both halves.  Mantissa bits 4..7 under this exponent
+// weigh exactly 1, so a code placed there reads as 64 + c.
+constexpr uint32_t kMagic64 = 0x54005400u;
+
+// 4-bit word -> (64 + c0, 64 + c4), (64 + c1, 64 + c5), (64 + c2, 64 + c6),
+// (64 + c3, 64 + c7) as f16 pairs, exact: every code is moved to bits 4..7 of
+// its half (shifts by +4, 0, -4, -8) and injected under the exponent of 64
+// (`magic` = kMagic64), 7 ops per word.  The offset is left in; callers remove
+// 64 * sum(x) through the group's bias.
+__device__ __forceinline__ void unpack_w4_off64(uint32_t w, uint32_t magic, uint32_t (&q)[4]) {
+  q[0] = and_or(w << 4, 0x00F000F0u, magic);
+  q[1] = and_or(w, 0x00F000F0u, magic);
+  q[2] = and_or(w >> 4, 0x00F000F0u, magic);
+  q[3] = and_or(w >> 8, 0x00F000F0u, magic);
 }
 
 // 8-bit word -> (c0, c2), (c1, c3) with one shift and two v_and_or_b32.

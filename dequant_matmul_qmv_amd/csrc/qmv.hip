@@ -356,14 +356,18 @@ __global__ __launch_bounds__(kQmvBlock) void qmv_kernel(const QmvBatch batch) {
     if (rb >= nrb) return;  // no block-level barrier follows
   }
 
-  const uint32_t magic = XB ? kMagicB : kMagic;
+  const uint32_t magic = XB ? kMagicB : BITS == 4 ? kMagic64 : kMagic;
   // the per-segment bias factor: b, or b - 128 s when the codes carry +128
-  // (bf16 4-bit), or b + 128 s when they carry -128 (int8 mode, 8-bit codes
-  // as signed bytes c - 128); exact in f32 for the scale and bias ranges in use
+  // (bf16 4-bit), b - 64 s when they carry +64 (f16 4-bit), or b + 128 s when
+  // they carry -128 (int8 mode, 8-bit codes as signed bytes c - 128); the
+  // offsets are powers of two, so the factor is exact in f32 whenever b and
+  // the multiple of s lie within 2^13 of each other in magnitude
   auto bias_term = [&](uint16_t bbits, float sc) {
     const float b = sb_to_f32<SB_BF16>(bbits);
     if constexpr (XB && BITS == 4) {
       return __builtin_fmaf(-128.0f, sc, b);
+    } else if constexpr (!XI && BITS == 4) {
+      return __builtin_fmaf(-64.0f, sc, b);
     } else if constexpr (XI && BITS == 8) {
       return __builtin_fmaf(128.0f, sc, b);
     } else {
@@ -377,7 +381,8 @@ __global__ __launch_bounds__(kQmvBlock) void qmv_kernel(const QmvBatch batch) {
     for (int m = 0; m < MT; ++m) acc[r][m] = 0.0f;
 
   // segment dot product of one row's codes with one activation row's pairs
-  // (bf16 4-bit codes carry +128 each; the bias term takes the 128 * sum(x) back)
+  // (4-bit codes carry +128 (bf16) or +64 (f16) each; the bias term takes the
+  // offset times sum(x) back)
   auto seg_dot = [&](const uint32_t (&q)[NP], const uint32_t (&xp)[NP]) {
     if constexpr (XI) {
       // int8 codes against int8 activations, four products per v_dot4, exact
@@ -398,14 +403,13 @@ __global__ __launch_bounds__(kQmvBlock) void qmv_kernel(const QmvBatch batch) {
       }
       return d0 + d1;
     } else if constexpr (BITS == 4) {
-      // even pairs carry codes, odd pairs 16 x codes (see unpack_w4_x16)
-      float de = 0.0f, dd = 0.0f;
+      float d0 = 0.0f, d1 = 0.0f;
 #pragma unroll
       for (int p = 0; p < NP; p += 2) {
-        de = __builtin_amdgcn_fdot2(as_h2(q[p]), as_h2(xp[p]), de, false);
-        dd = __builtin_amdgcn_fdot2(as_h2(q[p + 1]), as_h2(xp[p + 1]), dd, false);
+        d0 = __builtin_amdgcn_fdot2(as_h2(q[p]), as_h2(xp[p]), d0, false);
+        d1 = __builtin_amdgcn_fdot2(as_h2(q[p + 1]), as_h2(xp[p + 1]), d1, false);
       }
-      return __builtin_fmaf(dd, 0.0625f, de);
+      return d0 + d1;
     } else {
       float d = 0.0f;
 #pragma unroll
@@ -434,10 +438,10 @@ __global__ __launch_bounds__(kQmvBlock) void qmv_kernel(const QmvBatch batch) {
         q[2 * i] = t[0];
         q[2 * i + 1] = t[1];
       } else if constexpr (BITS == 4) {
-        h2 t[4];
-        unpack_w4_x16(wr[i], magic, t);
+        uint32_t t[4];
+        unpack_w4_off64(wr[i], magic, t);
 #pragma unroll
-        for (int p = 0; p < 4; ++p) q[4 * i + p] = as_u32(t[p]);
+        for (int p = 0; p < 4; ++p) q[4 * i + p] = t[p];
       } else {
         h2 t[2];
         unpack_w8_ao(wr[i], magic, t);

@@ -807,6 +807,22 @@ def test_few_rows_ksplit_scale_regimes(shape, sb, regime):
     assert_close(y, _ref(p), f"qsmk scale regime {shape} {sb} {regime}")
 
 
+@pytest.mark.parametrize("regime", ["big", "tiny"])
+@pytest.mark.parametrize("sb", ["f16", "bf16"])
+@pytest.mark.parametrize("shape", [(1, 4104, 2048, 64), (1, 2050, 8192, 128), (4, 1030, 2048, 64), (2, 514, 4096, 64)])
+def test_decode_kernel_scale_regimes(shape, sb, regime):
+    """The decode kernel's f16 4-bit codes carry an offset of 64 that leaves
+    through the bias factor b - 64 s: scales near the f16 range, f16 subnormal
+    scales and bf16 scales far below f16's range, random signs, zero biases."""
+    M, N, K, gs = shape
+    assert mxq.mxq_describe("qmv", M, N, K, 4, gs, sb).startswith("qmv_kernel"), shape
+    p = _scale_regime_problem(M, N, K, gs, sb, regime, seed=M + N + gs + 11)
+    note(f"decode kernel scale regime {shape} {sb} {regime}")
+    y = _run("qmv", p)
+    assert np.all(np.isfinite(y))
+    assert_close(y, _ref(p), f"decode kernel scale regime {shape} {sb} {regime}")
+
+
 def test_few_rows_ksplit_routing():
     """Shapes around the K-split kernel's bounds take the other kernels."""
     d = mxq.mxq_describe
