@@ -34,11 +34,13 @@ __device__ __forceinline__ float sb_to_f32(uint16_t u) {
 // ---------------------------------------------------------------------------
 // Exact f16 codes by exponent injection.  OR-ing a code c < 1024 into the
 // mantissa of the f16 1024.0 (bits 0x6400) gives the f16 value 1024 + c, and
-// subtracting 1024 afterwards is exact, so each half below holds the integer
-// code itself.  One v_and_or_b32 builds two codes at once; the pairs come out
-// as (c0, c4), (c1, c5), (c2, c6), (c3, c7) for a 4-bit word and (c0, c2),
-// (c1, c3) for an 8-bit word, and the activations are staged in that same
-// order, so each v_dot2 multiplies matching (code, x) pairs.
+// subtracting 1024 afterwards is exact, so each half holds the integer code
+// itself.  The helpers named _off leave a power-of-two offset in instead, for
+// callers that remove it through the group's bias.  One v_and_or_b32 builds
+// two codes at once; the pairs come out as (c0, c4), (c1, c5), (c2, c6),
+// (c3, c7) for a 4-bit word and (c0, c2), (c1, c3) for an 8-bit word, and the
+// decode kernel stages its activations in that same order, so each v_dot2
+// multiplies matching (code, x) pairs.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kMagic = 0x64006400u;
 

@@ -11,13 +11,16 @@
 //    codes).  All 64 lanes of a wave work on the same R rows; lane l takes
 //    segments l, l+64, ... of each row, so one global_load_dwordx4 per row
 //    moves 1 KiB of contiguous codes per wave.
-//  * Codes become exact f16 integers (exponent injection, two per v_and_or_b32)
-//    and meet the activations in v_dot2_f32_f16 with f32 accumulation.  A
+//  * Codes go under an f16 exponent (two per v_and_or_b32) and meet the
+//    activations in v_dot2_f32_f16 with f32 accumulation.  8-bit codes are
+//    exact integers (1024 + c, less 1024); 4-bit codes keep a power-of-two
+//    offset (64 + c, f16; 128 + c, bf16) that the bias factor removes.  A
 //    segment never straddles a group (group_size >= 32 codes), so its scale and
 //    bias are applied once per segment in f32:
 //        acc += s * sum(x*q) + b * sum(x)     (zero-point form, mlxcel #574
 //                                              "Upstream status refresh")
-//    where sum(x) over the segment is precomputed.
+//    where sum(x) over the segment is precomputed; with an offset E on the
+//    codes, sum(x*(E + q)) = sum(x*q) + E*sum(x) and b becomes b - E*s.
 //  * x is staged once per workgroup in LDS, already reordered into the pair
 //    order of the unpack, laid out [m][chunk][segment] so that the 64 lanes'
 //    16-byte reads hit consecutive addresses (no bank conflicts), together

@@ -215,10 +215,11 @@ __global__ __launch_bounds__(256) void qsm_kernel(const uint16_t* __restrict__ x
 //  * passes them through its own LDS region to the MFMA B layout (lane l:
 //    W row l % 16, codes [16 (l / 16), +16) of each 64-code group, so the two
 //    k-steps of a group never mix groups),
-//  * unpacks the codes to exact f16 values -- 4-bit: one v_and_or_b32 and one
-//    packed f16 fma per pair, one shift per word, the activation fragments
-//    permuted once into the matching k order; 8-bit: a byte select under the
-//    exponent of 1024 and an exact subtraction per pair, natural order --
+//  * unpacks the codes to f16 values -- 4-bit: 64 + c, exact, one shift and
+//    one v_and_or_b32 per pair (the offset 64 leaves through the bias factor
+//    b - 64 s), the activation fragments permuted once into the matching k
+//    order; 8-bit: exact codes, a byte select under the exponent of 1024 and
+//    an exact subtraction per pair, natural order --
 //    runs the two v_mfma_f32_16x16x32_f16 of every group back to back and then
 //    applies each group's scale and bias in f32 (s P + b X_g),
 // and the waves' partial 16 x 16 tiles are added in LDS in wave order (one
@@ -230,6 +231,16 @@ constexpr int kKsMaxWaves = 8;
 // staged row slice: 256 (4-bit) or 512 (8-bit) bytes + 16 bytes of pad
 __host__ __device__ constexpr int ks_row_bytes(int bits) { return kKsCodes * bits / 8 + 16; }
 }  // namespace
+
+// 4-bit word -> (64 + c0, 64 + c4), (64 + c1, 64 + c5), (64 + c2, 64 + c6),
+// (64 + c3, 64 + c7) as f16 pairs: each code moved to bits 4..7 of its half,
+// where under the exponent of 64 (`magic` = kMagic64) they weigh exactly 1.
+// Plain code, so that the compiler emits the v_and_or_b32 itself and knows to
+// insert the wait states its results need before an MFMA reads them.
+__device__ __forceinline__ u4 unpack_w4_off64_mfma(uint32_t w, uint32_t magic) {
+  constexpr uint32_t m = 0x00F000F0u;
+  return u4{((w << 4) & m) | magic, (w & m) | magic, ((w >> 4) & m) | magic, ((w >> 8) & m) | magic};
+}
 
 size_t qsmk_lds_bytes(int waves, int bits) {
   return static_cast<size_t>(waves) * 16 * ks_row_bytes(bits) + static_cast<size_t>(2 * waves) * 64 * 16;
@@ -312,10 +323,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     for (int g = 0; g < kKsGroups; ++g) {
       const u4 v0 = *reinterpret_cast<const u4*>(xp + 64 * g);
       const u4 v1 = *reinterpret_cast<const u4*>(xp + 64 * g + 8);
-      // k slots in the order of the code unpack: 4-bit pairs (x0, x5)
-      // (x1, x4) ..., 8-bit natural order
-      xa[g][0] = BITS == 4 ? perm_x_w4_mfma(c16 < M ? v0 : z) : (c16 < M ? v0 : z);
-      xa[g][1] = BITS == 4 ? perm_x_w4_mfma(c16 < M ? v1 : z) : (c16 < M ? v1 : z);
+      // k slots in the order of the code unpack: 4-bit pairs (x0, x4)
+      // (x1, x5) ..., 8-bit natural order
+      xa[g][0] = BITS == 4 ? perm_x_w4(c16 < M ? v0 : z) : (c16 < M ? v0 : z);
+      xa[g][1] = BITS == 4 ? perm_x_w4(c16 < M ? v1 : z) : (c16 < M ? v1 : z);
     }
 #pragma unroll
     for (int g = 0; g < kKsGroups; ++g) {
@@ -327,7 +338,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     }
   }
 
-  uint32_t magic = kMagic;
+  uint32_t magic = BITS == 4 ? kMagic64 : kMagic;
   asm volatile("" : "+v"(magic));  // opaque to the compiler: the unpack becomes v_and_or_b32 / v_bfi_b32
 
   // Loads of one block (indices clamped: branch-free; a block past the end
@@ -415,8 +426,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
         const v4i zi = {0, 0, 0, 0};
         pq[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, xa[g][0]), b, zi, 0, 0, 0);
       } else {
-        const u4 b0 = unpack_w4_mfma(wv.x, magic);  // exact f16 codes
-        const u4 b1 = unpack_w4_mfma(wv.y, magic);
+        const u4 b0 = unpack_w4_off64_mfma(wv.x, magic);  // 64 + c, exact
+        const u4 b1 = unpack_w4_off64_mfma(wv.y, magic);
         p[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, xa[g][0]), __builtin_bit_cast(h8, b0),
                                                       zero, 0, 0, 0);
         p[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, xa[g][1]), __builtin_bit_cast(h8, b1),
@@ -430,6 +441,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       const float sc = sb_to_f32<SB_BF16>(static_cast<uint16_t>(sw[r >> 1] >> (16 * (r & 1))));
       float bi = sb_to_f32<SB_BF16>(static_cast<uint16_t>(bw[r >> 1] >> (16 * (r & 1))));
       if constexpr (XI && BITS == 8) bi = __builtin_fmaf(128.0f, sc, bi);  // signed codes c - 128
+      if constexpr (!XI && BITS == 4) bi = __builtin_fmaf(-64.0f, sc, bi);  // codes 64 + c
       if constexpr (XI)
         p[g] = f4{static_cast<float>(pq[g][0]), static_cast<float>(pq[g][1]), static_cast<float>(pq[g][2]),
                   static_cast<float>(pq[g][3])};
