@@ -80,20 +80,6 @@ __device__ __forceinline__ void unpack_w8_ao(uint32_t w, uint32_t magic, h2 (&q)
   q[1] = sub1024(and_or(w >> 8, 0x00FF00FFu, magic));
 }
 
-// 4-bit word -> 4 pairs of exact f16 codes.
-__device__ __forceinline__ void unpack_w4(uint32_t w, h2 (&q)[4]) {
-  q[0] = sub1024((w & 0x000F000Fu) | kMagic);
-  q[1] = sub1024(((w >> 4) & 0x000F000Fu) | kMagic);
-  q[2] = sub1024(((w >> 8) & 0x000F000Fu) | kMagic);
-  q[3] = sub1024(((w >> 12) & 0x000F000Fu) | kMagic);
-}
-
-// 8-bit word -> 2 pairs of exact f16 codes.
-__device__ __forceinline__ void unpack_w8(uint32_t w, h2 (&q)[2]) {
-  q[0] = sub1024((w & 0x00FF00FFu) | kMagic);
-  q[1] = sub1024(((w >> 8) & 0x00FF00FFu) | kMagic);
-}
-
 // Codes in natural k order for the MFMA B operand (the x tile is then used as
 // stored, with no reordering).  A byte-select puts byte i of the word, twice,
 // under the f16 exponent of 1024 (the selector's byte 5 is magic's 0x64); the
@@ -123,7 +109,7 @@ __device__ __forceinline__ u4 unpack8_natural(uint32_t w0, uint32_t w1, uint32_t
 }
 
 // Reorder 8 consecutive f16 activations x0..x7 (as 4 dwords (x0,x1) (x2,x3)
-// (x4,x5) (x6,x7)) into the pair order of unpack_w4: (x0,x4) (x1,x5) (x2,x6)
+// (x4,x5) (x6,x7)) into the pair order of unpack_w4_off64: (x0,x4) (x1,x5) (x2,x6)
 // (x3,x7).  v_perm_b32 selects bytes from two dwords.
 __device__ __forceinline__ u4 perm_x_w4(u4 v) {
   u4 o;
@@ -136,7 +122,7 @@ __device__ __forceinline__ u4 perm_x_w4(u4 v) {
 }
 
 // Reorder two 8-bit words' activations x0..x3 | x4..x7 into (x0,x2) (x1,x3) |
-// (x4,x6) (x5,x7), the pair order of unpack_w8.
+// (x4,x6) (x5,x7), the pair order of unpack_w8_ao.
 __device__ __forceinline__ u4 perm_x_w8(u4 v) {
   u4 o;
   o.x = __builtin_amdgcn_perm(v.y, v.x, 0x05040100u);  // (x0, x2)
@@ -162,7 +148,7 @@ __device__ __forceinline__ float sum8_f32(u4 v) {
 //    half holds 128 + c exactly.  The offset is not subtracted per code; the
 //    caller folds it into the bias term (sum x*(128 + c) = sum x*c + 128 sum x).
 //    One shift per nibble position, pairs (c0, c4) (c1, c5) (c2, c6) (c3, c7)
-//    as in unpack_w4, so the same activation reorder (perm_x_w4) applies.
+//    as in unpack_w4_off64, so the same activation reorder (perm_x_w4) applies.
 //  * 8-bit codes (up to 255, beyond what the mantissa can hold under a power
 //    of two) are converted exactly: v_cvt_f32_ubyte then a packed f32 -> bf16
 //    conversion, pairs in natural order (c0, c1) (c2, c3).
@@ -182,41 +168,6 @@ __device__ __forceinline__ void unpack_w4_off(uint32_t w, uint32_t magic, uint32
   q[1] = and_or(w >> 4, 0x000F000Fu, magic);
   q[2] = and_or(w >> 8, 0x000F000Fu, magic);
   q[3] = and_or(w >> 12, 0x000F000Fu, magic);
-}
-
-// 4-bit word -> four pairs of exact f16 codes for the matrix cores, in the
-// pair order (c0, c5) (c1, c4) (c2, c7) (c3, c6): one shift and four
-// (w & mask) | magic put each pair under the exponent of 1024, as 1024 + c in
-// one half and 1024 + 16 c' in the other (c' taken from bits 4..7 of its half);
-// one packed f16 fma per pair, exact, maps (1024 + c, 1024 + 16 c') to (c, c').
-// Plain code, which the compiler turns into v_and_or_b32 / v_bfi_b32 when
-// `magic` is a value it cannot see (the caller hides the constant behind an
-// empty asm): the compiler inserts the wait states an MFMA needs after a VALU
-// write of its operand only for instructions it knows, not for inline asm,
-// whose result the MFMA could then read before it is written.
-__device__ __forceinline__ u4 unpack_w4_mfma(uint32_t w, uint32_t magic) {
-  constexpr uint32_t m_a = 0x00F0000Fu, m_b = 0x000F00F0u;
-  const h2 sa = {static_cast<_Float16>(1.0f), static_cast<_Float16>(0.0625f)};
-  const h2 oa = {static_cast<_Float16>(-1024.0f), static_cast<_Float16>(-64.0f)};
-  const h2 sb = {static_cast<_Float16>(0.0625f), static_cast<_Float16>(1.0f)};
-  const h2 ob = {static_cast<_Float16>(-64.0f), static_cast<_Float16>(-1024.0f)};
-  const uint32_t h = w >> 8;
-  const uint32_t t0 = (w & m_a) | (magic & ~m_a), t1 = (w & m_b) | (magic & ~m_b);
-  const uint32_t t2 = (h & m_a) | (magic & ~m_a), t3 = (h & m_b) | (magic & ~m_b);
-  return u4{as_u32(__builtin_elementwise_fma(as_h2(t0), sa, oa)), as_u32(__builtin_elementwise_fma(as_h2(t1), sb, ob)),
-            as_u32(__builtin_elementwise_fma(as_h2(t2), sa, oa)), as_u32(__builtin_elementwise_fma(as_h2(t3), sb, ob))};
-}
-
-// Reorder 8 consecutive f16 activations x0..x7 (dwords (x0,x1) (x2,x3)
-// (x4,x5) (x6,x7)) into the pair order of unpack_w4_mfma: (x0,x5) (x1,x4)
-// (x2,x7) (x3,x6).
-__device__ __forceinline__ u4 perm_x_w4_mfma(u4 v) {
-  u4 o;
-  o.x = __builtin_amdgcn_perm(v.z, v.x, 0x07060100u);  // (x0 from v.x bytes 0-1, x5 from v.z bytes 2-3)
-  o.y = __builtin_amdgcn_perm(v.z, v.x, 0x05040302u);  // (x1, x4)
-  o.z = __builtin_amdgcn_perm(v.w, v.y, 0x07060100u);  // (x2, x7)
-  o.w = __builtin_amdgcn_perm(v.w, v.y, 0x05040302u);  // (x3, x6)
-  return o;
 }
 
 // ---------------------------------------------------------------------------
