@@ -623,7 +623,7 @@ def test_int8_activations_deterministic():
 A8_FEW = [
     (3, 8192, 2048, 64, "f16"), (3, 4100, 1024, 128, "bf16"), (5, 8192, 512, 64, "f16"),
     (8, 16390, 4096, 64, "bf16"), (16, 65537, 4096, 128, "f16"), (11, 128256, 2048, 64, "f16"),
-    (4, 4111, 4096, 64, "f16"),
+    (4, 4111, 4096, 64, "f16"), (6, 8192, 3072, 64, "f16"), (13, 4100, 1536, 128, "bf16"),
 ]
 
 
@@ -645,7 +645,8 @@ def test_int8_few_rows_ksplit(case):
 
 # int8 activations with 8-bit codes on the integer-MFMA kernel: codes as
 # signed bytes c - 128, the offset folded into the bias factor b + 128 s.
-A8_FEW8 = [(3, 8192, 2048, 64, "f16"), (9, 4100, 1024, 128, "bf16"), (16, 65537, 4096, 64, "f16")]
+A8_FEW8 = [(3, 8192, 2048, 64, "f16"), (9, 4100, 1024, 128, "bf16"), (16, 65537, 4096, 64, "f16"),
+           (7, 8192, 3584, 64, "f16"), (4, 4100, 2560, 64, "bf16")]
 
 
 @pytest.mark.parametrize("case", A8_FEW8, ids=str)
@@ -753,7 +754,7 @@ QSMK = [
 QSMK8 = [
     (2, 8192, 2048, 64, "f16"), (4, 4100, 1536, 64, "bf16"), (10, 66000, 1024, 64, "bf16"),
     (13, 70001, 512, 64, "bf16"), (12, 65540, 4096, 128, "f16"), (16, 128256, 2048, 64, "f16"),
-    (7, 8192, 4096, 64, "f16"),
+    (7, 8192, 4096, 64, "f16"), (5, 8192, 3584, 128, "f16"), (3, 4100, 2560, 64, "bf16"),
 ]
 
 
