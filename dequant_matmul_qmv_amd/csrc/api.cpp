@@ -63,6 +63,19 @@ mxq_status hip_fail(const char* who, hipError_t e) {
 // Row counts the K-split few-row kernel takes (its shape test aside).
 bool qsmk_rows(int64_t M, int64_t K) { return M >= 3 || (M == 2 && K <= 2048); }
 
+// Whether the K-split kernel may run K in chunks on this stream: they need the
+// cached split workspace, which a stream being captured into a graph must not
+// use (such calls keep the other kernels).  Only asked when K needs chunks.
+bool qsmk_chunks_ok(int64_t K, void* stream) {
+  if (K <= 4096) return true;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(static_cast<hipStream_t>(stream), &cap) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return cap == hipStreamCaptureStatusNone;
+}
+
 // M-sliced qmv over the whole M range.
 mxq_status run_qmv(const char* who, const void* x, const uint32_t* w, const void* scales,
                    const void* biases, const void* out_bias, void* y, int64_t M, int64_t N, int64_t K,
@@ -99,7 +112,8 @@ mxq_status run_qmv(const char* who, const void* x, const uint32_t* w, const void
   // x in every workgroup; measured on lm_head: 28.3 against 31.2 us).
   const bool few_i8 = act == kActI8 && M >= 3;
   if ((act == kActF16 ? qsmk_rows(M, K) : few_i8) && aligned(x, 16) && aligned(scales, 16) &&
-      aligned(biases, 16) && mxq::qsmk_shape(M, N, K, bits, group_size, dev)) {
+      aligned(biases, 16) &&
+      mxq::qsmk_shape(M, N, K, bits, group_size, act == kActF16 && qsmk_chunks_ok(K, stream), dev)) {
     a.x = static_cast<const uint16_t*>(x);
     a.y = static_cast<uint16_t*>(y);
     a.x_vec = 1;
@@ -173,7 +187,8 @@ mxq_status run_matmul(const char* who, const void* x, const uint32_t* w, const v
   mxq::DeviceInfo dev;
   hipError_t e = mxq::device_info(&dev);
   if (e != hipSuccess) return hip_fail(who, e);
-  const bool few = act == kActF16 && qsmk_rows(M, K) && mxq::qsmk_shape(M, N, K, bits, group_size, dev);
+  const bool few = act == kActF16 && qsmk_rows(M, K) &&
+                   mxq::qsmk_shape(M, N, K, bits, group_size, qsmk_chunks_ok(K, stream), dev);
   if (act == kActI8 || few || !mxq::qmm_mfma_shape(M, K) || !aligned(x, 16))
     return run_qmv(who, x, w, scales, biases, out_bias, y, M, N, K, bits, group_size, sb_dtype, act, stream);
   mxq::QmmArgs a{};
@@ -403,12 +418,14 @@ const char* mxq_describe(const char* op, int64_t M, int64_t N, int64_t K, int bi
   }
   const char* sb = sb_dtype == MXQ_BF16 ? "bf16" : "f16";
   const bool a8 = o == "a8";
-  if ((a8 ? M >= 3 : qsmk_rows(M, K)) && mxq::qsmk_shape(M, N, K, bits, group_size, dev)) {
-    const int64_t nw = K / 512;
+  if ((a8 ? M >= 3 : qsmk_rows(M, K)) && mxq::qsmk_shape(M, N, K, bits, group_size, !a8, dev)) {
+    int nw = 0, chunks = 0;
+    mxq::qsmk_split(K, &nw, &chunks);
     desc = "qsmk_kernel<bits=" + std::to_string(bits) + ",sb=" + std::string(sb) + ",gs=" +
            std::to_string(group_size) + ",m=" + std::to_string(M) + ",waves=" + std::to_string(nw) +
-           (a8 ? ",act=i8" : "") + "> block=" + std::to_string(64 * nw) +
-           " lds=" + std::to_string(mxq::qsmk_lds_bytes(static_cast<int>(nw), bits));
+           (a8 ? ",act=i8" : "") + (chunks > 1 ? ",kchunks=" + std::to_string(chunks) : std::string()) +
+           "> block=" + std::to_string(64 * nw) + " lds=" + std::to_string(mxq::qsmk_lds_bytes(nw, bits)) +
+           (chunks > 1 ? "; qmm_split_reduce_kernel" : "");
     return desc.c_str();
   }
   const bool mfma = o == "qmm" && mxq::qmm_mfma_shape(M, K);

@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <mutex>
 #include <stdint.h>
 
 namespace mxq {
@@ -103,12 +104,29 @@ size_t qsm_lds_bytes(int M, int K);
 hipError_t launch_qsm(const QmvArgs& a, int M, const DeviceInfo& dev);
 
 // Few-row kernel with K split over the waves of a workgroup (2 <= M <= 16,
-// 4-bit codes, f16 activations, group size 64 or 128, K = 512, 1024, 2048 or
-// 4096, at least one 16-row block of W per compute unit); a.x and the scales
-// and biases 16-byte aligned.
-bool qsmk_shape(int64_t M, int64_t N, int64_t K, int bits, int group_size, const DeviceInfo& dev);
+// 4- or 8-bit codes, group size 64 or 128, K a multiple of 512); a.x and the
+// scales and biases 16-byte aligned.  K = 512 * waves * chunks with 1..8
+// waves; K beyond 4096 runs in chunks (the grid's second dimension), each
+// writing an f32 partial tile to the split workspace, added in a fixed order
+// by the split reduction.  Chunks need f16 activations (int8 activations take
+// one scale per row over all of K), M * N a multiple of 4, and a stream that
+// is not being captured (`chunks_ok`).  At least one 16-row block of W per
+// compute unit, counting every chunk.
+bool qsmk_split(int64_t K, int* waves, int* chunks);
+bool qsmk_shape(int64_t M, int64_t N, int64_t K, int bits, int group_size, bool chunks_ok, const DeviceInfo& dev);
 size_t qsmk_lds_bytes(int waves, int bits);
 hipError_t launch_qsmk(const QmvArgs& a, int M, const DeviceInfo& dev);
+
+// The split-K workspace cache of the prefill kernel (one f32 buffer per device
+// and stream, grown on demand) and its fixed-order reduction, shared with the
+// few-row kernel's K chunks.  Hold split_workspace_mutex() from the call of
+// split_workspace_locked() until the kernels that use the buffer are enqueued.
+std::mutex& split_workspace_mutex();
+float* split_workspace_locked(int device, hipStream_t stream, size_t bytes);
+// y[M, N] (f16) = RNE(sum over splits of part[split] in split order + out_bias);
+// M * N a multiple of 4, part 16-byte aligned.
+hipError_t launch_split_reduce_f16(const float* part, const uint16_t* ob, uint16_t* y, int64_t M, int64_t N,
+                                   int splits, hipStream_t stream);
 
 struct QmmArgs {
   const uint16_t* x;

@@ -612,6 +612,22 @@ void* cached_workspace(int device, hipStream_t stream, size_t bytes) {
 }
 }  // namespace
 
+std::mutex& split_workspace_mutex() { return g_ws_mu; }
+
+float* split_workspace_locked(int device, hipStream_t stream, size_t bytes) {
+  return static_cast<float*>(cached_workspace(device, stream, bytes));
+}
+
+hipError_t launch_split_reduce_f16(const float* part, const uint16_t* ob, uint16_t* y, int64_t M, int64_t N,
+                                   int splits, hipStream_t stream) {
+  const int64_t MN = M * N;
+  int64_t blocks = (MN / 4 + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(qmm_split_reduce_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, part,
+                     ob, y, MN, static_cast<int>(N), splits);
+  return hipGetLastError();
+}
+
 hipError_t launch_qmm(const QmmArgs& a0, const DeviceInfo& dev) {
   const QmmTile tl = qmm_pick_tile(a0.M, a0.N, a0.K, dev);
   QmmArgs a = a0;

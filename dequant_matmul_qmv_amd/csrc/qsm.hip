@@ -28,6 +28,9 @@
 // The activations, staged once per workgroup in LDS with padded rows, supply
 // the matching A fragments; rows at or past M read as zero.  Groups of 128
 // codes are two 64-code groups with the same scale and bias.
+#include <climits>
+#include <mutex>
+
 #include "mxq_device.h"
 #include "mxq_internal.h"
 
@@ -228,6 +231,7 @@ namespace {
 constexpr int kKsCodes = 512;                // codes per wave slice
 constexpr int kKsGroups = kKsCodes / 64;     // 64-code groups per slice
 constexpr int kKsMaxWaves = 8;
+constexpr int kKsMaxChunks = 64;             // K up to 64 * 4096 codes
 // staged row slice: 256 (4-bit) or 512 (8-bit) bytes + 16 bytes of pad
 __host__ __device__ constexpr int ks_row_bytes(int bits) { return kKsCodes * bits / 8 + 16; }
 }  // namespace
@@ -254,8 +258,8 @@ size_t qsmk_lds_bytes(int waves, int bits) {
 template <int BITS, bool SB_BF16, int GSH, int NW, bool XI>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void qsmk_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ W,
                                                    const uint16_t* __restrict__ S, const uint16_t* __restrict__ B,
-                                                   uint16_t* __restrict__ y, const uint16_t* __restrict__ ob, int M,
-                                                   int N, int K) {
+                                                   uint16_t* __restrict__ y, const uint16_t* __restrict__ ob,
+                                                   float* __restrict__ part, int M, int N, int K) {
   constexpr int nw = NW;
   constexpr int kKsRow = ks_row_bytes(BITS);
   constexpr int NLD = BITS;  // 16-byte loads per lane and block: 4 (4-bit) or 8 (8-bit)
@@ -266,7 +270,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int kg = lane >> 4;   // k-slot group of the operands; D rows 4 kg .. 4 kg + 3
   unsigned char* wst = smem + wave * 16 * kKsRow;                      // [16][kKsRow] this wave's codes
   float* red = reinterpret_cast<float*>(smem + nw * 16 * kKsRow);     // [2][nw][64][4] partial tiles
-  const int ks0 = wave * kKsCodes;
+  // this wave's 512 codes: chunk blockIdx.y of nw slices, then slice `wave`
+  const int ks0 = (static_cast<int>(blockIdx.y) * nw + wave) * kKsCodes;
   const int kw = K * BITS / 32;
   const int G = K >> (6 + GSH);
   constexpr int SBN = kKsGroups >> GSH;  // real groups per slice: 8 (g64) or 4 (g128)
@@ -360,7 +365,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       d.w[i] = __builtin_nontemporal_load(
           reinterpret_cast<const u4*>(wl + static_cast<size_t>(row) * kw + 64 * (i / 4)));
     }
-    const size_t so = static_cast<size_t>(min(16 * rb + c16, N - 1)) * G + wave * SBN;
+    const size_t so = static_cast<size_t>(min(16 * rb + c16, N - 1)) * G + (ks0 >> (6 + GSH));
     if constexpr (GSH == 0) {
       d.s = __builtin_nontemporal_load(reinterpret_cast<const u4*>(S + so));
       d.b = __builtin_nontemporal_load(reinterpret_cast<const u4*>(B + so));
@@ -461,7 +466,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       // the row scale of D row m from lane m (i is wave-uniform but not a
       // constant: an array indexed by it would live in scratch memory)
       const float sxi = XI ? __shfl(sxl, m) : 1.0f;
-      if (m < M && n < N) y[static_cast<size_t>(m) * N + n] = f32_to_f16_bits((XI ? v * sxi : v) + o);
+      if (m < M && n < N) {
+        if (part != nullptr)  // one K chunk's f32 partial, [chunk][m][n]
+          part[(static_cast<size_t>(blockIdx.y) * M + m) * N + n] = v;
+        else
+          y[static_cast<size_t>(m) * N + n] = f32_to_f16_bits((XI ? v * sxi : v) + o);
+      }
     }
     par ^= 1;
   };
@@ -483,12 +493,28 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   if (rb < nrb) step(cur, rb);
 }
 
-bool qsmk_shape(int64_t M, int64_t N, int64_t K, int bits, int group_size, const DeviceInfo& dev) {
+bool qsmk_split(int64_t K, int* waves, int* chunks) {
+  if (K < kKsCodes || K % kKsCodes != 0) return false;
+  const int64_t S = K / kKsCodes;  // 512-code slices
+  // the fewest chunks of at most kKsMaxWaves slices each that divide S
+  for (int64_t c = (S + kKsMaxWaves - 1) / kKsMaxWaves; c <= S && c <= kKsMaxChunks; ++c) {
+    if (S % c == 0) {
+      *waves = static_cast<int>(S / c);
+      *chunks = static_cast<int>(c);
+      return true;
+    }
+  }
+  return false;
+}
+
+bool qsmk_shape(int64_t M, int64_t N, int64_t K, int bits, int group_size, bool chunks_ok, const DeviceInfo& dev) {
   if ((bits != 4 && bits != 8) || M < 2 || M > 16 || (group_size != 64 && group_size != 128)) return false;
-  const int64_t nw = K / kKsCodes;  // waves per workgroup: 1 .. 8
-  if (K % kKsCodes != 0 || nw < 1 || nw > kKsMaxWaves) return false;
-  // at least one block of 16 rows per compute unit (smaller N stays on qmv)
-  return (N + 15) / 16 >= static_cast<int64_t>(dev.num_cu);
+  int nw = 0, chunks = 0;
+  if (!qsmk_split(K, &nw, &chunks)) return false;
+  if (chunks > 1 && (!chunks_ok || (M * N) % 4 != 0 || N > INT_MAX / 16)) return false;
+  // at least one block of 16 rows per compute unit, counting every chunk
+  // (smaller N stays on qmv)
+  return (N + 15) / 16 * chunks >= static_cast<int64_t>(dev.num_cu);
 }
 
 namespace {
@@ -513,10 +539,12 @@ const void* qsmk_ptr(int nw, int bits, bool xi) {
 }  // namespace
 
 hipError_t launch_qsmk(const QmvArgs& a, int M, const DeviceInfo& dev) {
-  const int nw = static_cast<int>(a.K / kKsCodes);
+  int nw = 0, chunks = 0;
+  if (!qsmk_split(a.K, &nw, &chunks)) return hipErrorInvalidValue;  // the caller checked qsmk_shape
   const size_t lds = qsmk_lds_bytes(nw, a.bits);
   const bool g128 = a.glog2 == 7;
   const bool xi = a.act == 2;  // int8 activations (quantized in the kernel)
+  if (chunks > 1 && xi) return hipErrorInvalidValue;
   const void* kern = a.sb_bf16 ? (g128 ? qsmk_ptr<true, 1>(nw, a.bits, xi) : qsmk_ptr<true, 0>(nw, a.bits, xi))
                                : (g128 ? qsmk_ptr<false, 1>(nw, a.bits, xi) : qsmk_ptr<false, 0>(nw, a.bits, xi));
   if (lds > 65536) {  // 8 waves of 8-bit slices
@@ -530,8 +558,8 @@ hipError_t launch_qsmk(const QmvArgs& a, int M, const DeviceInfo& dev) {
   }
   const int per_cu = occ < 2 ? occ : 2;
   const int64_t nrb = (a.N + 15) / 16;
-  const int64_t cap = static_cast<int64_t>(dev.num_cu) * per_cu;
-  const unsigned grid = static_cast<unsigned>(nrb < cap ? nrb : cap);
+  const int64_t cap = (static_cast<int64_t>(dev.num_cu) * per_cu + chunks - 1) / chunks;  // workgroups per chunk
+  const unsigned gx = static_cast<unsigned>(nrb < cap ? nrb : cap);
   const uint16_t* xp = a.x;
   const uint32_t* wp = a.w;
   const uint16_t* sp = a.s;
@@ -539,8 +567,22 @@ hipError_t launch_qsmk(const QmvArgs& a, int M, const DeviceInfo& dev) {
   uint16_t* yp = a.y;
   const uint16_t* obp = a.ob;
   int Mi = M, Ni = static_cast<int>(a.N), Ki = static_cast<int>(a.K);
-  void* args[] = {&xp, &wp, &sp, &bp, &yp, &obp, &Mi, &Ni, &Ki};
-  return hipLaunchKernel(kern, dim3(grid), dim3(64 * nw), args, lds, a.stream);
+  if (chunks == 1) {
+    float* partp = nullptr;
+    void* args[] = {&xp, &wp, &sp, &bp, &yp, &obp, &partp, &Mi, &Ni, &Ki};
+    return hipLaunchKernel(kern, dim3(gx), dim3(64 * nw), args, lds, a.stream);
+  }
+  // K in chunks: f32 partial tiles [chunks, M, N] in the stream's split
+  // workspace, then the fixed-order sum, the output bias and the f16 rounding
+  const size_t bytes = static_cast<size_t>(chunks) * static_cast<size_t>(M) * static_cast<size_t>(a.N) * 4;
+  std::lock_guard<std::mutex> lk(split_workspace_mutex());
+  float* partp = split_workspace_locked(dev.device, a.stream, bytes);
+  if (partp == nullptr) return hipErrorOutOfMemory;
+  const uint16_t* no_ob = nullptr;  // the output bias is added once, by the reduction
+  void* args[] = {&xp, &wp, &sp, &bp, &yp, &no_ob, &partp, &Mi, &Ni, &Ki};
+  hipError_t e = hipLaunchKernel(kern, dim3(gx, static_cast<unsigned>(chunks)), dim3(64 * nw), args, lds, a.stream);
+  if (e != hipSuccess) return e;
+  return launch_split_reduce_f16(partp, obp, yp, M, a.N, chunks, a.stream);
 }
 
 bool qsm_shape(int64_t M, int64_t N, int64_t K, int bits, int group_size, const DeviceInfo& dev) {

@@ -715,7 +715,7 @@ def test_int8_few_rows_integer_case_and_determinism():
 # oracle, including the ragged tail.
 QSM = [
     (9, 65600, 2112, 4, 64, "f16"), (10, 66000, 576, 8, 64, "bf16"), (16, 65536, 4352, 4, 128, "f16"),
-    (13, 70001, 2624, 8, 64, "bf16"), (12, 65540, 6144, 8, 128, "f16"), (16, 128256, 1088, 8, 64, "f16"),
+    (13, 70001, 2624, 8, 64, "bf16"), (12, 65540, 6272, 8, 128, "f16"), (16, 128256, 1088, 8, 64, "f16"),
 ]
 
 
@@ -808,6 +808,72 @@ def test_few_rows_ksplit_scale_regimes(shape, sb, regime):
     assert_close(y, _ref(p), f"qsmk scale regime {shape} {sb} {regime}")
 
 
+# K beyond 4096 on the K-split kernel: K chunks of up to eight 512-code
+# slices (the grid's second dimension), f32 partial tiles, fixed-order sum.
+# (M, N, K, bits, group, scale dtype); chunks x waves: 2 x 8, 4 x 7, 2 x 8,
+# 2 x 5, 2 x 8, 2 x 6, 2 x 8 (8-bit), 3 x 6 (8-bit)
+QSMK_LONGK = [
+    (4, 8192, 8192, 4, 64, "f16"), (16, 4100, 14336, 4, 128, "bf16"), (4, 2050, 8192, 4, 64, "f16"),
+    (8, 4104, 5120, 4, 64, "bf16"), (12, 16400, 8192, 4, 64, "f16"), (5, 4096, 6144, 4, 128, "f16"),
+    (6, 4100, 8192, 8, 64, "f16"), (9, 4104, 9216, 8, 128, "bf16"),
+]
+
+
+@pytest.mark.parametrize("entry", ["qmv", "qmm"])
+@pytest.mark.parametrize("case", QSMK_LONGK, ids=str)
+def test_few_rows_ksplit_long_k(case, entry):
+    M, N, K, bits, gs, sb = case
+    d = mxq.mxq_describe(entry, M, N, K, bits, gs, sb)
+    assert d.startswith(f"qsmk_kernel<bits={bits}") and ",kchunks=" in d, (case, d)
+    p = synth.make_problem(M, N, K, bits, gs, sb, seed=M + N + K + 53)
+    x, w, s, b = to_dev(p)
+    note(f"few-row k-split, K chunks {entry} {case}")
+    fn = mxq.mxq_qmv if entry == "qmv" else mxq.mxq_qmm
+    y = y_host(fn(x, w, s, b, bits=bits, group_size=gs))
+    cols = np.arange(N) if N * K <= 4104 * 8192 else _sampled_cols(N, M)
+    ref = oracle.matmul_ref_rows(p.x, p.w, p.scales, p.biases, cols, K, bits, gs, sb)
+    assert_close(y[:, cols], ref, f"qsmk long K {case}")
+    # the fixed-order chunk sum is deterministic
+    y2 = y_host(fn(x, w, s, b, bits=bits, group_size=gs))
+    assert np.array_equal(y.view(np.uint16), y2.view(np.uint16)), case
+
+
+def test_few_rows_ksplit_long_k_bias_and_capture():
+    """K chunks with an output bias (added once, by the reduction), and the
+    same call under graph capture, which keeps the other kernels (no cached
+    workspace inside a graph): both within the bar, every replay equal."""
+    M, N, K, gs = 8, 4100, 8192, 64
+    p = synth.make_problem(M, N, K, 4, gs, "f16", seed=611)
+    ob = synth.make_out_bias(N, seed=612)
+    x, w, s, b = to_dev(p)
+    obd = _bias_dev(ob)
+    note("few-row k-split, K chunks, bias and capture")
+    ref = oracle.linear_ref(p.x, p.w, p.scales, p.biases, ob, K, 4, gs, "f16")
+    y = y_host(mxq.mxq_linear(x, w, s, b, obd, bits=4, group_size=gs))
+    assert_close(y, ref, "qsmk long K with bias")
+    yg = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        mxq.mxq_linear(x, w, s, b, obd, y=yg, bits=4, group_size=gs)
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mxq.mxq_linear(x, w, s, b, obd, y=yg, bits=4, group_size=gs)
+    torch.cuda.synchronize()
+    first = None
+    for _ in range(3):
+        yg.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        got = yg.cpu().numpy()
+        assert_close(got, ref, "qsmk long K captured")
+        if first is None:
+            first = got.copy()
+        assert np.array_equal(got.view(np.uint16), first.view(np.uint16))
+
+
 @pytest.mark.parametrize("regime", ["big", "tiny"])
 @pytest.mark.parametrize("sb", ["f16", "bf16"])
 @pytest.mark.parametrize("shape", [(1, 4104, 2048, 64), (1, 2050, 8192, 128), (4, 1030, 2048, 64), (2, 514, 4096, 64)])
@@ -842,7 +908,10 @@ def test_few_rows_ksplit_routing():
     assert not d("qmv", 8, 128256, 2048, 4, 32, "f16").startswith("qsmk")   # group size 32
     assert d("qmv", 8, 128256, 1536, 4, 64, "f16").startswith("qsmk_kernel<bits=4,sb=f16,gs=64,m=8,waves=3>")
     assert not d("qmv", 8, 128256, 2112, 4, 64, "f16").startswith("qsmk")   # K not a multiple of 512
-    assert not d("qmv", 8, 128256, 8192, 4, 64, "f16").startswith("qsmk")   # K > 4096
+    assert d("qmv", 8, 128256, 8192, 4, 64, "f16").startswith("qsmk_kernel<bits=4,sb=f16,gs=64,m=8,waves=8,kchunks=2>")
+    assert d("a8", 8, 128256, 8192, 4, 64, "f16").startswith("qmv_kernel")       # int8 x: one row scale over all K
+    assert not d("qmv", 3, 128257, 8192, 4, 64, "f16").startswith("qsmk")   # chunks need M * N % 4 == 0
+    assert not d("qmv", 8, 1023, 8192, 4, 64, "f16").startswith("qsmk")     # 64 x 2 blocks: too few
     assert not d("qmv", 8, 2048, 2048, 4, 64, "f16").startswith("qsmk")     # too few W rows per CU
 
 
