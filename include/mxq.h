@@ -87,8 +87,12 @@ int mxq_abi_version(void);
  * ever leaving registers.  Accepts any M >= 0.  Routing by shape: one row
  * (and two at K > 2048) on the decode kernel; up to 16 rows on the matrix
  * cores when the shape fits them -- 4- or 8-bit codes, group size 64 or 128,
- * K a multiple of 512 up to 4096 and at least 16 rows of W per compute unit (from 3
- * rows, or 2 at K <= 2048), else 9..16 rows of any supported codes with at
+ * K a multiple of 512 and at least 16 rows of W per compute unit (from 3
+ * rows, or 2 at K <= 2048); K beyond 4096 runs in chunks of up to 4096 codes
+ * whose f32 partial results are added in a fixed order by a second kernel
+ * (M * N a multiple of 4, counting the chunks toward the rows of W per
+ * compute unit; calls on a stream being captured into a graph use the other
+ * kernels instead), else 9..16 rows of any supported codes with at
  * least 256 rows of W per compute unit -- both with x (and for the first, the
  * scales and biases) 16-byte aligned; otherwise the decode kernel in slices
  * of at most 8 rows (each slice re-reads W).  N need not be a multiple of
@@ -187,7 +191,8 @@ mxq_status mxq_linear_act(const void* x, const uint32_t* w, const void* scales, 
  * or 8-bit codes in exact integer arithmetic -- by v_dot4_i32_i8 (four
  * products per instruction) in the decode kernel, or, for 3..16 rows of
  * 4- or 8-bit codes on the shapes the K-split few-row kernel takes (group 64 or 128,
- * K a multiple of 512 up to 4096, at least 16 rows of W per compute unit, x, scales and
+ * K a multiple of 512 up to 4096 (int8 activations are not chunked: one row
+ * scale covers all of K), at least 16 rows of W per compute unit, x, scales and
  * biases 16-byte aligned), by v_mfma_i32_16x16x64_i8 (one 64-code group per
  * instruction) -- the "quantized dot lowered to the hardware's int8 path"
  * route of mlxcel #574 ("Upstream status refresh", "Next actionable step").
