@@ -208,7 +208,10 @@ __global__ __launch_bounds__(256) void qsm_kernel(const uint16_t* __restrict__ x
 // qsmk: the same contraction with K split over the waves of a workgroup.
 //
 // Wave w of a workgroup owns codes [512 w, 512 w + 512) of every row (K =
-// 512 * waves, 1 to 8 waves).  Its activation fragments for that slice
+// 512 * waves, 1 to 8 waves).  Longer K runs in chunks of 512 * waves codes,
+// chunk c as grid row c (codes offset by 512 * waves * c), each writing its
+// f32 partial tile [c][m][n] for a fixed-order reduction kernel to add.  Its
+// activation fragments for that slice
 // (16 rows x 512 codes, rows at or past M zero) and their per-group sums stay
 // in registers for the whole kernel.  The workgroup walks blocks of 16 W rows
 // with a grid stride; for each block a wave
