@@ -61,7 +61,10 @@ mxq_status hip_fail(const char* who, hipError_t e) {
 }
 
 // Row counts the K-split few-row kernel takes (its shape test aside).
-bool qsmk_rows(int64_t M, int64_t K) { return M >= 3 || (M == 2 && K <= 2048); }
+// Two rows: the K-split kernel up to K = 3072 (N = 65536: 24.5 against 32.7
+// us); at K = 4096 the two kernels trade places with N, and in K chunks the
+// decode kernel ties or wins.
+bool qsmk_rows(int64_t M, int64_t K) { return M >= 3 || (M == 2 && K <= 3072); }
 
 // Whether the K-split kernel may run K in chunks on this stream: they need the
 // cached split workspace, which a stream being captured into a graph must not

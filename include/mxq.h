@@ -88,7 +88,7 @@ int mxq_abi_version(void);
  * (and two at K > 2048) on the decode kernel; up to 16 rows on the matrix
  * cores when the shape fits them -- 4- or 8-bit codes, group size 64 or 128,
  * K a multiple of 512 and at least 16 rows of W per compute unit (from 3
- * rows, or 2 at K <= 2048); K beyond 4096 runs in chunks of up to 4096 codes
+ * rows, or 2 at K <= 3072); K beyond 4096 runs in chunks of up to 4096 codes
  * whose f32 partial results are added in a fixed order by a second kernel
  * (M * N a multiple of 4, counting the chunks toward the rows of W per
  * compute unit; calls on a stream being captured into a graph use the other

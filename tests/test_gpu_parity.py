@@ -745,7 +745,7 @@ QSMK = [
     (2, 128256, 2048, 64, "f16"), (3, 4100, 512, 64, "bf16"), (5, 8192, 1024, 128, "f16"),
     (8, 8192, 2048, 64, "bf16"), (16, 16390, 4096, 64, "f16"), (11, 65537, 4096, 128, "bf16"),
     (16, 128256, 2048, 64, "f16"), (4, 4111, 4096, 64, "f16"), (6, 8192, 3072, 64, "bf16"),
-    (9, 4300, 2560, 128, "f16"), (3, 8192, 3584, 64, "f16"),
+    (9, 4300, 2560, 128, "f16"), (3, 8192, 3584, 64, "f16"), (2, 8200, 3072, 64, "f16"), (2, 4100, 2560, 128, "bf16"),
 ]
 
 
@@ -897,7 +897,8 @@ def test_few_rows_ksplit_routing():
     assert d("a8", 2, 8192, 2048, 4, 64, "f16").startswith("qmv_kernel")       # two int8 rows: decode kernel
     assert d("a8", 12, 8192, 2048, 8, 64, "f16").startswith("qsmk_kernel<bits=8,sb=f16,gs=64,m=12,waves=4,act=i8>")
     assert d("qmv", 2, 8192, 2048, 4, 64, "f16").startswith("qsmk")
-    assert not d("qmv", 2, 16384, 4096, 4, 64, "f16").startswith("qsmk")   # two rows at K > 2048: decode kernel
+    assert not d("qmv", 2, 16384, 4096, 4, 64, "f16").startswith("qsmk")   # two rows at K > 3072: decode kernel
+    assert d("qmv", 2, 65536, 3072, 4, 64, "f16").startswith("qsmk_kernel<bits=4,sb=f16,gs=64,m=2,waves=6>")
     assert d("qmv", 3, 16384, 4096, 4, 64, "f16").startswith("qsmk")
     assert not d("qmv", 1, 128256, 2048, 4, 64, "f16").startswith("qsmk")
     assert not d("qmv", 17, 128256, 2048, 4, 64, "f16").startswith("qsmk")
