@@ -754,7 +754,7 @@ QSMK = [
 QSMK8 = [
     (2, 8192, 2048, 64, "f16"), (4, 4100, 1536, 64, "bf16"), (10, 66000, 1024, 64, "bf16"),
     (13, 70001, 512, 64, "bf16"), (12, 65540, 4096, 128, "f16"), (16, 128256, 2048, 64, "f16"),
-    (7, 8192, 4096, 64, "f16"), (5, 8192, 3584, 128, "f16"), (3, 4100, 2560, 64, "bf16"),
+    (7, 8192, 4096, 64, "f16"), (5, 8192, 3584, 128, "f16"), (3, 4100, 2560, 64, "bf16"), (2, 8196, 3072, 64, "f16"),
 ]
 
 
