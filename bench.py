@@ -242,6 +242,13 @@ def qmm_pass():
     import synth
     mxq.load()
     dev = "cuda:0"
+    # calibration: a copy of known size, as in the decode kernel's traffic pass
+    src = torch.randint(0, 1 << 30, (COPY_BYTES // 4,), dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
     for N, K in ((8192, 2048), (2048, 8192)):
         p = synth.make_problem(512, N, K, 4, 64, "f16", seed=3)
         x = torch.from_numpy(p.x).to(dev)
@@ -294,40 +301,230 @@ def write_traffic(fetch_csv: str, write_csv: str, meta_json: str):
     print(json.dumps(out))
 
 
-def cpu_baseline(synth, budget_s=12.0):
-    """The f64 oracle on a bounded sample, one BLAS thread: GB/s of algorithmic bytes."""
+POOL_BYTES = 1536 << 20  # rotation pool of the read probe: > the 256 MiB Infinity Cache
+
+
+def probe_curve(torch, lib, sizes, reps=40):
+    """Our own read kernel (mxq_read_probe, the decode kernel's load form) at
+    each size in bytes, reading from offsets that rotate through a 1.5 GiB pool
+    so the data comes from HBM: {size: {"GB/s": back-to-back, "bracketed_GB/s":
+    an event pair per launch, "us": ...}}."""
+    import ctypes
+    pool = torch.empty(POOL_BYTES, dtype=torch.uint8, device="cuda:0")
+    pool.fill_(1)
+    out = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    st = cur_stream(torch)
+    base = pool.data_ptr()
+    res = {}
+    for size in sizes:
+        size16 = (int(size) + 15) // 16 * 16
+        step = (size16 + 4095) // 4096 * 4096
+        nslots = max(1, (POOL_BYTES - size16) // step)
+
+        def launch(r):
+            off = (r % nslots) * step
+            stt = lib.mxq_read_probe(ctypes.c_void_p(base + off), size16, ctypes.c_void_p(out.data_ptr()), st)
+            if stt != 0:
+                raise RuntimeError(f"read probe: libmxq status {stt}")
+        for r in range(8):
+            launch(r)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for r in range(reps):
+            launch(r)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        pairs = []
+        for r in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            launch(r + reps)
+            b.record()
+            pairs.append((a, b))
+        torch.cuda.synchronize()
+        import statistics
+        bms = statistics.median(a.elapsed_time(b) for a, b in pairs)
+        res[int(size)] = {"us": round(ms * 1e3, 2), "GB/s": round(size16 / (ms / 1e3) / 1e9, 1),
+                          "bracketed_us": round(bms * 1e3, 2),
+                          "bracketed_GB/s": round(size16 / (bms / 1e3) / 1e9, 1)}
+    del pool, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def rotating_launch_time(torch, make_launch, nrep, reps=30):
+    """Back-to-back time (ms) per launch of make_launch(i) over i = 0, 1, ...
+    (the callable picks replica i % nrep), and the median with an event pair
+    around each launch."""
+    import statistics
+    for i in range(min(nrep, 6)):
+        make_launch(i)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        make_launch(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    pairs = []
+    for i in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        make_launch(i + reps)
+        b.record()
+        pairs.append((a, b))
+    torch.cuda.synchronize()
+    return ms, statistics.median(a.elapsed_time(b) for a, b in pairs)
+
+
+def config_legs(torch, lib, synth, dev):
+    """The small single problem (M=1, N=512, K=2048, 4-bit g64, f16, seed 0)
+    and the 48-case edge sweep (M in {1,2,4,8}, K=8192, N in {2048,1023,2050},
+    4/8-bit, f16/bf16 scales) through mxq_qmv and mxq_qmm: GB/s per launch,
+    weights replicated on the device (identical copies at distinct addresses)
+    so that each leg streams at least 512 MB and the data comes from HBM."""
     import numpy as np
+
+    def dev_problem(p, reps_min_bytes=512 << 20):
+        sbt = torch.float16 if p.sb_dtype == "f16" else torch.bfloat16
+        w = torch.from_numpy(p.w.view(np.int32)).to(dev)
+        s = torch.from_numpy(p.scales.view(np.int16)).view(sbt).to(dev)
+        b = torch.from_numpy(p.biases.view(np.int16)).view(sbt).to(dev)
+        x = torch.from_numpy(p.x).to(dev)
+        y = torch.empty((p.M, p.N), dtype=torch.float16, device=dev)
+        per = w.numel() * 4 + s.numel() * 4
+        nrep = max(2, -(-reps_min_bytes // per))
+        reps = [(w, s, b)] + [(w.clone(), s.clone(), b.clone()) for _ in range(nrep - 1)]
+        return x, y, reps
+
+    def leg(fn_name, p, x, y, reps):
+        fn = getattr(lib, fn_name)
+        sb = 0 if p.sb_dtype == "f16" else 1
+        st = cur_stream(torch)
+
+        def launch(i):
+            w, s, b = reps[i % len(reps)]
+            r = fn(x.data_ptr(), w.data_ptr(), s.data_ptr(), b.data_ptr(), y.data_ptr(), p.M, p.N, p.K, p.bits,
+                   p.group_size, sb, st)
+            if r != 0:
+                raise RuntimeError(f"{fn_name} M={p.M} N={p.N}: libmxq status {r}")
+        ms, bms = rotating_launch_time(torch, launch, len(reps))
+        nb = call_bytes(p.M, p.N, p.K, p.bits, p.group_size)
+        return {"us": round(ms * 1e3, 2), "GB/s": round(nb / (ms / 1e3) / 1e9, 1),
+                "bracketed_GB/s": round(nb / (bms / 1e3) / 1e9, 1)}
+
+    out = {}
+    p = synth.small_qmv_problem()
+    x, y, reps = dev_problem(p)
+    out["small_qmv_M1_N512_K2048"] = dict(leg("mxq_qmv", p, x, y, reps), bytes=call_bytes(1, 512, 2048),
+                                          note="latency-bound: 0.59 MB moves in 74 ns at 8 TB/s")
+    del reps
+    sweep = {}
+    for case in synth.edge_cases():
+        p = synth.make_problem(**case)
+        x, y, reps = dev_problem(p, 256 << 20)
+        key = f"M{p.M}_N{p.N}_b{p.bits}_{p.sb_dtype}"
+        sweep[key] = {"qmv": leg("mxq_qmv", p, x, y, reps)["GB/s"], "qmm": leg("mxq_qmm", p, x, y, reps)["GB/s"]}
+        del reps
+    torch.cuda.empty_cache()
+    vals = [v[e] for v in sweep.values() for e in ("qmv", "qmm")]
+    out["edge_sweep_K8192"] = {"GB/s": sweep, "median_GB/s": round(float(np.median(vals)), 1),
+                               "min_GB/s": min(vals), "max_GB/s": max(vals),
+                               "timing": "30 launches back to back per entry, replicated weights (>= 256 MB)"}
+    return out
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(synth, reps=5):
+    """The f64 oracle on a bounded sample, timed on the host's cores.
+
+    Sample: layer-0 q,k,v,o + lm_head rows 0..4095 (M=1, 4-bit g64, f16
+    scales).  Two legs: all available cores (numpy's BLAS with its default
+    thread count; unpack and dequant are single-threaded numpy) and one core
+    (affinity pinned to one CPU, one BLAS thread).  Each leg times the whole
+    oracle (oracle.matmul_ref: unpack, dequant, matmul) and its two phases
+    apart (oracle.dequant_f64; the f64 product of oracle.widen_act(x) with the
+    dequantized weights, as matmul_ref computes it) over the sample, median
+    of `reps` passes after one warm-up.  value = algorithmic bytes of the
+    sample / the whole oracle's time, all cores."""
+    import statistics
     import oracle
     try:
-        from threadpoolctl import threadpool_limits
+        from threadpoolctl import threadpool_info, threadpool_limits
     except ImportError:  # pragma: no cover
-        threadpool_limits = None
-    shapes = list(synth.LLAMA_1B_PROJ) + [("lm_head[0:8016]", 8016, 2048)]
+        threadpool_info = threadpool_limits = None
+    shapes = list(synth.LLAMA_1B_PROJ[:4]) + [("lm_head[0:4096]", 4096, 2048)]
     probs = []
     for idx, (name, N, K) in enumerate(shapes):
         w, s, b = synth.make_weights(N, K, 4, 64, "f16", seed=synth.proj_seed(1, 0, idx))
         x = synth.make_x(1, K, seed=synth.proj_seed(1, 0, idx) + 500)
         probs.append((x, w, s, b, N, K))
-    ctx = threadpool_limits(limits=1) if threadpool_limits else None
-    if ctx:
-        ctx.__enter__()
-    try:
-        done_bytes, t0, passes = 0, time.perf_counter(), 0
-        while True:
-            for x, w, s, b, N, K in probs:
-                oracle.matmul_ref(x, w, s, b, K, 4, 64, "f16")
-                done_bytes += call_bytes(1, N, K)
-            passes += 1
-            el = time.perf_counter() - t0
-            if el >= budget_s or passes >= 20:
-                break
-    finally:
+    sample_bytes = sum(call_bytes(1, N, K) for *_, N, K in probs)
+
+    def one_pass(fn):
+        t0 = time.perf_counter()
+        for x, w, s, b, N, K in probs:
+            fn(x, w, s, b, K)
+        return time.perf_counter() - t0
+
+    wdq = [oracle.dequant_f64(w, s, b, K, 4, 64, "f16") for x, w, s, b, N, K in probs]
+
+    def mm_pass():
+        t0 = time.perf_counter()
+        for (x, *_), w in zip(probs, wdq):
+            oracle.widen_act(x) @ w.T
+        return time.perf_counter() - t0
+
+    def leg(blas_threads):
+        whole = lambda x, w, s, b, K: oracle.matmul_ref(x, w, s, b, K, 4, 64, "f16")  # noqa: E731
+        dq = lambda x, w, s, b, K: oracle.dequant_f64(w, s, b, K, 4, 64, "f16")  # noqa: E731
+        ctx = threadpool_limits(limits=blas_threads) if threadpool_limits else None
         if ctx:
-            ctx.__exit__(None, None, None)
-    return {"value": round(done_bytes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{passes} pass(es) over layer-0 q,k,v,o,gate,up,down + lm_head rows 0..8015 "
-                      f"(M=1, 4-bit g64, f16 scales), f64 numpy oracle, 1 BLAS thread, "
-                      f"{el:.1f} s"}
+            ctx.__enter__()
+        try:
+            one_pass(whole)
+            t_whole = statistics.median(one_pass(whole) for _ in range(reps))
+            t_dq = statistics.median(one_pass(dq) for _ in range(reps))
+            mm_pass()
+            t_mm = statistics.median(mm_pass() for _ in range(reps))
+        finally:
+            if ctx:
+                ctx.__exit__(None, None, None)
+        return {"GB/s": round(sample_bytes / t_whole / 1e9, 4), "ms_per_pass": round(t_whole * 1e3, 1),
+                "unpack_dequant_ms": round(t_dq * 1e3, 1), "matmul_ms": round(t_mm * 1e3, 2)}
+
+    cpus = sorted(os.sched_getaffinity(0))
+    blas = None
+    if threadpool_info:
+        blas = [{"api": i.get("internal_api"), "threads": i.get("num_threads")} for i in threadpool_info()]
+    t0 = time.perf_counter()
+    all_cores = leg(None)
+    os.sched_setaffinity(0, {cpus[0]})
+    try:
+        one_core = leg(1)
+    finally:
+        os.sched_setaffinity(0, set(cpus))
+    el = time.perf_counter() - t0
+    blas_threads = max((b["threads"] or 1 for b in blas), default=1) if blas else None
+    return {"value": all_cores["GB/s"], "unit": "GB/s", "cores": blas_threads or len(cpus), "kind": "oracle",
+            "sample": f"layer-0 q,k,v,o + lm_head rows 0..4095 (M=1, 4-bit g64, f16 scales; "
+                      f"{sample_bytes} algorithmic bytes per pass), f64 numpy oracle, median of {reps} passes "
+                      f"after one warm-up per leg, {el:.1f} s in all",
+            "host": {"cpu_model": _cpu_model(), "cpus_available": len(cpus), "blas": blas},
+            "all_cores": dict(all_cores, blas_threads=blas_threads),
+            "one_core": dict(one_core, blas_threads=1, pinned_cpu=cpus[0])}
 
 
 def main():
@@ -453,7 +650,8 @@ def main():
         d["launches"] += 1
         name = "+".join(q.name for q in probs)
         d["names"].append(name)
-        per_launch[name] = {"us": round(ms * 1e3, 2), "GB/s": round(c.bytes / (ms / 1e3) / 1e9, 1)}
+        per_launch[name] = {"us": round(ms * 1e3, 2), "GB/s": round(c.bytes / (ms / 1e3) / 1e9, 1),
+                            "bytes": c.bytes}
     dom_desc, dom = max(by_kernel.items(), key=lambda kv: kv[1]["ms"])
     bracketed_ms = dom["ms"] / dom["launches"]
     avg_bytes = dom["bytes"] / dom["launches"]
@@ -503,8 +701,31 @@ def main():
     del sets, plans, fns, step_fns, graphs, head_launches
     torch.cuda.empty_cache()
 
+    # ---------------- our own read kernel at the same sizes -----------------
+    # (a fused launch is judged against what a plain read of the same bytes
+    # attains: small reads cannot reach the HBM peak however they are done)
+    log("read probe ...")
+    launch_sizes = {name: int(v["bytes"]) for name, v in per_launch.items()}
+    curve_sizes = sorted(set(launch_sizes.values()) | {1 << 20, 4 << 20, 16 << 20, 64 << 20, 512 << 20})
+    curve = probe_curve(torch, lib, curve_sizes)
+    for name, v in per_launch.items():
+        pr = curve[launch_sizes[name]]
+        v["probe_bracketed_GB/s"] = pr["bracketed_GB/s"]
+        v["frac_of_probe"] = round(v["GB/s"] / pr["bracketed_GB/s"], 3)
+    dom_probe = curve[int(avg_bytes)] if int(avg_bytes) in curve else None
+    if dom_probe:
+        roofline["probe_GB/s_same_size"] = dom_probe["GB/s"]
+        roofline["frac_of_probe"] = round(achieved / dom_probe["GB/s"], 3)
+    result["read_probe"] = {"kernel": "mxq_read_probe (16-byte non-temporal loads, 2 workgroups of 256 per CU)",
+                            "timing": "40 launches back to back (GB/s) and an event pair per launch "
+                                      "(bracketed), offsets rotating through a 1.5 GiB pool",
+                            "curve": {str(k): v for k, v in curve.items()}}
+
     # ---------------- extras ------------------------------------------------
     if not args.no_extras:
+        log("small problem and edge sweep ...")
+        result["configs"] = config_legs(torch, lib, synth, dev)
+
         log("decode step (16 layers + lm_head) ...")
         layers = []
         for layer in range(synth.LLAMA_1B_LAYERS):

@@ -5,7 +5,9 @@ The public calls mirror the C ABI of libmxq.so (``include/mxq.h``):
 launch), ``mxq_qmm`` (prefill), ``mxq_linear`` (either, plus an output bias),
 ``mxq_linear_act`` (the same for float16 or bfloat16 activations),
 ``mxq_linear_a8`` (int8 activations, quantized per row in the kernel),
-``mxq_dequant`` (bit-exact standalone dequant) and ``mxq_pack`` (host packer).
+``mxq_dequant`` (bit-exact standalone dequant) and ``mxq_pack`` (host packer),
+plus diagnostics (``mxq_describe``, ``mxq_describe_grouped``) and the split
+workspace controls (``mxq_release_workspaces``, ``mxq_workspace_bytes``).
 """
 
 from ._lib import (  # noqa: F401
@@ -21,6 +23,7 @@ from ._lib import (  # noqa: F401
     load,
     mxq_dequant,
     mxq_describe,
+    mxq_describe_grouped,
     mxq_linear,
     mxq_linear_a8,
     mxq_linear_act,
@@ -28,5 +31,7 @@ from ._lib import (  # noqa: F401
     mxq_qmm,
     mxq_qmv,
     mxq_qmv_grouped,
+    mxq_release_workspaces,
+    mxq_workspace_bytes,
     QmvProblem,
 )

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(HERE, "libmxq.so")
 
 MXQ_OK, MXQ_ERR_INVALID_ARG, MXQ_ERR_UNSUPPORTED, MXQ_ERR_MISALIGNED, MXQ_ERR_HIP = range(5)
 MXQ_F16, MXQ_BF16, MXQ_F32 = 0, 1, 2
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 _lock = threading.Lock()
 _lib = None
@@ -64,6 +64,11 @@ def _declare(lib):
     lib.mxq_pack.restype = c_int
     lib.mxq_describe.argtypes = [ctypes.c_char_p, c_i64, c_i64, c_i64, c_int, c_int, c_int]
     lib.mxq_describe.restype = ctypes.c_char_p
+    lib.mxq_describe_grouped.argtypes = [ctypes.POINTER(QmvProblem), c_int, c_i64, c_int, c_int, c_int]
+    lib.mxq_describe_grouped.restype = ctypes.c_char_p
+    lib.mxq_release_workspaces.argtypes, lib.mxq_release_workspaces.restype = [], c_int
+    lib.mxq_read_probe.argtypes, lib.mxq_read_probe.restype = [vp, c_i64, vp, vp], c_int
+    lib.mxq_workspace_bytes.argtypes, lib.mxq_workspace_bytes.restype = [], c_i64
     lib.mxq_status_str.argtypes, lib.mxq_status_str.restype = [c_int], ctypes.c_char_p
     lib.mxq_last_error.argtypes, lib.mxq_last_error.restype = [], ctypes.c_char_p
     lib.mxq_abi_version.argtypes, lib.mxq_abi_version.restype = [], c_int
@@ -307,6 +312,25 @@ def mxq_describe(op: str, M: int, N: int, K: int, bits: int = 4, group_size: int
     lib = load()
     sb = {"f16": MXQ_F16, "bf16": MXQ_BF16}[sb_dtype]
     return lib.mxq_describe(op.encode(), M, N, K, bits, group_size, sb).decode()
+
+
+def mxq_describe_grouped(shapes, M: int, bits: int = 4, group_size: int = 64, sb_dtype: str = "f16") -> str:
+    """Launches mxq_qmv_grouped would make for problems of these (N, K) shapes."""
+    lib = load()
+    sb = {"f16": MXQ_F16, "bf16": MXQ_BF16}[sb_dtype]
+    arr = (QmvProblem * len(shapes))(*[QmvProblem(None, None, None, None, None, N, K) for N, K in shapes])
+    return lib.mxq_describe_grouped(arr, len(shapes), M, bits, group_size, sb).decode()
+
+
+def mxq_release_workspaces() -> None:
+    """Free the cached split workspaces (waits for enqueued work first)."""
+    lib = load()
+    _check(lib, lib.mxq_release_workspaces())
+
+
+def mxq_workspace_bytes() -> int:
+    """Bytes of split workspace cached for the current device."""
+    return int(load().mxq_workspace_bytes())
 
 
 def mxq_pack(codes, bits: int = 4) -> np.ndarray:

@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmxq.so")
-SOURCES = ["api.cpp", "qmv.hip", "qmm.hip", "qsm.hip", "dequant.hip"]
+SOURCES = ["api.cpp", "workspace.cpp", "qmv.hip", "qmm.hip", "qsm.hip", "dequant.hip", "probe.hip"]
 ARCH = "gfx950"
 
 

@@ -104,15 +104,18 @@ mxq_status run_qmv(const char* who, const void* x, const uint32_t* w, const void
   a.rows_per_wave = 0;
   a.stream = static_cast<hipStream_t>(stream);
   // A few rows of f16 activations go to the matrix cores when the shape fills
-  // the GPU: the K-split kernel (4-bit codes) from 3 rows, or from 2 when K <=
-  // 2048 (where the decode kernel's two-row variant is slower; measured), else
-  // the 16-row-block kernel for 9..16 rows (one launch instead of two 8-row
-  // decode launches).  Both read x, and the K-split kernel the scales and
-  // biases, with 16-byte loads.
+  // the GPU (qsmk_shape): the K-split kernel for 4- or 8-bit codes, group 64
+  // or 128, K a multiple of 512 (in chunks beyond 4096), from 3 rows, or from
+  // 2 when K <= 3072 (qsmk_rows: there the decode kernel's two-row variant is
+  // slower; measured); else the 16-row-block kernel for 9..16 rows (one
+  // launch instead of two 8-row decode launches).  Both read x, and the
+  // K-split kernel the scales and biases, with 16-byte loads.
   // int8 activations take the K-split kernel's integer-MFMA variant from 3
-  // rows (the decode kernel's v_dot4 path is VALU-bound beyond a row or two;
-  // at two rows it is still faster than the kernel's per-row quantization of
-  // x in every workgroup; measured on lm_head: 28.3 against 31.2 us).
+  // rows, unchunked (K <= 4096: one row scale covers all of K); the decode
+  // kernel's v_dot4 path is VALU-bound beyond a row or two, and at two rows it
+  // is still faster than the kernel's per-row quantization of x in every
+  // workgroup (measured on lm_head: 28.3 against 31.2 us).  If the K-chunk
+  // workspace cannot be had, the call falls through to the kernels below.
   const bool few_i8 = act == kActI8 && M >= 3;
   if ((act == kActF16 ? qsmk_rows(M, K) : few_i8) && aligned(x, 16) && aligned(scales, 16) &&
       aligned(biases, 16) &&
@@ -121,7 +124,8 @@ mxq_status run_qmv(const char* who, const void* x, const uint32_t* w, const void
     a.y = static_cast<uint16_t*>(y);
     a.x_vec = 1;
     e = mxq::launch_qsmk(a, static_cast<int>(M), dev);
-    return e == hipSuccess ? MXQ_OK : hip_fail(who, e);
+    if (e != hipErrorOutOfMemory) return e == hipSuccess ? MXQ_OK : hip_fail(who, e);
+    (void)hipGetLastError();  // no workspace for the K chunks: nothing was enqueued
   }
   if (act == kActF16 && aligned(x, 16) && mxq::qsm_shape(M, N, K, bits, group_size, dev)) {
     a.x = static_cast<const uint16_t*>(x);
@@ -183,10 +187,10 @@ mxq_status run_matmul(const char* who, const void* x, const uint32_t* w, const v
                                          static_cast<hipStream_t>(stream));
     return e == hipSuccess ? MXQ_OK : hip_fail(who, e);
   }
-  // The MFMA kernel stages x with 16-byte loads and walks K in stages of 64;
-  // int8 activations run on the decode kernel's v_dot4 path at every M, and
-  // up to 16 rows of f16 activations on the K-split few-row kernel where it
-  // applies (run_qmv routes them).
+  // The MFMA kernel stages x with 16-byte loads and walks K in stages of 64.
+  // int8 activations and the few-row shapes of f16 activations (qsmk_rows and
+  // qsmk_shape) take run_qmv's routing: the K-split matrix-core kernel where
+  // it applies, else the decode kernel in 8-row slices.
   mxq::DeviceInfo dev;
   hipError_t e = mxq::device_info(&dev);
   if (e != hipSuccess) return hip_fail(who, e);
@@ -459,6 +463,88 @@ const char* mxq_describe(const char* op, int64_t M, int64_t N, int64_t K, int bi
             ",rows=" + std::to_string(p.rows) + (p.xdirect ? ",xreg" : "") + (a8 ? ",act=i8" : "") +
             "> grid=" + std::to_string(p.grid) +
             " block=256 lds=" + std::to_string(p.lds);
+  }
+  return desc.c_str();
+}
+
+mxq_status mxq_read_probe(const void* buf, int64_t bytes, void* out, void* stream) {
+  g_last_error.clear();
+  if (bytes < 0 || bytes % 16 != 0)
+    return fail(MXQ_ERR_INVALID_ARG, "mxq_read_probe: bytes must be a non-negative multiple of 16");
+  if (bytes == 0) return MXQ_OK;
+  if (!buf || !out) return fail(MXQ_ERR_INVALID_ARG, "mxq_read_probe: null pointer");
+  if (!aligned(buf, 16) || !aligned(out, 4))
+    return fail(MXQ_ERR_MISALIGNED, "mxq_read_probe: buf must be 16-byte and out 4-byte aligned");
+  mxq::DeviceInfo dev;
+  hipError_t e = mxq::device_info(&dev);
+  if (e != hipSuccess) return hip_fail("mxq_read_probe", e);
+  e = mxq::launch_read_probe(buf, bytes, static_cast<uint32_t*>(out), static_cast<hipStream_t>(stream), dev);
+  return e == hipSuccess ? MXQ_OK : hip_fail("mxq_read_probe", e);
+}
+
+mxq_status mxq_release_workspaces(void) {
+  g_last_error.clear();
+  (void)mxq::split_workspace_release_all();
+  return MXQ_OK;
+}
+
+int64_t mxq_workspace_bytes(void) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return static_cast<int64_t>(mxq::split_workspace_cached_bytes(dev));
+}
+
+const char* mxq_describe_grouped(const mxq_qmv_problem* problems, int count, int64_t M, int bits,
+                                 int group_size, mxq_dtype sb_dtype) {
+  thread_local std::string desc;
+  if (count <= 0 || !problems || M <= 0 || (bits != 4 && bits != 8) || log2_group(group_size) < 0 ||
+      (sb_dtype != MXQ_F16 && sb_dtype != MXQ_BF16)) {
+    desc = "invalid";
+    return desc.c_str();
+  }
+  // the problems mxq_qmv_grouped launches: N > 0 and K > 0 (K = 0 is a fill)
+  std::vector<int64_t> Ns, Ks;
+  for (int i = 0; i < count; ++i) {
+    const mxq_qmv_problem& q = problems[i];
+    if (q.N < 0 || q.K < 0 || q.K % group_size != 0) {
+      desc = "invalid";
+      return desc.c_str();
+    }
+    if (q.N > 0 && q.K > 0) {
+      Ns.push_back(q.N);
+      Ks.push_back(q.K);
+    }
+  }
+  if (Ns.empty()) {
+    desc = "none";
+    return desc.c_str();
+  }
+  mxq::DeviceInfo dev;
+  if (mxq::device_info(&dev) != hipSuccess) {
+    desc = "no device";
+    return desc.c_str();
+  }
+  int64_t kmax = 0;
+  for (int64_t k : Ks) kmax = k > kmax ? k : kmax;
+  int mt_max = 8;
+  while (mt_max > 1 && mxq::qmv_lds_need(bits, mt_max, kmax) > dev.lds_per_block) mt_max--;
+  const char* sb = sb_dtype == MXQ_BF16 ? "bf16" : "f16";
+  desc.clear();
+  const int n = static_cast<int>(Ns.size());
+  for (int64_t m0 = 0; m0 < M; m0 += mt_max) {
+    const int mt = static_cast<int>((M - m0) < mt_max ? (M - m0) : mt_max);
+    for (int c0 = 0; c0 < n; c0 += mxq::kMaxGroup) {
+      const int cnt = (n - c0) < mxq::kMaxGroup ? (n - c0) : mxq::kMaxGroup;
+      const mxq::QmvPlan p = mxq::qmv_plan_group(dev, Ns.data() + c0, Ks.data() + c0, cnt, bits,
+                                                 sb_dtype == MXQ_BF16, kActF16, mt, nullptr);
+      if (!desc.empty()) desc += "; ";
+      desc += "qmv_kernel<bits=" + std::to_string(bits) + ",sb=" + sb + ",mt=" + std::to_string(mt) +
+              ",rows=" + std::to_string(p.rows) + (p.xdirect ? ",xreg" : "") + "> problems=" +
+              std::to_string(cnt) + " grid=" + std::to_string(p.grid) + " block=256 lds=" + std::to_string(p.lds);
+    }
   }
   return desc.c_str();
 }

@@ -117,12 +117,17 @@ bool qsmk_shape(int64_t M, int64_t N, int64_t K, int bits, int group_size, bool 
 size_t qsmk_lds_bytes(int waves, int bits);
 hipError_t launch_qsmk(const QmvArgs& a, int M, const DeviceInfo& dev);
 
-// The split-K workspace cache of the prefill kernel (one f32 buffer per device
-// and stream, grown on demand) and its fixed-order reduction, shared with the
-// few-row kernel's K chunks.  Hold split_workspace_mutex() from the call of
-// split_workspace_locked() until the kernels that use the buffer are enqueued.
+// The split workspace cache (workspace.cpp): one f32 buffer per device and
+// stream, grown on demand, at most kWorkspaceEntries streams per device (the
+// least recently used is released first), shared by the prefill kernel's K
+// splits and the few-row kernel's K chunks.  Hold split_workspace_mutex() from
+// the call of split_workspace_locked() until the kernels that use the buffer
+// are enqueued.  split_workspace_locked returns null if no memory could be had.
+constexpr int kWorkspaceEntries = 4;
 std::mutex& split_workspace_mutex();
 float* split_workspace_locked(int device, hipStream_t stream, size_t bytes);
+size_t split_workspace_cached_bytes(int device);  // takes the mutex
+int split_workspace_release_all();                // takes the mutex; returns the buffers freed
 // y[M, N] (f16) = RNE(sum over splits of part[split] in split order + out_bias);
 // M * N a multiple of 4, part 16-byte aligned.
 hipError_t launch_split_reduce_f16(const float* part, const uint16_t* ob, uint16_t* y, int64_t M, int64_t N,
@@ -156,6 +161,11 @@ QmmTile qmm_pick_tile(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev);
 // multiple of its 64-code stage, and K < 2^24 so that every per-lane offset
 // within a tile (at most 128 rows of x, W, scales) fits in 32 bits.
 inline bool qmm_mfma_shape(int64_t M, int64_t K) { return M > 8 && K % 64 == 0 && K < (int64_t{1} << 24); }
+
+// Read probe (probe.hip): streams `bytes` (a multiple of 16) from a 16-byte
+// aligned buffer; out receives 4 bytes at most.
+hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* out, hipStream_t stream,
+                             const DeviceInfo& dev);
 
 struct DequantArgs {
   const uint32_t* w;

@@ -37,7 +37,6 @@
 // tiles on one XCD (dispatch is round-robin over the 8 XCDs) share a slice
 // of W, for L2 reuse.
 #include <cstdint>
-#include <map>
 #include <mutex>
 #include <type_traits>
 #include <utility>
@@ -582,42 +581,6 @@ QmmTile qmm_pick_tile(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) {
   return QmmTile{1, 1, 1};
 }
 
-// Split-K workspace, one per (device, stream): grown on demand with a
-// stream-ordered allocation (the old buffer is released in stream order, after
-// the work that used it) and kept until the process ends.  Calls on one stream
-// are ordered, so they may share it; calls on different streams use different
-// buffers.  A stream being captured into a graph never uses the cache: its
-// workspace is allocated and freed inside the graph (graph-owned memory is only
-// valid during replays).  An allocation and free per call cost ~4 us of stream
-// time at M = 512, which is why the cache exists.
-namespace {
-std::mutex g_ws_mu;
-std::map<std::pair<int, hipStream_t>, std::pair<void*, size_t>> g_ws;
-
-// Called with g_ws_mu held, which the caller keeps until its kernels are
-// enqueued: another thread growing the same stream's buffer then frees it only
-// after those kernels in stream order.
-void* cached_workspace(int device, hipStream_t stream, size_t bytes) {
-  auto& e = g_ws[std::make_pair(device, stream)];
-  if (e.first != nullptr && e.second >= bytes) return e.first;
-  if (e.first != nullptr) (void)hipFreeAsync(e.first, stream);
-  e = std::make_pair(nullptr, size_t{0});
-  void* p = nullptr;
-  if (hipMallocAsync(&p, bytes, stream) != hipSuccess) {
-    (void)hipGetLastError();
-    return nullptr;
-  }
-  e = std::make_pair(p, bytes);
-  return p;
-}
-}  // namespace
-
-std::mutex& split_workspace_mutex() { return g_ws_mu; }
-
-float* split_workspace_locked(int device, hipStream_t stream, size_t bytes) {
-  return static_cast<float*>(cached_workspace(device, stream, bytes));
-}
-
 hipError_t launch_split_reduce_f16(const float* part, const uint16_t* ob, uint16_t* y, int64_t M, int64_t N,
                                    int splits, hipStream_t stream) {
   const int64_t MN = M * N;
@@ -646,8 +609,8 @@ hipError_t launch_qmm(const QmmArgs& a0, const DeviceInfo& dev) {
   }
   a.splits = tl.splits;
   if (cap == hipStreamCaptureStatusNone) {
-    std::lock_guard<std::mutex> lk(g_ws_mu);
-    a.part = static_cast<float*>(cached_workspace(dev.device, a.stream, bytes));
+    std::lock_guard<std::mutex> lk(split_workspace_mutex());
+    a.part = split_workspace_locked(dev.device, a.stream, bytes);
     if (a.part == nullptr) {
       a.splits = 1;
       return launch_qmm_shape<1, 1>(a);  // no workspace: the unsplit small-tile kernel

@@ -49,6 +49,15 @@
 
 namespace mxq {
 
+// Pointers into the global address space: loads through them are global_load
+// instructions even when the compiler cannot trace them to a kernel argument.
+template <typename T>
+using gptr = __attribute__((address_space(1))) T*;
+template <typename T>
+__device__ __forceinline__ gptr<T> to_global(T* p) {
+  return reinterpret_cast<gptr<T>>(reinterpret_cast<uintptr_t>(p));
+}
+
 template <int BITS>
 struct SegTraits {
   static constexpr int kCodesPerSeg = 128 / BITS;          // 32 or 16
@@ -181,9 +190,9 @@ __global__ __launch_bounds__(kQmvBlock) void qmv_kernel(const QmvBatch batch) {
     if (live >= 2 && (lane & (32 >> s))) my_idx += live / 2;
   }
   const int my_r = min(my_idx, V - 1) / MT;
-  // wave-uniform values live in scalar registers: all row addressing is scalar,
-  // and each load adds one 32-bit per-lane offset to a scalar base (the caller
-  // guarantees W, S and B are each below 4 GiB)
+  // wave-uniform values live in scalar registers: all row addressing is scalar
+  // (64-bit row bases), and each load adds one 32-bit per-lane offset within
+  // the row to its row's base
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   constexpr int waves_per_block = kQmvBlock / kWave;
   const int nrb = (N + R - 1) / R;
@@ -214,11 +223,19 @@ __global__ __launch_bounds__(kQmvBlock) void qmv_kernel(const QmvBatch batch) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const uint32_t row = dummy ? 0u : static_cast<uint32_t>(min(rbl * R + r, N - 1));  // tail rows re-read the last row; never stored
+      // the row's base address is a wave-uniform 64-bit value (W may exceed
+      // 4 GiB); the lane adds its 32-bit offset within the row
+      // (the empty asm keeps the global row bases in SGPRs, so each load takes
+      // the SGPR-base + 32-bit lane-offset form instead of a 64-bit lane address)
+      gptr<const char> wrow = to_global(wbase + static_cast<size_t>(row) * wrow_bytes);
+      gptr<const char> srow = to_global(sbase + static_cast<size_t>(row) * sbrow_bytes);
+      gptr<const char> brow = to_global(bbase + static_cast<size_t>(row) * sbrow_bytes);
+      asm volatile("" : "+s"(wrow), "+s"(srow), "+s"(brow));
       // W, scales and biases are each read exactly once: non-temporal loads keep
       // them from displacing reusable lines (measured ~7% faster on lm_head)
-      it.w[r] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(wbase + (row * wrow_bytes + wl)));
-      it.s[r] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(sbase + (row * sbrow_bytes + sl)));
-      it.b[r] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(bbase + (row * sbrow_bytes + sl)));
+      it.w[r] = __builtin_nontemporal_load(reinterpret_cast<gptr<const u4>>(wrow + wl));
+      it.s[r] = __builtin_nontemporal_load(reinterpret_cast<gptr<const uint16_t>>(srow + sl));
+      it.b[r] = __builtin_nontemporal_load(reinterpret_cast<gptr<const uint16_t>>(brow + sl));
     }
     // the stored row's output bias, fetched with every item of the row block
     // (so the one the block ends with has it); without a bias, a harmless

@@ -20,7 +20,8 @@
  *   y       f16   [M, N]            output, round-to-nearest-even of an f32 sum
  *
  * Supported: bits in {4, 8}; group_size in {32, 64, 128}; K a multiple of
- * group_size.  M, N, K >= 0; M*N == 0 is a no-op that touches no pointer;
+ * group_size.  0 <= M, N, K < 2^31 (buffers may exceed 4 GiB); M*N == 0 is a
+ * no-op that touches no pointer;
  * K == 0 with M*N > 0 writes y = +0 and reads nothing (x, w, scales and
  * biases may then be null).
  *
@@ -31,15 +32,23 @@
  *
  * Ownership and threading: every pointer is owned by the caller and must stay
  * valid until the enqueued work has finished.  The library keeps a per-device
- * cache of device properties and allocates device memory on one path only: an
- * MFMA call (mxq_qmm / mxq_linear with M > 8) whose 128 x 128 output tiles are
- * too few to occupy every compute unit and whose K is long splits K and needs
- * an f32 workspace of splits * M * N floats.  It uses one workspace per
- * (device, stream), allocated stream-ordered (hipMallocAsync on `stream`),
- * grown the same way when a call needs more, and kept until the process ends
- * (16 MiB for a 512 x 2048 x 8192 call).  On a stream being captured into a
- * graph the workspace is instead allocated and freed inside the graph.  If the
- * allocation fails, the call runs the unsplit kernel.  Calls are thread-safe.
+ * cache of device properties.  It allocates device memory on two paths only,
+ * both for f32 partial results that a second kernel adds in a fixed order:
+ *   - an MFMA call (mxq_qmm / mxq_linear / mxq_linear_act with M > 8 and not
+ *     a few-row shape) whose 128 x 128 output tiles are too few to occupy
+ *     every compute unit and whose K is long splits K: splits * M * N floats
+ *     (16 MiB for a 512 x 2048 x 8192 call);
+ *   - a few-row call (f16 activations, 2..16 rows on the K-split matrix-core
+ *     kernel) with K > 4096 runs K in chunks: chunks * M * N floats.
+ * Both use one split workspace per (device, stream), from hipMalloc, grown
+ * when a call needs more (the old buffer freed with hipFree, which first waits
+ * for the device's enqueued work), at most 4 streams per device (the least
+ * recently used stream's buffer is freed to make room), and kept until
+ * mxq_release_workspaces() or the end of the process.  On a stream being
+ * captured into a graph, MFMA calls allocate their workspace inside the graph
+ * instead (hipMallocAsync / hipFreeAsync) and few-row calls with K > 4096 run
+ * on the other kernels.  If memory cannot be had, MFMA calls run the unsplit
+ * kernel and few-row calls the decode kernel.  Calls are thread-safe.
  *
  * Asynchrony: a call validates its arguments synchronously, enqueues its
  * kernel(s) on `stream` (a hipStream_t; NULL means the null stream) and
@@ -74,7 +83,7 @@ typedef enum mxq_dtype {
 } mxq_dtype;
 
 /* Bumped whenever a signature in this header changes. */
-#define MXQ_ABI_VERSION 3
+#define MXQ_ABI_VERSION 4
 int mxq_abi_version(void);
 
 /*
@@ -245,6 +254,41 @@ mxq_status mxq_pack(const uint8_t* codes, uint32_t* w, int64_t N, int64_t K, int
  */
 const char* mxq_describe(const char* op, int64_t M, int64_t N, int64_t K, int bits,
                          int group_size, mxq_dtype sb_dtype);
+
+/*
+ * mxq_describe_grouped -- diagnostic: the launches mxq_qmv_grouped would make
+ * for these problems on the current device (only N, K of each entry are read;
+ * pointers may be null), e.g. "qmv_kernel<bits=4,sb=f16,mt=1,rows=2,xreg>
+ * problems=3 grid=768 block=256 lds=0", one entry per launch separated by
+ * "; ".  ",xreg" marks the variant that keeps each lane's activations in
+ * registers (every K within one 64-segment step, at most two rows).  Returns
+ * a thread-local string; "invalid", "none" (nothing to launch) or "no device"
+ * as mxq_describe.  Enqueues nothing.
+ */
+const char* mxq_describe_grouped(const mxq_qmv_problem* problems, int count, int64_t M, int bits,
+                                 int group_size, mxq_dtype sb_dtype);
+
+/*
+ * mxq_release_workspaces -- free every cached split workspace (see
+ * "Ownership and threading" above) on every device.  Waits for each device's
+ * enqueued work first (hipFree).  Later calls allocate again as needed.
+ * Always MXQ_OK.
+ */
+mxq_status mxq_release_workspaces(void);
+
+/* Bytes of split workspace cached for the current device (0 without a GPU). */
+int64_t mxq_workspace_bytes(void);
+
+/*
+ * mxq_read_probe -- measurement aid: stream `bytes` (a multiple of 16) of
+ * device memory from `buf` (16-byte aligned) with the decode kernel's load
+ * form (16-byte non-temporal loads, two 256-thread workgroups per compute
+ * unit) and discard the data; `out` (4 bytes of device memory, 4-byte
+ * aligned) may be written with a data-dependent value.  Timing it at a size
+ * gives the read bandwidth attainable at that size, against which the fused
+ * kernels' figures are judged.  Errors as the fused calls.
+ */
+mxq_status mxq_read_probe(const void* buf, int64_t bytes, void* out, void* stream);
 
 /* Static, human-readable name of a status. */
 const char* mxq_status_str(mxq_status s);

@@ -20,7 +20,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 def _header_functions():
     text = open(os.path.join(ROOT, "include", "mxq.h")).read()
-    return sorted(set(re.findall(r"^\s*(?:mxq_status|const char\*|int)\s+(mxq_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:mxq_status|const char\*|int|int64_t)\s+(mxq_\w+)\s*\(", text, re.M)))
 
 
 def test_header_symbols_exported():
@@ -30,7 +30,7 @@ def test_header_symbols_exported():
             "mxq_last_error", "mxq_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.mxq_abi_version() == 3
+    assert lib.mxq_abi_version() == 4
 
 
 def test_describe_without_device_or_with_bad_args():
@@ -204,3 +204,35 @@ def test_grouped_validation():
     assert lib.mxq_qmv_grouped(None, 0, 1, 4, 64, 0, None) == mxq.MXQ_OK
     empty = (Q * 2)(Q(None, None, None, None, None, 0, 64), Q(None, None, None, None, None, 0, 0))
     assert lib.mxq_qmv_grouped(empty, 2, 1, 4, 64, 0, None) == mxq.MXQ_OK
+
+
+def test_describe_grouped_without_device_or_with_bad_args():
+    lib = mxq.load()
+    Q = mxq.QmvProblem
+    arr = (Q * 2)(Q(None, None, None, None, None, 2048, 2048), Q(None, None, None, None, None, 512, 2048))
+    assert lib.mxq_describe_grouped(arr, 2, 1, 4, 64, 0) in (b"no device",) or \
+        lib.mxq_describe_grouped(arr, 2, 1, 4, 64, 0).startswith(b"qmv_kernel")
+    assert lib.mxq_describe_grouped(arr, 0, 1, 4, 64, 0) == b"invalid"
+    assert lib.mxq_describe_grouped(arr, 2, 0, 4, 64, 0) == b"invalid"
+    assert lib.mxq_describe_grouped(arr, 2, 1, 5, 64, 0) == b"invalid"
+    assert lib.mxq_describe_grouped(None, 2, 1, 4, 64, 0) == b"invalid"
+    bad = (Q * 1)(Q(None, None, None, None, None, 4, 96))   # K not a multiple of the group
+    assert lib.mxq_describe_grouped(bad, 1, 1, 4, 64, 0) == b"invalid"
+    empty = (Q * 2)(Q(None, None, None, None, None, 0, 64), Q(None, None, None, None, None, 8, 0))
+    assert lib.mxq_describe_grouped(empty, 2, 1, 4, 64, 0) == b"none"
+
+
+def test_read_probe_validation():
+    lib = mxq.load()
+    assert lib.mxq_read_probe(FAKE, 24, FAKE, None) == mxq.MXQ_ERR_INVALID_ARG
+    assert lib.mxq_read_probe(FAKE, -16, FAKE, None) == mxq.MXQ_ERR_INVALID_ARG
+    assert lib.mxq_read_probe(None, 32, FAKE, None) == mxq.MXQ_ERR_INVALID_ARG
+    assert lib.mxq_read_probe(FAKE + 8, 32, FAKE, None) == mxq.MXQ_ERR_MISALIGNED
+    assert lib.mxq_read_probe(FAKE, 32, FAKE + 2, None) == mxq.MXQ_ERR_MISALIGNED
+    assert lib.mxq_read_probe(None, 0, None, None) == mxq.MXQ_OK
+
+
+def test_workspace_controls_without_device():
+    lib = mxq.load()
+    assert lib.mxq_release_workspaces() == mxq.MXQ_OK
+    assert lib.mxq_workspace_bytes() == 0
