@@ -29,6 +29,7 @@ from ._lib import (  # noqa: F401
     mxq_linear_act,
     mxq_pack,
     mxq_qmm,
+    mxq_qmm_noalloc,
     mxq_qmv,
     mxq_qmv_grouped,
     mxq_release_workspaces,

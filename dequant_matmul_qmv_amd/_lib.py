@@ -47,7 +47,7 @@ class QmvProblem(ctypes.Structure):
 def _declare(lib):
     c_i64, c_int, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
     fused = [vp, vp, vp, vp, vp, c_i64, c_i64, c_i64, c_int, c_int, c_int, vp]
-    for name in ("mxq_qmv", "mxq_qmm"):
+    for name in ("mxq_qmv", "mxq_qmm", "mxq_qmm_noalloc"):
         f = getattr(lib, name)
         f.argtypes, f.restype = fused, c_int
     lib.mxq_linear.argtypes = [vp, vp, vp, vp, vp, vp, c_i64, c_i64, c_i64, c_int, c_int, c_int, vp]
@@ -207,6 +207,13 @@ def mxq_qmv_grouped(problems, *, bits: int = 4, group_size: int = 64, stream=Non
 def mxq_qmm(x, w, scales, biases, y=None, *, bits: int = 4, group_size: int = 64, stream=None):
     """y = x @ dequant(w).T via the MFMA prefill kernel (any M; MFMA for M > 8)."""
     return _fused("mxq_qmm", x, w, scales, biases, y, bits, group_size, stream)
+
+
+def mxq_qmm_noalloc(x, w, scales, biases, y=None, *, bits: int = 4, group_size: int = 64, stream=None):
+    """mxq_qmm that allocates no device memory: split-K partial results go to
+    the library's fixed 32 MiB scratch per GPU (calls needing more are
+    rejected; calls that overlap on one GPU race)."""
+    return _fused("mxq_qmm_noalloc", x, w, scales, biases, y, bits, group_size, stream)
 
 
 def mxq_linear(x, w, scales, biases, bias=None, y=None, *, bits: int = 4, group_size: int = 64,

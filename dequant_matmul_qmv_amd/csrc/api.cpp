@@ -79,10 +79,25 @@ bool qsmk_chunks_ok(int64_t K, void* stream) {
   return cap == hipStreamCaptureStatusNone;
 }
 
+// A caller-provided split workspace (the fixed scratch of mxq_qmm_noalloc):
+// calls given one never allocate, may run K in chunks under graph capture,
+// and are rejected when they would need more than it holds.
+struct FixedWs {
+  float* ptr;
+  size_t bytes;
+};
+
+mxq_status scratch_too_small(const char* who, size_t need, size_t have) {
+  return fail(MXQ_ERR_UNSUPPORTED, std::string(who) + ": this call needs " + std::to_string(need) +
+                                       " bytes of scratch for its partial results; the fixed scratch holds " +
+                                       std::to_string(have));
+}
+
 // M-sliced qmv over the whole M range.
 mxq_status run_qmv(const char* who, const void* x, const uint32_t* w, const void* scales,
                    const void* biases, const void* out_bias, void* y, int64_t M, int64_t N, int64_t K,
-                   int bits, int group_size, mxq_dtype sb_dtype, int act, void* stream) {
+                   int bits, int group_size, mxq_dtype sb_dtype, int act, void* stream,
+                   const FixedWs* fws = nullptr) {
   mxq::DeviceInfo dev;
   hipError_t e = mxq::device_info(&dev);
   if (e != hipSuccess) return hip_fail(who, e);
@@ -119,10 +134,18 @@ mxq_status run_qmv(const char* who, const void* x, const uint32_t* w, const void
   const bool few_i8 = act == kActI8 && M >= 3;
   if ((act == kActF16 ? qsmk_rows(M, K) : few_i8) && aligned(x, 16) && aligned(scales, 16) &&
       aligned(biases, 16) &&
-      mxq::qsmk_shape(M, N, K, bits, group_size, act == kActF16 && qsmk_chunks_ok(K, stream), dev)) {
+      mxq::qsmk_shape(M, N, K, bits, group_size, act == kActF16 && (fws || qsmk_chunks_ok(K, stream)), dev)) {
     a.x = static_cast<const uint16_t*>(x);
     a.y = static_cast<uint16_t*>(y);
     a.x_vec = 1;
+    if (fws) {
+      int nw = 0, chunks = 0;
+      mxq::qsmk_split(K, &nw, &chunks);
+      const size_t need = chunks > 1 ? static_cast<size_t>(chunks) * static_cast<size_t>(M) * static_cast<size_t>(N) * 4 : 0;
+      if (need > fws->bytes) return scratch_too_small(who, need, fws->bytes);
+      a.fixed_ws = fws->ptr;
+      a.fixed_ws_bytes = fws->bytes;
+    }
     e = mxq::launch_qsmk(a, static_cast<int>(M), dev);
     if (e != hipErrorOutOfMemory) return e == hipSuccess ? MXQ_OK : hip_fail(who, e);
     (void)hipGetLastError();  // no workspace for the K chunks: nothing was enqueued
@@ -181,7 +204,8 @@ mxq_status run_qmv_grouped(const char* who, const mxq_qmv_problem* pr, int count
 // MFMA kernel does not take), MFMA kernel otherwise; out_bias may be null.
 mxq_status run_matmul(const char* who, const void* x, const uint32_t* w, const void* scales,
                       const void* biases, const void* out_bias, void* y, int64_t M, int64_t N, int64_t K,
-                      int bits, int group_size, mxq_dtype sb_dtype, int act, void* stream) {
+                      int bits, int group_size, mxq_dtype sb_dtype, int act, void* stream,
+                      const FixedWs* fws = nullptr) {
   if (K == 0) {
     hipError_t e = mxq::launch_fill_rows(static_cast<uint16_t*>(y), static_cast<const uint16_t*>(out_bias), M, N,
                                          static_cast<hipStream_t>(stream));
@@ -195,9 +219,9 @@ mxq_status run_matmul(const char* who, const void* x, const uint32_t* w, const v
   hipError_t e = mxq::device_info(&dev);
   if (e != hipSuccess) return hip_fail(who, e);
   const bool few = act == kActF16 && qsmk_rows(M, K) &&
-                   mxq::qsmk_shape(M, N, K, bits, group_size, qsmk_chunks_ok(K, stream), dev);
+                   mxq::qsmk_shape(M, N, K, bits, group_size, fws || qsmk_chunks_ok(K, stream), dev);
   if (act == kActI8 || few || !mxq::qmm_mfma_shape(M, K) || !aligned(x, 16))
-    return run_qmv(who, x, w, scales, biases, out_bias, y, M, N, K, bits, group_size, sb_dtype, act, stream);
+    return run_qmv(who, x, w, scales, biases, out_bias, y, M, N, K, bits, group_size, sb_dtype, act, stream, fws);
   mxq::QmmArgs a{};
   a.x = static_cast<const uint16_t*>(x);
   a.w = w;
@@ -213,6 +237,14 @@ mxq_status run_matmul(const char* who, const void* x, const uint32_t* w, const v
   a.sb_bf16 = sb_dtype == MXQ_BF16;
   a.x_bf16 = act == kActBF16;
   a.stream = static_cast<hipStream_t>(stream);
+  if (fws) {
+    const mxq::QmmTile tl = mxq::qmm_pick_tile(M, N, K, dev);
+    const bool split = tl.mb == 2 && tl.splits > 1 && (M * N) % 4 == 0;
+    const size_t need = split ? static_cast<size_t>(tl.splits) * static_cast<size_t>(M) * static_cast<size_t>(N) * 4 : 0;
+    if (need > fws->bytes) return scratch_too_small(who, need, fws->bytes);
+    a.fixed_ws = fws->ptr;
+    a.fixed_ws_bytes = fws->bytes;
+  }
   e = mxq::launch_qmm(a, dev);
   return e == hipSuccess ? MXQ_OK : hip_fail(who, e);
 }
@@ -329,6 +361,19 @@ mxq_status mxq_qmm(const void* x, const uint32_t* w, const void* scales, const v
   if (st != MXQ_OK || M == 0 || N == 0) return st;
   return run_matmul("mxq_qmm", x, w, scales, biases, nullptr, y, M, N, K, bits, group_size, sb_dtype, kActF16,
                     stream);
+}
+
+mxq_status mxq_qmm_noalloc(const void* x, const uint32_t* w, const void* scales, const void* biases,
+                           void* y, int64_t M, int64_t N, int64_t K, int bits, int group_size,
+                           mxq_dtype sb_dtype, void* stream) {
+  g_last_error.clear();
+  mxq_status st = check_fused("mxq_qmm_noalloc", x, w, scales, biases, y, M, N, K, bits, group_size, sb_dtype);
+  if (st != MXQ_OK || M == 0 || N == 0) return st;
+  FixedWs fws{nullptr, mxq::kStaticScratchBytes};
+  const hipError_t e = mxq::static_scratch(&fws.ptr);
+  if (e != hipSuccess) return hip_fail("mxq_qmm_noalloc", e);
+  return run_matmul("mxq_qmm_noalloc", x, w, scales, biases, nullptr, y, M, N, K, bits, group_size, sb_dtype,
+                    kActF16, stream, &fws);
 }
 
 mxq_status mxq_linear(const void* x, const uint32_t* w, const void* scales, const void* biases,

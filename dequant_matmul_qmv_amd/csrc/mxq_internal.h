@@ -75,6 +75,8 @@ struct QmvArgs {
   int x_vec;           // x is 16-byte aligned
   int rows_per_wave;   // 0 = pick automatically
   hipStream_t stream;
+  float* fixed_ws;        // caller-provided split workspace (no allocation), or null: the cache
+  size_t fixed_ws_bytes;
 };
 
 size_t qmv_lds_need(int bits, int mt, int64_t K);
@@ -128,6 +130,11 @@ std::mutex& split_workspace_mutex();
 float* split_workspace_locked(int device, hipStream_t stream, size_t bytes);
 size_t split_workspace_cached_bytes(int device);  // takes the mutex
 int split_workspace_release_all();                // takes the mutex; returns the buffers freed
+// Fixed device scratch (static_scratch.hip) for the entry point that never
+// allocates: kStaticScratchBytes per device, its address looked up once per
+// device on first use (with that device current).
+constexpr size_t kStaticScratchBytes = size_t{32} << 20;
+hipError_t static_scratch(float** out);
 // y[M, N] (f16) = RNE(sum over splits of part[split] in split order + out_bias);
 // M * N a multiple of 4, part 16-byte aligned.
 hipError_t launch_split_reduce_f16(const float* part, const uint16_t* ob, uint16_t* y, int64_t M, int64_t N,
@@ -148,6 +155,8 @@ struct QmmArgs {
   bool sb_bf16;
   bool x_bf16;         // activations (x, y, output bias) are bf16, else f16
   hipStream_t stream;
+  float* fixed_ws;        // caller-provided split workspace (no allocation), or null: the cache
+  size_t fixed_ws_bytes;
 };
 
 hipError_t launch_qmm(const QmmArgs& a, const DeviceInfo& dev);

@@ -608,6 +608,11 @@ hipError_t launch_qmm(const QmmArgs& a0, const DeviceInfo& dev) {
     cap = hipStreamCaptureStatusNone;
   }
   a.splits = tl.splits;
+  if (a0.fixed_ws != nullptr) {  // the caller's workspace: no allocation, capture or not
+    if (bytes > a0.fixed_ws_bytes) return hipErrorInvalidValue;  // the caller checks this first
+    a.part = a0.fixed_ws;
+    return launch_qmm_shape<2, 2>(a);
+  }
   if (cap == hipStreamCaptureStatusNone) {
     std::lock_guard<std::mutex> lk(split_workspace_mutex());
     a.part = split_workspace_locked(dev.device, a.stream, bytes);

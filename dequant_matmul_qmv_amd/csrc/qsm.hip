@@ -578,10 +578,18 @@ hipError_t launch_qsmk(const QmvArgs& a, int M, const DeviceInfo& dev) {
   // K in chunks: f32 partial tiles [chunks, M, N] in the stream's split
   // workspace, then the fixed-order sum, the output bias and the f16 rounding
   const size_t bytes = static_cast<size_t>(chunks) * static_cast<size_t>(M) * static_cast<size_t>(a.N) * 4;
+  const uint16_t* no_ob = nullptr;  // the output bias is added once, by the reduction
+  if (a.fixed_ws != nullptr) {  // the caller's workspace: no allocation
+    if (bytes > a.fixed_ws_bytes) return hipErrorInvalidValue;  // the caller checks this first
+    float* partp = a.fixed_ws;
+    void* args[] = {&xp, &wp, &sp, &bp, &yp, &no_ob, &partp, &Mi, &Ni, &Ki};
+    hipError_t e = hipLaunchKernel(kern, dim3(gx, static_cast<unsigned>(chunks)), dim3(64 * nw), args, lds, a.stream);
+    if (e != hipSuccess) return e;
+    return launch_split_reduce_f16(partp, obp, yp, M, a.N, chunks, a.stream);
+  }
   std::lock_guard<std::mutex> lk(split_workspace_mutex());
   float* partp = split_workspace_locked(dev.device, a.stream, bytes);
   if (partp == nullptr) return hipErrorOutOfMemory;
-  const uint16_t* no_ob = nullptr;  // the output bias is added once, by the reduction
   void* args[] = {&xp, &wp, &sp, &bp, &yp, &no_ob, &partp, &Mi, &Ni, &Ki};
   hipError_t e = hipLaunchKernel(kern, dim3(gx, static_cast<unsigned>(chunks)), dim3(64 * nw), args, lds, a.stream);
   if (e != hipSuccess) return e;

@@ -48,7 +48,8 @@
  * captured into a graph, MFMA calls allocate their workspace inside the graph
  * instead (hipMallocAsync / hipFreeAsync) and few-row calls with K > 4096 run
  * on the other kernels.  If memory cannot be had, MFMA calls run the unsplit
- * kernel and few-row calls the decode kernel.  Calls are thread-safe.
+ * kernel and few-row calls the decode kernel.  mxq_qmm_noalloc is the variant
+ * that never allocates.  Calls are thread-safe.
  *
  * Asynchrony: a call validates its arguments synchronously, enqueues its
  * kernel(s) on `stream` (a hipStream_t; NULL means the null stream) and
@@ -160,6 +161,28 @@ mxq_status mxq_qmv_grouped(const mxq_qmv_problem* problems, int count, int64_t M
 mxq_status mxq_qmm(const void* x, const uint32_t* w, const void* scales, const void* biases,
                    void* y, int64_t M, int64_t N, int64_t K, int bits, int group_size,
                    mxq_dtype sb_dtype, void* stream);
+
+/*
+ * mxq_qmm_noalloc -- mxq_qmm for callers that cannot allocate device memory:
+ * code being captured into a HIP graph, tight serving loops, and harnesses
+ * that forbid allocation.  Same arguments, routing, kernels, results (bit for
+ * bit) and errors as mxq_qmm, except that the f32 partial results of a split
+ * or chunked K go to a fixed scratch array of 32 MiB that each GPU holds from
+ * the library's load until the process ends, instead of the split workspace
+ * cache: the call allocates and frees nothing (also under graph capture,
+ * where it may run K in chunks).  A call that would need more than 32 MiB of
+ * scratch (splits * M * N * 4 or chunks * M * N * 4 bytes) is rejected with
+ * MXQ_ERR_UNSUPPORTED before anything is enqueued; mxq_last_error() names the
+ * bytes needed.  The first call on a device looks up that device's scratch
+ * address.  Every call on one GPU shares its scratch: calls (and replays of
+ * graphs holding such calls) that may overlap in time on one GPU, on
+ * different streams, race and give wrong results.  Calls ordered on one
+ * stream are safe; each writes every scratch value it reads, so nothing
+ * needs clearing between calls.
+ */
+mxq_status mxq_qmm_noalloc(const void* x, const uint32_t* w, const void* scales, const void* biases,
+                           void* y, int64_t M, int64_t N, int64_t K, int bits, int group_size,
+                           mxq_dtype sb_dtype, void* stream);
 
 /*
  * mxq_linear -- a quantized linear layer with an output bias:

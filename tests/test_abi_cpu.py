@@ -98,7 +98,8 @@ def _call(name, *args):
     return st, lib.mxq_last_error().decode()
 
 
-@pytest.mark.parametrize("name", ["mxq_qmv", "mxq_qmm", "mxq_linear", "mxq_linear_act", "mxq_linear_a8"])
+@pytest.mark.parametrize("name", ["mxq_qmv", "mxq_qmm", "mxq_qmm_noalloc", "mxq_linear", "mxq_linear_act",
+                                  "mxq_linear_a8"])
 def test_fused_validation(name):
     P = FAKE
     ok = dict(M=1, N=4, K=64, bits=4, gs=64, sb=mxq.MXQ_F16, act=mxq.MXQ_BF16)
