@@ -18,6 +18,15 @@ typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
+// Pointers into the global address space: loads through them are global_load
+// instructions even when the compiler cannot trace them to a kernel argument.
+template <typename T>
+using gptr = __attribute__((address_space(1))) T*;
+template <typename T>
+__device__ __forceinline__ gptr<T> to_global(T* p) {
+  return reinterpret_cast<gptr<T>>(reinterpret_cast<uintptr_t>(p));
+}
+
 __device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
 __device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
 

@@ -442,6 +442,44 @@ __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x
   if (pipe == 1) return;
   // lane holds column n, rows 8*(r/4) + 4*(lane/32) + r%4 of each 32x32 block
   float* pout = part != nullptr ? part + static_cast<size_t>(split) * M * N : nullptr;
+  if (pout == nullptr && m0 + BM <= M && n0 + BN <= N && (N & 7) == 0 &&
+      (reinterpret_cast<uintptr_t>(y) & 15) == 0) {
+    // Whole tile, rows of y 16-byte aligned: the wave's results go through its
+    // own part of the exchange area (each value read above before it is
+    // overwritten here) and leave as 16-byte row pieces, whole 64- or
+    // 128-byte row segments per group of lanes.  Stored straight from the MFMA
+    // layout they would be 2 bytes per lane, half a row segment per row and
+    // instruction.
+    constexpr int EP = TWN + 8;               // staged row stride in halves
+    constexpr int LPR = TWN / 8;              // lanes per row (16-byte pieces)
+    constexpr int RPI = kWave / LPR;          // rows per store instruction
+    static_assert(TWM * EP * 2 <= MB * NB * 16 * 64 * 4, "staging fits in the wave's exchange area");
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] += red[((q * MB * NB + i * NB + j) * 16 + r) * 64 + lane];
+    uint16_t* ep = reinterpret_cast<uint16_t*>(red + q * MB * NB * 16 * 64);
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int c = j * 32 + (lane & 31);
+        const float o = ob != nullptr ? sb_to_f32<XB>(ob[n0 + wn * TWN + c]) : 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          ep[(i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3)) * EP + c] = f32_to_act_bits<XB>(acc[i][j][r] + o);
+      }
+    const int pc = lane % LPR, pr = lane / LPR;
+    uint16_t* yt = y + static_cast<size_t>(m0 + wm * TWM) * N + n0 + wn * TWN + 8 * pc;
+#pragma unroll
+    for (int qq = 0; qq < TWM / RPI; ++qq) {
+      const int rr = RPI * qq + pr;
+      *reinterpret_cast<u4*>(yt + static_cast<size_t>(rr) * N) = *reinterpret_cast<const u4*>(&ep[rr * EP + 8 * pc]);
+    }
+    return;
+  }
   if (m0 + BM <= M && n0 + BN <= N && N < (1 << 26)) {
     // whole tile inside y: no bounds checks; each store takes a wave-uniform
     // row base in SGPRs and the lane's fixed 32-bit offset (4*hi rows + column)

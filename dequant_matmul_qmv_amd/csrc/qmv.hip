@@ -49,15 +49,6 @@
 
 namespace mxq {
 
-// Pointers into the global address space: loads through them are global_load
-// instructions even when the compiler cannot trace them to a kernel argument.
-template <typename T>
-using gptr = __attribute__((address_space(1))) T*;
-template <typename T>
-__device__ __forceinline__ gptr<T> to_global(T* p) {
-  return reinterpret_cast<gptr<T>>(reinterpret_cast<uintptr_t>(p));
-}
-
 template <int BITS>
 struct SegTraits {
   static constexpr int kCodesPerSeg = 128 / BITS;          // 32 or 16
