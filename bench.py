@@ -262,6 +262,119 @@ def qmm_pass():
         print(json.dumps({"kernel": mxq.mxq_describe("qmm", 512, N, K), "N": N, "K": K, "calls": 5}), flush=True)
 
 
+def step_pass(replays=20):
+    """Workload for the decode-step kernel trace: the 16-layer step (q,k,v,o,
+    gate,up,down per layer, then lm_head) as 65 launches -- {q,k,v}, {o},
+    {gate,up}, {down} per layer, lm_head last -- captured in one HIP graph and
+    replayed `replays` times."""
+    import torch
+
+    import dequant_matmul_qmv_amd as mxq
+    import synth
+    lib = mxq.load()
+    dev = "cuda:0"
+    layers = [make_qmv_set(mxq, lib, synth, torch, 3, layer, list(synth.LLAMA_1B_PROJ), dev)
+              for layer in range(synth.LLAMA_1B_LAYERS)]
+    head = make_qmv_set(mxq, lib, synth, torch, 3, 99, [synth.LLAMA_1B_LM_HEAD], dev)
+    launches = []
+    for lay in layers:
+        by = {c.name: c for c in lay}
+        launches += [GroupCall(lib, mxq, [by["q"], by["k"], by["v"]]), by["o"],
+                     GroupCall(lib, mxq, [by["gate"], by["up"]]), by["down"]]
+    launches += head
+
+    def fn():
+        st = cur_stream(torch)
+        for c in launches:
+            c(st)
+    g = capture(torch, fn)
+    for _ in range(replays):
+        g.replay()
+    torch.cuda.synchronize()
+    print(json.dumps({"launches_per_step": len(launches), "replays": replays}), flush=True)
+
+
+STEP_KINDS = ("q+k+v", "o", "gate+up", "down")
+
+
+def summarize_step_trace(trace_csv: str, launches=65, replays=20):
+    """Markdown summary of a rocprofv3 kernel trace of --step-pass: the last
+    `replays` x `launches` dispatches are the graph replays; per launch kind,
+    the mean kernel duration and the mean idle gap from the end of the
+    previous kernel to the start of this one (first launch of a replay
+    excluded from the gaps)."""
+    import csv
+    import statistics
+    rows = []
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]))
+    rows.sort()
+    rows = rows[-launches * replays:]
+    kinds = {}
+    spans, busy = [], []
+    for i in range(replays):
+        rep = rows[i * launches:(i + 1) * launches]
+        spans.append((rep[-1][1] - rep[0][0]) / 1e3)
+        busy.append(sum(e - s for s, e, _ in rep) / 1e3)
+        for j, (s, e, name) in enumerate(rep):
+            kind = "lm_head" if j == launches - 1 else STEP_KINDS[j % 4]
+            d = kinds.setdefault(kind, {"dur": [], "gap": [], "name": name.split("(")[0]})
+            d["dur"].append((e - s) / 1e3)
+            if j:
+                d["gap"].append((s - rep[j - 1][1]) / 1e3)
+    out = ["| launch | kernel | per step | mean duration (us) | mean gap before it (us) |", "|---|---|---|---|---|"]
+    for kind in STEP_KINDS + ("lm_head",):
+        d = kinds[kind]
+        out.append(f"| {kind} | `{d['name']}` | {len(d['dur']) // replays} | {statistics.mean(d['dur']):.2f} | "
+                   f"{statistics.mean(d['gap']):.2f} |")
+    span, b = statistics.median(spans), statistics.median(busy)
+    out.append("")
+    out.append(f"Step span (first kernel start to last kernel end), median of {replays} replays: {span:.1f} us; "
+               f"sum of kernel durations: {b:.1f} us; idle between kernels: {span - b:.1f} us "
+               f"({100 * (span - b) / span:.1f} %).")
+    print("\n".join(out))
+
+
+def few_pass():
+    """Workload for rocprofv3 passes over the few-row kernels: lm_head
+    (128256 x 2048, 4-bit g64, f16 scales) at M = 2, 4, 8 and 16 through
+    mxq_qmv (the K-split matrix-core kernel), then M = 16 at K = 2304 (not a
+    multiple of 512, so the 16-row-block kernel), five calls each on two
+    rotating weight sets, after the copy calibration."""
+    import numpy as np
+    import torch
+
+    import dequant_matmul_qmv_amd as mxq
+    import synth
+    mxq.load()
+    dev = "cuda:0"
+    src = torch.randint(0, 1 << 30, (COPY_BYTES // 4,), dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    N = synth.LLAMA_1B_LM_HEAD[1]
+    for K, Ms in ((2048, (2, 4, 8, 16)), (2304, (16,))):
+        sets = []
+        for r in range(2):
+            w, s, b = synth.make_weights(N, K, 4, 64, "f16", seed=900 + r)
+            sets.append((torch.from_numpy(w.view(np.int32)).to(dev),
+                         torch.from_numpy(s.view(np.int16)).view(torch.float16).to(dev),
+                         torch.from_numpy(b.view(np.int16)).view(torch.float16).to(dev)))
+        for M in Ms:
+            x = torch.from_numpy(synth.make_x(M, K, seed=910 + M)).to(dev)
+            y = torch.empty((M, N), dtype=torch.float16, device=dev)
+            for i in range(5):
+                w, s, b = sets[i % 2]
+                mxq.mxq_qmv(x, w, s, b, y, bits=4)
+            torch.cuda.synchronize()
+            print(json.dumps({"kernel": mxq.mxq_describe("qmv", M, N, K), "M": M, "N": N, "K": K,
+                              "alg_bytes": call_bytes(M, N, K), "calls": 5}), flush=True)
+        del sets
+
+
 def write_traffic(fetch_csv: str, write_csv: str, meta_json: str):
     """Turn two rocprofv3 counter CSVs into profiles/qmv_traffic.json.
 
@@ -548,7 +661,22 @@ def main():
                     help="only run the M=512 prefill workload of the rocprofv3 --pmc counter passes")
     ap.add_argument("--write-traffic", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "META_JSON"),
                     help="write profiles/qmv_traffic.json from two rocprofv3 counter CSVs")
+    ap.add_argument("--step-pass", action="store_true",
+                    help="only run the graph-replayed 16-layer decode step (kernel-trace workload)")
+    ap.add_argument("--step-trace-summary", metavar="KERNEL_TRACE_CSV",
+                    help="summarize a rocprofv3 kernel trace of --step-pass (durations and gaps)")
+    ap.add_argument("--few-pass", action="store_true",
+                    help="only run the few-row workload of the rocprofv3 counter passes")
     args = ap.parse_args()
+    if args.step_trace_summary:
+        summarize_step_trace(args.step_trace_summary)
+        return
+    if args.step_pass:
+        step_pass()
+        return
+    if args.few_pass:
+        few_pass()
+        return
     if args.write_traffic:
         write_traffic(*args.write_traffic)
         return
