@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmxq.so")
-SOURCES = ["api.cpp", "workspace.cpp", "qmv.hip", "qmm.hip", "qsm.hip", "dequant.hip", "probe.hip", "static_scratch.hip"]
+SOURCES = ["api.cpp", "workspace.cpp", "qmv.hip", "qmm.hip", "qsm.hip", "dequant.hip", "qmm_a8.hip", "probe.hip", "static_scratch.hip"]
 ARCH = "gfx950"
 
 

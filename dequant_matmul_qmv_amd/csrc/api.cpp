@@ -220,6 +220,28 @@ mxq_status run_matmul(const char* who, const void* x, const uint32_t* w, const v
   if (e != hipSuccess) return hip_fail(who, e);
   const bool few = act == kActF16 && qsmk_rows(M, K) &&
                    mxq::qsmk_shape(M, N, K, bits, group_size, fws || qsmk_chunks_ok(K, stream), dev);
+  // int8 activations from 17 rows: the integer-MFMA prefill kernel (x
+  // quantized once into a workspace, W read once); without a workspace, and
+  // for fewer rows, run_qmv's routing.
+  if (act == kActI8 && !fws && mxq::qmm_a8_shape(M, K) && aligned(x, 16)) {
+    mxq::QmmA8Args a8{};
+    a8.x = static_cast<const uint16_t*>(x);
+    a8.w = w;
+    a8.s = static_cast<const uint16_t*>(scales);
+    a8.b = static_cast<const uint16_t*>(biases);
+    a8.y = static_cast<uint16_t*>(y);
+    a8.ob = static_cast<const uint16_t*>(out_bias);
+    a8.M = M;
+    a8.N = N;
+    a8.K = K;
+    a8.bits = bits;
+    a8.group_size = group_size;
+    a8.sb_bf16 = sb_dtype == MXQ_BF16;
+    a8.stream = static_cast<hipStream_t>(stream);
+    e = mxq::launch_qmm_a8(a8, dev);
+    if (e != hipErrorOutOfMemory) return e == hipSuccess ? MXQ_OK : hip_fail(who, e);
+    (void)hipGetLastError();  // no workspace: nothing was enqueued
+  }
   if (act == kActI8 || few || !mxq::qmm_mfma_shape(M, K) || !aligned(x, 16))
     return run_qmv(who, x, w, scales, biases, out_bias, y, M, N, K, bits, group_size, sb_dtype, act, stream, fws);
   mxq::QmmArgs a{};
@@ -478,6 +500,16 @@ const char* mxq_describe(const char* op, int64_t M, int64_t N, int64_t K, int bi
            (a8 ? ",act=i8" : "") + (chunks > 1 ? ",kchunks=" + std::to_string(chunks) : std::string()) +
            "> block=" + std::to_string(64 * nw) + " lds=" + std::to_string(mxq::qsmk_lds_bytes(nw, bits)) +
            (chunks > 1 ? "; qmm_split_reduce_kernel" : "");
+    return desc.c_str();
+  }
+  if (a8 && mxq::qmm_a8_shape(M, K)) {
+    const mxq::QmmA8Plan p = mxq::qmm_a8_plan(M, N, K, group_size, dev);
+    desc = "quant_rows_i8_kernel grid=" + std::to_string(M) + " block=256; qmm_a8_kernel<bits=" + std::to_string(bits) +
+           ",sb=" + sb + ",gs=" + std::to_string(group_size) + ",tile=128x128" +
+           (p.splits > 1 ? ",ksplit=" + std::to_string(p.splits) : std::string()) + "> grid=" +
+           std::to_string(static_cast<int64_t>(p.tiles_m) * p.tiles_n * p.splits) +
+           " block=512 lds=" + std::to_string(mxq::qmm_a8_lds_bytes()) +
+           (p.splits > 1 ? "; qmm_split_reduce_kernel" : "");
     return desc.c_str();
   }
   const bool mfma = o == "qmm" && mxq::qmm_mfma_shape(M, K);

@@ -171,6 +171,46 @@ QmmTile qmm_pick_tile(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev);
 // within a tile (at most 128 rows of x, W, scales) fits in 32 bits.
 inline bool qmm_mfma_shape(int64_t M, int64_t K) { return M > 8 && K % 64 == 0 && K < (int64_t{1} << 24); }
 
+// int8-activation prefill kernel (qmm_a8.hip): x quantized per row once into
+// a workspace, then 128 x 128 tiles on the integer matrix cores (K split when
+// the tiles alone do not occupy the GPU).  Takes M >= 17, K a multiple of 64
+// below 2^24 (tile-relative byte offsets fit in 32 bits), x 16-byte aligned.
+inline bool qmm_a8_shape(int64_t M, int64_t K) { return M >= 17 && K % 64 == 0 && K < (int64_t{1} << 24); }
+struct QmmA8Args {
+  const uint16_t* x;   // f16 activations [M, K]
+  const uint32_t* w;
+  const uint16_t* s;
+  const uint16_t* b;
+  uint16_t* y;         // f16 [M, N]
+  const uint16_t* ob;  // f16 [N] or null
+  int64_t M, N, K;
+  int bits;
+  int group_size;
+  bool sb_bf16;
+  hipStream_t stream;
+};
+struct QmmA8Plan {
+  int tiles_m, tiles_n, splits, nks;
+  size_t part_bytes, xq_bytes, xsum_bytes, sx_bytes, workspace_bytes;
+};
+struct QmmA8Launch {
+  const uint16_t* x;
+  const uint32_t* w;
+  const uint16_t* s;
+  const uint16_t* b;
+  uint16_t* y;
+  const uint16_t* ob;
+  float* part;   // [splits, M, N] f32 partial tiles, or null (one split)
+  uint8_t* xq;   // [M, K] int8 activation codes
+  float* xsum;   // [M, K / min(group, 64)] integer code sums
+  float* sx;     // [M] row scales
+  int M, N, K, tiles_m, tiles_n, splits, nks;
+};
+QmmA8Plan qmm_a8_plan(int64_t M, int64_t N, int64_t K, int group_size, const DeviceInfo& dev);
+size_t qmm_a8_lds_bytes();
+// hipErrorOutOfMemory (nothing enqueued) when no workspace can be had.
+hipError_t launch_qmm_a8(const QmmA8Args& a, const DeviceInfo& dev);
+
 // Read probe (probe.hip): streams `bytes` (a multiple of 16) from a 16-byte
 // aligned buffer; out receives 4 bytes at most.
 hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* out, hipStream_t stream,

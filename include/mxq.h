@@ -32,15 +32,18 @@
  *
  * Ownership and threading: every pointer is owned by the caller and must stay
  * valid until the enqueued work has finished.  The library keeps a per-device
- * cache of device properties.  It allocates device memory on two paths only,
- * both for f32 partial results that a second kernel adds in a fixed order:
+ * cache of device properties.  It allocates device memory on three paths
+ * only:
  *   - an MFMA call (mxq_qmm / mxq_linear / mxq_linear_act with M > 8 and not
  *     a few-row shape) whose 128 x 128 output tiles are too few to occupy
  *     every compute unit and whose K is long splits K: splits * M * N floats
- *     (16 MiB for a 512 x 2048 x 8192 call);
+ *     of partial results, added in a fixed order by a second kernel (16 MiB
+ *     for a 512 x 2048 x 8192 call);
  *   - a few-row call (f16 activations, 2..16 rows on the K-split matrix-core
- *     kernel) with K > 4096 runs K in chunks: chunks * M * N floats.
- * Both use one split workspace per (device, stream), from hipMalloc, grown
+ *     kernel) with K > 4096 runs K in chunks: chunks * M * N floats;
+ *   - an int8-activation call from 17 rows (mxq_linear_a8) holds the
+ *     quantized activations, and, when K is split, the partial results.
+ * All use one split workspace per (device, stream), from hipMalloc, grown
  * when a call needs more (the old buffer freed with hipFree, which first waits
  * for the device's enqueued work), at most 4 streams per device (the least
  * recently used stream's buffer is freed to make room), and kept until
@@ -48,7 +51,7 @@
  * captured into a graph, MFMA calls allocate their workspace inside the graph
  * instead (hipMallocAsync / hipFreeAsync) and few-row calls with K > 4096 run
  * on the other kernels.  If memory cannot be had, MFMA calls run the unsplit
- * kernel and few-row calls the decode kernel.  mxq_qmm_noalloc is the variant
+ * kernel, and few-row and int8 prefill calls the decode kernel.  mxq_qmm_noalloc is the variant
  * that never allocates.  Calls are thread-safe.
  *
  * Asynchrony: a call validates its arguments synchronously, enqueues its
@@ -236,8 +239,16 @@ mxq_status mxq_linear_act(const void* x, const uint32_t* w, const void* scales, 
  *   y[m, n] = RNE_f16( sx[m] * sum_k xq[m, k] * (q[n, k] * s + b) + out_bias[n] ).
  * So y differs from mxq_linear's by the activation rounding (about 0.4 % of
  * a row's largest |x| per element); it matches the int8 method itself to the
- * tolerance of mxq_qmv.  x must be finite.  Other shapes run the decode
- * kernel in slices of 8 rows.  Arguments, layouts, out_bias and errors as
+ * tolerance of mxq_qmv.  x must be finite.
+ * From 17 rows (K a multiple of 64 below 2^24, x 16-byte aligned) the call is
+ * the prefill route on v_mfma_i32_32x32x32_i8: a first kernel quantizes each
+ * row of x once, writing the int8 codes, the row scale and the per-group code
+ * sums to a workspace (M * K + M * K / min(group, 64) * 4 + M * 4 bytes, plus
+ * the f32 partial tiles when K is split, splits * M * N * 4), then 128 x 128
+ * tiles read W once.  The workspace comes from the split workspace cache
+ * described above (inside the graph under capture); if none can be had the
+ * call takes the decode kernel instead.  Other shapes run the decode kernel
+ * in slices of 8 rows.  Arguments, layouts, out_bias and errors as
  * mxq_linear.
  */
 mxq_status mxq_linear_a8(const void* x, const uint32_t* w, const void* scales, const void* biases,
