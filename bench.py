@@ -17,14 +17,22 @@ Extra objects on the same line:
                 HIP events on the launch stream: algorithmic bytes / duration,
                 against the 8 TB/s HBM peak;  traffic from committed rocprofv3
                 PMC counters when they match the current kernel source;
-  cpu_baseline  the f64 CPU oracle on a bounded sample, single BLAS thread;
+  cpu_baseline  the f64 CPU oracle on a bounded sample (layer 0 and a slice
+                of lm_head), all cores and one pinned core, with the host's
+                CPU model and thread counts;
+  read_probe    GB/s of a plain 16-byte streaming read at the per-launch byte
+                counts (the floor small launches are judged against);
+  configs       the small single problem (N=512) and the 48-case edge sweep,
+                GB/s per launch;
   decode_step   16 layers x {q,k,v,o,gate,up,down} + lm_head, ~697 MB of
                 distinct weights, as 113 separate launches and as 65 grouped
                 launches (eager and graph replay): bytes/step, GB/s, steps/s;
   qmm           M=512 prefill on gate/up (8192x2048) and down (2048x8192),
                 f16 and bf16 scales, 20 calls back to back per projection:
                 TFLOP/s and MFMA utilisation (of the 2.5 PFLOP/s dense f16
-                peak);
+                peak); the same projections with int8 activations
+                (mxq_linear_a8, integer matrix cores): TOP/s against the
+                5.0 POP/s dense int8 peak;
   bf16_activations  the lm_head decode launch (GB/s) and the M=512 prefill
                 projections (TFLOP/s) with bf16 x and y;
   few_rows      the lm_head launch at M = 1, 2, 4, 8 and 16: the f16 route of
@@ -50,6 +58,7 @@ if ROOT not in sys.path:
 METRIC = "fused 4-bit qGEMV HBM GB/s (% of peak) at M=1; qGEMM TFLOP/s at M=512"
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
+MFMA_I8_PEAK_TOPS = 5000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qmv_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "dequant_matmul_qmv_amd", "csrc", f)
                   for f in ("qmv.hip", "mxq_device.h")]
@@ -105,6 +114,23 @@ class GroupCall:
         st = self.fn(self.arr, len(self.calls), 1, 4, 64, 0, stream_handle)
         if st != 0:
             raise RuntimeError(f"grouped launch: libmxq status {st}")
+
+
+class A8Call:
+    """One pre-marshalled mxq_linear_a8 launch (f16 x quantized per row to int8; no output bias)."""
+
+    def __init__(self, lib, x, w, s, b, y, M, N, K, name, bits=4, gs=64, sb_code=0):
+        self.fn = lib.mxq_linear_a8
+        self.tensors = (x, w, s, b, y)  # keep alive
+        self.args = (x.data_ptr(), w.data_ptr(), s.data_ptr(), b.data_ptr(), None, y.data_ptr(),
+                     M, N, K, bits, gs, sb_code)
+        self.name = name
+        self.M, self.N, self.K = M, N, K
+
+    def __call__(self, stream_handle):
+        st = self.fn(*self.args, stream_handle)
+        if st != 0:
+            raise RuntimeError(f"{self.name}: libmxq status {st}")
 
 
 class ActCall:
@@ -563,8 +589,8 @@ def _cpu_model() -> str:
 def cpu_baseline(synth, reps=5):
     """The f64 oracle on a bounded sample, timed on the host's cores.
 
-    Sample: layer-0 q,k,v,o + lm_head rows 0..4095 (M=1, 4-bit g64, f16
-    scales).  Two legs: all available cores (numpy's BLAS with its default
+    Sample: all seven layer-0 projections + lm_head rows 0..16383 (M=1,
+    4-bit g64, f16 scales; ~53 MB, 10-20 s for both legs).  Two legs: all available cores (numpy's BLAS with its default
     thread count; unpack and dequant are single-threaded numpy) and one core
     (affinity pinned to one CPU, one BLAS thread).  Each leg times the whole
     oracle (oracle.matmul_ref: unpack, dequant, matmul) and its two phases
@@ -578,7 +604,7 @@ def cpu_baseline(synth, reps=5):
         from threadpoolctl import threadpool_info, threadpool_limits
     except ImportError:  # pragma: no cover
         threadpool_info = threadpool_limits = None
-    shapes = list(synth.LLAMA_1B_PROJ[:4]) + [("lm_head[0:4096]", 4096, 2048)]
+    shapes = list(synth.LLAMA_1B_PROJ) + [("lm_head[0:16384]", 16384, 2048)]
     probs = []
     for idx, (name, N, K) in enumerate(shapes):
         w, s, b = synth.make_weights(N, K, 4, 64, "f16", seed=synth.proj_seed(1, 0, idx))
@@ -632,7 +658,7 @@ def cpu_baseline(synth, reps=5):
     el = time.perf_counter() - t0
     blas_threads = max((b["threads"] or 1 for b in blas), default=1) if blas else None
     return {"value": all_cores["GB/s"], "unit": "GB/s", "cores": blas_threads or len(cpus), "kind": "oracle",
-            "sample": f"layer-0 q,k,v,o + lm_head rows 0..4095 (M=1, 4-bit g64, f16 scales; "
+            "sample": f"layer-0 q,k,v,o,gate,up,down + lm_head rows 0..16383 (M=1, 4-bit g64, f16 scales; "
                       f"{sample_bytes} algorithmic bytes per pass), f64 numpy oracle, median of {reps} passes "
                       f"after one warm-up per leg, {el:.1f} s in all",
             "host": {"cpu_model": _cpu_model(), "cpus_available": len(cpus), "blas": blas},
@@ -921,6 +947,31 @@ def main():
             entry["mfma_util"] = round(tf / MFMA_F16_PEAK_TFLOPS, 4)
             entry["kernel"] = mxq.mxq_describe("qmm", 512, 8192, 2048, 4, 64, sb)
             qmm[sb] = entry
+            if sb == "f16":
+                # the same projections with int8 activations (mxq_linear_a8):
+                # rows quantized once, then the integer matrix cores
+                a8 = {}
+                a8_op, a8_ms = 0, 0.0
+                for c in calls:
+                    ac = A8Call(lib, *c.tensors, c.M, c.N, c.K, c.name)
+                    for _ in range(5):
+                        ac(st)
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    for _ in range(20):
+                        ac(st)
+                    e1.record()
+                    torch.cuda.synchronize()
+                    ms = e0.elapsed_time(e1) / 20
+                    op = 2 * c.M * c.N * c.K
+                    a8[c.name] = {"us": round(ms * 1e3, 2), "TOP/s": round(op / (ms / 1e3) / 1e12, 1)}
+                    a8_op += op
+                    a8_ms += ms
+                a8["TOP/s"] = round(a8_op / (a8_ms / 1e3) / 1e12, 1)
+                a8["frac_of_int8_peak"] = round(a8_op / (a8_ms / 1e3) / 1e12 / MFMA_I8_PEAK_TOPS, 4)
+                a8["kernel"] = mxq.mxq_describe("a8", 512, 8192, 2048, 4, 64, sb)
+                a8["timing"] = "20 calls back to back per projection, quantization of x included"
+                qmm["int8_activations"] = a8
         result["qmm"] = qmm
 
         # bf16 activations (x and y bf16) through mxq_linear_act: the lm_head
