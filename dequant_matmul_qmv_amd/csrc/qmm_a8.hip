@@ -29,8 +29,10 @@
 //
 // Tiling: 128 x 128 tiles, a workgroup of 8 waves (2 x 4), 64 x 32 per wave (2
 // x 1 blocks of 32 x 32): two waves per SIMD, so one wave's scale FMAs issue
-// while the other's MFMAs or loads wait.  K in stages of 64 codes through four LDS buffers;
-// global loads run two to three stages ahead in two register sets.  The scale
+// while the other's MFMAs or loads wait.  K in stages of 64 codes through four
+// LDS buffers; global loads run four stages ahead of their LDS store in four
+// register sets (x comes from other XCDs' writes and W's first reads from
+// HBM: a microsecond away, several stages of compute).  The scale
 // FMAs of stage t are issued after the MFMAs of stage t + 1, so they run on
 // the VALU while the matrix core works on the next stage.  Long K with too few
 // tiles to occupy the GPU is split, each split writing its f32 partial tile
@@ -98,7 +100,11 @@ __device__ __forceinline__ void split_bf16(const float (&v)[8], u4 (&out)[NP]) {
 // Row quantization: one workgroup per row of x.  xq holds each chunk of 8
 // activations as two dwords in the byte order of the code unpack (4-bit:
 // even then odd activations; 8-bit: natural), xs[m][j] the integer sum of the
-// codes of ring group j (RGC activations), sx[m] the row scale.
+// codes of ring group j (RGC activations), sx[m] the row scale.  Up to K = 8192
+// the row stays in registers between the two passes.  (One wave per row, four
+// rows per workgroup, measured slower: 4.4-5.3 against 3.8-4.1 us at K = 2048,
+// 9-10 against 6 us at K = 8192, M = 512 -- a row is then a longer serial chain
+// on half as many workgroups.)
 // ---------------------------------------------------------------------------
 template <int BITS, int RGC>
 __global__ __launch_bounds__(256) void quant_rows_i8_kernel(const uint16_t* __restrict__ x, uint32_t* __restrict__ xq,
@@ -239,7 +245,7 @@ __global__ __launch_bounds__(512) void qmm_a8_kernel(const uint8_t* __restrict__
     u4 x;
     std::conditional_t<BITS == 4, u2, u4> w;  // 16 codes
   };
-  Regs ra, rb;
+  Regs R[4];  // stage kt's loads live in R[kt % 4] from four stages before its LDS store
   auto gload = [&](Regs& R, int kt) __attribute__((always_inline)) {
     const int ks = kt0 + min(kt, nkt - 1);  // past the end: re-read the last stage (stored where nothing reads)
     size_t xo = static_cast<size_t>(ks) * A8_KT, wo = static_cast<size_t>(ks) * WB;
@@ -292,7 +298,7 @@ __global__ __launch_bounds__(512) void qmm_a8_kernel(const uint8_t* __restrict__
     for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-  i16v P0[RPS][MB][NB], P1[RPS][MB][NB];
+  i16v P[2][RPS][MB][NB];  // integer products of even / odd stages
 
   const int arow = wm * 32 * MB + (lane & 31);  // tile row of this lane's A operand (+ 32 i)
   const int bcol = wn * 32 * NB + (lane & 31);  // tile column of this lane's B operand and outputs (+ 32 j)
@@ -379,7 +385,11 @@ __global__ __launch_bounds__(512) void qmm_a8_kernel(const uint8_t* __restrict__
       const int rg = kt * RPS + e;
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        const float sc = sb_to_f32<SB_BF16>(sq[(bcol + 32 * j) * A8_SBS + rg % A8_RING]);
+        // the scale widened once, out of the compiler's sight: it would otherwise fold the
+        // widening into each FMA (v_fma_mix_f32, VOP3P), which issues at half the rate of the
+        // two-operand v_fmac_f32 used instead
+        float sc = sb_to_f32<SB_BF16>(sq[(bcol + 32 * j) * A8_SBS + rg % A8_RING]);
+        asm volatile("" : "+v"(sc));
 #pragma unroll
         for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -392,50 +402,86 @@ __global__ __launch_bounds__(512) void qmm_a8_kernel(const uint8_t* __restrict__
     }
   };
 
-  // ---- prologue: stages 0 and 1 in LDS, 2 and 3 in registers --------------
-  gload(ra, 0);
-  lstore(ra, 0);
-  gload(rb, 1);
-  lstore(rb, 1);
-  gload(ra, 2);
-  gload(rb, 3);
+  // ---- prologue: stages 0 and 1 in LDS, 2 .. 5 in registers ----------------
+#pragma unroll
+  for (int i = 0; i < 4; ++i) gload(R[i], i);
+  lstore(R[0], 0);
+  lstore(R[1], 1);
+  gload(R[0], 4);
+  gload(R[1], 5);
   __syncthreads();
-  if constexpr (DEFER) mma(P0, 0);
+  if constexpr (DEFER) mma(P[0], 0);
 
-  // Pair pr covers stages kt = 2 pr and kt + 1.  Every wave takes part in
-  // every barrier; a stage past the end is loaded and stored (clamped) but
-  // never computed.
-  const int npair = (nkt + 1) >> 1;
-  for (int pr = 0; pr < npair; ++pr) {
-    const int kt = 2 * pr;
-    if constexpr (DEFER) {
-      if (kt + 1 < nkt) mma(P1, kt + 1);
-      scale(P0, kt);
-    } else {
-      mma(P0, kt);
-      scale(P0, kt);
-    }
-    lstore(ra, kt + 2);
-    gload(ra, kt + 4);
-    __syncthreads();
-    if constexpr (DEFER) {
-      if (kt + 2 < nkt) mma(P0, kt + 2);
-      if (kt + 1 < nkt) scale(P1, kt + 1);
-    } else {
-      if (kt + 1 < nkt) {
-        mma(P0, kt + 1);
-        scale(P0, kt + 1);
+  // Step kt (four per iteration, so that register sets are named statically):
+  // MFMAs of stage kt + 1 and scale FMAs of stage kt (or both of stage kt
+  // when not deferred), LDS store of stage kt + 2, loads of stage kt + 6, one
+  // barrier.  Every wave takes part in every barrier; a stage past the end is
+  // loaded and stored (clamped) but never computed.
+  const int nquad = (nkt + 3) >> 2;
+  for (int qd = 0; qd < nquad; ++qd) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const int kt = 4 * qd + h;
+      if constexpr (DEFER) {
+        if (kt + 1 < nkt) mma(P[(h + 1) & 1], kt + 1);
+        if (kt < nkt) scale(P[h & 1], kt);
+      } else {
+        if (kt < nkt) {
+          mma(P[0], kt);
+          scale(P[0], kt);
+        }
       }
+      lstore(R[(h + 2) & 3], kt + 2);
+      gload(R[(h + 2) & 3], kt + 6);
+      __syncthreads();
     }
-    lstore(rb, kt + 3);
-    gload(rb, kt + 5);
-    __syncthreads();
   }
 
   // ---- store: lane holds column bcol + 32 j, rows 8 (r / 4) + 4 hi + r % 4
   // of each 32 x 32 block; y = RNE_f16(sx acc + out_bias), or the f32 partial
   // sx acc of this split
   float* pout = part != nullptr ? part + static_cast<size_t>(split) * M * N : nullptr;
+  if (pout == nullptr && m0 + BM <= M && n0 + BN <= N && (N & 7) == 0 &&
+      (reinterpret_cast<uintptr_t>(y) & 15) == 0) {
+    // Whole tile, rows of y 16-byte aligned: the wave's results go through its
+    // own LDS area (the stage buffers are free after the loop's last barrier)
+    // and leave as 16-byte row pieces, a 64-byte row segment per four lanes,
+    // instead of 2-byte stores straight from the MFMA layout.
+    constexpr int TWM = 32 * MB, TWN = 32 * NB;
+    constexpr int EP = TWN + 8;    // staged row stride in halves (16-byte aligned rows)
+    constexpr int LPR = TWN / 8;   // lanes per row
+    constexpr int RPI = 64 / LPR;  // rows per store instruction
+    static_assert(static_cast<size_t>(A8_NT / 64) * TWM * EP * 2 <= A8_TILE_BYTES, "staging fits the stage buffers");
+    uint16_t* ep = reinterpret_cast<uint16_t*>(smem) + wave * TWM * EP;
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      float rs[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(&sxs[wm * TWM + 32 * i + 8 * q + 4 * hi]);
+        rs[4 * q] = v.x;
+        rs[4 * q + 1] = v.y;
+        rs[4 * q + 2] = v.z;
+        rs[4 * q + 3] = v.w;
+      }
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int c = 32 * j + (lane & 31);
+        const float o = ob != nullptr ? sb_to_f32<false>(ob[n0 + wn * TWN + c]) : 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          ep[(32 * i + 8 * (r >> 2) + 4 * hi + (r & 3)) * EP + c] = f32_to_f16_bits(acc[i][j][r] * rs[r] + o);
+      }
+    }
+    const int pc = lane % LPR, pr = lane / LPR;
+    uint16_t* yt = y + static_cast<size_t>(m0 + wm * TWM) * N + n0 + wn * TWN + 8 * pc;
+#pragma unroll
+    for (int q = 0; q < TWM / RPI; ++q) {
+      const int rr = RPI * q + pr;
+      *reinterpret_cast<u4*>(yt + static_cast<size_t>(rr) * N) = *reinterpret_cast<const u4*>(&ep[rr * EP + 8 * pc]);
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
     float rs[16];
