@@ -120,11 +120,12 @@ mxq_status run_qmv(const char* who, const void* x, const uint32_t* w, const void
   a.stream = static_cast<hipStream_t>(stream);
   // A few rows of f16 activations go to the matrix cores when the shape fills
   // the GPU (qsmk_shape): the K-split kernel for 4- or 8-bit codes, group 64
-  // or 128, K a multiple of 512 (in chunks beyond 4096), from 3 rows, or from
-  // 2 when K <= 3072 (qsmk_rows: there the decode kernel's two-row variant is
-  // slower; measured); else the 16-row-block kernel for 9..16 rows (one
-  // launch instead of two 8-row decode launches).  Both read x, and the
-  // K-split kernel the scales and biases, with 16-byte loads.
+  // or 128, K from 512 (in chunks beyond 4096; K not a multiple of 512, or
+  // scales / biases not 16-byte aligned, on its ragged variant), from 3 rows,
+  // or from 2 when K <= 3072 (qsmk_rows: there the decode kernel's two-row
+  // variant is slower; measured); else the 16-row-block kernel for 9..16 rows
+  // (one launch instead of two 8-row decode launches).  Both read x with
+  // 16-byte loads.
   // int8 activations take the K-split kernel's integer-MFMA variant from 3
   // rows, unchunked (K <= 4096: one row scale covers all of K); the decode
   // kernel's v_dot4 path is VALU-bound beyond a row or two, and at two rows it
@@ -132,8 +133,7 @@ mxq_status run_qmv(const char* who, const void* x, const uint32_t* w, const void
   // workgroup (measured on lm_head: 28.3 against 31.2 us).  If the K-chunk
   // workspace cannot be had, the call falls through to the kernels below.
   const bool few_i8 = act == kActI8 && M >= 3;
-  if ((act == kActF16 ? qsmk_rows(M, K) : few_i8) && aligned(x, 16) && aligned(scales, 16) &&
-      aligned(biases, 16) &&
+  if ((act == kActF16 ? qsmk_rows(M, K) : few_i8) && aligned(x, 16) &&
       mxq::qsmk_shape(M, N, K, bits, group_size, act == kActF16 && (fws || qsmk_chunks_ok(K, stream)), dev)) {
     a.x = static_cast<const uint16_t*>(x);
     a.y = static_cast<uint16_t*>(y);
@@ -498,6 +498,7 @@ const char* mxq_describe(const char* op, int64_t M, int64_t N, int64_t K, int bi
     desc = "qsmk_kernel<bits=" + std::to_string(bits) + ",sb=" + std::string(sb) + ",gs=" +
            std::to_string(group_size) + ",m=" + std::to_string(M) + ",waves=" + std::to_string(nw) +
            (a8 ? ",act=i8" : "") + (chunks > 1 ? ",kchunks=" + std::to_string(chunks) : std::string()) +
+           (K % 512 != 0 ? ",ragged" : "") +
            "> block=" + std::to_string(64 * nw) + " lds=" + std::to_string(mxq::qsmk_lds_bytes(nw, bits)) +
            (chunks > 1 ? "; qmm_split_reduce_kernel" : "");
     return desc.c_str();

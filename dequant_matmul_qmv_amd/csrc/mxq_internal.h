@@ -115,6 +115,9 @@ hipError_t launch_qsm(const QmvArgs& a, int M, const DeviceInfo& dev);
 // is not being captured (`chunks_ok`).  At least one 16-row block of W per
 // compute unit, counting every chunk.
 bool qsmk_split(int64_t K, int* waves, int* chunks);
+// The kernel's ragged variant: K not a multiple of 512, or scales / biases not
+// 16-byte aligned (loaded as 2-byte values).
+bool qsmk_ragged(int64_t K, const void* s, const void* b);
 bool qsmk_shape(int64_t M, int64_t N, int64_t K, int bits, int group_size, bool chunks_ok, const DeviceInfo& dev);
 size_t qsmk_lds_bytes(int waves, int bits);
 hipError_t launch_qsmk(const QmvArgs& a, int M, const DeviceInfo& dev);

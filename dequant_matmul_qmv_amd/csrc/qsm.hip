@@ -258,7 +258,13 @@ size_t qsmk_lds_bytes(int waves, int bits) {
 // each word; 8-bit: signed c - 128, the offset folded into the bias factor
 // b + 128 s), one v_mfma_i32_16x16x64_i8 per 64-code group (exact integer dot
 // products), the row scale applied at the end.
-template <int BITS, bool SB_BF16, int GSH, int NW, bool XI>
+// RG ("ragged"): K a multiple of the group size but not of 512 per slice, or
+// scales / biases not 16-byte aligned.  Slices may then end early or be empty:
+// activation groups past K are zeros (no load), W segments past the row's end
+// are loaded from the row's start instead (in bounds; their codes meet zero
+// activations), and scales and biases are loaded as 2-byte values with the
+// group index clamped and the values zeroed past the last group.
+template <int BITS, bool SB_BF16, int GSH, int NW, bool XI, bool RG>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void qsmk_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ W,
                                                    const uint16_t* __restrict__ S, const uint16_t* __restrict__ B,
                                                    uint16_t* __restrict__ y, const uint16_t* __restrict__ ob,
@@ -278,6 +284,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int kw = K * BITS / 32;
   const int G = K >> (6 + GSH);
   constexpr int SBN = kKsGroups >> GSH;  // real groups per slice: 8 (g64) or 4 (g128)
+  // 64-code groups of this slice inside K (ragged: fewer than 8, or none)
+  const int gvalid = RG ? min(kKsGroups, (K - ks0) >> 6) : kKsGroups;
 
   // ---- activations of this slice, in the A layout, and the group sums of
   // the D rows this lane holds
@@ -295,8 +303,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     float am = 0.0f;
 #pragma unroll
     for (int g = 0; g < kKsGroups; ++g) {
-      v[g][0] = c16 < M ? *reinterpret_cast<const u4*>(xp + 64 * g) : z;
-      v[g][1] = c16 < M ? *reinterpret_cast<const u4*>(xp + 64 * g + 8) : z;
+      const bool live = c16 < M && (!RG || g < gvalid);
+      v[g][0] = live ? *reinterpret_cast<const u4*>(xp + 64 * g) : z;
+      v[g][1] = live ? *reinterpret_cast<const u4*>(xp + 64 * g + 8) : z;
       am = fmaxf(am, fmaxf(absmax8_f16(v[g][0]), absmax8_f16(v[g][1])));
     }
     am = fmaxf(am, __shfl_xor(am, 16));
@@ -329,8 +338,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     const u4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int g = 0; g < kKsGroups; ++g) {
-      const u4 v0 = *reinterpret_cast<const u4*>(xp + 64 * g);
-      const u4 v1 = *reinterpret_cast<const u4*>(xp + 64 * g + 8);
+      const bool in_k = !RG || g < gvalid;
+      const u4 v0 = in_k ? *reinterpret_cast<const u4*>(xp + 64 * g) : z;
+      const u4 v1 = in_k ? *reinterpret_cast<const u4*>(xp + 64 * g + 8) : z;
       // k slots in the order of the code unpack: 4-bit pairs (x0, x4)
       // (x1, x5) ..., 8-bit natural order
       xa[g][0] = BITS == 4 ? perm_x_w4(c16 < M ? v0 : z) : (c16 < M ? v0 : z);
@@ -354,10 +364,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   struct Ld {
     u4 w[NLD];
     u4 s, b;     // SBN scales / biases of column c16 (g128: the low 8 bytes)
+    uint32_t sp, bp;  // ragged: this lane's two scales / biases (groups 2 kg, 2 kg + 1 of the slice)
     uint16_t o;  // output bias of column c16 (unused without one)
   };
   const int nrb = (N + 15) >> 4;
-  const uint32_t* wl = W + ks0 * BITS / 32 + 4 * c16;
+  // this lane's 16-byte segment of the slice, per 256-byte half (8-bit slices
+  // have two); ragged: a segment past the row's end reads the row's start
+  const uint32_t* wlh[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int wo = ks0 * BITS / 32 + 4 * c16 + 64 * h;  // words into the row
+    wlh[h] = W + ((!RG || 4 * wo + 16 <= K * BITS / 8) ? wo : 0);
+  }
+  const int gbase = ks0 >> (6 + GSH);  // the slice's first real group
   const uint16_t* obs = ob != nullptr ? ob : S;  // without an output bias: any N readable halves
   auto load = [&](Ld& d, int rb) __attribute__((always_inline)) {
     rb = min(rb, nrb - 1);
@@ -366,10 +385,29 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     for (int i = 0; i < NLD; ++i) {
       const int row = min(16 * rb + 4 * (i % 4) + kg, N - 1);
       d.w[i] = __builtin_nontemporal_load(
-          reinterpret_cast<const u4*>(wl + static_cast<size_t>(row) * kw + 64 * (i / 4)));
+          reinterpret_cast<const u4*>(wlh[i / 4] + static_cast<size_t>(row) * kw));
     }
     const size_t so = static_cast<size_t>(min(16 * rb + c16, N - 1)) * G + (ks0 >> (6 + GSH));
-    if constexpr (GSH == 0) {
+    if constexpr (RG) {
+      // 2-byte loads shared by the four lane groups: lane (c16, kg) fetches
+      // the scales and biases of groups 2 kg and 2 kg + 1 of its column (index
+      // clamped into the row, zero past the last group or the slice's real
+      // groups); step() gathers the column's eight with shuffles (here they
+      // would wait for the loads and stall the prefetch)
+      const size_t sr = static_cast<size_t>(min(16 * rb + c16, N - 1)) * G;
+      d.sp = 0u;
+      d.bp = 0u;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int u = 2 * kg + q;
+        const int gi = gbase + u;
+        const size_t at = sr + static_cast<size_t>(max(0, min(gi, G - 1)));
+        const bool ok = u < SBN && gi < G;
+        const uint32_t sv = S[at], bv = B[at];
+        d.sp |= (ok ? sv : 0u) << (16 * q);
+        d.bp |= (ok ? bv : 0u) << (16 * q);
+      }
+    } else if constexpr (GSH == 0) {
       d.s = __builtin_nontemporal_load(reinterpret_cast<const u4*>(S + so));
       d.b = __builtin_nontemporal_load(reinterpret_cast<const u4*>(B + so));
     } else {
@@ -390,8 +428,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     for (int i = 0; i < NLD; ++i)
       *reinterpret_cast<u4*>(wst + (4 * (i % 4) + kg) * kKsRow + 256 * (i / 4) + 16 * c16) = d.w[i];
     __builtin_amdgcn_wave_barrier();
-    const uint32_t sw[4] = {d.s.x, d.s.y, d.s.z, d.s.w};
-    const uint32_t bw[4] = {d.b.x, d.b.y, d.b.z, d.b.w};
+    uint32_t sw[4] = {d.s.x, d.s.y, d.s.z, d.s.w};
+    uint32_t bw[4] = {d.b.x, d.b.y, d.b.z, d.b.w};
+    if constexpr (RG) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {  // groups 2k, 2k + 1 come from lane group k
+        sw[k] = static_cast<uint32_t>(__shfl(static_cast<int>(d.sp), c16 + 16 * k));
+        bw[k] = static_cast<uint32_t>(__shfl(static_cast<int>(d.bp), c16 + 16 * k));
+      }
+    }
     const f4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
     // all groups' MFMAs first, each into its own registers, so that the
     // matrix core runs them back to back while the codes of the next group
@@ -496,8 +541,23 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   if (rb < nrb) step(cur, rb);
 }
 
+bool qsmk_ragged(int64_t K, const void* s, const void* b) {
+  return K % kKsCodes != 0 || (reinterpret_cast<uintptr_t>(s) & 15) != 0 || (reinterpret_cast<uintptr_t>(b) & 15) != 0;
+}
+
 bool qsmk_split(int64_t K, int* waves, int* chunks) {
-  if (K < kKsCodes || K % kKsCodes != 0) return false;
+  if (K < 64 || K % 64 != 0) return false;
+  if (K % kKsCodes != 0) {
+    if (K < kKsCodes) return false;  // a single partial slice: the other kernels
+    // ragged: ceil(K / 512) slices over the fewest chunks of at most
+    // kKsMaxWaves waves (the last slices may end early or be empty)
+    const int64_t S = (K + kKsCodes - 1) / kKsCodes;
+    const int64_t c = (S + kKsMaxWaves - 1) / kKsMaxWaves;
+    if (c > kKsMaxChunks) return false;
+    *chunks = static_cast<int>(c);
+    *waves = static_cast<int>((S + c - 1) / c);
+    return true;
+  }
   const int64_t S = K / kKsCodes;  // 512-code slices
   // the fewest chunks of at most kKsMaxWaves slices each that divide S
   for (int64_t c = (S + kKsMaxWaves - 1) / kKsMaxWaves; c <= S && c <= kKsMaxChunks; ++c) {
@@ -511,7 +571,8 @@ bool qsmk_split(int64_t K, int* waves, int* chunks) {
 }
 
 bool qsmk_shape(int64_t M, int64_t N, int64_t K, int bits, int group_size, bool chunks_ok, const DeviceInfo& dev) {
-  if ((bits != 4 && bits != 8) || M < 2 || M > 16 || (group_size != 64 && group_size != 128)) return false;
+  if ((bits != 4 && bits != 8) || M < 2 || M > 16 || (group_size != 64 && group_size != 128) || K % group_size != 0)
+    return false;
   int nw = 0, chunks = 0;
   if (!qsmk_split(K, &nw, &chunks)) return false;
   if (chunks > 1 && (!chunks_ok || (M * N) % 4 != 0 || N > INT_MAX / 16)) return false;
@@ -521,23 +582,27 @@ bool qsmk_shape(int64_t M, int64_t N, int64_t K, int bits, int group_size, bool 
 }
 
 namespace {
-template <int BITS, bool SB_BF16, int GSH, bool XI>
+template <int BITS, bool SB_BF16, int GSH, bool XI, bool RG>
 const void* qsmk_ptr_x(int nw) {
   switch (nw) {
-    case 1: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 1, XI>);
-    case 2: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 2, XI>);
-    case 3: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 3, XI>);
-    case 4: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 4, XI>);
-    case 5: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 5, XI>);
-    case 6: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 6, XI>);
-    case 7: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 7, XI>);
-    default: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 8, XI>);
+    case 1: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 1, XI, RG>);
+    case 2: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 2, XI, RG>);
+    case 3: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 3, XI, RG>);
+    case 4: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 4, XI, RG>);
+    case 5: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 5, XI, RG>);
+    case 6: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 6, XI, RG>);
+    case 7: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 7, XI, RG>);
+    default: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 8, XI, RG>);
   }
 }
+template <bool SB_BF16, int GSH, bool RG>
+const void* qsmk_ptr_r(int nw, int bits, bool xi) {
+  if (bits == 8) return xi ? qsmk_ptr_x<8, SB_BF16, GSH, true, RG>(nw) : qsmk_ptr_x<8, SB_BF16, GSH, false, RG>(nw);
+  return xi ? qsmk_ptr_x<4, SB_BF16, GSH, true, RG>(nw) : qsmk_ptr_x<4, SB_BF16, GSH, false, RG>(nw);
+}
 template <bool SB_BF16, int GSH>
-const void* qsmk_ptr(int nw, int bits, bool xi) {
-  if (bits == 8) return xi ? qsmk_ptr_x<8, SB_BF16, GSH, true>(nw) : qsmk_ptr_x<8, SB_BF16, GSH, false>(nw);
-  return xi ? qsmk_ptr_x<4, SB_BF16, GSH, true>(nw) : qsmk_ptr_x<4, SB_BF16, GSH, false>(nw);
+const void* qsmk_ptr(int nw, int bits, bool xi, bool rg) {
+  return rg ? qsmk_ptr_r<SB_BF16, GSH, true>(nw, bits, xi) : qsmk_ptr_r<SB_BF16, GSH, false>(nw, bits, xi);
 }
 }  // namespace
 
@@ -548,8 +613,9 @@ hipError_t launch_qsmk(const QmvArgs& a, int M, const DeviceInfo& dev) {
   const bool g128 = a.glog2 == 7;
   const bool xi = a.act == 2;  // int8 activations (quantized in the kernel)
   if (chunks > 1 && xi) return hipErrorInvalidValue;
-  const void* kern = a.sb_bf16 ? (g128 ? qsmk_ptr<true, 1>(nw, a.bits, xi) : qsmk_ptr<true, 0>(nw, a.bits, xi))
-                               : (g128 ? qsmk_ptr<false, 1>(nw, a.bits, xi) : qsmk_ptr<false, 0>(nw, a.bits, xi));
+  const bool rg = qsmk_ragged(a.K, a.s, a.b);
+  const void* kern = a.sb_bf16 ? (g128 ? qsmk_ptr<true, 1>(nw, a.bits, xi, rg) : qsmk_ptr<true, 0>(nw, a.bits, xi, rg))
+                               : (g128 ? qsmk_ptr<false, 1>(nw, a.bits, xi, rg) : qsmk_ptr<false, 0>(nw, a.bits, xi, rg));
   if (lds > 65536) {  // 8 waves of 8-bit slices
     const hipError_t e = ensure_dynamic_lds(kern, lds);
     if (e != hipSuccess) return e;

@@ -112,15 +112,18 @@ hipError_t launch_qsm(const QmvArgs& a, int M, const DeviceInfo&) {
 }
 
 bool qsmk_split(int64_t K, int* waves, int* chunks) {
-  if (K % 512 != 0 || K <= 0) return false;
-  const int64_t slices = K / 512;
+  if (K < 512 || K % 64 != 0) return false;
+  const int64_t slices = (K + 511) / 512;  // the last one may be partial (ragged K)
   *chunks = static_cast<int>((slices + 7) / 8);
-  *waves = static_cast<int>(slices / *chunks);
-  return *waves * *chunks == slices;
+  *waves = static_cast<int>((slices + *chunks - 1) / *chunks);
+  return true;
+}
+bool qsmk_ragged(int64_t K, const void* s, const void* b) {
+  return K % 512 != 0 || (reinterpret_cast<uintptr_t>(s) & 15) != 0 || (reinterpret_cast<uintptr_t>(b) & 15) != 0;
 }
 bool qsmk_shape(int64_t M, int64_t N, int64_t K, int, int group_size, bool chunks_ok, const DeviceInfo&) {
   int w = 0, c = 0;
-  if (M < 2 || M > 16 || group_size < 64 || !qsmk_split(K, &w, &c)) return false;
+  if (M < 2 || M > 16 || group_size < 64 || K % group_size != 0 || !qsmk_split(K, &w, &c)) return false;
   if (c > 1 && (!chunks_ok || (M * N) % 4 != 0)) return false;
   return N >= 4096;
 }

@@ -709,13 +709,15 @@ def test_int8_few_rows_integer_case_and_determinism():
     assert_close(y1, oracle.matmul_ref_a8(xv, w, s, b, K, 4, 64, "f16"), "a8 qsmk integer")
 
 
-# Few activation rows (9..16) with N large enough to fill the GPU, on shapes
-# the K-split kernel does not take (K not a multiple of 512, or above 4096): the
-# 16-row-block matrix-core kernel (qsm).  Sampled output columns against the
-# oracle, including the ragged tail.
+# Few activation rows with K a multiple of the group size but not of 512: the
+# K-split kernel's ragged variant (the last 512-code slice ends early; beyond
+# 4096 in chunks, the last chunk's slices may be empty).  Sampled output
+# columns against the oracle, including the ragged tail of N.
 QSM = [
     (9, 65600, 2112, 4, 64, "f16"), (10, 66000, 576, 8, 64, "bf16"), (16, 65536, 4352, 4, 128, "f16"),
     (13, 70001, 2624, 8, 64, "bf16"), (12, 65540, 6272, 8, 128, "f16"), (16, 128256, 1088, 8, 64, "f16"),
+    (2, 8192, 640, 4, 64, "f16"), (3, 4100, 2944, 4, 128, "bf16"), (5, 8192, 4032, 8, 64, "f16"),
+    (8, 16390, 1216, 4, 64, "bf16"), (4, 4096, 4160, 4, 64, "f16"), (7, 4116, 9024, 8, 64, "bf16"),
 ]
 
 
@@ -725,17 +727,88 @@ def _sampled_cols(N, seed):
 
 
 @pytest.mark.parametrize("case", QSM, ids=str)
-def test_few_rows_mfma(case):
+def test_few_rows_ksplit_ragged_k(case):
     M, N, K, bits, gs, sb = case
-    assert mxq.mxq_describe("qmv", M, N, K, bits, gs, sb).startswith("qsm_kernel"), case
-    assert not mxq.mxq_describe("qmv", 8, N, K, bits, gs, sb).startswith("qsm"), case
+    d = mxq.mxq_describe("qmv", M, N, K, bits, gs, sb)
+    assert d.startswith("qsmk_kernel") and ",ragged" in d, (case, d)
     p = synth.make_problem(M, N, K, bits, gs, sb, seed=M + N + K + 31)
     x, w, s, b = to_dev(p)
-    note(f"few-row mfma {case}")
+    note(f"few-row k-split ragged K {case}: {d}")
     y = y_host(mxq.mxq_qmv(x, w, s, b, bits=bits, group_size=gs))
+    if N * K <= 8192 * 2048:
+        assert_close(y, _ref(p), f"qsmk ragged {case}")
+    else:
+        cols = _sampled_cols(N, M)
+        ref = oracle.matmul_ref_rows(p.x, p.w, p.scales, p.biases, cols, K, bits, gs, sb)
+        assert_close(y[:, cols], ref, f"qsmk ragged {case}")
+
+
+def _shifted(t):
+    """The same values in a buffer whose start is 2 bytes past a 16-byte boundary."""
+    big = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+    v = big[1:].view(t.shape)
+    v.copy_(t)
+    assert v.data_ptr() % 16 == 2
+    return v
+
+
+@pytest.mark.parametrize("case", [(4, 8192, 2048, 4, 64, "f16"), (12, 65536, 1536, 8, 128, "bf16"),
+                                  (6, 4100, 2112, 4, 64, "f16"), (9, 8192, 8192, 4, 64, "f16")], ids=str)
+def test_few_rows_ksplit_unaligned_scales(case):
+    """Scales and biases 2-byte but not 16-byte aligned: the ragged variant's
+    2-byte scale and bias loads (before, the call left the matrix cores)."""
+    M, N, K, bits, gs, sb = case
+    p = synth.make_problem(M, N, K, bits, gs, sb, seed=M + N + K + 33)
+    x, w, s, b = to_dev(p)
+    s2, b2 = _shifted(s), _shifted(b)
+    note(f"few-row k-split unaligned scales {case}")
+    y = y_host(mxq.mxq_qmv(x, w, s2, b2, bits=bits, group_size=gs))
+    y_aligned = y_host(mxq.mxq_qmv(x, w, s, b, bits=bits, group_size=gs))
+    if K % 512 == 0:  # the same kernel arithmetic either way: bit-identical
+        assert np.array_equal(y.view(np.uint16), y_aligned.view(np.uint16)), case
     cols = _sampled_cols(N, M)
     ref = oracle.matmul_ref_rows(p.x, p.w, p.scales, p.biases, cols, K, bits, gs, sb)
-    assert_close(y[:, cols], ref, f"qsm {case}")
+    assert_close(y[:, cols], ref, f"qsmk unaligned scales {case}")
+
+
+@pytest.mark.parametrize("case", [(3, 8192, 2112, 4, 64, "f16"), (9, 4100, 1152, 8, 128, "bf16"),
+                                  (16, 65540, 3008, 4, 64, "f16")], ids=str)
+def test_int8_few_rows_ragged_k(case):
+    M, N, K, bits, gs, sb = case
+    d = mxq.mxq_describe("a8", M, N, K, bits, gs, sb)
+    assert d.startswith("qsmk_kernel") and ",act=i8" in d and ",ragged" in d, (case, d)
+    p = synth.make_problem(M, N, K, bits, gs, sb, seed=M + N + K + 49)
+    x, w, s, b = to_dev(p)
+    note(f"int8 few rows ragged K {case}")
+    y = y_host(mxq.mxq_linear_a8(x, w, s, b, bits=bits, group_size=gs))
+    cols = _sampled_cols(N, M)
+    ref = oracle.matmul_ref_a8(p.x, p.w[cols], p.scales[cols], p.biases[cols], K, bits, gs, sb)
+    assert_close(y[:, cols], ref, f"a8 qsmk ragged {case}")
+
+
+def test_few_rows_16_row_blocks_under_capture():
+    """9..16 rows at a ragged K beyond 4096 on a stream being captured (no K
+    chunks inside a graph): the 16-row-block kernel, every replay against the
+    oracle."""
+    M, N, K, bits, gs, sb = 12, 65540, 6272, 8, 128, "f16"
+    p = synth.make_problem(M, N, K, bits, gs, sb, seed=77)
+    x, w, s, b = to_dev(p)
+    y = torch.empty((M, N), dtype=torch.float16, device="cuda:0")
+    note("16-row-block kernel under graph capture")
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=st):
+        mxq.mxq_qmv(x, w, s, b, y, bits=bits, group_size=gs)
+    cols = _sampled_cols(N, M)
+    ref = oracle.matmul_ref_rows(p.x, p.w, p.scales, p.biases, cols, K, bits, gs, sb)
+    for r in range(3):
+        y.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert_close(y.cpu().numpy()[:, cols], ref, f"qsm captured replay {r}")
 
 
 # 2..16 rows, 4-bit codes, K a multiple of 512 up to 4096, at least 16 W rows per
@@ -905,10 +978,13 @@ def test_few_rows_ksplit_routing():
     assert d("qmv", 8, 128256, 2048, 8, 64, "f16").startswith("qsmk_kernel<bits=8")   # 8-bit codes
     assert d("a8", 8, 128256, 2048, 8, 64, "f16").startswith("qsmk_kernel<bits=8")  # int8 x with 8-bit codes
     assert d("a8", 8, 128256, 1536, 8, 64, "f16").startswith("qsmk_kernel<bits=8")  # K = 3 x 512: 3 waves
-    assert d("a8", 8, 128256, 2112, 8, 64, "f16").startswith("qmv_kernel")         # K not a multiple of 512
+    assert d("a8", 8, 128256, 2112, 8, 64, "f16").startswith("qsmk_kernel<bits=8,sb=f16,gs=64,m=8,waves=5,act=i8,ragged>")
+    assert d("a8", 8, 128256, 4160, 8, 64, "f16").startswith("qmv_kernel")         # ragged K in chunks: int8 x
     assert not d("qmv", 8, 128256, 2048, 4, 32, "f16").startswith("qsmk")   # group size 32
     assert d("qmv", 8, 128256, 1536, 4, 64, "f16").startswith("qsmk_kernel<bits=4,sb=f16,gs=64,m=8,waves=3>")
-    assert not d("qmv", 8, 128256, 2112, 4, 64, "f16").startswith("qsmk")   # K not a multiple of 512
+    assert d("qmv", 8, 128256, 2112, 4, 64, "f16").startswith("qsmk_kernel<bits=4,sb=f16,gs=64,m=8,waves=5,ragged>")
+    assert d("qmv", 8, 128256, 4160, 4, 64, "f16").startswith("qsmk_kernel<bits=4,sb=f16,gs=64,m=8,waves=5,kchunks=2,ragged>")
+    assert not d("qmv", 8, 128256, 448, 4, 64, "f16").startswith("qsmk")    # K below one 512-code slice
     assert d("qmv", 8, 128256, 8192, 4, 64, "f16").startswith("qsmk_kernel<bits=4,sb=f16,gs=64,m=8,waves=8,kchunks=2>")
     assert d("a8", 8, 128256, 8192, 4, 64, "f16").startswith("qmv_kernel")       # int8 x: one row scale over all K
     assert not d("qmv", 3, 128257, 8192, 4, 64, "f16").startswith("qsmk")   # chunks need M * N % 4 == 0
@@ -917,9 +993,9 @@ def test_few_rows_ksplit_routing():
 
 
 def test_few_rows_ksplit_misaligned_scales_and_determinism():
-    """Scales and biases only 2-byte aligned leave the K-split kernel (it reads
-    them with 16-byte loads) with the same result bar rounding order; its own
-    result is bit-identical from run to run."""
+    """Scales and biases only 2-byte aligned stay on the K-split kernel (its
+    ragged variant reads them as 2-byte values) with a bit-identical result;
+    the result is also bit-identical from run to run."""
     M, N, K = 6, 8192, 2048
     p = synth.make_problem(M, N, K, 4, 64, "f16", seed=77)
     x, w, s, b = to_dev(p)
@@ -935,7 +1011,7 @@ def test_few_rows_ksplit_misaligned_scales_and_determinism():
     y3 = y_host(mxq.mxq_qmv(x, w, s_off[1:].view(N, G), b_off[1:].view(N, G), bits=4))
     ref = _ref(p)
     assert_close(y1, ref, "qsmk aligned")
-    assert_close(y3, ref, "misaligned scales route")
+    assert np.array_equal(y1.view(np.uint16), y3.view(np.uint16)), "2-byte scale loads change no bit"
 
 
 @pytest.mark.parametrize("M", list(range(2, 17)))
