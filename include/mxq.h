@@ -98,17 +98,18 @@ int mxq_abi_version(void);
  * applied per group to partial sums, which is the same value up to f32
  * rounding).  The sum of epic #570's "dequant -> matmul" without the weight
  * ever leaving registers.  Accepts any M >= 0.  Routing by shape: one row
- * (and two at K > 2048) on the decode kernel; up to 16 rows on the matrix
+ * (and two at K > 3072) on the decode kernel; up to 16 rows on the matrix
  * cores when the shape fits them -- 4- or 8-bit codes, group size 64 or 128,
- * K a multiple of 512 and at least 16 rows of W per compute unit (from 3
- * rows, or 2 at K <= 3072); K beyond 4096 runs in chunks of up to 4096 codes
- * whose f32 partial results are added in a fixed order by a second kernel
- * (M * N a multiple of 4, counting the chunks toward the rows of W per
- * compute unit; calls on a stream being captured into a graph use the other
- * kernels instead), else 9..16 rows of any supported codes with at
- * least 256 rows of W per compute unit -- both with x (and for the first, the
- * scales and biases) 16-byte aligned; otherwise the decode kernel in slices
- * of at most 8 rows (each slice re-reads W).  N need not be a multiple of
+ * K at least 512 and at least 16 rows of W per compute unit (from 3 rows, or
+ * 2 at K <= 3072); K beyond 4096 runs in chunks of up to 4096 codes whose f32
+ * partial results are added in a fixed order by a second kernel (M * N a
+ * multiple of 4, counting the chunks toward the rows of W per compute unit;
+ * calls on a stream being captured into a graph use the other kernels
+ * instead); K not a multiple of 512, or scales / biases only 2-byte aligned,
+ * take the same kernel's ragged variant -- else 9..16 rows of any supported
+ * codes with at least 256 rows of W per compute unit on a 16-row-block
+ * kernel -- both with x 16-byte aligned; otherwise the decode kernel in
+ * slices of at most 8 rows (each slice re-reads W).  N need not be a multiple of
  * anything (ExecuTorch PR #17187 "Description": M = 1 with N not a multiple
  * of 4).
  * Results match the f64 definition within |y - y_ref| <= 2e-3 (1 + |y_ref|)
