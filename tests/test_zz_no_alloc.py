@@ -48,7 +48,7 @@ def _check_pair(p, tag):
     assert_close(b[:, cols], ref, f"no-alloc {tag}")
 
 
-@pytest.mark.parametrize("route", ["split_k", "k_chunks", "no_scratch"])
+@pytest.mark.parametrize("route", ["split_k", "k_chunks", "ragged_k_chunks", "no_scratch"])
 def test_noalloc_matches_qmm_twice_second_smaller(route):
     if route == "split_k":      # 4 splits x 512 x 2048 floats = 16 MiB, then 8 x 128 x 512 = 2 MiB
         first = synth.make_problem(512, 2048, 8192, 4, 64, "f16", seed=901)
@@ -60,6 +60,12 @@ def test_noalloc_matches_qmm_twice_second_smaller(route):
         second = synth.make_problem(3, 8192, 8192, 4, 128, "bf16", seed=904)
         for p in (first, second):
             assert "kchunks=" in mxq.mxq_describe("qmm", p.M, p.N, p.K, p.bits, p.group_size, p.sb_dtype)
+    elif route == "ragged_k_chunks":  # K not a multiple of 512, in chunks: 2 x 8 x 8192, then 3 x 5 x 4100 floats
+        first = synth.make_problem(8, 8192, 4160, 4, 64, "f16", seed=907)
+        second = synth.make_problem(5, 4100, 9024, 8, 64, "bf16", seed=908)
+        for p in (first, second):
+            d = mxq.mxq_describe("qmm", p.M, p.N, p.K, p.bits, p.group_size, p.sb_dtype)
+            assert "kchunks=" in d and ",ragged" in d, d
     else:                       # tiles alone fill the GPU: no scratch at all
         first = synth.make_problem(512, 8192, 2048, 4, 64, "f16", seed=905)
         second = synth.make_problem(200, 4096, 1024, 8, 64, "f16", seed=906)
