@@ -212,7 +212,8 @@ mxq_status run_matmul(const char* who, const void* x, const uint32_t* w, const v
     return e == hipSuccess ? MXQ_OK : hip_fail(who, e);
   }
   // The MFMA kernel stages x with 16-byte loads and walks K in stages of 64.
-  // int8 activations and the few-row shapes of f16 activations (qsmk_rows and
+  // int8 activations from 17 rows take the integer prefill kernel (below);
+  // other int8 calls and the few-row shapes of f16 activations (qsmk_rows and
   // qsmk_shape) take run_qmv's routing: the K-split matrix-core kernel where
   // it applies, else the decode kernel in 8-row slices.
   mxq::DeviceInfo dev;
