@@ -49,9 +49,10 @@ namespace mxq {
 namespace {
 constexpr int KT = 64;            // codes per stage
 constexpr int LDK = KT;           // LDS row of the x / code tiles: 64 halves (128 B), 16-byte pieces XOR-swizzled
-constexpr int RING = 24;          // groups held by the x-sum / scale / bias rings (a bias block + lookahead)
-constexpr int XGS = RING + 4;     // x-sum ring row stride in floats (112 B)
-constexpr int SBS = RING + 4;     // scale / bias ring row stride in halves (56 B: rows on distinct banks)
+constexpr int XRING = 24;         // groups held by the x-sum ring (a bias block + lookahead)
+constexpr int XGS = XRING + 4;    // x-sum ring row stride in floats (112 B)
+constexpr int SRING = 32;         // groups held by the scale / bias rings (two bias blocks)
+constexpr int SBS = SRING + 4;    // scale / bias ring row stride in halves (72 B: 8-byte aligned rows, distinct banks)
 constexpr int BIAS_BLOCK = 16;    // groups per bias MFMA (its K)
 
 // Position of 16-byte piece c (8 halves) within LDS row r.  Rows are 128 B,
@@ -139,11 +140,14 @@ struct QmmCfg {
   static constexpr int RPS = KT / RGC;               // ring groups per stage: 2 or 1
   static constexpr int KSPR = RGC / 16;              // MFMA k-steps per ring group
   static constexpr int NBUF = 4;                     // stage buffers: two computed, two being staged
+  static constexpr int BS = BIAS_BLOCK / RPS;        // stages per bias block: 16 or 8
+  static constexpr int SBL = BN / 32;                // scale / bias load steps per block (32 rows each)
   static constexpr size_t tile_bytes = static_cast<size_t>(NBUF * (BM + BN) * LDK) * 2;
   static constexpr size_t lds_bytes = tile_bytes + static_cast<size_t>(BM * XGS) * 4 +
                                       static_cast<size_t>(2 * BN * SBS) * 2;
   static_assert(XCH >= 1 && XCS % PT == 0, "x staging");
-  static_assert(RPS * BN <= PT, "one scale/bias load per thread per stage");
+  static_assert(BS / 2 >= 4 && BS / 2 + SBL <= BS, "scale / bias load window inside the second half of a block");
+  static_assert(lds_bytes <= 160 * 1024, "LDS of one CU");
   static_assert(static_cast<size_t>(4 * 64 * 16 * MB * NB) * 4 <= tile_bytes, "pipeline reduction fits");
 };
 
@@ -208,10 +212,7 @@ __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x
 
   // Loads address a wave-uniform base advanced per stage plus a 32-bit lane
   // offset fixed for the kernel (the host routes shapes whose in-tile offsets
-  // would not fit in 32 bits to the qmv kernel).  Thread tl also fetches one
-  // scale and one bias per stage: tile row tl % BN, the stage's
-  // (tl / BN)-th ring group (clamped: extra threads duplicate a load and
-  // later store the same value to the same place).
+  // would not fit in 32 bits to the qmv kernel).
   const char* xbase = reinterpret_cast<const char*>(x + static_cast<size_t>(m0) * K);
   const char* wbase = reinterpret_cast<const char*>(W + static_cast<size_t>(n0) * kw);
   const char* sbase = reinterpret_cast<const char*>(S + static_cast<size_t>(n0) * G);
@@ -230,16 +231,68 @@ __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x
     const int row = min(n0 + c / U4R, N - 1) - n0;
     woff[i] = static_cast<uint32_t>(row * kw + (c % U4R) * 4) * 4u;
   }
-  const int sb_row = tl % BN;
-  const int sb_e = min(tl / BN, RPS - 1);
-  const uint32_t sboff = static_cast<uint32_t>(min(n0 + sb_row, N - 1) - n0) * static_cast<uint32_t>(G) * 2u;
-  // real group of ring group rg
+  // real group of (global) ring group rg
   auto group_of = [&](int rg) __attribute__((always_inline)) { return GS <= KT ? rg : rg >> 1; };
+
+  // Scales and biases move in whole bias blocks (16 ring groups): a load step
+  // covers 32 tile rows x 8 pairs of ring slots, so a wave reads 8 rows x 32
+  // consecutive bytes where one scale per row and stage would touch 64 rows.
+  // Block b + 1 is fetched during stages BS/2 .. BS/2 + SBL - 1 of block b and
+  // lands in the ring slots of block b - 1, which nothing reads any more: the
+  // stores of stage kt follow, across the barriers, the computes of every
+  // stage up to kt - 4 (and kt - 4 >= the last stage of block b - 1).  Block 0
+  // is loaded before the main loop.  Thread tl handles slot pair tl % 8 of
+  // tile row 32 * step + tl / 8.
+  const int sb_p = tl & 7;
+  const int rg0 = kt0 * RPS;  // global ring group of this unit's first
+  // 0: one 4-byte load per pair (both groups in one aligned word), 1: one
+  // 2-byte load for both slots (a 128-code group's two ring groups), 2: two
+  // 2-byte loads
+  int sb_mode = 2;
+  if constexpr (GS > KT) {
+    if ((rg0 & 1) == 0) sb_mode = 1;
+  } else {
+    if (((G | rg0) & 1) == 0 && ((reinterpret_cast<uintptr_t>(S) | reinterpret_cast<uintptr_t>(B)) & 3) == 0)
+      sb_mode = 0;
+  }
+  auto sbload = [&](int blk, int lrow, uint32_t& s2, uint32_t& b2) __attribute__((always_inline)) {
+    const uint32_t roff = static_cast<uint32_t>(min(n0 + lrow, N - 1) - n0) * static_cast<uint32_t>(G) * 2u;
+    const char* sp = sbase + roff;
+    const char* bp = bbase + roff;
+    const int ga = rg0 + blk * BIAS_BLOCK + 2 * sb_p;  // global ring group of the pair's first slot
+    if (sb_mode == 0) {
+      const size_t go = static_cast<size_t>(min(ga, G - 2)) * 2;  // G even here
+      s2 = *reinterpret_cast<const uint32_t*>(sp + go);
+      b2 = *reinterpret_cast<const uint32_t*>(bp + go);
+    } else if (sb_mode == 1) {
+      const size_t go = static_cast<size_t>(min(group_of(ga), G - 1)) * 2;
+      const uint32_t sh = *reinterpret_cast<const uint16_t*>(sp + go);
+      const uint32_t bh = *reinterpret_cast<const uint16_t*>(bp + go);
+      s2 = sh | (sh << 16);
+      b2 = bh | (bh << 16);
+    } else {
+      const size_t g0 = static_cast<size_t>(min(group_of(ga), G - 1)) * 2;
+      const size_t g1 = static_cast<size_t>(min(group_of(ga + 1), G - 1)) * 2;
+      s2 = static_cast<uint32_t>(*reinterpret_cast<const uint16_t*>(sp + g0)) |
+           (static_cast<uint32_t>(*reinterpret_cast<const uint16_t*>(sp + g1)) << 16);
+      b2 = static_cast<uint32_t>(*reinterpret_cast<const uint16_t*>(bp + g0)) |
+           (static_cast<uint32_t>(*reinterpret_cast<const uint16_t*>(bp + g1)) << 16);
+    }
+  };
+  auto sbstore = [&](int blk, int lrow, uint32_t s2, uint32_t b2) __attribute__((always_inline)) {
+    const int slot = (blk * BIAS_BLOCK + 2 * sb_p) & (SRING - 1);
+    *reinterpret_cast<uint32_t*>(&sq[lrow * SBS + slot]) = s2;
+    *reinterpret_cast<uint32_t*>(&bq[lrow * SBS + slot]) = b2;
+  };
 
   u4 xr[XCH];
   u4 wr[WCH];
-  uint16_t sv, bv;
+  uint32_t sv, bv;
   auto gload = [&](int kt) __attribute__((always_inline)) {
+    {
+      const int kb = kt / C::BS, st = kt - kb * C::BS - C::BS / 2;
+      if (st >= 0 && st < C::SBL) sbload(kb + 1, 32 * st + (tl >> 3), sv, bv);
+    }
     kt = kt0 + min(kt, nkt - 1);  // global stage; the tail re-reads the last one, never stored where it is read
     // the stage's offsets are wave-uniform: kept in SGPRs (the empty asm stops
     // the compiler from folding them into 64-bit per-lane pointers), so each
@@ -252,14 +305,11 @@ __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x
     for (int i = 0; i < XCH; ++i) xr[i] = *reinterpret_cast<const u4*>(xb + xoff[i]);
 #pragma unroll
     for (int i = 0; i < WCH; ++i) wr[i] = *reinterpret_cast<const u4*>(wb + woff[i]);
-    const size_t go = static_cast<size_t>(group_of(kt * RPS + sb_e)) * 2;
-    sv = *reinterpret_cast<const uint16_t*>(sbase + go + sboff);
-    bv = *reinterpret_cast<const uint16_t*>(bbase + go + sboff);
   };
 
   // registers -> LDS for stage kt: x as loaded, codes unpacked to exact f16,
-  // x sums, scale and bias per ring group.  Stages past the last go to a
-  // buffer and ring slots nothing reads.
+  // x sums per ring group, and a block load step's scales and biases.
+  // Stages past the last go to a buffer and ring slots nothing reads.
   auto lstore = [&](int kt) __attribute__((always_inline)) {
     uint16_t* xs = xA + (kt & 3) * BM * LDK;
     uint16_t* qs = qB + (kt & 3) * BN * LDK;
@@ -271,7 +321,7 @@ __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x
       // x sums over each ring group, over the 8 (32-code groups: 4) lanes that
       // hold one row; every lane of the group writes the same value
       const float gsum = lane_group_sum<C::RGC == 32 ? 4 : 8>(sum8_act<XB>(xr[i]));
-      xg[row * XGS + (kt * RPS + (RPS == 2 ? (ch >> 2) : 0)) % RING] = gsum;
+      xg[row * XGS + (kt * RPS + (RPS == 2 ? (ch >> 2) : 0)) % XRING] = gsum;
     }
 #pragma unroll
     for (int i = 0; i < WCH; ++i) {
@@ -290,9 +340,8 @@ __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x
               XB ? unpack8_bf16_natural(wv[2 * k], wv[2 * k + 1]) : unpack8_natural(wv[2 * k], wv[2 * k + 1], up4.magic);
       }
     }
-    const int slot = (kt * RPS + sb_e) % RING;
-    sq[sb_row * SBS + slot] = sv;
-    bq[sb_row * SBS + slot] = bv;
+    const int kb = kt / C::BS, st = kt - kb * C::BS - C::BS / 2;
+    if (st >= 0 && st < C::SBL) sbstore(kb + 1, 32 * st + (tl >> 3), sv, bv);
   };
 
   f16x acc[MB][NB], P[MB][NB];
@@ -310,7 +359,8 @@ __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x
   auto bias_block = [&](int g0, int ng) __attribute__((always_inline)) {
     const int gb = 8 * hi;                       // this lane's first group of the block
     const int cnt = min(max(ng - gb, 0), 8);     // valid groups among this lane's 8
-    const int slot = (g0 + gb) % RING;          // 8 consecutive slots (RING is a multiple of 8)
+    const int slot = (g0 + gb) & (SRING - 1);   // 8 consecutive slots of each ring (both
+    const int xslot = (g0 + gb) % XRING;        // ring sizes are multiples of 8)
     u4 bhi[NB], blo[NB];
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
@@ -331,7 +381,7 @@ __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x
     }
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
-      const float* xp = &xg[(arow + i * 32) * XGS + slot];
+      const float* xp = &xg[(arow + i * 32) * XGS + xslot];
       const float4 a0 = *reinterpret_cast<const float4*>(xp);
       const float4 a1 = *reinterpret_cast<const float4*>(xp + 4);
       float xv[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
@@ -381,7 +431,7 @@ __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x
         const int rg = kt * RPS + kk / C::KSPR;
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
-          const float sc = sb_to_f32<SB_BF16>(sq[(bcol + j * 32) * SBS + rg % RING]);
+          const float sc = sb_to_f32<SB_BF16>(sq[(bcol + j * 32) * SBS + (rg & (SRING - 1))]);
 #pragma unroll
           for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -395,7 +445,14 @@ __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x
     }
   };
 
-  // ---- prologue: each pipeline's first stage in LDS, its second in registers
+  // ---- prologue: scales and biases of block 0; each pipeline's first stage
+  // in LDS, its second in registers
+#pragma unroll
+  for (int i = 0; i < C::SBL / 2; ++i) {  // 64 rows per pass over both pipelines
+    uint32_t s2, b2;
+    sbload(0, 64 * i + (t >> 3), s2, b2);
+    sbstore(0, 64 * i + (t >> 3), s2, b2);
+  }
   gload(pipe);
   lstore(pipe);
   gload(pipe + 2);

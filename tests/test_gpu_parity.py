@@ -145,6 +145,30 @@ def test_qmm_mfma(case):
     assert_close(_run("qmm", p), _ref(p), f"qmm {case}")
 
 
+@pytest.mark.parametrize("case", [(128, 1024, 5760, 4, 128, "f16"), (128, 1024, 5760, 4, 64, "bf16"),
+                                  (130, 1000, 5760, 8, 32, "f16")], ids=str)
+def test_qmm_split_k_odd_stage_count_and_misaligned_scales(case):
+    """K split into units of 9 stages (90 stages, 10 units): units start on odd
+    stages, so the scale / bias block loads of groups of 64 and 128 cannot take
+    aligned pairs of groups in every unit.  Scales and biases only 2-byte
+    aligned give a bit-identical result."""
+    M, N, K, bits, gs, sb = case
+    assert ",ksplit=10>" in mxq.mxq_describe("qmm", M, N, K, bits, gs, sb)
+    p = synth.make_problem(M, N, K, bits, gs, sb, seed=M + N + gs)
+    note(f"qmm split-K odd stages {case}")
+    x, w, s, b = to_dev(p)
+    y1 = y_host(mxq.mxq_qmm(x, w, s, b, bits=bits, group_size=gs))
+    assert_close(y1, _ref(p), f"qmm split-K odd stages {case}")
+    G = K // gs
+    s_off = torch.empty(N * G + 1, dtype=s.dtype, device="cuda:0")
+    b_off = torch.empty(N * G + 1, dtype=b.dtype, device="cuda:0")
+    s_off[1:].copy_(s.reshape(-1))
+    b_off[1:].copy_(b.reshape(-1))
+    note(f"qmm split-K odd stages, misaligned scales {case}")
+    y2 = y_host(mxq.mxq_qmm(x, w, s_off[1:].view(N, G), b_off[1:].view(N, G), bits=bits, group_size=gs))
+    assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16)), "2-byte scale loads change no bit"
+
+
 def _scale_regime_problem(M, N, K, gs, sb, regime, seed):
     """4-bit problem whose scales sit in one magnitude regime, biases zero and
     x rescaled by a power of two so that y stays well inside f16.
