@@ -431,7 +431,11 @@ __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x
         const int rg = kt * RPS + kk / C::KSPR;
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
-          const float sc = sb_to_f32<SB_BF16>(sq[(bcol + j * 32) * SBS + (rg & (SRING - 1))]);
+          // widened once: the empty asm keeps the compiler from folding the f16
+          // widening into each FMA (v_fma_mix_f32, VOP3P), which issues at half
+          // the rate of the two-operand v_fmac_f32 used instead
+          float sc = sb_to_f32<SB_BF16>(sq[(bcol + j * 32) * SBS + (rg & (SRING - 1))]);
+          asm volatile("" : "+v"(sc));
 #pragma unroll
           for (int i = 0; i < MB; ++i)
 #pragma unroll

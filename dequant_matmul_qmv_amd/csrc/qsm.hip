@@ -491,10 +491,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
     for (int g = 0; g < kKsGroups; ++g) {
       const int r = g >> GSH;
-      const float sc = sb_to_f32<SB_BF16>(static_cast<uint16_t>(sw[r >> 1] >> (16 * (r & 1))));
+      // scale and bias widened once: the empty asm keeps the compiler from
+      // folding the f16 widening into each of the FMAs below (v_fma_mix_f32,
+      // VOP3P, issued at half the rate of the two-operand v_fmac_f32)
+      float sc = sb_to_f32<SB_BF16>(static_cast<uint16_t>(sw[r >> 1] >> (16 * (r & 1))));
+      asm volatile("" : "+v"(sc));
       float bi = sb_to_f32<SB_BF16>(static_cast<uint16_t>(bw[r >> 1] >> (16 * (r & 1))));
       if constexpr (XI && BITS == 8) bi = __builtin_fmaf(128.0f, sc, bi);  // signed codes c - 128
       if constexpr (!XI && BITS == 4) bi = __builtin_fmaf(-64.0f, sc, bi);  // codes 64 + c
+      asm volatile("" : "+v"(bi));
       if constexpr (XI)
         p[g] = f4{static_cast<float>(pq[g][0]), static_cast<float>(pq[g][1]), static_cast<float>(pq[g][2]),
                   static_cast<float>(pq[g][3])};
