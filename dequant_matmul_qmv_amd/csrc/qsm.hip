@@ -237,6 +237,9 @@ constexpr int kKsMaxWaves = 8;
 constexpr int kKsMaxChunks = 64;             // K up to 64 * 4096 codes
 // staged row slice: 256 (4-bit) or 512 (8-bit) bytes + 16 bytes of pad
 __host__ __device__ constexpr int ks_row_bytes(int bits) { return kKsCodes * bits / 8 + 16; }
+// output staging for whole-line stores: [2][16 rows][64 columns + 8] halves
+constexpr int kKsYs = 72;
+constexpr int kKsYBytes = 2 * 16 * kKsYs * 2;
 }  // namespace
 
 // 4-bit word -> (64 + c0, 64 + c4), (64 + c1, 64 + c5), (64 + c2, 64 + c6),
@@ -250,7 +253,7 @@ __device__ __forceinline__ u4 unpack_w4_off64_mfma(uint32_t w, uint32_t magic) {
 }
 
 size_t qsmk_lds_bytes(int waves, int bits) {
-  return static_cast<size_t>(waves) * 16 * ks_row_bytes(bits) + static_cast<size_t>(2 * waves) * 64 * 16;
+  return static_cast<size_t>(waves) * 16 * ks_row_bytes(bits) + static_cast<size_t>(2 * waves) * 64 * 16 + kKsYBytes;
 }
 
 // XI: int8 activations -- each x row quantized in the kernel (per-row
@@ -264,11 +267,17 @@ size_t qsmk_lds_bytes(int waves, int bits) {
 // are loaded from the row's start instead (in bounds; their codes meet zero
 // activations), and scales and biases are loaded as 2-byte values with the
 // group index clamped and the values zeroed past the last group.
+// yq (whole-line y stores): workgroups take quads of 4 consecutive 16-row
+// blocks (64 columns of y) instead of single blocks; each block's outputs go
+// to an LDS tile and each quad leaves as 16-byte pieces, whole 128-byte row
+// segments of y, one block later.  A block's own 16 columns are only 32 bytes
+// of each y row, a quarter of a line.  Needs y 16-byte aligned, N a multiple
+// of 8 and no K chunks.
 template <int BITS, bool SB_BF16, int GSH, int NW, bool XI, bool RG>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void qsmk_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ W,
                                                    const uint16_t* __restrict__ S, const uint16_t* __restrict__ B,
                                                    uint16_t* __restrict__ y, const uint16_t* __restrict__ ob,
-                                                   float* __restrict__ part, int M, int N, int K) {
+                                                   float* __restrict__ part, int M, int N, int K, int yq) {
   constexpr int nw = NW;
   constexpr int kKsRow = ks_row_bytes(BITS);
   constexpr int NLD = BITS;  // 16-byte loads per lane and block: 4 (4-bit) or 8 (8-bit)
@@ -279,6 +288,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int kg = lane >> 4;   // k-slot group of the operands; D rows 4 kg .. 4 kg + 3
   unsigned char* wst = smem + wave * 16 * kKsRow;                      // [16][kKsRow] this wave's codes
   float* red = reinterpret_cast<float*>(smem + nw * 16 * kKsRow);     // [2][nw][64][4] partial tiles
+  uint16_t* ybuf = reinterpret_cast<uint16_t*>(red + 2 * nw * 64 * 4);  // [2][16][kKsYs] quads of y (yq)
   // this wave's 512 codes: chunk blockIdx.y of nw slices, then slice `wave`
   const int ks0 = (static_cast<int>(blockIdx.y) * nw + wave) * kKsCodes;
   const int kw = K * BITS / 32;
@@ -420,8 +430,20 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     d.o = obs[min(16 * rb + c16, N - 1)];  // unconditional: a load under a branch would drain the prefetch
   };
 
+  // yq: quad qi of this workgroup (rows 0..15, its 64 columns) from LDS to y
+  auto store_quad = [&](int qi) __attribute__((always_inline)) {
+    const int q = static_cast<int>(blockIdx.x) + qi * static_cast<int>(gridDim.x);
+    const uint16_t* yb = ybuf + (qi & 1) * 16 * kKsYs;
+    for (int idx = static_cast<int>(threadIdx.x); idx < 16 * 8; idx += 64 * nw) {
+      const int m = idx >> 3, pc = idx & 7;
+      const int n = 64 * q + 8 * pc;
+      if (m < M && n < N)
+        *reinterpret_cast<u4*>(y + static_cast<size_t>(m) * N + n) = *reinterpret_cast<const u4*>(yb + m * kKsYs + 8 * pc);
+    }
+  };
+
   int par = 0;
-  auto step = [&](const Ld& d, int rb) __attribute__((always_inline)) {
+  auto step = [&](const Ld& d, int rb, int t) __attribute__((always_inline)) {
     // codes to this wave's LDS region (row 4 (i % 4) + kg, bytes 256 (i / 4) +
     // 16 c16 .. of the slice)
 #pragma unroll
@@ -519,31 +541,45 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       // the row scale of D row m from lane m (i is wave-uniform but not a
       // constant: an array indexed by it would live in scratch memory)
       const float sxi = XI ? __shfl(sxl, m) : 1.0f;
-      if (m < M && n < N) {
+      if (yq) {
+        // position t & 3 of quad t >> 2; rows past M and columns past N are never stored
+        if (m < M) ybuf[(((t >> 2) & 1) * 16 + m) * kKsYs + 16 * (t & 3) + c16] = f32_to_f16_bits((XI ? v * sxi : v) + o);
+      } else if (m < M && n < N) {
         if (part != nullptr)  // one K chunk's f32 partial, [chunk][m][n]
           part[(static_cast<size_t>(blockIdx.y) * M + m) * N + n] = v;
         else
           y[static_cast<size_t>(m) * N + n] = f32_to_f16_bits((XI ? v * sxi : v) + o);
       }
     }
+    // the previous quad is complete in LDS: every wave passed this block's
+    // barrier after writing its last block
+    if (yq && (t & 3) == 0 && t > 0) store_quad((t >> 2) - 1);
     par ^= 1;
   };
 
-  // two register sets in ping-pong over this workgroup's blocks; a single
-  // loop exit keeps the load counters exact
-  const int stride = gridDim.x;
-  int rb = blockIdx.x;
+  // Block t of this workgroup: a grid stride over blocks, or (yq) over quads
+  // of 4 consecutive blocks.  Two register sets in ping-pong; a single loop
+  // exit keeps the load counters exact.
+  const int gs = static_cast<int>(gridDim.x), bx = static_cast<int>(blockIdx.x);
+  const int nq = (nrb + 3) >> 2;
+  const int nt = yq ? 4 * ((nq - bx + gs - 1) / gs) : (nrb - bx + gs - 1) / gs;  // the host launches gs <= nq (yq) or nrb
+  auto rb_of = [&](int t) __attribute__((always_inline)) { return yq ? 4 * (bx + (t >> 2) * gs) + (t & 3) : bx + t * gs; };
   Ld cur, alt;
-  load(cur, rb);
-  for (; rb + stride < nrb; rb += 2 * stride) {
-    load(alt, rb + stride);
+  load(cur, rb_of(0));
+  int t = 0;
+  for (; t + 1 < nt; t += 2) {
+    load(alt, rb_of(t + 1));
     __builtin_amdgcn_sched_barrier(0);
-    step(cur, rb);
-    load(cur, rb + 2 * stride);
+    step(cur, rb_of(t), t);
+    load(cur, rb_of(t + 2));
     __builtin_amdgcn_sched_barrier(0);
-    step(alt, rb + stride);
+    step(alt, rb_of(t + 1), t + 1);
   }
-  if (rb < nrb) step(cur, rb);
+  if (t < nt) step(cur, rb_of(t), t);
+  if (yq) {
+    __syncthreads();
+    store_quad((nt >> 2) - 1);
+  }
 }
 
 bool qsmk_ragged(int64_t K, const void* s, const void* b) {
@@ -633,7 +669,14 @@ hipError_t launch_qsmk(const QmvArgs& a, int M, const DeviceInfo& dev) {
   const int per_cu = occ < 2 ? occ : 2;
   const int64_t nrb = (a.N + 15) / 16;
   const int64_t cap = (static_cast<int64_t>(dev.num_cu) * per_cu + chunks - 1) / chunks;  // workgroups per chunk
-  const unsigned gx = static_cast<unsigned>(nrb < cap ? nrb : cap);
+  // whole-line y stores when there are quads of 4 blocks for every workgroup,
+  // from 10 rows: measured on lm_head's N (K = 2048), they save up to 1.4 us
+  // at 10-16 rows and cost 0.5-1.7 us at 2-8, where the stores are few and
+  // the strided order of the blocks that quads bring weighs more
+  const int64_t nq = (nrb + 3) / 4;
+  int yq = (chunks == 1 && M >= 10 && (reinterpret_cast<uintptr_t>(a.y) & 15) == 0 && a.N % 8 == 0 && nq >= cap)
+               ? 1 : 0;
+  const unsigned gx = static_cast<unsigned>(yq ? cap : (nrb < cap ? nrb : cap));
   const uint16_t* xp = a.x;
   const uint32_t* wp = a.w;
   const uint16_t* sp = a.s;
@@ -643,7 +686,7 @@ hipError_t launch_qsmk(const QmvArgs& a, int M, const DeviceInfo& dev) {
   int Mi = M, Ni = static_cast<int>(a.N), Ki = static_cast<int>(a.K);
   if (chunks == 1) {
     float* partp = nullptr;
-    void* args[] = {&xp, &wp, &sp, &bp, &yp, &obp, &partp, &Mi, &Ni, &Ki};
+    void* args[] = {&xp, &wp, &sp, &bp, &yp, &obp, &partp, &Mi, &Ni, &Ki, &yq};
     return hipLaunchKernel(kern, dim3(gx), dim3(64 * nw), args, lds, a.stream);
   }
   // K in chunks: f32 partial tiles [chunks, M, N] in the stream's split
@@ -653,7 +696,7 @@ hipError_t launch_qsmk(const QmvArgs& a, int M, const DeviceInfo& dev) {
   if (a.fixed_ws != nullptr) {  // the caller's workspace: no allocation
     if (bytes > a.fixed_ws_bytes) return hipErrorInvalidValue;  // the caller checks this first
     float* partp = a.fixed_ws;
-    void* args[] = {&xp, &wp, &sp, &bp, &yp, &no_ob, &partp, &Mi, &Ni, &Ki};
+    void* args[] = {&xp, &wp, &sp, &bp, &yp, &no_ob, &partp, &Mi, &Ni, &Ki, &yq};
     hipError_t e = hipLaunchKernel(kern, dim3(gx, static_cast<unsigned>(chunks)), dim3(64 * nw), args, lds, a.stream);
     if (e != hipSuccess) return e;
     return launch_split_reduce_f16(partp, obp, yp, M, a.N, chunks, a.stream);
@@ -661,7 +704,7 @@ hipError_t launch_qsmk(const QmvArgs& a, int M, const DeviceInfo& dev) {
   std::lock_guard<std::mutex> lk(split_workspace_mutex());
   float* partp = split_workspace_locked(dev.device, a.stream, bytes);
   if (partp == nullptr) return hipErrorOutOfMemory;
-  void* args[] = {&xp, &wp, &sp, &bp, &yp, &no_ob, &partp, &Mi, &Ni, &Ki};
+  void* args[] = {&xp, &wp, &sp, &bp, &yp, &no_ob, &partp, &Mi, &Ni, &Ki, &yq};
   hipError_t e = hipLaunchKernel(kern, dim3(gx, static_cast<unsigned>(chunks)), dim3(64 * nw), args, lds, a.stream);
   if (e != hipSuccess) return e;
   return launch_split_reduce_f16(partp, obp, yp, M, a.N, chunks, a.stream);

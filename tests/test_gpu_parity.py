@@ -1038,6 +1038,39 @@ def test_few_rows_ksplit_misaligned_scales_and_determinism():
     assert np.array_equal(y1.view(np.uint16), y3.view(np.uint16)), "2-byte scale loads change no bit"
 
 
+@pytest.mark.parametrize("case", [(11, 32776, 2048, 4, 64, "f16", "f16"), (16, 32776, 1024, 8, 128, "bf16", "f16"),
+                                  (12, 40000, 2048, 4, 64, "f16", "i8"), (10, 65544, 1536, 4, 64, "bf16", "f16")],
+                         ids=str)
+def test_few_rows_whole_line_y_stores(case):
+    """10-16 rows on the K-split kernel store y a quad of 4 blocks (64
+    columns) at a time from LDS.  N a multiple of 8 but not of 16 or 64 (a
+    last quad with one block of 8 columns), an output bias, int8 activations:
+    sampled columns against the oracle, and bit-identical to the same call
+    with y only 2-byte aligned, which stores each block directly."""
+    M, N, K, bits, gs, sb, act = case
+    assert mxq.mxq_describe("a8" if act == "i8" else "qmv", M, N, K, bits, gs, sb).startswith("qsmk_kernel")
+    p = synth.make_problem(M, N, K, bits, gs, sb, seed=M + N + 77)
+    ob = synth.make_out_bias(N, seed=78)
+    x, w, s, b = to_dev(p)
+    obt = torch.from_numpy(ob.view(np.int16)).view(torch.float16).to("cuda:0")
+    call = mxq.mxq_linear_a8 if act == "i8" else mxq.mxq_linear
+    note(f"few-row whole-line y {case}")
+    y1 = torch.empty((M, N), dtype=torch.float16, device="cuda:0")
+    call(x, w, s, b, obt, y1, bits=bits, group_size=gs)
+    y_off = torch.empty(M * N + 1, dtype=torch.float16, device="cuda:0")
+    y2 = y_off[1:].view(M, N)
+    call(x, w, s, b, obt, y2, bits=bits, group_size=gs)
+    y1h, y2h = y_host(y1), y_host(y2)
+    assert np.array_equal(y1h.view(np.uint16), y2h.view(np.uint16)), "quad stores change no bit"
+    cols = _sampled_cols(N, 300 + M)
+    if act == "i8":
+        ref = oracle.matmul_ref_a8(p.x, p.w[cols], p.scales[cols], p.biases[cols], K, bits, gs, sb)
+        ref = ref + ob.view(np.float16)[cols].astype(np.float64)
+    else:
+        ref = oracle.linear_ref(p.x, p.w[cols], p.scales[cols], p.biases[cols], ob[cols], K, bits, gs, sb)
+    assert_close(y1h[:, cols], ref, f"whole-line y {case}")
+
+
 @pytest.mark.parametrize("M", list(range(2, 17)))
 def test_few_rows_mfma_every_m(M):
     """Every row count the K-split few-row kernel takes, through mxq_linear
