@@ -267,18 +267,19 @@ size_t qsmk_lds_bytes(int waves, int bits) {
 // are loaded from the row's start instead (in bounds; their codes meet zero
 // activations), and scales and biases are loaded as 2-byte values with the
 // group index clamped and the values zeroed past the last group.
-// yq (whole-line y stores): workgroups take quads of 4 consecutive 16-row
+// YQ (whole-line y stores): workgroups take quads of 4 consecutive 16-row
 // blocks (64 columns of y) instead of single blocks; each block's outputs go
 // to an LDS tile and each quad leaves as 16-byte pieces, whole 128-byte row
 // segments of y, one block later.  A block's own 16 columns are only 32 bytes
 // of each y row, a quarter of a line.  Needs y 16-byte aligned, N a multiple
 // of 8 and no K chunks.
-template <int BITS, bool SB_BF16, int GSH, int NW, bool XI, bool RG>
+template <int BITS, bool SB_BF16, int GSH, int NW, bool XI, bool RG, bool YQ>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void qsmk_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ W,
                                                    const uint16_t* __restrict__ S, const uint16_t* __restrict__ B,
                                                    uint16_t* __restrict__ y, const uint16_t* __restrict__ ob,
-                                                   float* __restrict__ part, int M, int N, int K, int yq) {
+                                                   float* __restrict__ part, int M, int N, int K) {
   constexpr int nw = NW;
+  constexpr bool yq = YQ;
   constexpr int kKsRow = ks_row_bytes(BITS);
   constexpr int NLD = BITS;  // 16-byte loads per lane and block: 4 (4-bit) or 8 (8-bit)
   extern __shared__ __align__(16) unsigned char smem[];
@@ -288,7 +289,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int kg = lane >> 4;   // k-slot group of the operands; D rows 4 kg .. 4 kg + 3
   unsigned char* wst = smem + wave * 16 * kKsRow;                      // [16][kKsRow] this wave's codes
   float* red = reinterpret_cast<float*>(smem + nw * 16 * kKsRow);     // [2][nw][64][4] partial tiles
-  uint16_t* ybuf = reinterpret_cast<uint16_t*>(red + 2 * nw * 64 * 4);  // [2][16][kKsYs] quads of y (yq)
+  uint16_t* ybuf = reinterpret_cast<uint16_t*>(red + 2 * nw * 64 * 4);  // [2][16][kKsYs] quads of y (YQ)
   // this wave's 512 codes: chunk blockIdx.y of nw slices, then slice `wave`
   const int ks0 = (static_cast<int>(blockIdx.y) * nw + wave) * kKsCodes;
   const int kw = K * BITS / 32;
@@ -541,7 +542,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       // the row scale of D row m from lane m (i is wave-uniform but not a
       // constant: an array indexed by it would live in scratch memory)
       const float sxi = XI ? __shfl(sxl, m) : 1.0f;
-      if (yq) {
+      if constexpr (yq) {
         // position t & 3 of quad t >> 2; rows past M and columns past N are never stored
         if (m < M) ybuf[(((t >> 2) & 1) * 16 + m) * kKsYs + 16 * (t & 3) + c16] = f32_to_f16_bits((XI ? v * sxi : v) + o);
       } else if (m < M && n < N) {
@@ -553,30 +554,45 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     }
     // the previous quad is complete in LDS: every wave passed this block's
     // barrier after writing its last block
-    if (yq && (t & 3) == 0 && t > 0) store_quad((t >> 2) - 1);
+    if constexpr (yq) {
+      if ((t & 3) == 0 && t > 0) store_quad((t >> 2) - 1);
+    }
     par ^= 1;
   };
 
-  // Block t of this workgroup: a grid stride over blocks, or (yq) over quads
-  // of 4 consecutive blocks.  Two register sets in ping-pong; a single loop
-  // exit keeps the load counters exact.
-  const int gs = static_cast<int>(gridDim.x), bx = static_cast<int>(blockIdx.x);
-  const int nq = (nrb + 3) >> 2;
-  const int nt = yq ? 4 * ((nq - bx + gs - 1) / gs) : (nrb - bx + gs - 1) / gs;  // the host launches gs <= nq (yq) or nrb
-  auto rb_of = [&](int t) __attribute__((always_inline)) { return yq ? 4 * (bx + (t >> 2) * gs) + (t & 3) : bx + t * gs; };
+  // Two register sets in ping-pong over this workgroup's blocks; a single
+  // loop exit keeps the load counters exact.
   Ld cur, alt;
-  load(cur, rb_of(0));
-  int t = 0;
-  for (; t + 1 < nt; t += 2) {
-    load(alt, rb_of(t + 1));
-    __builtin_amdgcn_sched_barrier(0);
-    step(cur, rb_of(t), t);
-    load(cur, rb_of(t + 2));
-    __builtin_amdgcn_sched_barrier(0);
-    step(alt, rb_of(t + 1), t + 1);
-  }
-  if (t < nt) step(cur, rb_of(t), t);
-  if (yq) {
+  if constexpr (!yq) {
+    // a grid stride over blocks
+    const int stride = gridDim.x;
+    int rb = blockIdx.x;
+    load(cur, rb);
+    for (; rb + stride < nrb; rb += 2 * stride) {
+      load(alt, rb + stride);
+      __builtin_amdgcn_sched_barrier(0);
+      step(cur, rb, 0);
+      load(cur, rb + 2 * stride);
+      __builtin_amdgcn_sched_barrier(0);
+      step(alt, rb + stride, 0);
+    }
+    if (rb < nrb) step(cur, rb, 0);
+  } else {
+    // a grid stride over quads of 4 consecutive blocks: block t of this
+    // workgroup is position t & 3 of its quad t >> 2 (the host launches at
+    // most one workgroup per quad)
+    const int gs = static_cast<int>(gridDim.x), bx = static_cast<int>(blockIdx.x);
+    const int nt = 4 * ((((nrb + 3) >> 2) - bx + gs - 1) / gs);
+    auto rb_of = [&](int t) __attribute__((always_inline)) { return 4 * (bx + (t >> 2) * gs) + (t & 3); };
+    load(cur, rb_of(0));
+    for (int t = 0; t < nt; t += 2) {  // nt is a multiple of 4
+      load(alt, rb_of(t + 1));
+      __builtin_amdgcn_sched_barrier(0);
+      step(cur, rb_of(t), t);
+      load(cur, rb_of(t + 2));
+      __builtin_amdgcn_sched_barrier(0);
+      step(alt, rb_of(t + 1), t + 1);
+    }
     __syncthreads();
     store_quad((nt >> 2) - 1);
   }
@@ -623,27 +639,30 @@ bool qsmk_shape(int64_t M, int64_t N, int64_t K, int bits, int group_size, bool 
 }
 
 namespace {
-template <int BITS, bool SB_BF16, int GSH, bool XI, bool RG>
+template <int BITS, bool SB_BF16, int GSH, bool XI, bool RG, bool YQ>
 const void* qsmk_ptr_x(int nw) {
   switch (nw) {
-    case 1: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 1, XI, RG>);
-    case 2: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 2, XI, RG>);
-    case 3: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 3, XI, RG>);
-    case 4: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 4, XI, RG>);
-    case 5: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 5, XI, RG>);
-    case 6: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 6, XI, RG>);
-    case 7: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 7, XI, RG>);
-    default: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 8, XI, RG>);
+    case 1: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 1, XI, RG, YQ>);
+    case 2: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 2, XI, RG, YQ>);
+    case 3: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 3, XI, RG, YQ>);
+    case 4: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 4, XI, RG, YQ>);
+    case 5: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 5, XI, RG, YQ>);
+    case 6: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 6, XI, RG, YQ>);
+    case 7: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 7, XI, RG, YQ>);
+    default: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 8, XI, RG, YQ>);
   }
 }
-template <bool SB_BF16, int GSH, bool RG>
+template <bool SB_BF16, int GSH, bool RG, bool YQ>
 const void* qsmk_ptr_r(int nw, int bits, bool xi) {
-  if (bits == 8) return xi ? qsmk_ptr_x<8, SB_BF16, GSH, true, RG>(nw) : qsmk_ptr_x<8, SB_BF16, GSH, false, RG>(nw);
-  return xi ? qsmk_ptr_x<4, SB_BF16, GSH, true, RG>(nw) : qsmk_ptr_x<4, SB_BF16, GSH, false, RG>(nw);
+  if (bits == 8)
+    return xi ? qsmk_ptr_x<8, SB_BF16, GSH, true, RG, YQ>(nw) : qsmk_ptr_x<8, SB_BF16, GSH, false, RG, YQ>(nw);
+  return xi ? qsmk_ptr_x<4, SB_BF16, GSH, true, RG, YQ>(nw) : qsmk_ptr_x<4, SB_BF16, GSH, false, RG, YQ>(nw);
 }
+// whole-line stores (YQ) only on the aligned variant
 template <bool SB_BF16, int GSH>
-const void* qsmk_ptr(int nw, int bits, bool xi, bool rg) {
-  return rg ? qsmk_ptr_r<SB_BF16, GSH, true>(nw, bits, xi) : qsmk_ptr_r<SB_BF16, GSH, false>(nw, bits, xi);
+const void* qsmk_ptr(int nw, int bits, bool xi, bool rg, bool yq) {
+  if (rg) return qsmk_ptr_r<SB_BF16, GSH, true, false>(nw, bits, xi);
+  return yq ? qsmk_ptr_r<SB_BF16, GSH, false, true>(nw, bits, xi) : qsmk_ptr_r<SB_BF16, GSH, false, false>(nw, bits, xi);
 }
 }  // namespace
 
@@ -655,8 +674,11 @@ hipError_t launch_qsmk(const QmvArgs& a, int M, const DeviceInfo& dev) {
   const bool xi = a.act == 2;  // int8 activations (quantized in the kernel)
   if (chunks > 1 && xi) return hipErrorInvalidValue;
   const bool rg = qsmk_ragged(a.K, a.s, a.b);
-  const void* kern = a.sb_bf16 ? (g128 ? qsmk_ptr<true, 1>(nw, a.bits, xi, rg) : qsmk_ptr<true, 0>(nw, a.bits, xi, rg))
-                               : (g128 ? qsmk_ptr<false, 1>(nw, a.bits, xi, rg) : qsmk_ptr<false, 0>(nw, a.bits, xi, rg));
+  auto pick = [&](bool yq) {
+    return a.sb_bf16 ? (g128 ? qsmk_ptr<true, 1>(nw, a.bits, xi, rg, yq) : qsmk_ptr<true, 0>(nw, a.bits, xi, rg, yq))
+                     : (g128 ? qsmk_ptr<false, 1>(nw, a.bits, xi, rg, yq) : qsmk_ptr<false, 0>(nw, a.bits, xi, rg, yq));
+  };
+  const void* kern = pick(false);
   if (lds > 65536) {  // 8 waves of 8-bit slices
     const hipError_t e = ensure_dynamic_lds(kern, lds);
     if (e != hipSuccess) return e;
@@ -673,9 +695,18 @@ hipError_t launch_qsmk(const QmvArgs& a, int M, const DeviceInfo& dev) {
   // from 10 rows: measured on lm_head's N (K = 2048), they save up to 1.4 us
   // at 10-16 rows and cost 0.5-1.7 us at 2-8, where the stores are few and
   // the strided order of the blocks that quads bring weighs more
+  // (the aligned variant only; the same registers and LDS as the kernel the
+  // occupancy above was taken for)
   const int64_t nq = (nrb + 3) / 4;
-  int yq = (chunks == 1 && M >= 10 && (reinterpret_cast<uintptr_t>(a.y) & 15) == 0 && a.N % 8 == 0 && nq >= cap)
-               ? 1 : 0;
+  const bool yq = chunks == 1 && !rg && M >= 10 && (reinterpret_cast<uintptr_t>(a.y) & 15) == 0 && a.N % 8 == 0 &&
+                  nq >= cap;
+  if (yq) {
+    kern = pick(true);
+    if (lds > 65536) {
+      const hipError_t e = ensure_dynamic_lds(kern, lds);
+      if (e != hipSuccess) return e;
+    }
+  }
   const unsigned gx = static_cast<unsigned>(yq ? cap : (nrb < cap ? nrb : cap));
   const uint16_t* xp = a.x;
   const uint32_t* wp = a.w;
@@ -686,7 +717,7 @@ hipError_t launch_qsmk(const QmvArgs& a, int M, const DeviceInfo& dev) {
   int Mi = M, Ni = static_cast<int>(a.N), Ki = static_cast<int>(a.K);
   if (chunks == 1) {
     float* partp = nullptr;
-    void* args[] = {&xp, &wp, &sp, &bp, &yp, &obp, &partp, &Mi, &Ni, &Ki, &yq};
+    void* args[] = {&xp, &wp, &sp, &bp, &yp, &obp, &partp, &Mi, &Ni, &Ki};
     return hipLaunchKernel(kern, dim3(gx), dim3(64 * nw), args, lds, a.stream);
   }
   // K in chunks: f32 partial tiles [chunks, M, N] in the stream's split
@@ -696,7 +727,7 @@ hipError_t launch_qsmk(const QmvArgs& a, int M, const DeviceInfo& dev) {
   if (a.fixed_ws != nullptr) {  // the caller's workspace: no allocation
     if (bytes > a.fixed_ws_bytes) return hipErrorInvalidValue;  // the caller checks this first
     float* partp = a.fixed_ws;
-    void* args[] = {&xp, &wp, &sp, &bp, &yp, &no_ob, &partp, &Mi, &Ni, &Ki, &yq};
+    void* args[] = {&xp, &wp, &sp, &bp, &yp, &no_ob, &partp, &Mi, &Ni, &Ki};
     hipError_t e = hipLaunchKernel(kern, dim3(gx, static_cast<unsigned>(chunks)), dim3(64 * nw), args, lds, a.stream);
     if (e != hipSuccess) return e;
     return launch_split_reduce_f16(partp, obp, yp, M, a.N, chunks, a.stream);
@@ -704,7 +735,7 @@ hipError_t launch_qsmk(const QmvArgs& a, int M, const DeviceInfo& dev) {
   std::lock_guard<std::mutex> lk(split_workspace_mutex());
   float* partp = split_workspace_locked(dev.device, a.stream, bytes);
   if (partp == nullptr) return hipErrorOutOfMemory;
-  void* args[] = {&xp, &wp, &sp, &bp, &yp, &no_ob, &partp, &Mi, &Ni, &Ki, &yq};
+  void* args[] = {&xp, &wp, &sp, &bp, &yp, &no_ob, &partp, &Mi, &Ni, &Ki};
   hipError_t e = hipLaunchKernel(kern, dim3(gx, static_cast<unsigned>(chunks)), dim3(64 * nw), args, lds, a.stream);
   if (e != hipSuccess) return e;
   return launch_split_reduce_f16(partp, obp, yp, M, a.N, chunks, a.stream);
