@@ -290,8 +290,9 @@ __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x
   uint32_t sv, bv;
   auto gload = [&](int kt) __attribute__((always_inline)) {
     {
+      // (block kb + 1 only if this unit has one)
       const int kb = kt / C::BS, st = kt - kb * C::BS - C::BS / 2;
-      if (st >= 0 && st < C::SBL) sbload(kb + 1, 32 * st + (tl >> 3), sv, bv);
+      if (st >= 0 && st < C::SBL && (kb + 1) * C::BS < nkt) sbload(kb + 1, 32 * st + (tl >> 3), sv, bv);
     }
     kt = kt0 + min(kt, nkt - 1);  // global stage; the tail re-reads the last one, never stored where it is read
     // the stage's offsets are wave-uniform: kept in SGPRs (the empty asm stops
@@ -341,7 +342,7 @@ __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x
       }
     }
     const int kb = kt / C::BS, st = kt - kb * C::BS - C::BS / 2;
-    if (st >= 0 && st < C::SBL) sbstore(kb + 1, 32 * st + (tl >> 3), sv, bv);
+    if (st >= 0 && st < C::SBL && (kb + 1) * C::BS < nkt) sbstore(kb + 1, 32 * st + (tl >> 3), sv, bv);
   };
 
   f16x acc[MB][NB], P[MB][NB];
