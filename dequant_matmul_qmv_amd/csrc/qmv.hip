@@ -541,12 +541,28 @@ __global__ __launch_bounds__(kQmvBlock) void qmv_kernel(const QmvBatch batch) {
       const int live = VP >> s;  // values still live per lane before this stage
       if (live >= 2) {
         const int h = live / 2;
-        const bool upper = (lane & off) != 0;
+        if (off >= 16) {
+          // gfx950's lane swaps do the exchange in one VALU op per pair, no
+          // LDS crossbar and no selects: v_permlane32_swap trades the upper
+          // half of v[i] for the lower half of v[i + h] (v_permlane16_swap:
+          // the odd 16-lane rows for the even ones), so that v[i] + v[i + h]
+          // afterwards is the sum with the partner lane `off` away of v[i] in
+          // the lanes with bit `off` clear and of v[i + h] in the others
 #pragma unroll
-        for (int i = 0; i < h; ++i) {
-          const float send = upper ? v[i] : v[i + h];
-          const float keep = upper ? v[i + h] : v[i];
-          v[i] = keep + __shfl_xor(send, off, kWave);
+          for (int i = 0; i < h; ++i) {
+            const auto sw = off == 32
+                                ? __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i + h]), false, false)
+                                : __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i + h]), false, false);
+            v[i] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+          }
+        } else {
+          const bool upper = (lane & off) != 0;
+#pragma unroll
+          for (int i = 0; i < h; ++i) {
+            const float send = upper ? v[i] : v[i + h];
+            const float keep = upper ? v[i + h] : v[i];
+            v[i] = keep + __shfl_xor(send, off, kWave);
+          }
         }
       }
     }
