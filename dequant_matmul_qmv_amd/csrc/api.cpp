@@ -3,9 +3,11 @@
 // mid-run" guards in "What is already in-tree"), dispatch, and the host packer.
 #include <hip/hip_runtime.h>
 
+#include <map>
 #include <mutex>
+#include <set>
 #include <string>
-#include <unordered_set>
+#include <tuple>
 #include <vector>
 
 #include "../../include/mxq.h"
@@ -30,7 +32,9 @@ constexpr int kActF16 = 0, kActBF16 = 1, kActI8 = 2;
 constexpr int kMaxDevices = 64;
 std::mutex g_mu;
 mxq::DeviceInfo g_dev[kMaxDevices];
-std::unordered_set<std::string>* g_lds_done = nullptr;
+// kernels whose dynamic-LDS limit was raised, and cached occupancies, per device
+std::set<std::tuple<const void*, int, size_t>>* g_lds_done = nullptr;
+std::map<std::tuple<const void*, int, int, size_t>, int>* g_occ = nullptr;
 
 // Shared validation of the fused entry points; fills the common fields.
 mxq_status check_fused(const char* who, const void* x, const uint32_t* w, const void* scales,
@@ -302,11 +306,10 @@ hipError_t ensure_dynamic_lds(const void* kernel, size_t bytes) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  const std::string key = std::to_string(reinterpret_cast<uintptr_t>(kernel)) + ":" +
-                          std::to_string(dev) + ":" + std::to_string(bytes);
+  const auto key = std::make_tuple(kernel, dev, bytes);
   {
     std::lock_guard<std::mutex> lk(g_mu);
-    if (!g_lds_done) g_lds_done = new std::unordered_set<std::string>();
+    if (!g_lds_done) g_lds_done = new std::set<std::tuple<const void*, int, size_t>>();
     if (g_lds_done->count(key)) return hipSuccess;
   }
   e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
@@ -314,6 +317,29 @@ hipError_t ensure_dynamic_lds(const void* kernel, size_t bytes) {
   std::lock_guard<std::mutex> lk(g_mu);
   g_lds_done->insert(key);
   return hipSuccess;
+}
+
+int occupancy_blocks(const void* kernel, int threads, size_t lds) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 1;
+  }
+  const auto key = std::make_tuple(kernel, dev, threads, lds);
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (!g_occ) g_occ = new std::map<std::tuple<const void*, int, int, size_t>, int>();
+    const auto it = g_occ->find(key);
+    if (it != g_occ->end()) return it->second;
+  }
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, threads, lds) != hipSuccess || nb < 1) {
+    (void)hipGetLastError();
+    nb = 1;
+  }
+  std::lock_guard<std::mutex> lk(g_mu);
+  (*g_occ)[key] = nb;
+  return nb;
 }
 
 }  // namespace mxq

@@ -21,6 +21,12 @@ hipError_t device_info(DeviceInfo* out);
 // Raise a kernel's dynamic-LDS limit once per (kernel, device).
 hipError_t ensure_dynamic_lds(const void* kernel, size_t bytes);
 
+// Workgroups of `threads` threads with `lds` bytes of dynamic LDS that fit on
+// one compute unit of the current device (at least 1), queried once per
+// (kernel, device, threads, lds) and cached: the query costs host time on
+// every launch otherwise.
+int occupancy_blocks(const void* kernel, int threads, size_t lds);
+
 // Up to kMaxGroup independent qmv problems sharing one launch (bits, group
 // size, scale dtype and the activation row count are common).  Passed by value
 // as the kernel argument: no device allocation, safe under graph capture.

@@ -683,11 +683,7 @@ hipError_t launch_qsmk(const QmvArgs& a, int M, const DeviceInfo& dev) {
     const hipError_t e = ensure_dynamic_lds(kern, lds);
     if (e != hipSuccess) return e;
   }
-  int occ = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, 64 * nw, lds) != hipSuccess || occ < 1) {
-    (void)hipGetLastError();
-    occ = 1;
-  }
+  const int occ = occupancy_blocks(kern, 64 * nw, lds);
   const int per_cu = occ < 2 ? occ : 2;
   const int64_t nrb = (a.N + 15) / 16;
   const int64_t cap = (static_cast<int64_t>(dev.num_cu) * per_cu + chunks - 1) / chunks;  // workgroups per chunk

@@ -40,6 +40,10 @@ hipError_t hipDeviceGetAttribute(int* v, hipDeviceAttribute_t attr, int d) {
 }
 
 hipError_t hipFuncSetAttribute(const void*, hipFuncAttribute, int) { return hipSuccess; }
+hipError_t hipOccupancyMaxActiveBlocksPerMultiprocessor(int* n, const void*, int, size_t) {
+  *n = 2;
+  return hipSuccess;
+}
 hipError_t hipGetLastError(void) { return hipSuccess; }
 const char* hipGetErrorName(hipError_t) { return "hipErrorStub"; }
 const char* hipGetErrorString(hipError_t) { return "stub error"; }
