@@ -298,6 +298,73 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   // 64-code groups of this slice inside K (ragged: fewer than 8, or none)
   const int gvalid = RG ? min(kKsGroups, (K - ks0) >> 6) : kKsGroups;
 
+  // Loads of one block (indices clamped: branch-free; a block past the end
+  // re-reads the last one and is never stored).
+  struct Ld {
+    u4 w[NLD];
+    u4 s, b;     // SBN scales / biases of column c16 (g128: the low 8 bytes)
+    uint32_t sp, bp;  // ragged: this lane's two scales / biases (groups 2 kg, 2 kg + 1 of the slice)
+    uint16_t o;  // output bias of column c16 (unused without one)
+  };
+  const int nrb = (N + 15) >> 4;
+  // this lane's 16-byte segment of the slice, per 256-byte half (8-bit slices
+  // have two); ragged: a segment past the row's end reads the row's start
+  const uint32_t* wlh[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int wo = ks0 * BITS / 32 + 4 * c16 + 64 * h;  // words into the row
+    wlh[h] = W + ((!RG || 4 * wo + 16 <= K * BITS / 8) ? wo : 0);
+  }
+  const int gbase = ks0 >> (6 + GSH);  // the slice's first real group
+  const uint16_t* obs = ob != nullptr ? ob : S;  // without an output bias: any N readable halves
+  auto load = [&](Ld& d, int rb) __attribute__((always_inline)) {
+    rb = min(rb, nrb - 1);
+    // instruction i: rows 4 (i % 4) + kg, the (i / 4)-th 256 bytes of the slice
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int row = min(16 * rb + 4 * (i % 4) + kg, N - 1);
+      d.w[i] = __builtin_nontemporal_load(
+          reinterpret_cast<const u4*>(wlh[i / 4] + static_cast<size_t>(row) * kw));
+    }
+    const size_t so = static_cast<size_t>(min(16 * rb + c16, N - 1)) * G + (ks0 >> (6 + GSH));
+    if constexpr (RG) {
+      // 2-byte loads shared by the four lane groups: lane (c16, kg) fetches
+      // the scales and biases of groups 2 kg and 2 kg + 1 of its column (index
+      // clamped into the row, zero past the last group or the slice's real
+      // groups); step() gathers the column's eight with shuffles (here they
+      // would wait for the loads and stall the prefetch)
+      const size_t sr = static_cast<size_t>(min(16 * rb + c16, N - 1)) * G;
+      d.sp = 0u;
+      d.bp = 0u;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int u = 2 * kg + q;
+        const int gi = gbase + u;
+        const size_t at = sr + static_cast<size_t>(max(0, min(gi, G - 1)));
+        const bool ok = u < SBN && gi < G;
+        const uint32_t sv = S[at], bv = B[at];
+        d.sp |= (ok ? sv : 0u) << (16 * q);
+        d.bp |= (ok ? bv : 0u) << (16 * q);
+      }
+    } else if constexpr (GSH == 0) {
+      d.s = __builtin_nontemporal_load(reinterpret_cast<const u4*>(S + so));
+      d.b = __builtin_nontemporal_load(reinterpret_cast<const u4*>(B + so));
+    } else {
+      typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+      const u2 sv = __builtin_nontemporal_load(reinterpret_cast<const u2*>(S + so));
+      const u2 bv = __builtin_nontemporal_load(reinterpret_cast<const u2*>(B + so));
+      d.s = u4{sv.x, sv.y, 0u, 0u};
+      d.b = u4{bv.x, bv.y, 0u, 0u};
+    }
+    d.o = obs[min(16 * rb + c16, N - 1)];  // unconditional: a load under a branch would drain the prefetch
+  };
+
+  Ld cur, alt;
+  // The first block's loads go out before the activation work below: the
+  // weight stream starts while the activations are loaded, summed (and, for
+  // int8 activations, quantized across the waves).
+  load(cur, YQ ? 4 * static_cast<int>(blockIdx.x) : static_cast<int>(blockIdx.x));
+
   // ---- activations of this slice, in the A layout, and the group sums of
   // the D rows this lane holds
   u4 xa[kKsGroups][2];
@@ -369,67 +436,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 
   uint32_t magic = BITS == 4 ? kMagic64 : kMagic;
   asm volatile("" : "+v"(magic));  // opaque to the compiler: the unpack becomes v_and_or_b32 / v_bfi_b32
-
-  // Loads of one block (indices clamped: branch-free; a block past the end
-  // re-reads the last one and is never stored).
-  struct Ld {
-    u4 w[NLD];
-    u4 s, b;     // SBN scales / biases of column c16 (g128: the low 8 bytes)
-    uint32_t sp, bp;  // ragged: this lane's two scales / biases (groups 2 kg, 2 kg + 1 of the slice)
-    uint16_t o;  // output bias of column c16 (unused without one)
-  };
-  const int nrb = (N + 15) >> 4;
-  // this lane's 16-byte segment of the slice, per 256-byte half (8-bit slices
-  // have two); ragged: a segment past the row's end reads the row's start
-  const uint32_t* wlh[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int wo = ks0 * BITS / 32 + 4 * c16 + 64 * h;  // words into the row
-    wlh[h] = W + ((!RG || 4 * wo + 16 <= K * BITS / 8) ? wo : 0);
-  }
-  const int gbase = ks0 >> (6 + GSH);  // the slice's first real group
-  const uint16_t* obs = ob != nullptr ? ob : S;  // without an output bias: any N readable halves
-  auto load = [&](Ld& d, int rb) __attribute__((always_inline)) {
-    rb = min(rb, nrb - 1);
-    // instruction i: rows 4 (i % 4) + kg, the (i / 4)-th 256 bytes of the slice
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int row = min(16 * rb + 4 * (i % 4) + kg, N - 1);
-      d.w[i] = __builtin_nontemporal_load(
-          reinterpret_cast<const u4*>(wlh[i / 4] + static_cast<size_t>(row) * kw));
-    }
-    const size_t so = static_cast<size_t>(min(16 * rb + c16, N - 1)) * G + (ks0 >> (6 + GSH));
-    if constexpr (RG) {
-      // 2-byte loads shared by the four lane groups: lane (c16, kg) fetches
-      // the scales and biases of groups 2 kg and 2 kg + 1 of its column (index
-      // clamped into the row, zero past the last group or the slice's real
-      // groups); step() gathers the column's eight with shuffles (here they
-      // would wait for the loads and stall the prefetch)
-      const size_t sr = static_cast<size_t>(min(16 * rb + c16, N - 1)) * G;
-      d.sp = 0u;
-      d.bp = 0u;
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int u = 2 * kg + q;
-        const int gi = gbase + u;
-        const size_t at = sr + static_cast<size_t>(max(0, min(gi, G - 1)));
-        const bool ok = u < SBN && gi < G;
-        const uint32_t sv = S[at], bv = B[at];
-        d.sp |= (ok ? sv : 0u) << (16 * q);
-        d.bp |= (ok ? bv : 0u) << (16 * q);
-      }
-    } else if constexpr (GSH == 0) {
-      d.s = __builtin_nontemporal_load(reinterpret_cast<const u4*>(S + so));
-      d.b = __builtin_nontemporal_load(reinterpret_cast<const u4*>(B + so));
-    } else {
-      typedef uint32_t u2 __attribute__((ext_vector_type(2)));
-      const u2 sv = __builtin_nontemporal_load(reinterpret_cast<const u2*>(S + so));
-      const u2 bv = __builtin_nontemporal_load(reinterpret_cast<const u2*>(B + so));
-      d.s = u4{sv.x, sv.y, 0u, 0u};
-      d.b = u4{bv.x, bv.y, 0u, 0u};
-    }
-    d.o = obs[min(16 * rb + c16, N - 1)];  // unconditional: a load under a branch would drain the prefetch
-  };
 
   // yq: quad qi of this workgroup (rows 0..15, its 64 columns) from LDS to y
   auto store_quad = [&](int qi) __attribute__((always_inline)) {
@@ -560,14 +566,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     par ^= 1;
   };
 
-  // Two register sets in ping-pong over this workgroup's blocks; a single
-  // loop exit keeps the load counters exact.
-  Ld cur, alt;
+  // Two register sets in ping-pong over this workgroup's blocks (the first
+  // block is in cur); a single loop exit keeps the load counters exact.
   if constexpr (!yq) {
     // a grid stride over blocks
     const int stride = gridDim.x;
     int rb = blockIdx.x;
-    load(cur, rb);
     for (; rb + stride < nrb; rb += 2 * stride) {
       load(alt, rb + stride);
       __builtin_amdgcn_sched_barrier(0);
@@ -584,7 +588,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     const int gs = static_cast<int>(gridDim.x), bx = static_cast<int>(blockIdx.x);
     const int nt = 4 * ((((nrb + 3) >> 2) - bx + gs - 1) / gs);
     auto rb_of = [&](int t) __attribute__((always_inline)) { return 4 * (bx + (t >> 2) * gs) + (t & 3); };
-    load(cur, rb_of(0));
     for (int t = 0; t < nt; t += 2) {  // nt is a multiple of 4
       load(alt, rb_of(t + 1));
       __builtin_amdgcn_sched_barrier(0);
