@@ -237,9 +237,6 @@ constexpr int kKsMaxWaves = 8;
 constexpr int kKsMaxChunks = 64;             // K up to 64 * 4096 codes
 // staged row slice: 256 (4-bit) or 512 (8-bit) bytes + 16 bytes of pad
 __host__ __device__ constexpr int ks_row_bytes(int bits) { return kKsCodes * bits / 8 + 16; }
-// output staging for whole-line stores: [2][16 rows][64 columns + 8] halves
-constexpr int kKsYs = 72;
-constexpr int kKsYBytes = 2 * 16 * kKsYs * 2;
 }  // namespace
 
 // 4-bit word -> (64 + c0, 64 + c4), (64 + c1, 64 + c5), (64 + c2, 64 + c6),
@@ -253,7 +250,7 @@ __device__ __forceinline__ u4 unpack_w4_off64_mfma(uint32_t w, uint32_t magic) {
 }
 
 size_t qsmk_lds_bytes(int waves, int bits) {
-  return static_cast<size_t>(waves) * 16 * ks_row_bytes(bits) + static_cast<size_t>(2 * waves) * 64 * 16 + kKsYBytes;
+  return static_cast<size_t>(waves) * 16 * ks_row_bytes(bits) + static_cast<size_t>(2 * waves) * 64 * 16;
 }
 
 // XI: int8 activations -- each x row quantized in the kernel (per-row
@@ -267,19 +264,12 @@ size_t qsmk_lds_bytes(int waves, int bits) {
 // are loaded from the row's start instead (in bounds; their codes meet zero
 // activations), and scales and biases are loaded as 2-byte values with the
 // group index clamped and the values zeroed past the last group.
-// YQ (whole-line y stores): workgroups take quads of 4 consecutive 16-row
-// blocks (64 columns of y) instead of single blocks; each block's outputs go
-// to an LDS tile and each quad leaves as 16-byte pieces, whole 128-byte row
-// segments of y, one block later.  A block's own 16 columns are only 32 bytes
-// of each y row, a quarter of a line.  Needs y 16-byte aligned, N a multiple
-// of 8 and no K chunks.
-template <int BITS, bool SB_BF16, int GSH, int NW, bool XI, bool RG, bool YQ>
+template <int BITS, bool SB_BF16, int GSH, int NW, bool XI, bool RG>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void qsmk_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ W,
                                                    const uint16_t* __restrict__ S, const uint16_t* __restrict__ B,
                                                    uint16_t* __restrict__ y, const uint16_t* __restrict__ ob,
                                                    float* __restrict__ part, int M, int N, int K) {
   constexpr int nw = NW;
-  constexpr bool yq = YQ;
   constexpr int kKsRow = ks_row_bytes(BITS);
   constexpr int NLD = BITS;  // 16-byte loads per lane and block: 4 (4-bit) or 8 (8-bit)
   extern __shared__ __align__(16) unsigned char smem[];
@@ -289,7 +279,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int kg = lane >> 4;   // k-slot group of the operands; D rows 4 kg .. 4 kg + 3
   unsigned char* wst = smem + wave * 16 * kKsRow;                      // [16][kKsRow] this wave's codes
   float* red = reinterpret_cast<float*>(smem + nw * 16 * kKsRow);     // [2][nw][64][4] partial tiles
-  uint16_t* ybuf = reinterpret_cast<uint16_t*>(red + 2 * nw * 64 * 4);  // [2][16][kKsYs] quads of y (YQ)
   // this wave's 512 codes: chunk blockIdx.y of nw slices, then slice `wave`
   const int ks0 = (static_cast<int>(blockIdx.y) * nw + wave) * kKsCodes;
   const int kw = K * BITS / 32;
@@ -359,11 +348,22 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     d.o = obs[min(16 * rb + c16, N - 1)];  // unconditional: a load under a branch would drain the prefetch
   };
 
+  // Workgroups walk the blocks with a grid stride.  In each round of the
+  // stride, workgroup w = 32 a + 8 j + x takes block 32 a + 4 x + j: the
+  // workgroups are dispatched to the 8 XCDs in turn (x = w % 8 is w's XCD),
+  // so the 4 blocks that share each 128-byte line of y (64 columns) are
+  // computed on one XCD at the same time, and their 32-byte pieces of the
+  // line meet in that XCD's L2 before it is written back (lm_head at 8-16
+  // rows about 1 us faster).  Grids that are not a multiple of 32 keep the
+  // plain order.
+  const int first_rb = (gridDim.x % 32 == 0) ? static_cast<int>((blockIdx.x & ~31u) | ((blockIdx.x & 7u) << 2) |
+                                                                ((blockIdx.x >> 3) & 3u))
+                                             : static_cast<int>(blockIdx.x);
   Ld cur, alt;
   // The first block's loads go out before the activation work below: the
   // weight stream starts while the activations are loaded, summed (and, for
   // int8 activations, quantized across the waves).
-  load(cur, YQ ? 4 * static_cast<int>(blockIdx.x) : static_cast<int>(blockIdx.x));
+  load(cur, first_rb);
 
   // ---- activations of this slice, in the A layout, and the group sums of
   // the D rows this lane holds
@@ -437,20 +437,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   uint32_t magic = BITS == 4 ? kMagic64 : kMagic;
   asm volatile("" : "+v"(magic));  // opaque to the compiler: the unpack becomes v_and_or_b32 / v_bfi_b32
 
-  // yq: quad qi of this workgroup (rows 0..15, its 64 columns) from LDS to y
-  auto store_quad = [&](int qi) __attribute__((always_inline)) {
-    const int q = static_cast<int>(blockIdx.x) + qi * static_cast<int>(gridDim.x);
-    const uint16_t* yb = ybuf + (qi & 1) * 16 * kKsYs;
-    for (int idx = static_cast<int>(threadIdx.x); idx < 16 * 8; idx += 64 * nw) {
-      const int m = idx >> 3, pc = idx & 7;
-      const int n = 64 * q + 8 * pc;
-      if (m < M && n < N)
-        *reinterpret_cast<u4*>(y + static_cast<size_t>(m) * N + n) = *reinterpret_cast<const u4*>(yb + m * kKsYs + 8 * pc);
-    }
-  };
-
   int par = 0;
-  auto step = [&](const Ld& d, int rb, int t) __attribute__((always_inline)) {
+  auto step = [&](const Ld& d, int rb) __attribute__((always_inline)) {
     // codes to this wave's LDS region (row 4 (i % 4) + kg, bytes 256 (i / 4) +
     // 16 c16 .. of the slice)
 #pragma unroll
@@ -548,57 +536,29 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       // the row scale of D row m from lane m (i is wave-uniform but not a
       // constant: an array indexed by it would live in scratch memory)
       const float sxi = XI ? __shfl(sxl, m) : 1.0f;
-      if constexpr (yq) {
-        // position t & 3 of quad t >> 2; rows past M and columns past N are never stored
-        if (m < M) ybuf[(((t >> 2) & 1) * 16 + m) * kKsYs + 16 * (t & 3) + c16] = f32_to_f16_bits((XI ? v * sxi : v) + o);
-      } else if (m < M && n < N) {
+      if (m < M && n < N) {
         if (part != nullptr)  // one K chunk's f32 partial, [chunk][m][n]
           part[(static_cast<size_t>(blockIdx.y) * M + m) * N + n] = v;
         else
           y[static_cast<size_t>(m) * N + n] = f32_to_f16_bits((XI ? v * sxi : v) + o);
       }
     }
-    // the previous quad is complete in LDS: every wave passed this block's
-    // barrier after writing its last block
-    if constexpr (yq) {
-      if ((t & 3) == 0 && t > 0) store_quad((t >> 2) - 1);
-    }
     par ^= 1;
   };
 
   // Two register sets in ping-pong over this workgroup's blocks (the first
   // block is in cur); a single loop exit keeps the load counters exact.
-  if constexpr (!yq) {
-    // a grid stride over blocks
-    const int stride = gridDim.x;
-    int rb = blockIdx.x;
-    for (; rb + stride < nrb; rb += 2 * stride) {
-      load(alt, rb + stride);
-      __builtin_amdgcn_sched_barrier(0);
-      step(cur, rb, 0);
-      load(cur, rb + 2 * stride);
-      __builtin_amdgcn_sched_barrier(0);
-      step(alt, rb + stride, 0);
-    }
-    if (rb < nrb) step(cur, rb, 0);
-  } else {
-    // a grid stride over quads of 4 consecutive blocks: block t of this
-    // workgroup is position t & 3 of its quad t >> 2 (the host launches at
-    // most one workgroup per quad)
-    const int gs = static_cast<int>(gridDim.x), bx = static_cast<int>(blockIdx.x);
-    const int nt = 4 * ((((nrb + 3) >> 2) - bx + gs - 1) / gs);
-    auto rb_of = [&](int t) __attribute__((always_inline)) { return 4 * (bx + (t >> 2) * gs) + (t & 3); };
-    for (int t = 0; t < nt; t += 2) {  // nt is a multiple of 4
-      load(alt, rb_of(t + 1));
-      __builtin_amdgcn_sched_barrier(0);
-      step(cur, rb_of(t), t);
-      load(cur, rb_of(t + 2));
-      __builtin_amdgcn_sched_barrier(0);
-      step(alt, rb_of(t + 1), t + 1);
-    }
-    __syncthreads();
-    store_quad((nt >> 2) - 1);
+  const int stride = gridDim.x;
+  int rb = first_rb;
+  for (; rb + stride < nrb; rb += 2 * stride) {
+    load(alt, rb + stride);
+    __builtin_amdgcn_sched_barrier(0);
+    step(cur, rb);
+    load(cur, rb + 2 * stride);
+    __builtin_amdgcn_sched_barrier(0);
+    step(alt, rb + stride);
   }
+  if (rb < nrb) step(cur, rb);
 }
 
 bool qsmk_ragged(int64_t K, const void* s, const void* b) {
@@ -642,30 +602,27 @@ bool qsmk_shape(int64_t M, int64_t N, int64_t K, int bits, int group_size, bool 
 }
 
 namespace {
-template <int BITS, bool SB_BF16, int GSH, bool XI, bool RG, bool YQ>
+template <int BITS, bool SB_BF16, int GSH, bool XI, bool RG>
 const void* qsmk_ptr_x(int nw) {
   switch (nw) {
-    case 1: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 1, XI, RG, YQ>);
-    case 2: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 2, XI, RG, YQ>);
-    case 3: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 3, XI, RG, YQ>);
-    case 4: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 4, XI, RG, YQ>);
-    case 5: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 5, XI, RG, YQ>);
-    case 6: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 6, XI, RG, YQ>);
-    case 7: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 7, XI, RG, YQ>);
-    default: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 8, XI, RG, YQ>);
+    case 1: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 1, XI, RG>);
+    case 2: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 2, XI, RG>);
+    case 3: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 3, XI, RG>);
+    case 4: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 4, XI, RG>);
+    case 5: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 5, XI, RG>);
+    case 6: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 6, XI, RG>);
+    case 7: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 7, XI, RG>);
+    default: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 8, XI, RG>);
   }
 }
-template <bool SB_BF16, int GSH, bool RG, bool YQ>
+template <bool SB_BF16, int GSH, bool RG>
 const void* qsmk_ptr_r(int nw, int bits, bool xi) {
-  if (bits == 8)
-    return xi ? qsmk_ptr_x<8, SB_BF16, GSH, true, RG, YQ>(nw) : qsmk_ptr_x<8, SB_BF16, GSH, false, RG, YQ>(nw);
-  return xi ? qsmk_ptr_x<4, SB_BF16, GSH, true, RG, YQ>(nw) : qsmk_ptr_x<4, SB_BF16, GSH, false, RG, YQ>(nw);
+  if (bits == 8) return xi ? qsmk_ptr_x<8, SB_BF16, GSH, true, RG>(nw) : qsmk_ptr_x<8, SB_BF16, GSH, false, RG>(nw);
+  return xi ? qsmk_ptr_x<4, SB_BF16, GSH, true, RG>(nw) : qsmk_ptr_x<4, SB_BF16, GSH, false, RG>(nw);
 }
-// whole-line stores (YQ) only on the aligned variant
 template <bool SB_BF16, int GSH>
-const void* qsmk_ptr(int nw, int bits, bool xi, bool rg, bool yq) {
-  if (rg) return qsmk_ptr_r<SB_BF16, GSH, true, false>(nw, bits, xi);
-  return yq ? qsmk_ptr_r<SB_BF16, GSH, false, true>(nw, bits, xi) : qsmk_ptr_r<SB_BF16, GSH, false, false>(nw, bits, xi);
+const void* qsmk_ptr(int nw, int bits, bool xi, bool rg) {
+  return rg ? qsmk_ptr_r<SB_BF16, GSH, true>(nw, bits, xi) : qsmk_ptr_r<SB_BF16, GSH, false>(nw, bits, xi);
 }
 }  // namespace
 
@@ -677,11 +634,8 @@ hipError_t launch_qsmk(const QmvArgs& a, int M, const DeviceInfo& dev) {
   const bool xi = a.act == 2;  // int8 activations (quantized in the kernel)
   if (chunks > 1 && xi) return hipErrorInvalidValue;
   const bool rg = qsmk_ragged(a.K, a.s, a.b);
-  auto pick = [&](bool yq) {
-    return a.sb_bf16 ? (g128 ? qsmk_ptr<true, 1>(nw, a.bits, xi, rg, yq) : qsmk_ptr<true, 0>(nw, a.bits, xi, rg, yq))
-                     : (g128 ? qsmk_ptr<false, 1>(nw, a.bits, xi, rg, yq) : qsmk_ptr<false, 0>(nw, a.bits, xi, rg, yq));
-  };
-  const void* kern = pick(false);
+  const void* kern = a.sb_bf16 ? (g128 ? qsmk_ptr<true, 1>(nw, a.bits, xi, rg) : qsmk_ptr<true, 0>(nw, a.bits, xi, rg))
+                               : (g128 ? qsmk_ptr<false, 1>(nw, a.bits, xi, rg) : qsmk_ptr<false, 0>(nw, a.bits, xi, rg));
   if (lds > 65536) {  // 8 waves of 8-bit slices
     const hipError_t e = ensure_dynamic_lds(kern, lds);
     if (e != hipSuccess) return e;
@@ -690,23 +644,7 @@ hipError_t launch_qsmk(const QmvArgs& a, int M, const DeviceInfo& dev) {
   const int per_cu = occ < 2 ? occ : 2;
   const int64_t nrb = (a.N + 15) / 16;
   const int64_t cap = (static_cast<int64_t>(dev.num_cu) * per_cu + chunks - 1) / chunks;  // workgroups per chunk
-  // whole-line y stores when there are quads of 4 blocks for every workgroup,
-  // from 10 rows: measured on lm_head's N (K = 2048), they save up to 1.4 us
-  // at 10-16 rows and cost 0.5-1.7 us at 2-8, where the stores are few and
-  // the strided order of the blocks that quads bring weighs more
-  // (the aligned variant only; the same registers and LDS as the kernel the
-  // occupancy above was taken for)
-  const int64_t nq = (nrb + 3) / 4;
-  const bool yq = chunks == 1 && !rg && M >= 10 && (reinterpret_cast<uintptr_t>(a.y) & 15) == 0 && a.N % 8 == 0 &&
-                  nq >= cap;
-  if (yq) {
-    kern = pick(true);
-    if (lds > 65536) {
-      const hipError_t e = ensure_dynamic_lds(kern, lds);
-      if (e != hipSuccess) return e;
-    }
-  }
-  const unsigned gx = static_cast<unsigned>(yq ? cap : (nrb < cap ? nrb : cap));
+  const unsigned gx = static_cast<unsigned>(nrb < cap ? nrb : cap);
   const uint16_t* xp = a.x;
   const uint32_t* wp = a.w;
   const uint16_t* sp = a.s;

@@ -1041,12 +1041,13 @@ def test_few_rows_ksplit_misaligned_scales_and_determinism():
 @pytest.mark.parametrize("case", [(11, 32776, 2048, 4, 64, "f16", "f16"), (16, 32776, 1024, 8, 128, "bf16", "f16"),
                                   (12, 40000, 2048, 4, 64, "f16", "i8"), (10, 65544, 1536, 4, 64, "bf16", "f16")],
                          ids=str)
-def test_few_rows_whole_line_y_stores(case):
-    """10-16 rows on the K-split kernel store y a quad of 4 blocks (64
-    columns) at a time from LDS.  N a multiple of 8 but not of 16 or 64 (a
-    last quad with one block of 8 columns), an output bias, int8 activations:
-    sampled columns against the oracle, and bit-identical to the same call
-    with y only 2-byte aligned, which stores each block directly."""
+def test_few_rows_xcd_block_order_and_tails(case):
+    """10-16 rows on the K-split kernel with a full grid (512 workgroups), whose
+    blocks are taken in the XCD-grouped order within each round of the grid
+    stride: N a multiple of 8 but not of 16 or 64 (a last block of 8 columns,
+    a partial last round), an output bias, int8 activations; sampled columns
+    against the oracle, and bit-identical to the same call with y only 2-byte
+    aligned."""
     M, N, K, bits, gs, sb, act = case
     assert mxq.mxq_describe("a8" if act == "i8" else "qmv", M, N, K, bits, gs, sb).startswith("qsmk_kernel")
     p = synth.make_problem(M, N, K, bits, gs, sb, seed=M + N + 77)
@@ -1054,21 +1055,21 @@ def test_few_rows_whole_line_y_stores(case):
     x, w, s, b = to_dev(p)
     obt = torch.from_numpy(ob.view(np.int16)).view(torch.float16).to("cuda:0")
     call = mxq.mxq_linear_a8 if act == "i8" else mxq.mxq_linear
-    note(f"few-row whole-line y {case}")
+    note(f"few-row xcd block order {case}")
     y1 = torch.empty((M, N), dtype=torch.float16, device="cuda:0")
     call(x, w, s, b, obt, y1, bits=bits, group_size=gs)
     y_off = torch.empty(M * N + 1, dtype=torch.float16, device="cuda:0")
     y2 = y_off[1:].view(M, N)
     call(x, w, s, b, obt, y2, bits=bits, group_size=gs)
     y1h, y2h = y_host(y1), y_host(y2)
-    assert np.array_equal(y1h.view(np.uint16), y2h.view(np.uint16)), "quad stores change no bit"
+    assert np.array_equal(y1h.view(np.uint16), y2h.view(np.uint16)), "y alignment changes no bit"
     cols = _sampled_cols(N, 300 + M)
     if act == "i8":
         ref = oracle.matmul_ref_a8(p.x, p.w[cols], p.scales[cols], p.biases[cols], K, bits, gs, sb)
         ref = ref + ob.view(np.float16)[cols].astype(np.float64)
     else:
         ref = oracle.linear_ref(p.x, p.w[cols], p.scales[cols], p.biases[cols], ob[cols], K, bits, gs, sb)
-    assert_close(y1h[:, cols], ref, f"whole-line y {case}")
+    assert_close(y1h[:, cols], ref, f"xcd block order {case}")
 
 
 @pytest.mark.parametrize("M", list(range(2, 17)))
