@@ -28,7 +28,8 @@ Extra objects on the same line:
                 distinct weights, as 113 separate launches and as 65 grouped
                 launches (eager and graph replay): bytes/step, GB/s, steps/s;
   qmm           M=512 prefill on gate/up (8192x2048) and down (2048x8192),
-                f16 and bf16 scales, 20 calls back to back per projection:
+                f16 and bf16 scales, after a 200 ms warm-up the median of three
+                rounds of 20 calls back to back per projection:
                 TFLOP/s and MFMA utilisation (of the 2.5 PFLOP/s dense f16
                 peak); the same projections with int8 activations
                 (mxq_linear_a8, integer matrix cores): TOP/s against the
@@ -142,6 +143,7 @@ class ActCall:
         self.args = (x.data_ptr(), w.data_ptr(), s.data_ptr(), b.data_ptr(), None, y.data_ptr(),
                      M, N, K, bits, gs, 0, 1)
         self.name = name
+        self.M, self.N, self.K = M, N, K
 
     def __call__(self, stream_handle):
         st = self.fn(*self.args, stream_handle)
@@ -196,6 +198,35 @@ def capture(torch, fn):
 def cur_stream(torch):
     import ctypes
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def timed_rounds(torch, launches, st, n=20, rounds=3, warm_ms=200.0):
+    """{name: ms per call} for a list of (name, launch) pairs: the launches run
+    in turn until warm_ms of GPU time has passed (the part settles into its
+    sustained clocks under matrix-core load), then `rounds` rounds over all of
+    them, n calls back to back per launch and round between one event pair;
+    the median round per launch."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    while True:
+        for _, f in launches:
+            for _ in range(10):
+                f(st)
+        e1.record()
+        torch.cuda.synchronize()
+        if e0.elapsed_time(e1) >= warm_ms:
+            break
+    res = {}
+    for _ in range(rounds):
+        for name, f in launches:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(n):
+                f(st)
+            b.record()
+            torch.cuda.synchronize()
+            res.setdefault(name, []).append(a.elapsed_time(b) / n)
+    return {k: sorted(v)[len(v) // 2] for k, v in res.items()}
 
 
 def per_launch_times(torch, sets, reps):
@@ -924,20 +955,13 @@ def main():
                                   torch.empty((512, N), dtype=torch.float16, device=dev),
                                   512, N, K, 4, 64, 0 if sb == "f16" else 1, name))
             # back-to-back calls per projection (a prefill runs them in a row):
-            # one event pair around 20 calls after warm-up
+            # after a 200 ms warm-up, the median of three rounds of 20 calls
             st = cur_stream(torch)
             entry = {}
             tot_flop, tot_ms = 0, 0.0
+            times = timed_rounds(torch, [(c.name, c) for c in calls], st)
             for c in calls:
-                for _ in range(5):
-                    c(st)
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
-                for _ in range(20):
-                    c(st)
-                e1.record()
-                torch.cuda.synchronize()
-                ms = e0.elapsed_time(e1) / 20
+                ms = times[c.name]
                 flop = 2 * c.M * c.N * c.K
                 entry[c.name] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(flop / (ms / 1e3) / 1e12, 1)}
                 tot_flop += flop
@@ -952,17 +976,10 @@ def main():
                 # rows quantized once, then the integer matrix cores
                 a8 = {}
                 a8_op, a8_ms = 0, 0.0
+                acs = [A8Call(lib, *c.tensors, c.M, c.N, c.K, c.name) for c in calls]
+                times = timed_rounds(torch, [(ac.name, ac) for ac in acs], st)
                 for c in calls:
-                    ac = A8Call(lib, *c.tensors, c.M, c.N, c.K, c.name)
-                    for _ in range(5):
-                        ac(st)
-                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                    e0.record()
-                    for _ in range(20):
-                        ac(st)
-                    e1.record()
-                    torch.cuda.synchronize()
-                    ms = e0.elapsed_time(e1) / 20
+                    ms = times[c.name]
                     op = 2 * c.M * c.N * c.K
                     a8[c.name] = {"us": round(ms * 1e3, 2), "TOP/s": round(op / (ms / 1e3) / 1e12, 1)}
                     a8_op += op
@@ -970,7 +987,8 @@ def main():
                 a8["TOP/s"] = round(a8_op / (a8_ms / 1e3) / 1e12, 1)
                 a8["frac_of_int8_peak"] = round(a8_op / (a8_ms / 1e3) / 1e12 / MFMA_I8_PEAK_TOPS, 4)
                 a8["kernel"] = mxq.mxq_describe("a8", 512, 8192, 2048, 4, 64, sb)
-                a8["timing"] = "20 calls back to back per projection, quantization of x included"
+                a8["timing"] = ("after a 200 ms warm-up, the median of three rounds of 20 calls back to back per "
+                                "projection, quantization of x included")
                 qmm["int8_activations"] = a8
         result["qmm"] = qmm
 
@@ -1005,23 +1023,19 @@ def main():
         torch.cuda.empty_cache()
         tot_flop, tot_ms = 0, 0.0
         prefill = {}
+        acalls = []
         for idx, (name, N, K) in enumerate([("gate", 8192, 2048), ("up", 8192, 2048), ("down", 2048, 8192)]):
             w, s, b = synth.make_weights(N, K, 4, 64, "f16", seed=synth.proj_seed(4, 0, idx))
             xb = synth.make_x(512, K, seed=synth.proj_seed(4, 0, idx) + 500, act_dtype="bf16")
-            c = ActCall(lib, torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev),
-                        torch.from_numpy(w.view(np.int32)).to(dev),
-                        torch.from_numpy(s.view(np.int16)).view(torch.float16).to(dev),
-                        torch.from_numpy(b.view(np.int16)).view(torch.float16).to(dev),
-                        torch.empty((512, N), dtype=torch.bfloat16, device=dev), 512, N, K, name)
-            for _ in range(5):
-                c(st)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(20):
-                c(st)
-            e1.record()
-            torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1) / 20
+            acalls.append(ActCall(lib, torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev),
+                                  torch.from_numpy(w.view(np.int32)).to(dev),
+                                  torch.from_numpy(s.view(np.int16)).view(torch.float16).to(dev),
+                                  torch.from_numpy(b.view(np.int16)).view(torch.float16).to(dev),
+                                  torch.empty((512, N), dtype=torch.bfloat16, device=dev), 512, N, K, name))
+        times = timed_rounds(torch, [(c.name, c) for c in acalls], st)
+        for c in acalls:
+            name, N, K = c.name, c.N, c.K
+            ms = times[name]
             flop = 2 * 512 * N * K
             prefill[name] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(flop / (ms / 1e3) / 1e12, 1)}
             tot_flop += flop
@@ -1044,7 +1058,6 @@ def main():
                           torch.from_numpy(b.view(np.int16)).view(torch.float16).to(dev)))
         sfew = cur_stream(torch)
         wptrs = [(tw.data_ptr(), ts.data_ptr(), tb.data_ptr()) for tw, ts, tb in wsets]
-        few_ms = {}
         cases = []
         for M in (1, 2, 4, 8, 16):
             x8 = torch.from_numpy(synth.make_x(M, 2048, seed=91 + M)).to(dev)
@@ -1064,21 +1077,37 @@ def main():
             if st_ != 0:
                 raise RuntimeError(f"{label} lm_head M={M}: libmxq status {st_}")
 
-        # three rounds over all cases (so that a slow spell of the part does not
-        # land on one case), 20 launches back to back per case and round, after
-        # 6 warm-up launches; the median of the three rounds
+        # a 200 ms warm-up, then three rounds over all cases (so that a slow
+        # spell of the part does not land on one case), 20 launches back to
+        # back per case and round; the median of the three rounds
+        few_ms = {}
+
+        def few_rec(case):
+            def f(st_):
+                few_launch(case, f.i)
+                f.i += 1
+            f.i = 0
+            return f
+        launches = [(case[:2], few_rec(case)) for case in cases]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        while True:
+            for _, f in launches:
+                for _ in range(10):
+                    f(sfew)
+            e1.record()
+            torch.cuda.synchronize()
+            if e0.elapsed_time(e1) >= 200.0:
+                break
         for rnd in range(3):
-            for case in cases:
-                if rnd == 0:
-                    for i in range(6):
-                        few_launch(case, i)
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
-                for i in range(20):
-                    few_launch(case, i)
-                e1.record()
+            for key, f in launches:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                for _ in range(20):
+                    f(sfew)
+                b.record()
                 torch.cuda.synchronize()
-                few_ms.setdefault(case[:2], []).append(e0.elapsed_time(e1) / 20)
+                few_ms.setdefault(key, []).append(a.elapsed_time(b) / 20)
         for M in (1, 2, 4, 8, 16):
             row = {}
             for label in ("f16", "int8"):
@@ -1133,20 +1162,17 @@ def main():
                "packed_speedup_vs_f16": round(fsec / packed_sec, 3)}
         del dense
         prefill = {}
-        for name, N, K in (("gate", 8192, 2048), ("down", 2048, 8192)):
-            wd = (torch.randn((N, K), device=dev, generator=gen) * 0.02).half()
-            xd = torch.randn((512, K), device=dev, generator=gen).half()
-            for _ in range(3):
-                torch.nn.functional.linear(xd, wd)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(20):
-                torch.nn.functional.linear(xd, wd)
-            e1.record()
-            torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1) / 20
+        # timed like the packed prefill legs: a 200 ms warm-up, then the
+        # median of three rounds of 20 calls per projection
+        dshapes = (("gate", 8192, 2048), ("down", 2048, 8192))
+        dts = {name: ((torch.randn((N, K), device=dev, generator=gen) * 0.02).half(),
+                      torch.randn((512, K), device=dev, generator=gen).half()) for name, N, K in dshapes}
+        times = timed_rounds(torch, [(name, (lambda st_, w_=wd, x_=xd: torch.nn.functional.linear(x_, w_)))
+                                     for name, (wd, xd) in dts.items()], cur_stream(torch))
+        for name, N, K in dshapes:
+            ms = times[name]
             prefill[name] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(2 * 512 * N * K / (ms / 1e3) / 1e12, 1)}
-            del wd, xd
+        del dts
         cmp["prefill_m512"] = prefill
         result["dense_f16_comparator"] = cmp
         torch.cuda.empty_cache()
