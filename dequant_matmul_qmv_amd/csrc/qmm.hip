@@ -589,13 +589,16 @@ __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x
 
 // y = RNE_f16(sum over splits of part[split] (in split order) + out_bias);
 // four consecutive elements per thread (the workspace is 256-byte aligned and
-// MN is a multiple of 4 on this path, checked by the host).
+// MN is a multiple of 4 on this path, checked by the host).  The column of
+// the first element is taken once per step (one 64-bit remainder, not four),
+// and the four results leave as one 8-byte store when y allows it.
 template <bool XB>
 __global__ __launch_bounds__(256) void qmm_split_reduce_kernel(const float* __restrict__ part,
                                                                const uint16_t* __restrict__ ob,
                                                                uint16_t* __restrict__ y, int64_t MN, int N,
                                                                int splits) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x * 4;
+  const bool yvec = (reinterpret_cast<uintptr_t>(y) & 7) == 0;
   for (int64_t i = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 4; i < MN; i += stride) {
     float4 v = *reinterpret_cast<const float4*>(part + i);
     for (int sp = 1; sp < splits; ++sp) {
@@ -606,10 +609,23 @@ __global__ __launch_bounds__(256) void qmm_split_reduce_kernel(const float* __re
       v.w += u.w;
     }
     float o[4] = {v.x, v.y, v.z, v.w};
+    if (ob != nullptr) {
+      int c = static_cast<int>(i % N);  // column of element i; the next ones wrap to column 0 past N - 1
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (ob != nullptr) o[e] += sb_to_f32<XB>(ob[(i + e) % N]);
-      y[i + e] = f32_to_act_bits<XB>(o[e]);
+      for (int e = 0; e < 4; ++e) {
+        o[e] += sb_to_f32<XB>(ob[c]);
+        c = c + 1 == N ? 0 : c + 1;
+      }
+    }
+    uint16_t h[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) h[e] = f32_to_act_bits<XB>(o[e]);
+    if (yvec) {
+      *reinterpret_cast<uint2*>(y + i) = uint2{static_cast<uint32_t>(h[0]) | (static_cast<uint32_t>(h[1]) << 16),
+                                               static_cast<uint32_t>(h[2]) | (static_cast<uint32_t>(h[3]) << 16)};
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[i + e] = h[e];
     }
   }
 }
