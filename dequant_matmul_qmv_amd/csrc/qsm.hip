@@ -386,8 +386,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       v[g][1] = live ? *reinterpret_cast<const u4*>(xp + 64 * g + 8) : z;
       am = fmaxf(am, fmaxf(absmax8_f16(v[g][0]), absmax8_f16(v[g][1])));
     }
-    am = fmaxf(am, __shfl_xor(am, 16));
-    am = fmaxf(am, __shfl_xor(am, 32));
+    {
+      // the maximum over the row's four lane groups (lanes l, l ^ 16, l ^ 32):
+      // gfx950's lane swaps, no LDS crossbar
+      auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(am), __float_as_uint(am), false, false);
+      am = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+      auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(am), __float_as_uint(am), false, false);
+      am = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+    }
     float* ams = red;  // [nw][16], free until the first block
     if (kg == 0) ams[wave * 16 + c16] = am;
     __syncthreads();
@@ -397,6 +403,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     const bool zr = !(amax > 0.0f);
     const float r = zr ? 0.0f : 127.0f / amax;
     const float sx = zr ? 0.0f : amax / 127.0f;
+    typedef int v4i_ __attribute__((ext_vector_type(4)));
+    const v4i_ ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+    const v4i_ zi = {0, 0, 0, 0};
 #pragma unroll
     for (int g = 0; g < kKsGroups; ++g) {
       uint32_t a0, b0, a1, b1;
@@ -404,11 +413,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       quant_chunk_i8<BITS>(v[g][0], r, a0, b0, sum);
       quant_chunk_i8<BITS>(v[g][1], r, a1, b1, sum);
       xa[g][0] = u4{a0, b0, a1, b1};
-      float ps = static_cast<float>(sum);  // integer, exact
-      ps += __shfl_xor(ps, 16);
-      ps += __shfl_xor(ps, 32);  // sum of the codes of x row c16 over the group
+      // the group sums of the codes of the D rows this lane holds (4 kg + i),
+      // straight in the D layout: the codes times a column of ones on the
+      // matrix core (exact integers)
+      const v4i_ d = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i_, xa[g][0]), ones, zi, 0, 0, 0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xs[g][i] = __shfl(ps, 4 * kg + i);
+      for (int i = 0; i < 4; ++i) xs[g][i] = static_cast<float>(d[i]);
     }
     sxl = sx;
   } else {
@@ -424,13 +434,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       xa[g][0] = BITS == 4 ? perm_x_w4(c16 < M ? v0 : z) : (c16 < M ? v0 : z);
       xa[g][1] = BITS == 4 ? perm_x_w4(c16 < M ? v1 : z) : (c16 < M ? v1 : z);
     }
+    // X_g of the D rows this lane holds (4 kg + i), straight in the D layout:
+    // the activation fragments times a column of ones on the matrix core
+    // (exact products, f32 sums)
+    const u4 ones = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
 #pragma unroll
     for (int g = 0; g < kKsGroups; ++g) {
-      float p = sum8_f32(xa[g][0]) + sum8_f32(xa[g][1]);
-      p += __shfl_xor(p, 16);
-      p += __shfl_xor(p, 32);  // X_g of x row c16, in all four lane groups
+      const f4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
+      f4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, xa[g][0]), __builtin_bit_cast(h8, ones), z4,
+                                                    0, 0, 0);
+      d = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, xa[g][1]), __builtin_bit_cast(h8, ones), d, 0, 0,
+                                                 0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xs[g][i] = __shfl(p, 4 * kg + i);
+      for (int i = 0; i < 4; ++i) xs[g][i] = d[i];
     }
   }
 
