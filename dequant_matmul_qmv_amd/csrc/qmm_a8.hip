@@ -106,6 +106,13 @@ __device__ __forceinline__ void split_bf16(const float (&v)[8], u4 (&out)[NP]) {
 // 9-10 against 6 us at K = 8192, M = 512 -- a row is then a longer serial chain
 // on half as many workgroups.)
 // ---------------------------------------------------------------------------
+// DPP move of a float (rows outside the row mask read 0, which neither a sum
+// nor a maximum of non-negative values notices)
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float a8_dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xF, false));
+}
+
 template <int BITS, int RGC>
 __global__ __launch_bounds__(256) void quant_rows_i8_kernel(const uint16_t* __restrict__ x, uint32_t* __restrict__ xq,
                                                             float* __restrict__ xs, float* __restrict__ sx, int K) {
@@ -122,10 +129,17 @@ __global__ __launch_bounds__(256) void quant_rows_i8_kernel(const uint16_t* __re
     am = fmaxf(am, absmax8_f16(keep[i]));
   }
   for (int c = static_cast<int>(threadIdx.x) + 256 * KEEP; c < nch; c += 256) am = fmaxf(am, absmax8_f16(xr[c]));
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) am = fmaxf(am, __shfl_xor(am, o));
+  // the wave's maximum (non-negative values) folded into lane 63 by DPP moves
+  // (quad swaps, half-row and row mirrors, then row_bcast:15 / :31), no LDS
+  // crossbar
+  am = fmaxf(am, a8_dpp<0xB1, 0xF>(am));
+  am = fmaxf(am, a8_dpp<0x4E, 0xF>(am));
+  am = fmaxf(am, a8_dpp<0x141, 0xF>(am));
+  am = fmaxf(am, a8_dpp<0x140, 0xF>(am));
+  am = fmaxf(am, a8_dpp<0x142, 0xA>(am));
+  am = fmaxf(am, a8_dpp<0x143, 0xC>(am));
   __shared__ float wmax[4];
-  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = am;
+  if ((threadIdx.x & 63) == 63) wmax[threadIdx.x >> 6] = am;
   __syncthreads();
   const float amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
   const bool zr = !(amax > 0.0f);
@@ -150,9 +164,13 @@ __global__ __launch_bounds__(256) void quant_rows_i8_kernel(const uint16_t* __re
       qr[2 * c] = a;
       qr[2 * c + 1] = b;
     }
-#pragma unroll
-    for (int o = 1; o < L; o <<= 1) sum += __shfl_xor(sum, o);
-    if (live && (c % L) == 0) xs[static_cast<size_t>(m) * GR + c / L] = static_cast<float>(sum);
+    // the ring group's code sum over its L aligned lanes, by DPP moves (the
+    // sums are integers below 2^24: exact in f32)
+    float fs = static_cast<float>(sum);
+    fs += a8_dpp<0xB1, 0xF>(fs);  // quad_perm 1,0,3,2
+    fs += a8_dpp<0x4E, 0xF>(fs);  // quad_perm 2,3,0,1
+    if constexpr (L == 8) fs += a8_dpp<0x141, 0xF>(fs);  // row_half_mirror: the other quad of the 8
+    if (live && (c % L) == 0) xs[static_cast<size_t>(m) * GR + c / L] = fs;
   }
 }
 
