@@ -107,6 +107,27 @@ __device__ __forceinline__ void split2_f16_to_bf16(const u4& v, u4& hi, u4& lo) 
   hi = u4{pack_hi16(h[0], h[1]), pack_hi16(h[2], h[3]), pack_hi16(h[4], h[5]), pack_hi16(h[6], h[7])};
   lo = u4{pack_hi16(l[0], l[1]), pack_hi16(l[2], l[3]), pack_hi16(l[4], l[5]), pack_hi16(l[6], l[7])};
 }
+
+// 4-bit codes as f16 subnormals 16c * 2^-24 = c * 2^-20, in natural k order:
+// exact values, and exact products with f16 activations.  The caller
+// multiplies the group's f16 scale by 2^20 (exact).  The low nibbles of all
+// bytes are shifted up and masked into one word, the high nibbles masked in
+// place into another, and one byte select per pair places (low, high) nibble
+// of byte i under zero bytes: 7 operations per word where an exponent
+// injection and a packed f16 fma take 12.
+// Measured on the matrix cores: products of subnormal operands keep fewer
+// low-order bits in the MFMA's sum than those of normal operands with the same
+// value.  With the codes at mantissa bits 0..3 one output in 30 rounded
+// differently from the exponent-injected codes; at bits 4..7, as here, about
+// one in 2000 (never by more than one f16 rounding step), with the error
+// against an exact f64 result unchanged to four digits.  8-bit codes fill the
+// low mantissa byte and keep the exact route.
+__device__ __forceinline__ u4 unpack4_subn(uint32_t w) {
+  const uint32_t lo = (w << 4) & 0xF0F0F0F0u, hi = w & 0xF0F0F0F0u;
+  // __builtin_amdgcn_perm(a, b, sel): selectors 0-3 pick bytes of b, 4-7 of a, 0x0C a zero byte
+  return u4{__builtin_amdgcn_perm(hi, lo, 0x0C040C00u), __builtin_amdgcn_perm(hi, lo, 0x0C050C01u),
+            __builtin_amdgcn_perm(hi, lo, 0x0C060C02u), __builtin_amdgcn_perm(hi, lo, 0x0C070C03u)};
+}
 }  // namespace
 
 // Sum of v over aligned groups of 8 lanes (4 when GS == 32), in every lane of
@@ -172,6 +193,10 @@ __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x
   constexpr int BM = C::BM, BN = C::BN, TWM = C::TWM, TWN = C::TWN, PT = C::PT;
   constexpr int XCH = C::XCH, WCH = C::WCH, U4R = C::U4R, WPS = C::WPS, RPS = C::RPS;
   constexpr int XCS = C::XCS, WCS = C::WCS;
+  // 4-bit codes with f16 activations and f16 scales are staged as f16
+  // subnormals (a bf16 scale times 2^20 could overflow; bf16 subnormal
+  // products would leave f32's normal range)
+  constexpr bool SUBN = BITS == 4 && !XB && !SB_BF16;
 
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t* xA = reinterpret_cast<uint16_t*>(smem);              // [NBUF][BM][LDK] x, natural k order
@@ -333,7 +358,8 @@ __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x
       if constexpr (BITS == 4) {
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-          *reinterpret_cast<u4*>(dst + swz(row, c0 + k)) = XB ? unpack4_bf16_natural(wv[k]) : unpack4_natural(wv[k], up4);
+          *reinterpret_cast<u4*>(dst + swz(row, c0 + k)) =
+              XB ? unpack4_bf16_natural(wv[k]) : SUBN ? unpack4_subn(wv[k]) : unpack4_natural(wv[k], up4);
       } else {
 #pragma unroll
         for (int k = 0; k < 2; ++k)
@@ -436,6 +462,7 @@ __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x
           // widening into each FMA (v_fma_mix_f32, VOP3P), which issues at half
           // the rate of the two-operand v_fmac_f32 used instead
           float sc = sb_to_f32<SB_BF16>(sq[(bcol + j * 32) * SBS + (rg & (SRING - 1))]);
+          if constexpr (SUBN) sc *= 0x1p20f;  // P is in units of 2^-20
           asm volatile("" : "+v"(sc));
 #pragma unroll
           for (int i = 0; i < MB; ++i)
