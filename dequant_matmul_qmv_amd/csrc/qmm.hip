@@ -202,6 +202,9 @@ __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x
   uint16_t* xA = reinterpret_cast<uint16_t*>(smem);              // [NBUF][BM][LDK] x, natural k order
   uint16_t* qB = xA + C::NBUF * BM * LDK;                        // [NBUF][BN][LDK] codes as exact f16
   float* xg = reinterpret_cast<float*>(smem + C::tile_bytes);    // [BM][XGS]: x sums, ring of groups
+  // this pipeline's first stage buffer (stages kt with kt % 2 == pipe use kt & 3)
+  uint16_t* const xAp = xA + (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >> 2) * BM * LDK;
+  uint16_t* const qBp = qB + (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >> 2) * BN * LDK;
   uint16_t* sq = reinterpret_cast<uint16_t*>(xg + BM * XGS);     // [BN][SBS]: scales, ring of groups
   uint16_t* bq = sq + BN * SBS;                                  // [BN][SBS]: biases, ring of groups
 
@@ -336,9 +339,10 @@ __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x
   // registers -> LDS for stage kt: x as loaded, codes unpacked to exact f16,
   // x sums per ring group, and a block load step's scales and biases.
   // Stages past the last go to a buffer and ring slots nothing reads.
-  auto lstore = [&](int kt) __attribute__((always_inline)) {
-    uint16_t* xs = xA + (kt & 3) * BM * LDK;
-    uint16_t* qs = qB + (kt & 3) * BN * LDK;
+  auto lstore = [&](int kt, auto par) __attribute__((always_inline)) {
+    constexpr int pb = decltype(par)::value;  // stage buffer pipe + 2 pb, i.e. kt & 3
+    uint16_t* xs = xAp + pb * 2 * BM * LDK;
+    uint16_t* qs = qBp + pb * 2 * BN * LDK;
 #pragma unroll
     for (int i = 0; i < XCH; ++i) {
       const int c = tl + PT * i;
@@ -434,9 +438,10 @@ __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x
   // This pipeline's stage kt from its LDS buffer: per ring group, P from the
   // MFMAs, acc += s * P on the VALU, and the bias MFMAs when the ring group
   // closes a block of 16.
-  auto compute = [&](int kt) __attribute__((always_inline)) {
-    const uint16_t* xs = xA + (kt & 3) * BM * LDK;
-    const uint16_t* qs = qB + (kt & 3) * BN * LDK;
+  auto compute = [&](int kt, auto par) __attribute__((always_inline)) {
+    constexpr int pb = decltype(par)::value;  // stage buffer pipe + 2 pb, i.e. kt & 3
+    const uint16_t* xs = xAp + pb * 2 * BM * LDK;
+    const uint16_t* qs = qBp + pb * 2 * BN * LDK;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const bool first = kk % C::KSPR == 0;
@@ -486,7 +491,7 @@ __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x
     sbstore(0, 64 * i + (t >> 3), s2, b2);
   }
   gload(pipe);
-  lstore(pipe);
+  lstore(pipe, std::integral_constant<int, 0>{});
   gload(pipe + 2);
   __syncthreads();
 
@@ -497,24 +502,34 @@ __global__ __launch_bounds__(512) void qmm_kernel(const uint16_t* __restrict__ x
   // The staging work (the longer dependent chain of the two) runs at a raised
   // wave priority, so on each SIMD it wins issue slots over the other wave's
   // scale FMAs and LDS reads while that wave's MFMAs run (measured 2-6 %).
-  const int npair = (nkt + 1) >> 1;
-  for (int pr = 0; pr < npair; ++pr) {
+  // Pipeline p uses stage buffers p and p + 2 in turn; the loop runs two
+  // iterations per trip so that each buffer's address is a constant offset
+  // from the pipeline's first (LDS immediates instead of an add per access).
+  auto iteration = [&](int pr, auto par) __attribute__((always_inline)) {
+    constexpr int pb = decltype(par)::value;  // pr & 1
     const int kt = 2 * pr + pipe;
     if (pipe == 1) {
       __builtin_amdgcn_s_setprio(1);
-      lstore(kt + 2);
+      lstore(kt + 2, std::integral_constant<int, pb ^ 1>{});
       gload(kt + 4);
       __builtin_amdgcn_s_setprio(0);
     }
-    if (kt < nkt) compute(kt);
+    if (kt < nkt) compute(kt, par);
     if (pipe == 0) {
       __builtin_amdgcn_s_setprio(1);
-      lstore(kt + 2);
+      lstore(kt + 2, std::integral_constant<int, pb ^ 1>{});
       gload(kt + 4);
       __builtin_amdgcn_s_setprio(0);
     }
     __syncthreads();
+  };
+  const int npair = (nkt + 1) >> 1;
+  int pr = 0;
+  for (; pr + 1 < npair; pr += 2) {
+    iteration(pr, std::integral_constant<int, 0>{});
+    iteration(pr + 1, std::integral_constant<int, 1>{});
   }
+  if (pr < npair) iteration(pr, std::integral_constant<int, 0>{});
 
   // ---- add the two pipelines' accumulators, store -------------------------
   float* red = reinterpret_cast<float*>(smem);  // [4 waves][MB*NB*16][64], over the stage buffers
