@@ -525,8 +525,8 @@ const char* mxq_describe(const char* op, int64_t M, int64_t N, int64_t K, int bi
     desc = "qsmk_kernel<bits=" + std::to_string(bits) + ",sb=" + std::string(sb) + ",gs=" +
            std::to_string(group_size) + ",m=" + std::to_string(M) + ",waves=" + std::to_string(nw) +
            (a8 ? ",act=i8" : "") + (chunks > 1 ? ",kchunks=" + std::to_string(chunks) : std::string()) +
-           (K % 512 != 0 ? ",ragged" : "") +
-           "> block=" + std::to_string(64 * nw) + " lds=" + std::to_string(mxq::qsmk_lds_bytes(nw, bits)) +
+           (K % 512 != 0 ? ",ragged" : "") + (mxq::qsmk_xstage(M, a8) ? ",xstage" : "") +
+           "> block=" + std::to_string(64 * nw) + " lds=" + std::to_string(mxq::qsmk_lds_bytes(nw, bits, mxq::qsmk_xstage(M, a8))) +
            (chunks > 1 ? "; qmm_split_reduce_kernel" : "");
     return desc.c_str();
   }

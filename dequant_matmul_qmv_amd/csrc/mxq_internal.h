@@ -125,7 +125,10 @@ bool qsmk_split(int64_t K, int* waves, int* chunks);
 // 16-byte aligned (loaded as 2-byte values).
 bool qsmk_ragged(int64_t K, const void* s, const void* b);
 bool qsmk_shape(int64_t M, int64_t N, int64_t K, int bits, int group_size, bool chunks_ok, const DeviceInfo& dev);
-size_t qsmk_lds_bytes(int waves, int bits);
+// LDS of one workgroup; `xstage`: the activations pass through LDS first
+// (f16 activations at 9..16 rows, qsmk_xstage).
+size_t qsmk_lds_bytes(int waves, int bits, bool xstage);
+bool qsmk_xstage(int64_t M, bool int8_act);
 hipError_t launch_qsmk(const QmvArgs& a, int M, const DeviceInfo& dev);
 
 // The split workspace cache (workspace.cpp): one f32 buffer per device and

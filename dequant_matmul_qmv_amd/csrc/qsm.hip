@@ -237,6 +237,7 @@ constexpr int kKsMaxWaves = 8;
 constexpr int kKsMaxChunks = 64;             // K up to 64 * 4096 codes
 // staged row slice: 256 (4-bit) or 512 (8-bit) bytes + 16 bytes of pad
 __host__ __device__ constexpr int ks_row_bytes(int bits) { return kKsCodes * bits / 8 + 16; }
+constexpr int kXsRow = kKsCodes / 2 + 8;  // halves per row of the activation staging (half a slice + 16 bytes)
 }  // namespace
 
 // 4-bit word -> (64 + c0, 64 + c4), (64 + c1, 64 + c5), (64 + c2, 64 + c6),
@@ -249,9 +250,13 @@ __device__ __forceinline__ u4 unpack_w4_off64_mfma(uint32_t w, uint32_t magic) {
   return u4{((w << 4) & m) | magic, (w & m) | magic, ((w >> 4) & m) | magic, ((w >> 8) & m) | magic};
 }
 
-size_t qsmk_lds_bytes(int waves, int bits) {
-  return static_cast<size_t>(waves) * 16 * ks_row_bytes(bits) + static_cast<size_t>(2 * waves) * 64 * 16;
+size_t qsmk_lds_bytes(int waves, int bits, bool xstage) {
+  const size_t blocks = static_cast<size_t>(waves) * 16 * ks_row_bytes(bits) + static_cast<size_t>(2 * waves) * 64 * 16;
+  const size_t xs = xstage ? static_cast<size_t>(waves) * 16 * kXsRow * 2 : 0;  // the activations' pass, before the blocks
+  return blocks > xs ? blocks : xs;
 }
+
+bool qsmk_xstage(int64_t M, bool int8_act) { return !int8_act && M >= 9; }
 
 // XI: int8 activations -- each x row quantized in the kernel (per-row
 // symmetric, f32 decisions), codes as bytes (4-bit: even then odd nibbles of
@@ -264,7 +269,7 @@ size_t qsmk_lds_bytes(int waves, int bits) {
 // are loaded from the row's start instead (in bounds; their codes meet zero
 // activations), and scales and biases are loaded as 2-byte values with the
 // group index clamped and the values zeroed past the last group.
-template <int BITS, bool SB_BF16, int GSH, int NW, bool XI, bool RG>
+template <int BITS, bool SB_BF16, int GSH, int NW, bool XI, bool RG, bool XS>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void qsmk_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ W,
                                                    const uint16_t* __restrict__ S, const uint16_t* __restrict__ B,
                                                    uint16_t* __restrict__ y, const uint16_t* __restrict__ ob,
@@ -421,6 +426,44 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       for (int i = 0; i < 4; ++i) xs[g][i] = static_cast<float>(d[i]);
     }
     sxl = sx;
+  } else if constexpr (XS) {
+    // XS (9..16 rows): the slice's activations (16 rows x 512, rows >= M as zeros) pass
+    // through LDS in two halves of four groups: each load instruction reads
+    // two rows' whole 512-byte pieces, and the A-layout fragments are read
+    // back (a row stride of kXsRow halves puts the 16 rows one read touches on
+    // distinct banks).  Loaded in the A layout directly, every instruction
+    // would take half of a 128-byte line from each of 16 rows.  The area is
+    // this wave's share of the whole LDS, which the blocks' code staging
+    // reuses after the barrier below.  (At 2..8 rows the direct loads touch
+    // few distinct rows, and the pass through LDS cost more than it saved.)
+    uint16_t* xst = reinterpret_cast<uint16_t*>(smem) + wave * 16 * kXsRow;
+    const u4 z = {0u, 0u, 0u, 0u};
+    const int lr = lane >> 5, lc = 8 * (lane & 31);  // row of the load pair, halves into the half slice
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        const int row = 2 * p + lr;
+        const int col = 256 * h + lc;  // within the slice
+        const bool ok = row < M && (!RG || (col >> 6) < gvalid);
+        const u4 v = *reinterpret_cast<const u4*>(x + static_cast<size_t>(min(row, M - 1)) * K + (ok ? ks0 + col : 0));
+        *reinterpret_cast<u4*>(xst + row * kXsRow + lc) = ok ? v : z;
+      }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int g = 4 * h + q;
+        const uint16_t* xr = xst + c16 * kXsRow + 64 * q + 16 * kg;
+        const u4 v0 = *reinterpret_cast<const u4*>(xr);
+        const u4 v1 = *reinterpret_cast<const u4*>(xr + 8);
+        // k slots in the order of the code unpack: 4-bit pairs (x0, x4)
+        // (x1, x5) ..., 8-bit natural order
+        xa[g][0] = BITS == 4 ? perm_x_w4(v0) : v0;
+        xa[g][1] = BITS == 4 ? perm_x_w4(v1) : v1;
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+    __syncthreads();  // every wave's fragments read before any block's codes land in LDS
   } else {
     const uint16_t* xp = x + static_cast<size_t>(min(c16, M - 1)) * K + ks0 + 16 * kg;
     const u4 z = {0u, 0u, 0u, 0u};
@@ -434,6 +477,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       xa[g][0] = BITS == 4 ? perm_x_w4(c16 < M ? v0 : z) : (c16 < M ? v0 : z);
       xa[g][1] = BITS == 4 ? perm_x_w4(c16 < M ? v1 : z) : (c16 < M ? v1 : z);
     }
+  }
+  if constexpr (!XI) {
     // X_g of the D rows this lane holds (4 kg + i), straight in the D layout:
     // the activation fragments times a column of ones on the matrix core
     // (exact products, f32 sums)
@@ -618,40 +663,49 @@ bool qsmk_shape(int64_t M, int64_t N, int64_t K, int bits, int group_size, bool 
 }
 
 namespace {
-template <int BITS, bool SB_BF16, int GSH, bool XI, bool RG>
+template <int BITS, bool SB_BF16, int GSH, bool XI, bool RG, bool XS>
 const void* qsmk_ptr_x(int nw) {
   switch (nw) {
-    case 1: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 1, XI, RG>);
-    case 2: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 2, XI, RG>);
-    case 3: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 3, XI, RG>);
-    case 4: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 4, XI, RG>);
-    case 5: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 5, XI, RG>);
-    case 6: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 6, XI, RG>);
-    case 7: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 7, XI, RG>);
-    default: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 8, XI, RG>);
+    case 1: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 1, XI, RG, XS>);
+    case 2: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 2, XI, RG, XS>);
+    case 3: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 3, XI, RG, XS>);
+    case 4: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 4, XI, RG, XS>);
+    case 5: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 5, XI, RG, XS>);
+    case 6: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 6, XI, RG, XS>);
+    case 7: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 7, XI, RG, XS>);
+    default: return reinterpret_cast<const void*>(&qsmk_kernel<BITS, SB_BF16, GSH, 8, XI, RG, XS>);
   }
 }
+// activations: 0 f16 loaded in the A layout, 1 int8 (quantized in the
+// kernel), 2 f16 staged through LDS
+template <int BITS, bool SB_BF16, int GSH, bool RG>
+const void* qsmk_ptr_a(int nw, int act) {
+  return act == 1   ? qsmk_ptr_x<BITS, SB_BF16, GSH, true, RG, false>(nw)
+         : act == 2 ? qsmk_ptr_x<BITS, SB_BF16, GSH, false, RG, true>(nw)
+                    : qsmk_ptr_x<BITS, SB_BF16, GSH, false, RG, false>(nw);
+}
 template <bool SB_BF16, int GSH, bool RG>
-const void* qsmk_ptr_r(int nw, int bits, bool xi) {
-  if (bits == 8) return xi ? qsmk_ptr_x<8, SB_BF16, GSH, true, RG>(nw) : qsmk_ptr_x<8, SB_BF16, GSH, false, RG>(nw);
-  return xi ? qsmk_ptr_x<4, SB_BF16, GSH, true, RG>(nw) : qsmk_ptr_x<4, SB_BF16, GSH, false, RG>(nw);
+const void* qsmk_ptr_r(int nw, int bits, int act) {
+  return bits == 8 ? qsmk_ptr_a<8, SB_BF16, GSH, RG>(nw, act) : qsmk_ptr_a<4, SB_BF16, GSH, RG>(nw, act);
 }
 template <bool SB_BF16, int GSH>
-const void* qsmk_ptr(int nw, int bits, bool xi, bool rg) {
-  return rg ? qsmk_ptr_r<SB_BF16, GSH, true>(nw, bits, xi) : qsmk_ptr_r<SB_BF16, GSH, false>(nw, bits, xi);
+const void* qsmk_ptr(int nw, int bits, int act, bool rg) {
+  return rg ? qsmk_ptr_r<SB_BF16, GSH, true>(nw, bits, act) : qsmk_ptr_r<SB_BF16, GSH, false>(nw, bits, act);
 }
 }  // namespace
 
 hipError_t launch_qsmk(const QmvArgs& a, int M, const DeviceInfo& dev) {
   int nw = 0, chunks = 0;
   if (!qsmk_split(a.K, &nw, &chunks)) return hipErrorInvalidValue;  // the caller checked qsmk_shape
-  const size_t lds = qsmk_lds_bytes(nw, a.bits);
   const bool g128 = a.glog2 == 7;
   const bool xi = a.act == 2;  // int8 activations (quantized in the kernel)
   if (chunks > 1 && xi) return hipErrorInvalidValue;
+  const bool xstage = qsmk_xstage(M, xi);
+  const size_t lds = qsmk_lds_bytes(nw, a.bits, xstage);
   const bool rg = qsmk_ragged(a.K, a.s, a.b);
-  const void* kern = a.sb_bf16 ? (g128 ? qsmk_ptr<true, 1>(nw, a.bits, xi, rg) : qsmk_ptr<true, 0>(nw, a.bits, xi, rg))
-                               : (g128 ? qsmk_ptr<false, 1>(nw, a.bits, xi, rg) : qsmk_ptr<false, 0>(nw, a.bits, xi, rg));
+  const int act = xi ? 1 : xstage ? 2 : 0;
+  const void* kern = a.sb_bf16 ? (g128 ? qsmk_ptr<true, 1>(nw, a.bits, act, rg) : qsmk_ptr<true, 0>(nw, a.bits, act, rg))
+                               : (g128 ? qsmk_ptr<false, 1>(nw, a.bits, act, rg) : qsmk_ptr<false, 0>(nw, a.bits, act, rg));
   if (lds > 65536) {  // 8 waves of 8-bit slices
     const hipError_t e = ensure_dynamic_lds(kern, lds);
     if (e != hipSuccess) return e;

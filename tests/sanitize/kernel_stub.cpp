@@ -127,7 +127,10 @@ bool qsmk_shape(int64_t M, int64_t N, int64_t K, int, int group_size, bool chunk
   if (c > 1 && (!chunks_ok || (M * N) % 4 != 0)) return false;
   return N >= 4096;
 }
-size_t qsmk_lds_bytes(int waves, int bits) { return static_cast<size_t>(waves) * 16 * (bits == 8 ? 1040 : 528) + 4096; }
+size_t qsmk_lds_bytes(int waves, int bits, bool xstage) {
+  return static_cast<size_t>(waves) * 16 * (bits == 8 ? 1040 : 528) + 4096 + (xstage ? 1024 : 0);
+}
+bool qsmk_xstage(int64_t M, bool int8_act) { return !int8_act && M >= 9; }
 hipError_t launch_qsmk(const QmvArgs& a, int M, const DeviceInfo&) {
   int w = 0, c = 0;
   qsmk_split(a.K, &w, &c);

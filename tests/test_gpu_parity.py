@@ -1072,6 +1072,29 @@ def test_few_rows_xcd_block_order_and_tails(case):
     assert_close(y1h[:, cols], ref, f"xcd block order {case}")
 
 
+@pytest.mark.parametrize("case", [(9, 32768, 2112, 4, 64, "f16"), (13, 32768, 4096, 8, 64, "bf16"),
+                                  (16, 65536, 2304, 4, 128, "f16"), (9, 40000, 2048, 8, 128, "f16")], ids=str)
+def test_few_rows_staged_activations(case):
+    """From 9 rows (f16 activations) the K-split kernel passes each wave's
+    activation slice through LDS, whole row pieces per load, before the first
+    block: 9 rows (half of the last load pair past M), a ragged K whose last
+    slice holds one group, 8 waves, 8-bit codes, groups of 128; sampled
+    columns against the oracle.  At 8 rows, and with int8 activations, the
+    kernel loads the activations in the A layout directly."""
+    M, N, K, bits, gs, sb = case
+    d = mxq.mxq_describe("qmv", M, N, K, bits, gs, sb)
+    assert d.startswith("qsmk_kernel") and ",xstage>" in d, d
+    assert ",xstage" not in mxq.mxq_describe("qmv", 8, N, K, bits, gs, sb)
+    assert ",xstage" not in mxq.mxq_describe("a8", M, N, K, bits, gs, sb)
+    p = synth.make_problem(M, N, K, bits, gs, sb, seed=M + K + 91)
+    x, w, s, b = to_dev(p)
+    note(f"few-row staged activations {case}")
+    y = y_host(mxq.mxq_qmv(x, w, s, b, bits=bits, group_size=gs))
+    cols = _sampled_cols(N, 500 + M)
+    ref = oracle.matmul_ref(p.x, p.w[cols], p.scales[cols], p.biases[cols], K, bits, gs, sb)
+    assert_close(y[:, cols], ref, f"staged activations {case}")
+
+
 @pytest.mark.parametrize("M", list(range(2, 17)))
 def test_few_rows_mfma_every_m(M):
     """Every row count the K-split few-row kernel takes, through mxq_linear
