@@ -212,6 +212,31 @@ def test_qmm_scale_regimes(shape, sb, regime):
     assert_close(y, _ref(p), f"qmm scale regime {shape} {sb} {regime}")
 
 
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("sb", ["f16", "bf16"])
+def test_qmm_subnormal_activations(bits, sb):
+    """Every activation an f16 subnormal (random mantissa and sign) against
+    scales of 1000-4000, so that y is O(10): on the MFMA path the 4-bit codes
+    with f16 scales are themselves staged as f16 subnormals, and every product
+    here has two subnormal operands.  The result must meet the same bound as
+    any other input."""
+    M, N, K, gs = 96, 384, 1024, 64
+    p = synth.make_problem(M, N, K, bits, gs, sb, seed=4242 + bits)
+    rng = np.random.default_rng(4243 + bits)
+    mant = rng.integers(1, 1024, (M, K)).astype(np.uint16)
+    sign = (rng.random((M, K)) < 0.5).astype(np.uint16) << 15
+    p.x = (mant | sign).view(np.float16)
+    G = K // gs
+    p.scales = synth._round_sb(rng.uniform(1000, 4000, (N, G)) * np.where(rng.random((N, G)) < 0.5, -1.0, 1.0), sb)
+    p.biases = synth._round_sb(rng.uniform(-2e4, 2e4, (N, G)), sb)
+    assert mxq.mxq_describe("qmm", M, N, K, bits, gs, sb).startswith("qmm_kernel")
+    note(f"qmm subnormal activations bits={bits} sb={sb}")
+    y = _run("qmm", p)
+    ref = _ref(p)
+    assert np.abs(ref).max() > 1.0  # the sums are not lost below f16's range
+    assert_close(y, ref, f"qmm subnormal activations bits={bits} sb={sb}")
+
+
 @pytest.mark.parametrize("proj", ["gate", "down"])
 @pytest.mark.parametrize("sb", ["f16", "bf16"])
 def test_prefill_full_size_sampled(proj, sb):
