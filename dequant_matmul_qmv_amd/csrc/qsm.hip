@@ -366,9 +366,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
                                              : static_cast<int>(blockIdx.x);
   Ld cur, alt;
   // The first block's loads go out before the activation work below: the
-  // weight stream starts while the activations are loaded, summed (and, for
-  // int8 activations, quantized across the waves).
-  load(cur, first_rb);
+  // weight stream starts while the activations are loaded and summed.  With
+  // int8 activations they go out right after the activations' loads instead:
+  // the wait for the activations (loads complete in order) then does not also
+  // wait for the weights, and the quantization runs while they are in flight.
+  if constexpr (!XI) load(cur, first_rb);
 
   // ---- activations of this slice, in the A layout, and the group sums of
   // the D rows this lane holds
@@ -383,14 +385,17 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     const uint16_t* xp = x + static_cast<size_t>(min(c16, M - 1)) * K + ks0 + 16 * kg;
     const u4 z = {0u, 0u, 0u, 0u};
     u4 v[kKsGroups][2];
-    float am = 0.0f;
 #pragma unroll
     for (int g = 0; g < kKsGroups; ++g) {
       const bool live = c16 < M && (!RG || g < gvalid);
       v[g][0] = live ? *reinterpret_cast<const u4*>(xp + 64 * g) : z;
       v[g][1] = live ? *reinterpret_cast<const u4*>(xp + 64 * g + 8) : z;
-      am = fmaxf(am, fmaxf(absmax8_f16(v[g][0]), absmax8_f16(v[g][1])));
     }
+    load(cur, first_rb);
+    __builtin_amdgcn_sched_barrier(0);  // the weight loads stay behind the activations' and ahead of their use
+    float am = 0.0f;
+#pragma unroll
+    for (int g = 0; g < kKsGroups; ++g) am = fmaxf(am, fmaxf(absmax8_f16(v[g][0]), absmax8_f16(v[g][1])));
     {
       // the maximum over the row's four lane groups (lanes l, l ^ 16, l ^ 32):
       // gfx950's lane swaps, no LDS crossbar
