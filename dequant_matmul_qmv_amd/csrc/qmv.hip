@@ -710,8 +710,9 @@ const void* qmv_kernel_ptr(int bits, bool bf16, int act, int mt, int R, bool xd)
 //    and 2 workgroups of 4 waves per CU, each wave holding two items in flight;
 //  * mid (N >= 16 rows per CU): R = 2, 2 workgroups per CU (fewer, longer
 //    waves beat one row per wave by ~15 %; R = 4 measured the same);
-//  * small: one row per wave step and as many waves as the rows allow; such
-//    launches are dominated by their fixed cost (~4 us on this part).
+//  * small: one row per wave step; as many waves as the rows allow when x is
+//    staged in LDS, one workgroup per CU when x sits in registers (below);
+//    such launches are dominated by their fixed cost (~3-4 us on this part).
 enum class SizeClass { kSmall, kMid, kLarge };
 
 SizeClass qmv_class(const DeviceInfo& dev, int64_t N) {
@@ -729,11 +730,16 @@ int qmv_pick_rows(const DeviceInfo& dev, int64_t N, int64_t K, int bits, int mt)
   return rows;
 }
 
-int qmv_blocks_per_cu_cap(const DeviceInfo& dev, int64_t N, int occ) {
+// Small launches with the activations in registers take one workgroup per CU
+// per problem, so that a wave holds two or more items and the item pipeline
+// has something to overlap (q+k+v: 3.92 -> 3.65 us); with x staged in LDS once
+// per workgroup (long K) more workgroups stay faster (down: 5.11 against 5.72
+// us at one per CU).
+int qmv_blocks_per_cu_cap(const DeviceInfo& dev, int64_t N, int occ, bool xd) {
   switch (qmv_class(dev, N)) {
     case SizeClass::kLarge:
     case SizeClass::kMid: return occ < 2 ? occ : 2;
-    default: return occ;
+    default: return xd ? (occ < 1 ? occ : 1) : occ;
   }
 }
 
@@ -791,7 +797,7 @@ QmvPlan qmv_plan_group(const DeviceInfo& dev, const int64_t* Ns, const int64_t* 
   for (int i = 0; i < count; ++i) {
     const int64_t nrb = (Ns[i] + p.rows - 1) / p.rows;
     const int64_t blocks_needed = (nrb + 3) / 4;
-    const int per_cu = qmv_blocks_per_cu_cap(dev, Ns[i], occ);
+    const int per_cu = qmv_blocks_per_cu_cap(dev, Ns[i], occ, p.xdirect);
     const int64_t cap = static_cast<int64_t>(dev.num_cu) * per_cu;
     const int g = static_cast<int>(blocks_needed < cap ? blocks_needed : cap);
     if (grids) grids[i] = g;
