@@ -599,9 +599,9 @@ __global__ __launch_bounds__(kQmvBlock) void qmv_kernel(const QmvBatch batch) {
   // dummies of load_item, which keeps the compiler's load counters exact.  The
   // loop has a single exit: with two exits the compiler's wait analysis merges
   // them into the loop header and makes every iteration wait for the prefetch.
-  // Items in flight per wave: two at four rows per item (the large class;
-  // lm_head streams fastest with about 8-16 MiB in flight over the GPU, and a
-  // third item there measured 2 % slower), three otherwise (the mid and small
+  // Items in flight per wave: two at four rows per item (the large class,
+  // which runs as many workgroups as fit instead; a third item there measured
+  // 2-3 % slower), three otherwise (the mid and small
   // classes: each wave has only a few items, and the third hides more of each
   // item's compute behind the loads -- gate+up 6.4 -> 6.0 us, down 5.5 -> 5.2 us)
   constexpr int NBUF = R == 4 ? 2 : 3;
@@ -704,10 +704,11 @@ const void* qmv_kernel_ptr(int bits, bool bf16, int act, int mt, int R, bool xd)
 
 // Rows of W per wave step and the grid, by size class of N (measured on
 // MI355X with a read probe and traced launch-shape sweeps):
-//  * large (N >= 64 rows per CU, e.g. a vocabulary projection): streaming
-//    peaks with about 8-16 MiB of loads in flight in total -- R = 4 rows of one
-//    16-byte segment per lane (R = 2 when a row spans several segment steps)
-//    and 2 workgroups of 4 waves per CU, each wave holding two items in flight;
+//  * large (N >= 64 rows per CU, e.g. a vocabulary projection): R = 4 rows
+//    of one 16-byte segment per lane (R = 2 when a row spans several segment
+//    steps), as many workgroups of 4 waves per CU as fit (5 at 94 VGPRs), each
+//    wave holding two items in flight (a third measured slower at every
+//    workgroup count);
 //  * mid (N >= 16 rows per CU): R = 2, 2 workgroups per CU (fewer, longer
 //    waves beat one row per wave by ~15 %; R = 4 measured the same);
 //  * small: one row per wave step; as many waves as the rows allow when x is
@@ -737,7 +738,7 @@ int qmv_pick_rows(const DeviceInfo& dev, int64_t N, int64_t K, int bits, int mt)
 // us at one per CU).
 int qmv_blocks_per_cu_cap(const DeviceInfo& dev, int64_t N, int occ, bool xd) {
   switch (qmv_class(dev, N)) {
-    case SizeClass::kLarge:
+    case SizeClass::kLarge: return occ;  // as many as fit: lm_head 24.9 / 24.3 / 24.2 / 23.9 us at 2 / 3 / 4 / 5
     case SizeClass::kMid: return occ < 2 ? occ : 2;
     default: return xd ? (occ < 1 ? occ : 1) : occ;
   }
