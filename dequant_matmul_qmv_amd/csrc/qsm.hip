@@ -270,7 +270,7 @@ bool qsmk_xstage(int64_t M, bool int8_act) { return !int8_act && M >= 9; }
 // activations), and scales and biases are loaded as 2-byte values with the
 // group index clamped and the values zeroed past the last group.
 template <int BITS, bool SB_BF16, int GSH, int NW, bool XI, bool RG, bool XS>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void qsmk_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ W,
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu((XI && BITS == 4) ? 3 : 2))) void qsmk_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ W,
                                                    const uint16_t* __restrict__ S, const uint16_t* __restrict__ B,
                                                    uint16_t* __restrict__ y, const uint16_t* __restrict__ ob,
                                                    float* __restrict__ part, int M, int N, int K) {
@@ -715,8 +715,12 @@ hipError_t launch_qsmk(const QmvArgs& a, int M, const DeviceInfo& dev) {
     const hipError_t e = ensure_dynamic_lds(kern, lds);
     if (e != hipSuccess) return e;
   }
+  // two workgroups per CU; three with int8 activations and 4-bit codes, whose
+  // variants fit three waves per SIMD without spilling (lm_head, 4-8 rows: 1 us
+  // faster; the f16 and 8-bit variants would spill at that register budget)
   const int occ = occupancy_blocks(kern, 64 * nw, lds);
-  const int per_cu = occ < 2 ? occ : 2;
+  const int want = (xi && a.bits == 4) ? 3 : 2;
+  const int per_cu = occ < want ? occ : want;
   const int64_t nrb = (a.N + 15) / 16;
   const int64_t cap = (static_cast<int64_t>(dev.num_cu) * per_cu + chunks - 1) / chunks;  // workgroups per chunk
   const unsigned gx = static_cast<unsigned>(nrb < cap ? nrb : cap);
