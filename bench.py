@@ -1094,9 +1094,9 @@ def main():
             if st_ != 0:
                 raise RuntimeError(f"{label} lm_head M={M}: libmxq status {st_}")
 
-        # a 200 ms warm-up, then three rounds over all cases (so that a slow
+        # a 200 ms warm-up, then five rounds over all cases (so that a slow
         # spell of the part does not land on one case), 20 launches back to
-        # back per case and round; the median of the three rounds
+        # back per case and round; the median of the five rounds
         few_ms = {}
 
         def few_rec(case):
@@ -1116,7 +1116,7 @@ def main():
             torch.cuda.synchronize()
             if e0.elapsed_time(e1) >= 200.0:
                 break
-        for rnd in range(3):
+        for rnd in range(5):
             for key, f in launches:
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 a.record()
@@ -1128,7 +1128,7 @@ def main():
         for M in (1, 2, 4, 8, 16):
             row = {}
             for label in ("f16", "int8"):
-                ms = sorted(few_ms[(M, label)])[1]
+                ms = sorted(few_ms[(M, label)])[2]  # median of five rounds
                 row[label] = {"us": round(ms * 1e3, 2),
                               "GB/s": round(call_bytes(M, 128256, 2048) / (ms / 1e3) / 1e9, 1),
                               "rounds_us": [round(v * 1e3, 2) for v in few_ms[(M, label)]]}
