@@ -601,9 +601,9 @@ __global__ __launch_bounds__(kQmvBlock) void qmv_kernel(const QmvBatch batch) {
   // them into the loop header and makes every iteration wait for the prefetch.
   // Items in flight per wave: two at four rows per item (the large class,
   // which runs as many workgroups as fit instead; a third item there measured
-  // 2-3 % slower), three otherwise (the mid and small
-  // classes: each wave has only a few items, and the third hides more of each
-  // item's compute behind the loads -- gate+up 6.4 -> 6.0 us, down 5.5 -> 5.2 us)
+  // 2-3 % slower), three otherwise (the mid and small classes: each wave has
+  // only a few items, and the third hides more of each item's compute behind
+  // the loads -- gate+up 6.4 -> 6.0 us, down 5.5 -> 5.2 us).
   constexpr int NBUF = R == 4 ? 2 : 3;
   auto advance = [&](int& rbv, int& jv) {
     if (++jv == jn) {

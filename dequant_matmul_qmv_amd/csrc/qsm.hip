@@ -269,11 +269,15 @@ bool qsmk_xstage(int64_t M, bool int8_act) { return !int8_act && M >= 9; }
 // are loaded from the row's start instead (in bounds; their codes meet zero
 // activations), and scales and biases are loaded as 2-byte values with the
 // group index clamped and the values zeroed past the last group.
+// XS (f16 activations, 9..16 rows): the activation slice passes through LDS in
+// whole row pieces before the first block (see the prologue).
+// Register budget: two waves per SIMD; three for int8 activations with 4-bit
+// codes, whose variants fit it without spilling.
 template <int BITS, bool SB_BF16, int GSH, int NW, bool XI, bool RG, bool XS>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu((XI && BITS == 4) ? 3 : 2))) void qsmk_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ W,
-                                                   const uint16_t* __restrict__ S, const uint16_t* __restrict__ B,
-                                                   uint16_t* __restrict__ y, const uint16_t* __restrict__ ob,
-                                                   float* __restrict__ part, int M, int N, int K) {
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu((XI && BITS == 4) ? 3 : 2))) void qsmk_kernel(
+    const uint16_t* __restrict__ x, const uint32_t* __restrict__ W, const uint16_t* __restrict__ S,
+    const uint16_t* __restrict__ B, uint16_t* __restrict__ y, const uint16_t* __restrict__ ob, float* __restrict__ part,
+    int M, int N, int K) {
   constexpr int nw = NW;
   constexpr int kKsRow = ks_row_bytes(BITS);
   constexpr int NLD = BITS;  // 16-byte loads per lane and block: 4 (4-bit) or 8 (8-bit)
@@ -432,8 +436,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu((XI && 
     }
     sxl = sx;
   } else if constexpr (XS) {
-    // XS (9..16 rows): the slice's activations (16 rows x 512, rows >= M as zeros) pass
-    // through LDS in two halves of four groups: each load instruction reads
+    // XS (9..16 rows): the slice's activations (16 rows x 512, rows >= M as
+    // zeros) pass through LDS in two halves of four groups: each load reads
     // two rows' whole 512-byte pieces, and the A-layout fragments are read
     // back (a row stride of kXsRow halves puts the 16 rows one read touches on
     // distinct banks).  Loaded in the A layout directly, every instruction
