@@ -238,7 +238,7 @@ __global__ __launch_bounds__(kQmvBlock) void qmv_kernel(const QmvBatch batch) {
   // The first item's loads go out before the x staging, to overlap the two.
   int rb = blk * waves_per_block + wave;
   int j = 0;
-  QmvItem<R> cur, alt, third;  // third: with three items in flight
+  QmvItem<R> cur;
   load_item(cur, min(rb, nrb - 1), 0, false);
 
   // ---- activations -------------------------------------------------------
@@ -592,18 +592,19 @@ __global__ __launch_bounds__(kQmvBlock) void qmv_kernel(const QmvBatch batch) {
       for (int m = 0; m < MT; ++m) acc[r][m] = 0.0f;
   };
 
-  // Ping-pong over two (three) item buffers: the next item's (two items')
-  // loads are in flight while the current item is computed, and no register
-  // copy of in-flight data is ever made (a copy would force a wait for those
-  // loads).  Loads are never conditional: loads past a wave's last item are
-  // dummies of load_item, which keeps the compiler's load counters exact.  The
-  // loop has a single exit: with two exits the compiler's wait analysis merges
-  // them into the loop header and makes every iteration wait for the prefetch.
+  // A ring of item buffers: while an item is computed, the loads of the next
+  // NBUF - 1 items are in flight, and no register copy of in-flight data is
+  // ever made (a copy would force a wait for those loads).  Loads are never
+  // conditional: loads past a wave's last item are dummies of load_item, which
+  // keeps the compiler's load counters exact.  The loop has a single exit:
+  // with two exits the compiler's wait analysis merges them into the loop
+  // header and makes every iteration wait for the prefetch.
   // Items in flight per wave: two at four rows per item (the large class,
   // which runs as many workgroups as fit instead; a third item there measured
   // 2-3 % slower), three otherwise (the mid and small classes: each wave has
   // only a few items, and the third hides more of each item's compute behind
-  // the loads -- gate+up 6.4 -> 6.0 us, down 5.5 -> 5.2 us).
+  // the loads -- gate+up 6.4 -> 6.0 us, down 5.5 -> 5.2 us; a fourth measured
+  // slower, gate+up 6.5 us).
   constexpr int NBUF = R == 4 ? 2 : 3;
   auto advance = [&](int& rbv, int& jv) {
     if (++jv == jn) {
@@ -612,52 +613,38 @@ __global__ __launch_bounds__(kQmvBlock) void qmv_kernel(const QmvBatch batch) {
     }
   };
   const int n_items = ((nrb - 1 - rb) / stride + 1) * jn;  // this wave's items, >= 1
-  if constexpr (NBUF == 2) {
-    int rb2 = rb, j2 = j;
-    int i = 0;  // index of the item held in cur
-    for (; i + 1 < n_items; i += 2) {
-      advance(rb2, j2);  // item i + 1 exists
-      load_item(alt, rb2, j2, false);
-      __builtin_amdgcn_sched_barrier(0);  // keep the whole load block ahead of the compute
-      step(cur, rb, j, j2 == 0);
-      rb = rb2;
-      j = j2;
-      advance(rb2, j2);  // item i + 2, a dummy past the end
-      load_item(cur, rb2, j2, i + 2 >= n_items);
-      __builtin_amdgcn_sched_barrier(0);
-      step(alt, rb, j, j2 == 0);
-      rb = rb2;
-      j = j2;
-    }
-    if (i < n_items) step(cur, rb, j, true);  // odd count: the last item, which ends its row block
-  } else {
-    int rbA = rb, jA = j;  // item i, in cur
-    int rbB = rbA, jB = jA;
-    advance(rbB, jB);  // item i + 1, in alt (a dummy past the end)
-    load_item(alt, rbB, jB, 1 >= n_items);
-    int i = 0;
-    for (; i + 2 < n_items; i += 3) {
-      int rbC = rbB, jC = jB;
-      advance(rbC, jC);  // item i + 2 exists
-      load_item(third, rbC, jC, false);
-      __builtin_amdgcn_sched_barrier(0);  // keep the whole load block ahead of the compute
-      step(cur, rbA, jA, jB == 0);
-      rbA = rbC;
-      jA = jC;
-      advance(rbA, jA);  // item i + 3
-      load_item(cur, rbA, jA, i + 3 >= n_items);
-      __builtin_amdgcn_sched_barrier(0);
-      step(alt, rbB, jB, jC == 0);
-      rbB = rbA;
-      jB = jA;
-      advance(rbB, jB);  // item i + 4
-      load_item(alt, rbB, jB, i + 4 >= n_items);
-      __builtin_amdgcn_sched_barrier(0);
-      step(third, rbC, jC, jA == 0);
-    }
-    if (i < n_items) step(cur, rbA, jA, jB == 0);
-    if (i + 1 < n_items) step(alt, rbB, jB, true);  // the last item ends its row block
+  // A ring of NBUF item buffers: buffer k holds item i + k at the top of a
+  // trip; each step first issues the loads of item i + k + NBUF - 1 into the
+  // buffer the previous trip's last step freed, then computes item i + k.
+  QmvItem<R> buf[NBUF];
+  int prb[NBUF], pj[NBUF];  // (row block, segment step) of the item in each buffer
+  buf[0] = cur;
+  prb[0] = rb;
+  pj[0] = j;
+#pragma unroll
+  for (int k = 1; k < NBUF - 1; ++k) {
+    prb[k] = prb[k - 1];
+    pj[k] = pj[k - 1];
+    advance(prb[k], pj[k]);
+    load_item(buf[k], prb[k], pj[k], k >= n_items);  // a dummy past the end
   }
+  int i = 0;  // the item in buf[0]
+  for (; i + NBUF - 1 < n_items; i += NBUF) {
+#pragma unroll
+    for (int k = 0; k < NBUF; ++k) {
+      const int kl = (k + NBUF - 1) % NBUF, kp = (k + NBUF - 2) % NBUF;
+      prb[kl] = prb[kp];
+      pj[kl] = pj[kp];
+      advance(prb[kl], pj[kl]);  // item i + k + NBUF - 1
+      load_item(buf[kl], prb[kl], pj[kl], i + k + NBUF - 1 >= n_items);
+      __builtin_amdgcn_sched_barrier(0);  // keep the whole load block ahead of the compute
+      step(buf[k], prb[k], pj[k], pj[(k + 1) % NBUF] == 0);
+    }
+  }
+  // fewer than NBUF items left, in buf[0 .. NBUF - 2]; the last ends its row block
+#pragma unroll
+  for (int k = 0; k < NBUF - 1; ++k)
+    if (i + k < n_items) step(buf[k], prb[k], pj[k], i + k + 1 >= n_items || pj[(k + 1) % NBUF] == 0);
 }
 
 // ---------------------------------------------------------------------------
