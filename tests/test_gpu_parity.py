@@ -113,6 +113,30 @@ def test_small_qmv_problem():
     assert_close(_run("qmv", p), _ref(p), "qmv small problem")
 
 
+@pytest.mark.parametrize("case", [(1, 1000, 2048), (1, 2047, 2048), (1, 3000, 2048), (1, 4095, 2048),
+                                  (1, 3000, 4096), (1, 4095, 4096), (1, 2048, 8192), (1, 3333, 8192),
+                                  (1, 8192, 2048), (1, 12000, 2048), (1, 16383, 2048), (1, 6000, 8192),
+                                  (2, 3000, 2048), (2, 12000, 4096), (1, 50000, 2048), (1, 40000, 4096)],
+                         ids=str)
+def test_decode_item_ring_tails(case):
+    """The decode kernel's ring of item buffers (two items in flight at four
+    rows per item, three below) ends with 0, 1 or 2 items left over whatever
+    each wave's item count is.  N and K are chosen so that the waves of the
+    small class (one row per item, x in registers, or in LDS with 2 or 4
+    segment steps per row at K 4096 / 8192), of the mid class (two rows per
+    item) and of the large class (four rows per item at K 2048, two at 4096)
+    hold 1 to 8 items, every residue of both ring sizes; sampled outputs
+    against the oracle."""
+    M, N, K = case
+    assert mxq.mxq_describe("qmv", M, N, K, 4, 64, "f16").startswith("qmv_kernel"), case
+    p = synth.make_problem(M, N, K, 4, 64, "f16", seed=N + K + 31 * M)
+    note(f"decode item ring {case}")
+    y = _run("qmv", p)
+    rows = _sampled_cols(N, N + K)
+    ref = oracle.matmul_ref_rows(p.x, p.w, p.scales, p.biases, rows, K, 4, 64, "f16")
+    assert_close(y[:, rows], ref, f"decode item ring {case}")
+
+
 @pytest.mark.parametrize("entry", ["qmv", "qmm"])
 @pytest.mark.parametrize("case", list(synth.edge_cases()), ids=lambda c: f"M{c['M']}N{c['N']}b{c['bits']}{c['sb_dtype']}")
 def test_edge_cases_8bit_and_tails(entry, case):
