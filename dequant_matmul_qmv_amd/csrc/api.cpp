@@ -132,9 +132,10 @@ mxq_status run_qmv(const char* who, const void* x, const uint32_t* w, const void
   // 16-byte loads.
   // int8 activations take the K-split kernel's integer-MFMA variant from 3
   // rows, unchunked (K <= 4096: one row scale covers all of K); the decode
-  // kernel's v_dot4 path is VALU-bound beyond a row or two, and at two rows it
-  // is still faster than the kernel's per-row quantization of x in every
-  // workgroup (measured on lm_head: 28.3 against 31.2 us).  If the K-chunk
+  // kernel's v_dot4 path is VALU-bound beyond a row or two.  At two rows the
+  // two kernels trade places with N (K = 2048: N = 8192 7.6 against 8.8 us on
+  // the K-split kernel, which quantizes x in every workgroup; lm_head 26.4
+  // against 26.1 us), so two rows stay on the decode kernel.  If the K-chunk
   // workspace cannot be had, the call falls through to the kernels below.
   const bool few_i8 = act == kActI8 && M >= 3;
   if ((act == kActF16 ? qsmk_rows(M, K) : few_i8) && aligned(x, 16) &&
